@@ -1,0 +1,395 @@
+"""Pins of the CPU oracle to facts outside itself (no GPU needed).
+
+Each test checks the oracle against something it does not share code with:
+the closed form of the OCP E4M3FN format, torch's own e4m3 cast (a library
+routine), hand-derived UE8M0 exponents, exact integer matmuls, a numpy matmul
+of the dequantized matrices, scipy's logistic function, and the accuracy figure
+printed on the DeepGEMM benchmark post (section 3.3 / 4.4).
+"""
+import math
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import workloads as W
+
+
+# ---------------------------------------------------------------- e4m3 format
+
+def test_e4m3_decode_closed_form_points():
+    # OCP E4M3FN: bias 7, max normal 448 = 1.75 * 2^8, min normal 2^-6, min subnormal 2^-9
+    assert O.e4m3_decode(0x7E) == 448.0
+    assert O.e4m3_decode(0x08) == 2.0 ** -6
+    assert O.e4m3_decode(0x01) == 2.0 ** -9
+    assert O.e4m3_decode(0x07) == 7 * 2.0 ** -9
+    assert O.e4m3_decode(0x38) == 1.0
+    assert O.e4m3_decode(0x40) == 2.0
+    assert O.e4m3_decode(0x44) == 3.0
+    assert O.e4m3_decode(0xB8) == -1.0
+    assert math.isnan(O.e4m3_decode(0x7F)) and math.isnan(O.e4m3_decode(0xFF))
+    z = O.e4m3_decode(0x80)
+    assert z == 0.0 and math.copysign(1.0, z) == -1.0
+
+
+def test_e4m3_decode_table_matches_torch():
+    tab = O.e4m3_table()
+    ref = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    fin = ~np.isnan(ref)
+    assert np.array_equal(np.isnan(tab), np.isnan(ref))
+    assert np.array_equal(tab[fin], ref[fin])
+    pos = tab[:0x7F]
+    assert np.all(np.diff(pos) > 0), "codes 0x00..0x7E must be strictly increasing"
+    assert np.array_equal(tab[0x80:0xFF], -tab[:0x7F])
+
+
+def test_e4m3_encode_roundtrip_all_codes():
+    tab = O.e4m3_table()
+    for b in range(256):
+        if b in (0x7F, 0xFF):
+            continue
+        assert O.e4m3_encode(tab[b]) == b, hex(b)
+
+
+def test_e4m3_encode_matches_torch_cast():
+    """All bf16 bit patterns, scaled by several powers of two, and random fp32 values:
+    wherever torch's RNE cast is defined (|v| < 464) the oracle agrees bit for bit."""
+    bits = np.arange(65536, dtype=np.uint32) << 16
+    base = bits.view(np.float32)
+    with np.errstate(over="ignore", invalid="ignore"):
+        vals = [base * np.float32(2.0 ** s) for s in (0, -3, 5, -20, 9)]
+    rng = np.random.default_rng(7)
+    vals.append((rng.standard_normal(200000) * 60).astype(np.float32))
+    vals.append((rng.random(200000) * 2.0 ** -6).astype(np.float32))
+    v = np.concatenate(vals)
+    v = v[np.isfinite(v) & (np.abs(v) < 464)]
+    want = torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = O.e4m3_encode_array(v.astype(np.float64))
+    bad = np.nonzero(got != want)[0]
+    assert bad.size == 0, [(float(v[i]), hex(got[i]), hex(want[i])) for i in bad[:5]]
+
+
+def test_e4m3_encode_saturates_and_keeps_sign_of_zero():
+    assert O.e4m3_encode(448.0) == 0x7E
+    assert O.e4m3_encode(470.0) == 0x7E
+    assert O.e4m3_encode(1e30) == 0x7E
+    assert O.e4m3_encode(-1e30) == 0xFE
+    assert O.e4m3_encode(-0.0) == 0x80
+    assert O.e4m3_encode(-1e-9) == 0x80
+    assert O.e4m3_encode(1e-9) == 0x00
+    # ties go to the even mantissa: 1.0625 lies halfway between 1.0 (0x38) and 1.125 (0x39)
+    assert O.e4m3_encode(1.0625) == 0x38
+    assert O.e4m3_encode(1.1875) == 0x3A  # halfway between 1.125 (0x39) and 1.25 (0x3A)
+    # smallest subnormal tie: 2^-10 is halfway between 0 and 2^-9 -> 0
+    assert O.e4m3_encode(2.0 ** -10) == 0x00
+    assert O.e4m3_encode(3 * 2.0 ** -10) == 0x02
+
+
+def test_e4m3_encode_error_bound():
+    rng = np.random.default_rng(11)
+    v = np.concatenate([rng.standard_normal(20000) * s for s in (1e-3, 0.1, 10, 100)])
+    v = v[np.abs(v) < 448]
+    tab = O.e4m3_table()
+    q = O.e4m3_encode_array(v)
+    err = np.abs(tab[q] - v)
+    # half an ulp: ulp = 2^(floor(log2|v|) - 3) in the normal range, 2^-9 below 2^-6
+    a = np.abs(v)
+    ulp = np.where(a < 2.0 ** -6, 2.0 ** -9, 2.0 ** (np.floor(np.log2(np.maximum(a, 2.0 ** -6))) - 3))
+    assert np.all(err <= ulp / 2)
+
+
+# ---------------------------------------------------------------- UE8M0 scale
+
+@pytest.mark.parametrize("amax,byte", [(448.0, 127), (449.0, 128), (224.0, 126), (224.5, 127),
+                                       (1.0, 119), (0.0, 85), (1e-30, 85), (896.0, 128),
+                                       (448.0 * 2 ** 20, 147), (3.3895313892515355e38, 247)])
+def test_ue8m0_hand_cases(amax, byte):
+    # the scale is amax/448 rounded UP to a power of two; the byte is e + 127; amax floored at 1e-10
+    assert O.ue8m0_exponent(amax) + 127 == byte
+
+
+def test_ue8m0_bracket_invariant():
+    rng = np.random.default_rng(3)
+    vals = np.concatenate([np.exp(rng.uniform(-30, 80, 5000)), 448.0 * 2.0 ** rng.integers(-40, 100, 500)])
+    for a in vals:
+        e = O.ue8m0_exponent(float(a))
+        fa = max(Fraction(float(a)), Fraction(1e-10))  # amax is floored at 1e-10
+        assert Fraction(448) * Fraction(2) ** e >= fa
+        assert Fraction(448) * Fraction(2) ** (e - 1) < fa
+
+
+# ---------------------------------------------------------------- quant + pack
+
+def test_quant_roundtrip_bound_and_group_max():
+    x = W.normal_bf16((6, 1024), seed=5)
+    xf = W.bf16_bits_to_f32(x).astype(np.float64)
+    q, sf = O.quant_group_pack(x)
+    tab = O.e4m3_table()
+    for r in range(6):
+        for g in range(8):
+            e = int((sf[g // 4, r] >> (8 * (g % 4))) & 0xFF) - 127
+            seg = xf[r, 128 * g:128 * g + 128]
+            deq = tab[q[r, 128 * g:128 * g + 128]] * 2.0 ** e
+            scaled = np.abs(seg) * 2.0 ** -e
+            ulp = np.where(scaled < 2.0 ** -6, 2.0 ** -9,
+                           2.0 ** (np.floor(np.log2(np.maximum(scaled, 2.0 ** -6))) - 3))
+            assert np.all(np.abs(deq - seg) <= ulp / 2 * 2.0 ** e)
+            m = np.max(np.abs(tab[q[r, 128 * g:128 * g + 128]]))
+            assert 224 <= m <= 448
+
+
+def test_pack_layout_closed_form():
+    """Row r, group g gets amax = 448 * 2^(r + 2g - 6) exactly, so its byte is 121 + r + 2g;
+    K = 640 gives 5 groups (word 1 only has byte 0), M = 5 with ld_sf = 8."""
+    M, K = 5, 640
+    x = np.zeros((M, K), np.float32)
+    rng = np.random.default_rng(1)
+    for r in range(M):
+        for g in range(5):
+            amax = 448.0 * 2.0 ** (r + 2 * g - 6)
+            seg = rng.uniform(-amax, amax, 128).astype(np.float32)
+            seg[int(rng.integers(128))] = -amax
+            x[r, 128 * g:128 * g + 128] = seg
+    xb = W.f32_to_bf16_bits(x)
+    q, sf = O.quant_group_pack(xb, ld_sf=8)
+    assert sf.shape == (2, 8)
+    for r in range(M):
+        b = [121 + r + 2 * g for g in range(5)]
+        assert sf[0, r] == b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24)
+        assert sf[1, r] == b[4]
+        # the element that equals -amax encodes to -448 (0xFE)
+        for g in range(5):
+            assert 0xFE in q[r, 128 * g:128 * g + 128]
+
+
+def test_zero_group_and_negative_zero():
+    x = np.zeros((1, 128), np.uint16)
+    x[0, 5] = 0x8000  # -0.0
+    q, sf = O.quant_group_pack(x)
+    assert sf[0, 0] == 85
+    assert q[0, 5] == 0x80 and np.count_nonzero(q) == 1
+
+
+# ---------------------------------------------------------------- weight block quant
+
+def test_block_quant_weight_blocks():
+    N, K = 200, 384  # partial last row block
+    w = W.normal_bf16((N, K), std=0.02, seed=9, tensor_id=W.T_B)
+    wf = W.bf16_bits_to_f32(w).astype(np.float64)
+    # plant one large value in block (1, 2) to make the block exponents differ
+    wf_big = wf.copy()
+    wf_big[150, 300] = 3.0
+    w2 = W.f32_to_bf16_bits(wf_big.astype(np.float32))
+    q, sfb = O.block_quant_128x128(w2)
+    assert sfb.shape == (2, 3)
+    tab = O.e4m3_table()
+    wf2 = W.bf16_bits_to_f32(w2).astype(np.float64)
+    for nb in range(2):
+        for kb in range(3):
+            blk = wf2[128 * nb:min(N, 128 * nb + 128), 128 * kb:128 * kb + 128]
+            s = float(sfb[nb, kb])
+            assert s == 2.0 ** round(math.log2(s))
+            amax = np.max(np.abs(blk))
+            assert 448 * s >= amax > 224 * s
+            deq = tab[q[128 * nb:min(N, 128 * nb + 128), 128 * kb:128 * kb + 128]] * s
+            assert np.max(np.abs(deq - blk)) <= s * 16  # half ulp at the top binade (32/2)
+    assert sfb[1, 2] == 2.0 ** -7  # 3.0 / 448 -> 2^-7.2 -> rounded up to 2^-7
+    assert sfb[0, 0] == 2.0 ** -12  # N(0, 0.02) blocks: amax ~ 0.09 -> 2^-12.2 -> 2^-12
+
+
+# ---------------------------------------------------------------- GEMM
+
+def _int_e4m3_codes(vals):
+    """e4m3 codes of small integers via the format's closed form (not the oracle encoder)."""
+    out = np.zeros(vals.shape, np.uint8)
+    for idx, v in np.ndenumerate(vals):
+        v = int(v)
+        if v == 0:
+            out[idx] = 0
+            continue
+        s = 0x80 if v < 0 else 0
+        a = abs(v)
+        E = a.bit_length() - 1           # a = 2^E * (1 + m/8)
+        m = (a - (1 << E)) * 8 // (1 << E)
+        assert (1 << E) + m * (1 << E) // 8 == a
+        out[idx] = s | ((E + 7) << 3) | m
+    return out
+
+
+def test_gemm_integer_identity():
+    rng = np.random.default_rng(2)
+    M, N, K = 7, 130, 384
+    # integers in [-16, 16] that are exact in e4m3 (all are)
+    ai = rng.integers(-16, 17, (M, K))
+    bi = rng.integers(-16, 17, (N, K))
+    qa, qb = _int_e4m3_codes(ai), _int_e4m3_codes(bi)
+    sfa = np.full((1, 8), 127 | (127 << 8) | (127 << 16), np.uint32)  # 3 groups, scale 1
+    sfb = np.ones((2, 3), np.float32)
+    c = O.gemm_nt(qa, sfa, qb, sfb)
+    assert np.array_equal(c, (ai @ bi.T).astype(np.float64))
+
+
+def test_gemm_equals_dequantized_matmul_with_varied_scales():
+    """Block-scaled GEMM == plain matmul of the dequantized operands (torch decodes e4m3)."""
+    rng = np.random.default_rng(4)
+    for (M, N, K) in [(1, 1, 128), (3, 129, 256), (129, 3, 640), (5, 300, 640)]:
+        G = K // 128
+        Wd = (G + 3) // 4
+        qa = rng.integers(0, 256, (M, K), dtype=np.uint8)
+        qb = rng.integers(0, 256, (N, K), dtype=np.uint8)
+        qa[(qa & 0x7F) == 0x7F] = 0x3C  # no NaN codes
+        qb[(qb & 0x7F) == 0x7F] = 0x41
+        ea = rng.integers(-20, 21, (M, G))
+        sfa = np.zeros((Wd, M + 3), np.uint32)
+        for m in range(M):
+            for g in range(G):
+                sfa[g // 4, m] |= np.uint32((ea[m, g] + 127) << (8 * (g % 4)))
+        eb = rng.integers(-20, 21, ((N + 127) // 128, G))
+        sfb = (2.0 ** eb).astype(np.float32)
+        c = O.gemm_nt(qa, sfa, qb, sfb)
+        dec = lambda q: torch.from_numpy(q).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+        A = dec(qa) * np.repeat(2.0 ** ea, 128, axis=1)
+        B = dec(qb) * np.repeat(np.repeat(2.0 ** eb, 128, axis=0)[:N], 128, axis=1)
+        ref = A @ B.T
+        bound = (np.abs(A) @ np.abs(B).T) * 2.0 ** -50
+        assert np.all(np.abs(c - ref) <= bound)
+        # and one entry exactly, with rational arithmetic
+        fa = [Fraction(float(v)) for v in A[M - 1]]
+        fb = [Fraction(float(v)) for v in B[N - 1]]
+        exact = sum(x * y for x, y in zip(fa, fb))
+        assert abs(Fraction(c[M - 1, N - 1]) - exact) <= abs(exact) * Fraction(1, 2 ** 52)
+
+
+def test_gemm_row_col_selection_matches_full():
+    rng = np.random.default_rng(8)
+    a = W.normal_bf16((9, 256), seed=1)
+    b = W.normal_bf16((140, 256), std=0.02, seed=1, tensor_id=W.T_B)
+    qa, sfa = O.quant_group_pack(a)
+    qb, sfb = O.block_quant_128x128(b)
+    full = O.gemm_nt(qa, sfa, qb, sfb)
+    rows = np.array([8, 0, 3])
+    cols = np.array([139, 0, 128, 127])
+    sub = O.gemm_nt(qa, sfa, qb, sfb, rows=rows, cols=cols)
+    assert np.array_equal(sub, full[np.ix_(rows, cols)])
+
+
+def test_calc_diff_closed_forms():
+    x = np.random.default_rng(0).standard_normal(1000)
+    assert O.calc_diff(x, x) == pytest.approx(0.0, abs=1e-15)
+    assert O.calc_diff(x, -x) == pytest.approx(2.0)
+    assert O.calc_diff(x, 2 * x) == pytest.approx(0.2)
+
+
+def _golden_calc_diff():
+    import os
+    p = os.path.join(os.path.dirname(__file__), "golden", "deepgemm_h100_summary.txt")
+    for line in open(p):
+        if line.startswith("deepgemm"):
+            return float(line.split()[4])
+    raise AssertionError("fixture missing")
+
+
+def test_whole_scheme_accuracy_matches_published_calc_diff():
+    """A, B ~ randn in bf16, B in 128x128 blocks and A in 1x128 groups with UE8M0 scales:
+    calc_diff of the quantized GEMM against the unquantized product is ~0.000684 on the post."""
+    want = _golden_calc_diff()
+    m, n, k = 128, 512, 7168
+    a = W.normal_bf16((m, k), seed=42, tensor_id=W.T_A)
+    b = W.normal_bf16((n, k), seed=42, tensor_id=W.T_B)
+    qa, sfa = O.quant_group_pack(a)
+    qb, sfb = O.block_quant_128x128(b)
+    c = O.gemm_nt(qa, sfa, qb, sfb)
+    ref = W.bf16_bits_to_f32(a).astype(np.float64) @ W.bf16_bits_to_f32(b).astype(np.float64).T
+    d = O.calc_diff(c, ref)
+    assert 0.9 * want <= d <= 1.1 * want, d
+
+
+# ---------------------------------------------------------------- masked grouped GEMM
+
+def _moe_inputs(E, M_max, N, K, seed=0):
+    x = W.normal_bf16((E * M_max, K), seed=seed)
+    qa, sfa_flat = O.quant_group_pack(x, ld_sf=E * M_max)
+    Wd = (K // 128 + 3) // 4
+    a = qa.reshape(E, M_max, K)
+    # [W][E*M_max] -> [E][W][M_max]
+    sfa = np.ascontiguousarray(sfa_flat.reshape(Wd, E, M_max).transpose(1, 0, 2))
+    bs, sfbs = [], []
+    for e in range(E):
+        w = W.normal_bf16((N, K), std=0.02, seed=seed + 100 + e, tensor_id=W.T_B)
+        qb, sfb = O.block_quant_128x128(w)
+        bs.append(qb)
+        sfbs.append(sfb)
+    return a, sfa, np.stack(bs), np.stack(sfbs)
+
+
+def test_masked_full_counts_equal_dense_per_expert():
+    E, M_max, N, K = 3, 8, 136, 256
+    a, sfa, b, sfb = _moe_inputs(E, M_max, N, K)
+    out = O.gemm_grouped_masked(a, sfa, b, sfb, np.full(E, M_max, np.int32))
+    for e in range(E):
+        assert np.array_equal(out[e], O.gemm_nt(a[e], sfa[e], b[e], sfb[e]))
+
+
+def test_masked_counts_clamped_and_rows_untouched():
+    E, M_max, N, K = 4, 8, 128, 128
+    a, sfa, b, sfb = _moe_inputs(E, M_max, N, K, seed=3)
+    mm = np.array([0, 3, 99, -5], np.int32)
+    out = O.gemm_grouped_masked(a, sfa, b, sfb, mm)
+    assert np.all(np.isnan(out[0])) and np.all(np.isnan(out[3]))
+    assert np.all(np.isnan(out[1, 3:])) and not np.any(np.isnan(out[1, :3]))
+    assert not np.any(np.isnan(out[2]))  # 99 clamps to M_max
+    assert np.array_equal(out[1, :3], O.gemm_nt(a[1], sfa[1], b[1], sfb[1])[:3])
+
+
+# ---------------------------------------------------------------- SiLU-mul-quant
+
+def test_silu_mul_matches_logistic_closed_form():
+    from scipy.special import expit
+    E, M_max, H = 2, 4, 256
+    x = W.normal_bf16((E, M_max, 2 * H), seed=6, tensor_id=W.T_X)
+    mm = np.array([3, 1], np.int32)
+    q, sf, y = O.silu_mul_quant_group_pack(x, mm, want_y=True)
+    xf = W.bf16_bits_to_f32(x).astype(np.float64)
+    g, u = xf[..., :H], xf[..., H:]
+    ref = g * expit(g) * u
+    for e in range(E):
+        c = mm[e]
+        assert np.allclose(y[e, :c], ref[e, :c], rtol=1e-14, atol=1e-300)
+        assert np.all(np.isnan(y[e, c:]))
+        assert np.all(q[e, c:] == 0) and np.all(sf[e, :, c:] == 0)
+
+
+def test_silu_mul_special_values():
+    H = 128
+    x = np.zeros((1, 4, 2 * H), np.float32)
+    x[0, 1, :H] = 30.0       # silu(30) = 30 (to double precision) -> y = 30 * u
+    x[0, 1, H:] = 0.5
+    x[0, 2, :H] = 1.0        # u = 0 -> y = 0 -> all-zero group
+    x[0, 3, 7] = -2.0
+    x[0, 3, H + 7] = 3.0     # single nonzero: silu(-2) * 3 = -0.7153...
+    xb = W.f32_to_bf16_bits(x)
+    q, sf = O.silu_mul_quant_group_pack(xb, np.array([4], np.int32))
+    assert sf[0, 0, 0] == 85 and np.all(q[0, 0] == 0)          # g = u = 0
+    assert sf[0, 0, 2] == 85 and np.all((q[0, 2] & 0x7F) == 0)
+    # y = 15 everywhere: e = ceil(log2(15/448)) = -4 -> 15 * 16 = 240 exactly (0x77)
+    assert sf[0, 0, 1] == 123 and np.all(q[0, 1] == 0x77)
+    yv = -2.0 / (1 + math.exp(2.0)) * 3.0
+    e = math.ceil(math.log2(abs(yv) / 448))
+    assert sf[0, 0, 3] == 127 + e
+    want = torch.tensor([yv * 2.0 ** -e], dtype=torch.float32).to(torch.float8_e4m3fn).view(torch.uint8)
+    assert q[0, 3, 7] == int(want[0]) == 0xFB  # -366.2 -> -352
+
+
+# ---------------------------------------------------------------- bf16 rounding
+
+def test_bf16_rne_matches_torch():
+    rng = np.random.default_rng(12)
+    v = np.concatenate([rng.standard_normal(3000).astype(np.float32) * 100,
+                        np.array([1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -(1.0 + 2 ** -8), 3.0e38, 1e-40],
+                                 np.float32)])
+    want = torch.from_numpy(v).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = O.bf16_rne_array(v.astype(np.float64))
+    assert np.array_equal(got, want)
+    assert np.array_equal(W.f32_to_bf16_bits(v), want)
