@@ -1,0 +1,404 @@
+#!/usr/bin/env python3
+"""Benchmark of the block-scaled FP8 hot path on one MI355X.
+
+Headline step (the workload the metric is quoted on): the dense decode GEMM
+M=64, N=7168, K=18432 -- per-token 1x128 quant + UE8M0 pack of A (bf16, N(0,1)
+with 1% x50 outliers) followed by the block-scaled NT GEMM against e4m3 weights
+with 128x128 UE8M0 block scales, bf16 out.  Weights are quantized once, outside
+the timed region (as the DeepGEMM benchmark post does, section 4.1).  Several
+weight copies are rotated so that every step streams its weights from HBM rather
+than from the 256 MB last-level cache.
+
+Prints one JSON line on stdout.  --sweep also times every workload (dense small
+case, decode, prefill sweep, masked MoE gate_up, fused SiLU-quant + masked down)
+and prints a table on stderr (and JSON lines to --sweep-out).
+
+Metric definitions follow the benchmark post (section 4.3): TFLOPS = 2*M*N*K/t,
+GB/s = (M*K + N*K + 2*M*N)/t (FP8 inputs 1 byte/element, bf16 output 2 bytes;
+scale bytes not counted).  For masked GEMMs only valid rows count: flops
+2*S*N*K and bytes S*K + E_active*N*K + 2*S*N.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
+FP8_PEAK_TFLOPS = 5000.0     # MI355X dense FP8 MFMA, published
+H100_DEEPGEMM_DECODE_TFLOPS = 243.6  # benchmark post, section 3.2, m=64 n=7168 k=18432 (context)
+
+
+# ----------------------------------------------------------------------------- metrics
+
+def gemm_flops(M, N, K):
+    return 2.0 * M * N * K
+
+
+def gemm_bytes(M, N, K):
+    return float(M * K + N * K + 2 * M * N)
+
+
+def masked_flops(S, N, K):
+    return 2.0 * S * N * K
+
+
+def masked_bytes(S, E_active, N, K):
+    return float(S * K + E_active * N * K + 2 * S * N)
+
+
+def quant_bytes(M, K):
+    W = (K // 128 + 3) // 4
+    return float(2 * M * K + M * K + 4 * W * M)
+
+
+def silu_bytes(S, H):
+    W = (H // 128 + 3) // 4
+    return float(4 * H * S + H * S + 4 * W * S)
+
+
+# ----------------------------------------------------------------------------- inputs (device)
+
+def _gen(seed):
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    return g
+
+
+def randn_bf16(shape, std=1.0, seed=0):
+    return (torch.randn(shape, generator=_gen(seed), device="cuda", dtype=torch.float32) * std).to(torch.bfloat16)
+
+
+def randn_bf16_outliers(shape, seed=0, frac=0.01, factor=50.0):
+    v = torch.randn(shape, generator=_gen(seed), device="cuda", dtype=torch.float32)
+    mask = torch.rand(shape, generator=_gen(seed + 7919), device="cuda") < frac
+    return torch.where(mask, v * factor, v).to(torch.bfloat16)
+
+
+def quantized_weights(F, n_copies, N, K, seed, experts=1):
+    """Weight copies quantized on the GPU with the 128x128 block quant kernel."""
+    out = []
+    for c in range(n_copies):
+        qs, ss = [], []
+        for e in range(experts):
+            w = randn_bf16((N, K), std=0.02, seed=seed + 1000 * c + e)
+            q, s = F.fp8_block_quant_128x128(w)
+            del w
+            qs.append(q)
+            ss.append(s)
+        if experts == 1:
+            out.append((qs[0], ss[0]))
+        else:
+            out.append((torch.stack(qs), torch.stack(ss)))
+        del qs, ss
+    torch.cuda.synchronize()
+    return out
+
+
+def n_copies_for(bytes_per_copy, cache_bytes=256 << 20, floor=1):
+    """Enough rotating copies that the working set exceeds the last-level cache twice."""
+    n = int(np.ceil(2 * cache_bytes / max(bytes_per_copy, 1)))
+    return max(floor, min(n, 16))
+
+
+# ----------------------------------------------------------------------------- timing
+
+def kernel_times(stream, launches, steps):
+    """Average GPU duration of each launch in a step, from HIP events recorded on the
+    launch stream around every launch.  A spin kernel first keeps the GPU busy while
+    the host enqueues, so the events bracket back-to-back kernels, not host gaps."""
+    n = len(launches)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(n + 1)] for _ in range(steps)]
+    with torch.cuda.stream(stream):
+        torch.cuda._sleep(int(2e7))
+        for s in range(steps):
+            ev[s][0].record(stream)
+            for j, fn in enumerate(launches):
+                fn(s)
+                ev[s][j + 1].record(stream)
+    stream.synchronize()
+    return [float(np.mean([ev[s][j].elapsed_time(ev[s][j + 1]) for s in range(steps)])) for j in range(n)]
+
+
+def graph_step_time(stream, step_fn, n_variants, steps, warmup):
+    """Capture one graph per input variant, replay `steps` of them round-robin, and
+    return wall ms per step with synchronizations on both sides of the timed loop."""
+    graphs = []
+    with torch.cuda.stream(stream):
+        for _ in range(2):
+            for v in range(n_variants):
+                step_fn(v)
+    stream.synchronize()
+    for v in range(n_variants):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            step_fn(v)
+        graphs.append(g)
+    with torch.cuda.stream(stream):
+        for i in range(warmup):
+            graphs[i % n_variants].replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    with torch.cuda.stream(stream):
+        for i in range(steps):
+            graphs[i % n_variants].replay()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    return (t1 - t0) * 1e3 / steps
+
+
+# ----------------------------------------------------------------------------- workloads
+
+def setup_dense(F, M, N, K, outliers, seed=0):
+    a = randn_bf16_outliers((M, K), seed=seed) if outliers else randn_bf16((M, K), seed=seed)
+    copies = quantized_weights(F, n_copies_for(N * K), N, K, seed + 1)
+    qa = torch.empty((M, K), dtype=torch.uint8, device="cuda")
+    sfa = torch.empty(((K // 128 + 3) // 4, max(4, (M + 3) // 4 * 4)), dtype=torch.int32, device="cuda")
+    c = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    return a, copies, qa, sfa, c
+
+
+def bench_dense(F, stream, shape, steps, warmup):
+    M, N, K = shape.M, shape.N, shape.K
+    a, copies, qa, sfa, c = setup_dense(F, M, N, K, shape.outliers)
+    nv = len(copies)
+
+    def quant(s):
+        F.fp8_quant_group_pack(a, q=qa, sf=sfa, stream=stream)
+
+    def gemm(s):
+        qb, sfb = copies[s % nv]
+        F.fp8_block_gemm_nt(qa, sfa, qb, sfb, c=c, stream=stream)
+
+    def step(v):
+        quant(v)
+        gemm(v)
+
+    with torch.cuda.stream(stream):
+        for i in range(warmup):
+            step(i)
+    t_quant, t_gemm = kernel_times(stream, [quant, gemm], steps)
+    ms = graph_step_time(stream, step, nv, steps, warmup)
+    r = {
+        "workload": shape.name, "M": M, "N": N, "K": K, "ms_per_step": ms,
+        "step_tflops": gemm_flops(M, N, K) / (ms * 1e-3) / 1e12,
+        "quant_us": t_quant * 1e3, "gemm_us": t_gemm * 1e3,
+        "gemm_tflops": gemm_flops(M, N, K) / (t_gemm * 1e-3) / 1e12,
+        "gemm_gbs": gemm_bytes(M, N, K) / (t_gemm * 1e-3) / 1e9,
+        "quant_gbs": quant_bytes(M, K) / (t_quant * 1e-3) / 1e9,
+        "config": F.gemm_config(False, M, N, K), "weight_copies": nv,
+    }
+    r["frac_hbm"] = r["gemm_gbs"] / HBM_PEAK_GBS
+    r["frac_mfma"] = r["gemm_tflops"] / FP8_PEAK_TFLOPS
+    del a, copies, qa, sfa, c
+    return r
+
+
+def bench_masked_gate_up(F, W, stream, steps, warmup):
+    E, M_max, N, K = W.MOE_E, W.MOE_M_MAX, W.MOE_GATE_UP["N"], W.MOE_GATE_UP["K"]
+    counts = torch.from_numpy(W.zipf_counts()).to("cuda")
+    S = int(counts.clamp(0, M_max).sum())
+    E_active = int((counts > 0).sum())
+    x = randn_bf16((E * M_max, K), seed=11)
+    qa, sfa_flat = F.fp8_quant_group_pack(x, ld_sf=E * M_max)
+    Wd = (K // 128 + 3) // 4
+    a = qa.view(E, M_max, K)
+    sfa = sfa_flat.view(Wd, E, M_max).permute(1, 0, 2).contiguous()
+    del x
+    copies = quantized_weights(F, n_copies_for(E * N * K, floor=1), N, K, 21, experts=E)
+    nv = len(copies)
+    c = torch.empty((E, M_max, N), dtype=torch.bfloat16, device="cuda")
+
+    def gemm(s):
+        qb, sfb = copies[s % nv]
+        F.fp8_block_gemm_grouped_masked(a, sfa, qb, sfb, counts, c=c, stream=stream)
+
+    with torch.cuda.stream(stream):
+        for i in range(warmup):
+            gemm(i)
+    (t,) = kernel_times(stream, [gemm], steps)
+    r = {"workload": "moe_gate_up_masked_E32_Mmax256_N4096_K7168", "S": S, "E_active": E_active,
+         "gemm_us": t * 1e3, "gemm_tflops": masked_flops(S, N, K) / (t * 1e-3) / 1e12,
+         "gemm_gbs": masked_bytes(S, E_active, N, K) / (t * 1e-3) / 1e9, "weight_copies": nv,
+         "config": F.gemm_config(True, M_max, N, K)}
+    r["frac_hbm"] = r["gemm_gbs"] / HBM_PEAK_GBS
+    r["frac_mfma"] = r["gemm_tflops"] / FP8_PEAK_TFLOPS
+    del copies, a, sfa, c
+    return r
+
+
+def bench_silu_down(F, W, stream, steps, warmup):
+    E, M_max, H, N = W.MOE_E, W.MOE_M_MAX, W.MOE_DOWN["H"], W.MOE_DOWN["N"]
+    K = H
+    counts = torch.from_numpy(W.zipf_counts()).to("cuda")
+    S = int(counts.clamp(0, M_max).sum())
+    E_active = int((counts > 0).sum())
+    x = randn_bf16((E, M_max, 2 * H), seed=31)
+    copies = quantized_weights(F, n_copies_for(E * N * K, floor=1), N, K, 41, experts=E)
+    nv = len(copies)
+    q = torch.empty((E, M_max, H), dtype=torch.uint8, device="cuda")
+    sf = torch.empty((E, (H // 128 + 3) // 4, M_max), dtype=torch.int32, device="cuda")
+    c = torch.empty((E, M_max, N), dtype=torch.bfloat16, device="cuda")
+
+    def silu(s):
+        F.silu_mul_quant_group_pack(x, counts, q=q, sf=sf, stream=stream)
+
+    def gemm(s):
+        qb, sfb = copies[s % nv]
+        F.fp8_block_gemm_grouped_masked(q, sf, qb, sfb, counts, c=c, stream=stream)
+
+    with torch.cuda.stream(stream):
+        for i in range(warmup):
+            silu(i)
+            gemm(i)
+    t_silu, t_gemm = kernel_times(stream, [silu, gemm], steps)
+    r = {"workload": "moe_silu_quant_then_down_masked_E32_Mmax256_H2048_N7168", "S": S,
+         "silu_us": t_silu * 1e3, "silu_gbs": silu_bytes(S, H) / (t_silu * 1e-3) / 1e9,
+         "gemm_us": t_gemm * 1e3, "gemm_tflops": masked_flops(S, N, K) / (t_gemm * 1e-3) / 1e12,
+         "gemm_gbs": masked_bytes(S, E_active, N, K) / (t_gemm * 1e-3) / 1e9, "weight_copies": nv}
+    r["frac_hbm"] = r["gemm_gbs"] / HBM_PEAK_GBS
+    r["frac_mfma"] = r["gemm_tflops"] / FP8_PEAK_TFLOPS
+    del copies, x, q, sf, c
+    return r
+
+
+# ----------------------------------------------------------------------------- CPU baseline
+
+def cpu_baseline(W, shape, budget_s):
+    """The oracle (as it stands) running the headline step -- quant/pack of A, then the
+    block-scaled GEMM in double -- on host copies of the same workload, for a bounded
+    sample: whole output rows, as many as fit the time budget."""
+    import oracle as O
+    M, N, K = shape.M, shape.N, shape.K
+    a, b = W.dense_inputs(shape)
+    qb, sfb = O.block_quant_128x128(b)  # offline weight step: not timed
+    del b
+    rows_done = 0
+    t_total = 0.0
+    rows_per_call = 8
+    while t_total < budget_s and rows_done < 4 * M:
+        sel = np.arange(rows_done, rows_done + rows_per_call) % M
+        t0 = time.perf_counter()
+        qa, sfa = O.quant_group_pack(np.ascontiguousarray(a[sel]))
+        O.gemm_nt(qa, sfa, qb, sfb)
+        t_total += time.perf_counter() - t0
+        rows_done += rows_per_call
+    flops = 2.0 * rows_done * N * K
+    return {"value": flops / t_total / 1e12, "unit": "TFLOPS", "cores": O.num_threads(), "kind": "oracle",
+            "sample": "%d output rows (x all %d columns, K=%d) of the %dx%dx%d step: quant/pack of those rows "
+                      "+ double-accumulated block GEMM; %.1f s" % (rows_done, N, K, M, N, K, t_total)}
+
+
+# ----------------------------------------------------------------------------- main
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--sweep", action="store_true", help="time every workload, table on stderr")
+    ap.add_argument("--sweep-out", default=None, help="file for per-workload JSON lines")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic_decode_gemm.json"),
+                    help="HBM traffic per GEMM launch measured with rocprofv3 counters")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        if int(os.environ.get("RANK", "0")) == 0:
+            print("bench.py measures one GPU: this library runs on a single MI355X (no sharding, no "
+                  "collectives); run it with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import block_scaled_fp8_token_amd as F
+    import workloads as W
+
+    torch.cuda.set_device(0)
+    stream = torch.cuda.Stream()
+    shape = W.DENSE_DECODE
+    r = bench_dense(F, stream, shape, args.steps, args.warmup)
+    print("[bench] %s" % json.dumps(r), file=sys.stderr, flush=True)
+
+    traffic = None
+    if args.traffic_json and os.path.exists(args.traffic_json):
+        try:
+            t = json.load(open(args.traffic_json))
+            if t.get("kernel_source_hash") == _kernel_hash():
+                traffic = t.get("bytes_per_launch")
+        except (OSError, ValueError):
+            traffic = None
+
+    gb = gemm_bytes(shape.M, shape.N, shape.K)
+    line = {
+        "metric": "TFLOPS and HBM GB/s per (M,N,K) shape; % of FP8 MFMA / HBM roofline",
+        "value": round(r["step_tflops"], 2),
+        "unit": "TFLOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": round(r["step_tflops"] / H100_DEEPGEMM_DECODE_TFLOPS, 3),
+        "dtype": "fp8_e4m3",
+        "data": "synthetic",
+        "config": {"workload": "dense_decode_gemm_M64_N7168_K18432", "M": shape.M, "N": shape.N,
+                   "K": shape.K, "step": "fp8_quant_group_pack(A) + fp8_block_gemm_nt",
+                   "weights": "e4m3 + 128x128 UE8M0 block scales, %d rotating copies (HBM-cold)" % r["weight_copies"],
+                   "tile": r["config"]},
+        "gemm_us": round(r["gemm_us"], 2),
+        "gemm_gbs": round(r["gemm_gbs"], 1),
+        "gemm_tflops": round(r["gemm_tflops"], 2),
+        "quant_us": round(r["quant_us"], 2),
+        "roofline": {"bound": "hbm", "kernel": "fp8_block_gemm_nt", "achieved": round(r["gemm_gbs"], 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(r["gemm_gbs"] / HBM_PEAK_GBS, 4),
+                     "algorithmic_bytes_per_launch": gb, "traffic": traffic},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(W, shape, args.cpu_seconds)
+
+    if args.sweep:
+        rows = [r]
+        rows.append(bench_dense(F, stream, W.DENSE_SMALL, args.steps, args.warmup))
+        for s in W.DENSE_PREFILL:
+            rows.append(bench_dense(F, stream, s, max(10, args.steps // 4), args.warmup))
+            print("[bench] %s" % json.dumps(rows[-1]), file=sys.stderr, flush=True)
+        rows.append(bench_masked_gate_up(F, W, stream, max(10, args.steps // 4), args.warmup))
+        print("[bench] %s" % json.dumps(rows[-1]), file=sys.stderr, flush=True)
+        rows.append(bench_silu_down(F, W, stream, max(10, args.steps // 4), args.warmup))
+        print("[bench] %s" % json.dumps(rows[-1]), file=sys.stderr, flush=True)
+        print("%-58s %10s %10s %10s %8s %8s" % ("workload", "gemm_us", "TFLOPS", "GB/s", "%MFMA", "%HBM"),
+              file=sys.stderr)
+        for x in rows:
+            print("%-58s %10.2f %10.1f %10.1f %8.1f %8.1f" % (x["workload"], x["gemm_us"], x["gemm_tflops"],
+                                                             x["gemm_gbs"], 100 * x["frac_mfma"],
+                                                             100 * x["frac_hbm"]), file=sys.stderr)
+        if args.sweep_out:
+            with open(args.sweep_out, "w") as f:
+                for x in rows:
+                    f.write(json.dumps(x) + "\n")
+    print(json.dumps(line), flush=True)
+
+
+def _kernel_hash():
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "block_scaled_fp8_token_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".hpp")):
+            h.update(open(os.path.join(csrc, name), "rb").read())
+    return h.hexdigest()[:16]
+
+
+if __name__ == "__main__":
+    main()

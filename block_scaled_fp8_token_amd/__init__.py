@@ -1,0 +1,273 @@
+"""Python binding of the MI355X block-scaled FP8 library (libfp8bs.so).
+
+A thin ctypes layer: it checks tensor dtypes, devices and layouts, allocates
+outputs with torch when the caller does not pass them, and forwards raw device
+pointers and the current HIP stream to the C ABI declared in include/fp8bs.h.
+Every step of the computation runs in the library's gfx950 kernels; there is no
+fallback path.  If libfp8bs.so is missing the import fails.
+
+Bit-pattern conventions: bf16 tensors are torch.bfloat16 (or int16/uint16
+views of them), e4m3 tensors are torch.uint8 (or torch.float8_e4m3fn), packed
+scale words are torch.int32 holding uint32 bits, weight block scales are
+torch.float32, and masked counts are torch.int32.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import torch
+
+__all__ = [
+    "Fp8bsError", "fp8_quant_group_pack", "silu_mul_quant_group_pack", "fp8_block_quant_128x128",
+    "fp8_block_gemm_nt", "fp8_block_gemm_grouped_masked", "gemm_config", "gemm_config_count",
+    "library_path", "header_path", "declared_functions",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libfp8bs.so")
+_HEADER = os.path.join(os.path.dirname(_HERE), "include", "fp8bs.h")
+
+if not os.path.exists(_LIB_PATH):
+    raise ImportError("libfp8bs.so is not built; run `python -m block_scaled_fp8_token_amd.build` "
+                      "(or __graft_entry__.build())")
+
+_lib = ctypes.CDLL(_LIB_PATH)
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_I32 = ctypes.c_int32
+_I32P = ctypes.POINTER(ctypes.c_int32)
+
+_SIGS = {
+    "fp8_quant_group_pack": [_P, _I64, _I64, _I64, _P, _I64, _P, _I64, _P],
+    "silu_mul_quant_group_pack": [_P, _P, _I64, _I64, _I64, _P, _P, _P],
+    "fp8_block_quant_128x128": [_P, _I64, _I64, _P, _P, _P],
+    "fp8_block_gemm_nt": [_P, _P, _I64, _P, _P, _P, _I64, _I64, _I64, _I64, _P],
+    "fp8_block_gemm_nt_cfg": [_P, _P, _I64, _P, _P, _P, _I64, _I64, _I64, _I64, _I32, _I32, _P],
+    "fp8_block_gemm_grouped_masked": [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _P],
+    "fp8_block_gemm_grouped_masked_cfg": [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I32, _P],
+    "fp8bs_gemm_config_count": [],
+    "fp8bs_gemm_config": [ctypes.c_int, _I64, _I64, _I64, _I32P, _I32P, _I32P, _I32P],
+    "fp8bs_status_string": [ctypes.c_int],
+    "fp8bs_last_hip_error": [],
+}
+for _name, _args in _SIGS.items():
+    _fn = getattr(_lib, _name)
+    _fn.argtypes = _args
+    _fn.restype = ctypes.c_char_p if _name == "fp8bs_status_string" else ctypes.c_int
+
+
+class Fp8bsError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        msg = _lib.fp8bs_status_string(status).decode()
+        if status == -5:
+            msg += " (hipError %d)" % _lib.fp8bs_last_hip_error()
+        super().__init__("%s: %s [status %d]" % (fn, msg, status))
+        self.status = status
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def header_path() -> str:
+    return _HEADER
+
+
+def declared_functions() -> list[str]:
+    """Names of the functions include/fp8bs.h declares."""
+    text = open(_HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        raise Fp8bsError(fn, status)
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _dev(t: torch.Tensor, name: str) -> None:
+    if not t.is_cuda:
+        raise ValueError("%s must be a device tensor" % name)
+
+
+_BF16 = (torch.bfloat16, torch.int16, torch.uint16)
+_E4M3 = (torch.uint8, torch.float8_e4m3fn, torch.int8)
+
+
+def _expect(t: torch.Tensor, name: str, dtypes, ndim: int) -> None:
+    _dev(t, name)
+    if t.dtype not in dtypes:
+        raise TypeError("%s: dtype %s not in %s" % (name, t.dtype, dtypes))
+    if t.dim() != ndim:
+        raise ValueError("%s must have %d dims, got %d" % (name, ndim, t.dim()))
+    if t.stride(-1) != 1:
+        raise ValueError("%s must have unit stride in its last dim" % name)
+
+
+def _contig(t: torch.Tensor, name: str) -> None:
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+# ----------------------------------------------------------------------------
+
+def fp8_quant_group_pack(x: torch.Tensor, q: torch.Tensor | None = None, sf: torch.Tensor | None = None,
+                         ld_sf: int | None = None, stream=None):
+    """1x128 per-token group quant + UE8M0 pack.  x bf16 [M, K] -> (q uint8 [M, K],
+    sf int32 [ceil(K/512), ld_sf]); ld_sf defaults to round_up(M, 4)."""
+    _expect(x, "x", _BF16, 2)
+    M, K = x.shape
+    W = (K // 128 + 3) // 4
+    if q is None:
+        q = torch.empty((M, K), dtype=torch.uint8, device=x.device)
+    if sf is None:
+        ld = ld_sf if ld_sf is not None else max(4, (M + 3) // 4 * 4)
+        sf = torch.empty((W, ld), dtype=torch.int32, device=x.device)
+    _expect(q, "q", _E4M3, 2)
+    _expect(sf, "sf", (torch.int32, torch.uint32), 2)
+    if tuple(q.shape) != (M, K) or sf.shape[0] != W:
+        raise ValueError("output shapes do not match x")
+    st = _lib.fp8_quant_group_pack(x.data_ptr(), x.stride(0), M, K, q.data_ptr(), q.stride(0),
+                                   sf.data_ptr(), sf.stride(0), _stream(stream))
+    _check("fp8_quant_group_pack", st)
+    return q, sf
+
+
+def silu_mul_quant_group_pack(x: torch.Tensor, masked_m: torch.Tensor, q: torch.Tensor | None = None,
+                              sf: torch.Tensor | None = None, stream=None):
+    """Fused SiLU-mul + quant/pack over a masked batch.  x bf16 [E, M_max, 2H], masked_m int32 [E]
+    -> (q uint8 [E, M_max, H], sf int32 [E, ceil(H/512), M_max]); padded rows are not written."""
+    _expect(x, "x", _BF16, 3)
+    _contig(x, "x")
+    E, M_max, H2 = x.shape
+    if H2 % 2:
+        raise ValueError("last dim of x must be 2H")
+    H = H2 // 2
+    W = (H // 128 + 3) // 4
+    _expect(masked_m, "masked_m", (torch.int32,), 1)
+    if masked_m.shape[0] != E:
+        raise ValueError("masked_m must have E entries")
+    if q is None:
+        q = torch.empty((E, M_max, H), dtype=torch.uint8, device=x.device)
+    if sf is None:
+        sf = torch.empty((E, W, M_max), dtype=torch.int32, device=x.device)
+    _expect(q, "q", _E4M3, 3)
+    _contig(q, "q")
+    _expect(sf, "sf", (torch.int32, torch.uint32), 3)
+    _contig(sf, "sf")
+    if tuple(q.shape) != (E, M_max, H) or tuple(sf.shape) != (E, W, M_max):
+        raise ValueError("output shapes do not match x")
+    st = _lib.silu_mul_quant_group_pack(x.data_ptr(), masked_m.data_ptr(), E, M_max, H, q.data_ptr(),
+                                        sf.data_ptr(), _stream(stream))
+    _check("silu_mul_quant_group_pack", st)
+    return q, sf
+
+
+def fp8_block_quant_128x128(w: torch.Tensor, q: torch.Tensor | None = None, sfb: torch.Tensor | None = None,
+                            stream=None):
+    """128x128 weight block quant.  w bf16 [N, K] -> (q uint8 [N, K], sfb float32 [ceil(N/128), K/128])."""
+    _expect(w, "w", _BF16, 2)
+    _contig(w, "w")
+    N, K = w.shape
+    if q is None:
+        q = torch.empty((N, K), dtype=torch.uint8, device=w.device)
+    if sfb is None:
+        sfb = torch.empty(((N + 127) // 128, K // 128), dtype=torch.float32, device=w.device)
+    _expect(q, "q", _E4M3, 2)
+    _contig(q, "q")
+    _expect(sfb, "sfb", (torch.float32,), 2)
+    _contig(sfb, "sfb")
+    st = _lib.fp8_block_quant_128x128(w.data_ptr(), N, K, q.data_ptr(), sfb.data_ptr(), _stream(stream))
+    _check("fp8_block_quant_128x128", st)
+    return q, sfb
+
+
+def fp8_block_gemm_nt(a: torch.Tensor, sfa: torch.Tensor, b: torch.Tensor, sfb: torch.Tensor,
+                      c: torch.Tensor | None = None, kernel: int | None = None, splits: int | None = None,
+                      stream=None) -> torch.Tensor:
+    """Dense block-scaled C = A . B^T -> bf16 [M, N].  a uint8 [M, K], sfa int32 [ceil(K/512), ld_sfa],
+    b uint8 [N, K], sfb float32 [ceil(N/128), K/128].  kernel/splits force a tile-table entry."""
+    _expect(a, "a", _E4M3, 2)
+    _contig(a, "a")
+    _expect(b, "b", _E4M3, 2)
+    _contig(b, "b")
+    _expect(sfa, "sfa", (torch.int32, torch.uint32), 2)
+    _expect(sfb, "sfb", (torch.float32,), 2)
+    _contig(sfb, "sfb")
+    M, K = a.shape
+    N = b.shape[0]
+    if b.shape[1] != K:
+        raise ValueError("a and b disagree on K")
+    if c is None:
+        c = torch.empty((M, N), dtype=torch.bfloat16, device=a.device)
+    _expect(c, "c", _BF16, 2)
+    if tuple(c.shape) != (M, N):
+        raise ValueError("c must be [M, N]")
+    s = _stream(stream)
+    if kernel is None and splits is None:
+        st = _lib.fp8_block_gemm_nt(a.data_ptr(), sfa.data_ptr(), sfa.stride(0), b.data_ptr(), sfb.data_ptr(),
+                                    c.data_ptr(), c.stride(0), M, N, K, s)
+    else:
+        if kernel is None:
+            kernel = gemm_config(False, M, N, K)["kernel"]
+        st = _lib.fp8_block_gemm_nt_cfg(a.data_ptr(), sfa.data_ptr(), sfa.stride(0), b.data_ptr(),
+                                        sfb.data_ptr(), c.data_ptr(), c.stride(0), M, N, K, int(kernel),
+                                        int(splits or 1), s)
+    _check("fp8_block_gemm_nt", st)
+    return c
+
+
+def fp8_block_gemm_grouped_masked(a: torch.Tensor, sfa: torch.Tensor, b: torch.Tensor, sfb: torch.Tensor,
+                                  masked_m: torch.Tensor, c: torch.Tensor | None = None,
+                                  kernel: int | None = None, stream=None) -> torch.Tensor:
+    """Masked grouped GEMM -> bf16 [E, M_max, N].  a uint8 [E, M_max, K], sfa int32 [E, ceil(K/512), M_max],
+    b uint8 [E, N, K], sfb float32 [E, ceil(N/128), K/128], masked_m int32 [E]."""
+    for t, n in ((a, "a"), (b, "b")):
+        _expect(t, n, _E4M3, 3)
+        _contig(t, n)
+    _expect(sfa, "sfa", (torch.int32, torch.uint32), 3)
+    _contig(sfa, "sfa")
+    _expect(sfb, "sfb", (torch.float32,), 3)
+    _contig(sfb, "sfb")
+    _expect(masked_m, "masked_m", (torch.int32,), 1)
+    E, M_max, K = a.shape
+    N = b.shape[1]
+    if b.shape[0] != E or b.shape[2] != K or masked_m.shape[0] != E:
+        raise ValueError("inconsistent expert shapes")
+    if c is None:
+        c = torch.empty((E, M_max, N), dtype=torch.bfloat16, device=a.device)
+    _expect(c, "c", _BF16, 3)
+    _contig(c, "c")
+    s = _stream(stream)
+    if kernel is None:
+        st = _lib.fp8_block_gemm_grouped_masked(a.data_ptr(), sfa.data_ptr(), b.data_ptr(), sfb.data_ptr(),
+                                                c.data_ptr(), masked_m.data_ptr(), E, M_max, N, K, s)
+    else:
+        st = _lib.fp8_block_gemm_grouped_masked_cfg(a.data_ptr(), sfa.data_ptr(), b.data_ptr(), sfb.data_ptr(),
+                                                    c.data_ptr(), masked_m.data_ptr(), E, M_max, N, K,
+                                                    int(kernel), s)
+    _check("fp8_block_gemm_grouped_masked", st)
+    return c
+
+
+def gemm_config_count() -> int:
+    return int(_lib.fp8bs_gemm_config_count())
+
+
+def gemm_config(masked: bool, M: int, N: int, K: int) -> dict:
+    k, bm, bn, sp = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+    st = _lib.fp8bs_gemm_config(1 if masked else 0, M, N, K, ctypes.byref(k), ctypes.byref(bm),
+                                ctypes.byref(bn), ctypes.byref(sp))
+    _check("fp8bs_gemm_config", st)
+    return {"kernel": k.value, "bm": bm.value, "bn": bn.value, "splits": sp.value}

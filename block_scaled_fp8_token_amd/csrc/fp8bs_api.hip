@@ -1,0 +1,292 @@
+// C-ABI layer of the block-scaled FP8 library: argument validation, status codes,
+// the per-(device, stream) split-K workspace, and dispatch to the gfx950 kernels.
+// The operations and their preconditions are stated in include/fp8bs.h.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <utility>
+
+#include "../../include/fp8bs.h"
+#include "fp8bs_launch.hpp"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+int fail_hip(hipError_t e) {
+  g_last_hip_error = (int)e;
+  return FP8BS_ERR_LAUNCH;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// gfx950 check, cached per device.
+int check_device() {
+  static std::mutex mu;
+  static std::map<int, bool> ok;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail_hip(e);
+  std::lock_guard<std::mutex> lk(mu);
+  auto it = ok.find(dev);
+  if (it == ok.end()) {
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess) return fail_hip(e);
+    const bool is950 = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    it = ok.emplace(dev, is950).first;
+  }
+  return it->second ? FP8BS_OK : FP8BS_ERR_DEVICE;
+}
+
+// Split-K workspace: one buffer per (device, stream), grown on demand.  Freshly
+// allocated memory is zeroed on the same stream (the tile counters must start at
+// zero; the GEMM returns every counter it uses to zero).
+struct Workspace {
+  void* ptr = nullptr;
+  size_t bytes = 0;
+};
+
+int get_workspace(size_t need, hipStream_t stream, void** out) {
+  static std::mutex mu;
+  static std::map<std::pair<int, uintptr_t>, Workspace> pool;
+  *out = nullptr;
+  if (need == 0) return FP8BS_OK;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail_hip(e);
+  std::lock_guard<std::mutex> lk(mu);
+  Workspace& w = pool[std::make_pair(dev, reinterpret_cast<uintptr_t>(stream))];
+  if (w.bytes >= need) {
+    *out = w.ptr;
+    return FP8BS_OK;
+  }
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  e = hipStreamIsCapturing(stream, &cap);
+  if (e != hipSuccess) return fail_hip(e);
+  if (cap != hipStreamCaptureStatusNone) return FP8BS_ERR_ALLOC;
+  if (w.ptr) {
+    // earlier work on this stream may still use the old buffer
+    e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) return fail_hip(e);
+    (void)hipFree(w.ptr);
+    w.ptr = nullptr;
+    w.bytes = 0;
+  }
+  size_t sz = need < (size_t(1) << 20) ? (size_t(1) << 20) : need;
+  sz = (sz + (size_t(1) << 20) - 1) & ~((size_t(1) << 20) - 1);
+  void* p = nullptr;
+  e = hipMalloc(&p, sz);
+  if (e != hipSuccess) {
+    g_last_hip_error = (int)e;
+    return FP8BS_ERR_ALLOC;
+  }
+  e = hipMemsetAsync(p, 0, sz, stream);
+  if (e != hipSuccess) {
+    (void)hipFree(p);
+    return fail_hip(e);
+  }
+  w.ptr = p;
+  w.bytes = sz;
+  *out = p;
+  return FP8BS_OK;
+}
+
+int run_gemm(const fp8bs::GemmProblem& prob, const fp8bs::GemmConfig& cfg, hipStream_t stream) {
+  void* ws = nullptr;
+  const size_t need = fp8bs::gemm_workspace_bytes(prob, cfg);
+  int st = get_workspace(need, stream, &ws);
+  if (st != FP8BS_OK) return st;
+  hipError_t e = fp8bs::launch_gemm(prob, cfg, ws, stream);
+  return e == hipSuccess ? FP8BS_OK : fail_hip(e);
+}
+
+int check_dense(const void* a, const uint32_t* sfa, int64_t ld_sfa, const void* b, const float* sfb,
+                const void* c, int64_t ldc, int64_t M, int64_t N, int64_t K) {
+  if (M < 0 || N < 0 || K < 0) return FP8BS_ERR_SHAPE;
+  if (K < 128 || K % 128 != 0 || N % 64 != 0) return FP8BS_ERR_SHAPE;
+  if (M == 0 || N == 0) return 1;  // no-op
+  if (!a || !sfa || !b || !sfb || !c) return FP8BS_ERR_NULL;
+  if (ld_sfa < M || ldc < N) return FP8BS_ERR_SHAPE;
+  if (!aligned(a, 16) || !aligned(b, 16) || !aligned(c, 16) || ldc % 8 != 0) return FP8BS_ERR_ALIGN;
+  if (!aligned(sfa, 4) || !aligned(sfb, 4)) return FP8BS_ERR_ALIGN;
+  return FP8BS_OK;
+}
+
+int check_masked(const void* a, const uint32_t* sfa, const void* b, const float* sfb, const void* c,
+                 const int32_t* masked_m, int64_t E, int64_t M_max, int64_t N, int64_t K) {
+  if (E < 0 || M_max < 0 || N < 0 || K < 0) return FP8BS_ERR_SHAPE;
+  if (K < 128 || K % 128 != 0 || N % 64 != 0) return FP8BS_ERR_SHAPE;
+  if (E == 0 || M_max == 0 || N == 0) return 1;  // no-op
+  if (!a || !sfa || !b || !sfb || !c || !masked_m) return FP8BS_ERR_NULL;
+  if (!aligned(a, 16) || !aligned(b, 16) || !aligned(c, 16)) return FP8BS_ERR_ALIGN;
+  if (!aligned(sfa, 4) || !aligned(sfb, 4) || !aligned(masked_m, 4)) return FP8BS_ERR_ALIGN;
+  return FP8BS_OK;
+}
+
+fp8bs::GemmProblem dense_problem(const void* a, const uint32_t* sfa, int64_t ld_sfa, const void* b,
+                                 const float* sfb, void* c, int64_t ldc, int64_t M, int64_t N, int64_t K) {
+  fp8bs::GemmProblem p;
+  p.a = static_cast<const uint8_t*>(a);
+  p.sfa = sfa;
+  p.b = static_cast<const uint8_t*>(b);
+  p.sfb = sfb;
+  p.c = static_cast<uint16_t*>(c);
+  p.masked_m = nullptr;
+  p.E = 1;
+  p.M = M;
+  p.N = N;
+  p.K = K;
+  p.ld_sfa = ld_sfa;
+  p.ldc = ldc;
+  return p;
+}
+
+fp8bs::GemmProblem masked_problem(const void* a, const uint32_t* sfa, const void* b, const float* sfb,
+                                  void* c, const int32_t* masked_m, int64_t E, int64_t M_max, int64_t N,
+                                  int64_t K) {
+  fp8bs::GemmProblem p;
+  p.a = static_cast<const uint8_t*>(a);
+  p.sfa = sfa;
+  p.b = static_cast<const uint8_t*>(b);
+  p.sfb = sfb;
+  p.c = static_cast<uint16_t*>(c);
+  p.masked_m = masked_m;
+  p.E = E;
+  p.M = M_max;
+  p.N = N;
+  p.K = K;
+  p.ld_sfa = M_max;
+  p.ldc = N;
+  return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fp8_quant_group_pack(const void* x, int64_t ldx, int64_t M, int64_t K, void* q, int64_t ldq,
+                         uint32_t* sf, int64_t ld_sf, void* stream) {
+  if (M < 0 || K < 0 || K % 128 != 0) return FP8BS_ERR_SHAPE;
+  if (M == 0 || K == 0) return FP8BS_OK;
+  if (!x || !q || !sf) return FP8BS_ERR_NULL;
+  if (ldx < K || ldq < K || ld_sf < M) return FP8BS_ERR_SHAPE;
+  if (!aligned(x, 16) || !aligned(q, 16) || ldx % 8 != 0 || ldq % 16 != 0 || !aligned(sf, 4))
+    return FP8BS_ERR_ALIGN;
+  int st = check_device();
+  if (st != FP8BS_OK) return st;
+  hipError_t e = fp8bs::launch_quant_group_pack(static_cast<const uint16_t*>(x), ldx, M, K,
+                                                static_cast<uint8_t*>(q), ldq, sf, ld_sf,
+                                                static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FP8BS_OK : fail_hip(e);
+}
+
+int silu_mul_quant_group_pack(const void* x, const int32_t* masked_m, int64_t E, int64_t M_max, int64_t H,
+                              void* q, uint32_t* sf, void* stream) {
+  if (E < 0 || M_max < 0 || H < 0 || H % 128 != 0) return FP8BS_ERR_SHAPE;
+  if (E == 0 || M_max == 0 || H == 0) return FP8BS_OK;
+  if (!x || !masked_m || !q || !sf) return FP8BS_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(q, 16) || !aligned(sf, 4) || !aligned(masked_m, 4)) return FP8BS_ERR_ALIGN;
+  int st = check_device();
+  if (st != FP8BS_OK) return st;
+  hipError_t e = fp8bs::launch_silu_mul_quant(static_cast<const uint16_t*>(x), masked_m, E, M_max, H,
+                                              static_cast<uint8_t*>(q), sf, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FP8BS_OK : fail_hip(e);
+}
+
+int fp8_block_quant_128x128(const void* w, int64_t N, int64_t K, void* q, float* sfb, void* stream) {
+  if (N < 0 || K < 0 || K % 128 != 0) return FP8BS_ERR_SHAPE;
+  if (N == 0 || K == 0) return FP8BS_OK;
+  if (!w || !q || !sfb) return FP8BS_ERR_NULL;
+  if (!aligned(w, 16) || !aligned(q, 16) || !aligned(sfb, 4)) return FP8BS_ERR_ALIGN;
+  int st = check_device();
+  if (st != FP8BS_OK) return st;
+  hipError_t e = fp8bs::launch_block_quant(static_cast<const uint16_t*>(w), N, K, static_cast<uint8_t*>(q),
+                                           sfb, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FP8BS_OK : fail_hip(e);
+}
+
+int fp8_block_gemm_nt(const void* a, const uint32_t* sfa, int64_t ld_sfa, const void* b, const float* sfb,
+                      void* c, int64_t ldc, int64_t M, int64_t N, int64_t K, void* stream) {
+  int st = check_dense(a, sfa, ld_sfa, b, sfb, c, ldc, M, N, K);
+  if (st != FP8BS_OK) return st > 0 ? FP8BS_OK : st;
+  st = check_device();
+  if (st != FP8BS_OK) return st;
+  const fp8bs::GemmProblem p = dense_problem(a, sfa, ld_sfa, b, sfb, c, ldc, M, N, K);
+  return run_gemm(p, fp8bs::choose_gemm_config(p), static_cast<hipStream_t>(stream));
+}
+
+int fp8_block_gemm_nt_cfg(const void* a, const uint32_t* sfa, int64_t ld_sfa, const void* b, const float* sfb,
+                          void* c, int64_t ldc, int64_t M, int64_t N, int64_t K, int32_t kernel, int32_t splits,
+                          void* stream) {
+  int st = check_dense(a, sfa, ld_sfa, b, sfb, c, ldc, M, N, K);
+  if (st != FP8BS_OK) return st > 0 ? FP8BS_OK : st;
+  st = check_device();
+  if (st != FP8BS_OK) return st;
+  const fp8bs::GemmProblem p = dense_problem(a, sfa, ld_sfa, b, sfb, c, ldc, M, N, K);
+  fp8bs::GemmConfig cfg;
+  if (!fp8bs::gemm_config_by_index(kernel, p, splits < 1 ? 1 : splits, &cfg)) return FP8BS_ERR_SHAPE;
+  return run_gemm(p, cfg, static_cast<hipStream_t>(stream));
+}
+
+int fp8_block_gemm_grouped_masked(const void* a, const uint32_t* sfa, const void* b, const float* sfb, void* c,
+                                  const int32_t* masked_m, int64_t E, int64_t M_max, int64_t N, int64_t K,
+                                  void* stream) {
+  int st = check_masked(a, sfa, b, sfb, c, masked_m, E, M_max, N, K);
+  if (st != FP8BS_OK) return st > 0 ? FP8BS_OK : st;
+  st = check_device();
+  if (st != FP8BS_OK) return st;
+  const fp8bs::GemmProblem p = masked_problem(a, sfa, b, sfb, c, masked_m, E, M_max, N, K);
+  return run_gemm(p, fp8bs::choose_gemm_config(p), static_cast<hipStream_t>(stream));
+}
+
+int fp8_block_gemm_grouped_masked_cfg(const void* a, const uint32_t* sfa, const void* b, const float* sfb,
+                                      void* c, const int32_t* masked_m, int64_t E, int64_t M_max, int64_t N,
+                                      int64_t K, int32_t kernel, void* stream) {
+  int st = check_masked(a, sfa, b, sfb, c, masked_m, E, M_max, N, K);
+  if (st != FP8BS_OK) return st > 0 ? FP8BS_OK : st;
+  st = check_device();
+  if (st != FP8BS_OK) return st;
+  const fp8bs::GemmProblem p = masked_problem(a, sfa, b, sfb, c, masked_m, E, M_max, N, K);
+  fp8bs::GemmConfig cfg;
+  if (!fp8bs::gemm_config_by_index(kernel, p, 1, &cfg)) return FP8BS_ERR_SHAPE;
+  return run_gemm(p, cfg, static_cast<hipStream_t>(stream));
+}
+
+int fp8bs_gemm_config_count(void) { return fp8bs::gemm_config_count(); }
+
+int fp8bs_gemm_config(int masked, int64_t M, int64_t N, int64_t K, int32_t* kernel, int32_t* bm, int32_t* bn,
+                      int32_t* splits) {
+  if (M < 0 || N < 0 || K < 128 || K % 128 != 0 || N % 64 != 0) return FP8BS_ERR_SHAPE;
+  if (!kernel || !bm || !bn || !splits) return FP8BS_ERR_NULL;
+  static const int32_t dummy_count = 0;
+  fp8bs::GemmProblem p = masked ? masked_problem(nullptr, nullptr, nullptr, nullptr, nullptr, &dummy_count, 1,
+                                                 M, N, K)
+                                : dense_problem(nullptr, nullptr, M, nullptr, nullptr, nullptr, N, M, N, K);
+  const fp8bs::GemmConfig cfg = fp8bs::choose_gemm_config(p);
+  *kernel = cfg.kernel;
+  *bm = cfg.bm;
+  *bn = cfg.bn;
+  *splits = cfg.splits;
+  return FP8BS_OK;
+}
+
+const char* fp8bs_status_string(int status) {
+  switch (status) {
+    case FP8BS_OK: return "ok";
+    case FP8BS_ERR_NULL: return "null pointer";
+    case FP8BS_ERR_SHAPE: return "invalid shape or leading dimension";
+    case FP8BS_ERR_ALIGN: return "misaligned pointer or row stride";
+    case FP8BS_ERR_DEVICE: return "device is not gfx950";
+    case FP8BS_ERR_LAUNCH: return "HIP call failed";
+    case FP8BS_ERR_ALLOC: return "workspace allocation failed or refused during graph capture";
+    default: return "unknown status";
+  }
+}
+
+int fp8bs_last_hip_error(void) { return g_last_hip_error; }
+
+}  // extern "C"

@@ -1,0 +1,47 @@
+// Internal launchers of the gfx950 kernels.  The C-ABI layer validates every
+// argument before calling these; the launchers only pick grid shapes and launch
+// on the caller's stream.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp8bs {
+
+hipError_t launch_quant_group_pack(const uint16_t* x, int64_t ldx, int64_t M, int64_t K, uint8_t* q,
+                                   int64_t ldq, uint32_t* sf, int64_t ld_sf, hipStream_t stream);
+
+hipError_t launch_silu_mul_quant(const uint16_t* x, const int32_t* masked_m, int64_t E, int64_t M_max,
+                                 int64_t H, uint8_t* q, uint32_t* sf, hipStream_t stream);
+
+hipError_t launch_block_quant(const uint16_t* w, int64_t N, int64_t K, uint8_t* q, float* sfb,
+                              hipStream_t stream);
+
+// One GEMM problem: dense (masked_m == nullptr, E == 1) or masked grouped.
+struct GemmProblem {
+  const uint8_t* a;          // e4m3 [E][M][K]
+  const uint32_t* sfa;       // packed UE8M0 [E][W][ld_sfa]
+  const uint8_t* b;          // e4m3 [E][N][K]
+  const float* sfb;          // fp32 [E][ceil(N/128)][K/128]
+  uint16_t* c;               // bf16 [E][M][ldc]
+  const int32_t* masked_m;   // [E] valid rows per group, or nullptr (all M rows valid)
+  int64_t E, M, N, K;
+  int64_t ld_sfa, ldc;
+};
+
+// Tile configuration chosen for a problem (exposed for reporting and tuning).
+struct GemmConfig {
+  int kernel;   // index into the compiled tile table
+  int bm, bn;   // workgroup tile
+  int splits;   // K splits (1 = no split)
+  int kb_per_split;  // K-blocks per split; every split owns at least one
+};
+
+GemmConfig choose_gemm_config(const GemmProblem& p);
+size_t gemm_workspace_bytes(const GemmProblem& p, const GemmConfig& cfg);
+// ws: a fixed 64 KiB region of 32-bit tile counters (zero on entry, returned to
+// zero by the kernel) followed by the fp32 split partials.
+hipError_t launch_gemm(const GemmProblem& p, const GemmConfig& cfg, void* ws, hipStream_t stream);
+int gemm_config_count();
+bool gemm_config_by_index(int idx, const GemmProblem& p, int splits, GemmConfig* out);
+
+}  // namespace fp8bs

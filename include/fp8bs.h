@@ -1,0 +1,160 @@
+/*
+ * fp8bs.h -- C ABI of the MI355X (gfx950) block-scaled FP8 W8A8 GEMM library.
+ *
+ * The method: activations are quantized per token in 1x128 groups to OCP e4m3
+ * with power-of-two (UE8M0) scales packed four to a 32-bit word; weights are
+ * e4m3 with one scale per 128x128 block; the GEMM accumulates in fp32, applying
+ * the two scales to each 128-wide K-block before adding it, and writes bf16.
+ * Sources: vLLM DeepGEMM FP8 block GEMM benchmark post (sections 4.1-4.2:
+ * quantization layouts, the three dense GEMM calls and their preconditions);
+ * vLLM PR #29546 "Deepgemm fused layout kernel for activations" (quant with the
+ * uint32 scale pack fused in); vLLM PR #19885 "Optimize the little operations
+ * in the DeepGEMM + DeepEP low latency case" (fused SiLU-mul-quant that skips
+ * padded tokens); vLLM PR #19111 "Integrate batched/masked deepgemm kernel"
+ * (masked grouped GEMM over [experts, max_tokens, K] with per-expert counts).
+ *
+ * Conventions shared by every entry point
+ *   - Data pointers are DEVICE pointers owned by the caller.  bf16 is passed as
+ *     its 16-bit pattern, e4m3 as bytes (OCP E4M3FN, max 448).
+ *   - stream is a hipStream_t passed as void* (NULL = the default stream).  Every
+ *     call is asynchronous and stream-ordered; nothing reads device data on the
+ *     host, so masked counts never leave the device.
+ *   - Return value: FP8BS_OK (0) or a negative status; on error nothing is
+ *     launched.  fp8bs_status_string() names a status; after FP8BS_ERR_LAUNCH,
+ *     fp8bs_last_hip_error() gives the hipError_t of the failed call (per thread).
+ *   - Sizes of zero are a successful no-op, except K (see each call).
+ *   - Outputs must not overlap inputs.
+ *   - Alignment: every data pointer and every row of an e4m3/bf16 tensor must be
+ *     16-byte aligned (FP8BS_ERR_ALIGN otherwise); scale pointers 4-byte aligned.
+ *   - The device must be gfx950 (FP8BS_ERR_DEVICE otherwise).
+ *
+ * Packed activation-scale layout ("sf"): for K columns there are G = K/128 groups
+ * per row and W = ceil(G/4) words per row.  Group g's exponent byte (e + 127,
+ * where the group's scale is 2^e) sits in bits 8*(g%4)..8*(g%4)+7 of word g/4;
+ * bytes of groups past G are zero.  Words are stored M-major: word w of row r is
+ * sf[w*ld_sf + r] (the column-major, padded layout the benchmark post's section
+ * 4.1 describes for DeepGEMM; ld_sf = round_up(M, 4) gives 16-byte columns).
+ * Weight block scales ("sfb") are fp32 [ceil(N/128)][K/128], row-major, and
+ * must be powers of two (UE8M0 values), as the weight block quant produces.
+ */
+#ifndef FP8BS_H
+#define FP8BS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  FP8BS_OK = 0,
+  FP8BS_ERR_NULL = -1,   /* a required pointer is NULL                              */
+  FP8BS_ERR_SHAPE = -2,  /* a size or leading dimension is out of its allowed range */
+  FP8BS_ERR_ALIGN = -3,  /* a pointer or row stride breaks the alignment rule       */
+  FP8BS_ERR_DEVICE = -4, /* the current device is not gfx950                        */
+  FP8BS_ERR_LAUNCH = -5, /* a HIP call failed; see fp8bs_last_hip_error()           */
+  FP8BS_ERR_ALLOC = -6   /* the split-K workspace could not be allocated            */
+};
+
+/*
+ * Per-token 1x128 group quant with the UE8M0 scale pack in the same pass
+ * (PR #29546, Purpose; benchmark post section 4.1, per_token_group_quant with
+ * column-major, aligned scales).  For every row r < M and group g:
+ *   e = smallest integer with 448 * 2^e >= max(amax of the group, 1e-10),
+ *   q[r][k] = e4m3_rne_saturating(x[r][k] * 2^-e),  byte e + 127 into sf.
+ *   x   : bf16 [M][ldx], ldx >= K
+ *   q   : e4m3 [M][ldq], ldq >= K, ldq % 16 == 0
+ *   sf  : uint32 [ceil(K/512)][ld_sf], ld_sf >= M; entries of rows >= M untouched
+ *   K % 128 == 0.
+ */
+int fp8_quant_group_pack(const void* x, int64_t ldx, int64_t M, int64_t K,
+                         void* q, int64_t ldq, uint32_t* sf, int64_t ld_sf, void* stream);
+
+/*
+ * Fused SiLU-and-mul + the quant/pack above over a masked expert batch
+ * (PR #19885, Summary item 2: outputs in the GEMM's layout, padded tokens
+ * neither loaded nor computed).  For e < E and r < clamp(masked_m[e], 0, M_max):
+ *   y = silu(gate) * up = gate / (1 + exp(-gate)) * up, in fp32, with gate =
+ *   x[e][r][0:H] and up = x[e][r][H:2H]; then 1x128 quant/pack of y.
+ *   x        : bf16 [E][M_max][2H] contiguous
+ *   masked_m : int32 [E] on the device (clamped to [0, M_max] in the kernel)
+ *   q        : e4m3 [E][M_max][H] contiguous
+ *   sf       : uint32 [E][ceil(H/512)][M_max] contiguous
+ *   H % 128 == 0.  Rows r >= count of q and sf are left untouched.
+ */
+int silu_mul_quant_group_pack(const void* x, const int32_t* masked_m, int64_t E, int64_t M_max,
+                              int64_t H, void* q, uint32_t* sf, void* stream);
+
+/*
+ * 128x128 weight block quant (benchmark post section 4.1, per_block_cast with
+ * UE8M0: scale = block amax / 448 rounded up to a power of two).
+ *   w   : bf16 [N][K] contiguous;  q : e4m3 [N][K] contiguous
+ *   sfb : fp32 [ceil(N/128)][K/128]; the last row block may be partial.
+ *   K % 128 == 0.
+ */
+int fp8_block_quant_128x128(const void* w, int64_t N, int64_t K, void* q, float* sfb, void* stream);
+
+/*
+ * Dense block-scaled GEMM, NT form (benchmark post section 4.2, fp8_gemm_nt
+ * writing into a preallocated output; preconditions there: bf16 output,
+ * N % 64 == 0, K % 128 == 0):
+ *   C[m][n] = bf16_rne( sum_kb 2^ea[m][kb] * sfb[n/128][kb]
+ *                       * sum_{k in block kb} a[m][k] * b[n][k] )
+ *   a   : e4m3 [M][K] contiguous;    sfa : packed scales [ceil(K/512)][ld_sfa], ld_sfa >= M
+ *   b   : e4m3 [N][K] contiguous;    sfb : fp32 [ceil(N/128)][K/128]
+ *   c   : bf16 [M][ldc], ldc >= N, ldc % 8 == 0
+ *   K >= 128, K % 128 == 0, N % 64 == 0.
+ * Decode-sized M splits K across workgroups; the split partials live in a
+ * library-owned device workspace kept per (device, stream), allocated on the
+ * first call that needs it (make that call outside HIP graph capture: during
+ * capture an allocation is refused with FP8BS_ERR_ALLOC).  Calls on different
+ * streams never share a workspace.
+ */
+int fp8_block_gemm_nt(const void* a, const uint32_t* sfa, int64_t ld_sfa, const void* b,
+                      const float* sfb, void* c, int64_t ldc, int64_t M, int64_t N, int64_t K,
+                      void* stream);
+
+/*
+ * Masked grouped GEMM (PR #19111: m_grouped GEMM, masked, over [E, max_tokens, K]
+ * with per-expert valid counts; 128x128 blocks).  For each expert e and row
+ * r < clamp(masked_m[e], 0, M_max), row r of C[e] is the dense NT result of
+ * a[e], sfa[e], b[e], sfb[e].  Rows at or past the count are not written, and
+ * workgroup tiles that start past the count issue no loads and no MFMA.
+ *   a        : e4m3 [E][M_max][K];      sfa : uint32 [E][ceil(K/512)][M_max]
+ *   b        : e4m3 [E][N][K];          sfb : fp32 [E][ceil(N/128)][K/128]
+ *   c        : bf16 [E][M_max][N];      masked_m : int32 [E] on the device
+ *   K >= 128, K % 128 == 0, N % 64 == 0.
+ */
+int fp8_block_gemm_grouped_masked(const void* a, const uint32_t* sfa, const void* b,
+                                  const float* sfb, void* c, const int32_t* masked_m, int64_t E,
+                                  int64_t M_max, int64_t N, int64_t K, void* stream);
+
+/*
+ * Tile-table access, for tuning and for tests that cover every compiled tile
+ * shape.  fp8bs_gemm_config reports what the automatic choice would be for a
+ * dense (masked = 0) or masked (masked = 1) problem: kernel index into the tile
+ * table, workgroup tile bm x bn, and the number of K splits.  The _cfg variants
+ * run the same GEMMs with an explicit kernel index and split count (splits is
+ * clamped to [1, K/128]; the masked form accepts splits == 1 only).
+ */
+int fp8bs_gemm_config_count(void);
+int fp8bs_gemm_config(int masked, int64_t M, int64_t N, int64_t K, int32_t* kernel, int32_t* bm,
+                      int32_t* bn, int32_t* splits);
+int fp8_block_gemm_nt_cfg(const void* a, const uint32_t* sfa, int64_t ld_sfa, const void* b,
+                          const float* sfb, void* c, int64_t ldc, int64_t M, int64_t N, int64_t K,
+                          int32_t kernel, int32_t splits, void* stream);
+int fp8_block_gemm_grouped_masked_cfg(const void* a, const uint32_t* sfa, const void* b,
+                                      const float* sfb, void* c, const int32_t* masked_m, int64_t E,
+                                      int64_t M_max, int64_t N, int64_t K, int32_t kernel,
+                                      void* stream);
+
+/* Status helpers. */
+const char* fp8bs_status_string(int status);
+int fp8bs_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8BS_H */

@@ -1,0 +1,105 @@
+"""Host-side tests of the C ABI (no GPU): the library loads, exports every function
+the header declares, and rejects bad arguments with the documented status
+before touching the device (the validation runs ahead of any HIP call)."""
+import ctypes
+
+import pytest
+
+import block_scaled_fp8_token_amd as F
+
+OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN = 0, -1, -2, -3
+
+lib = ctypes.CDLL(F.library_path())
+lib.fp8bs_status_string.restype = ctypes.c_char_p
+
+# fake but 256-byte aligned addresses: validation never dereferences them
+A, B, C, S, T = 0x100000, 0x200000, 0x300000, 0x400000, 0x500000
+
+
+def test_header_declares_the_entry_points():
+    names = F.declared_functions()
+    for n in ("fp8_quant_group_pack", "silu_mul_quant_group_pack", "fp8_block_gemm_nt",
+              "fp8_block_gemm_grouped_masked", "fp8_block_quant_128x128", "fp8bs_status_string"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    for n in F.declared_functions():
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    for st in range(-6, 1):
+        s = lib.fp8bs_status_string(st).decode()
+        assert s and s != "unknown status"
+    assert lib.fp8bs_status_string(-99).decode() == "unknown status"
+
+
+def _gemm(a=A, sfa=S, ld_sfa=64, b=B, sfb=T, c=C, ldc=512, M=64, N=512, K=512):
+    f = F._lib.fp8_block_gemm_nt
+    return f(a, sfa, ld_sfa, b, sfb, c, ldc, M, N, K, None)
+
+
+def test_gemm_nt_validation():
+    assert _gemm(K=100) == ERR_SHAPE
+    assert _gemm(K=0) == ERR_SHAPE
+    assert _gemm(N=96) == ERR_SHAPE            # N % 64
+    assert _gemm(M=-1) == ERR_SHAPE
+    assert _gemm(ld_sfa=63) == ERR_SHAPE        # ld_sfa < M
+    assert _gemm(ldc=500) == ERR_SHAPE          # ldc < N
+    assert _gemm(a=None) == ERR_NULL
+    assert _gemm(sfb=None) == ERR_NULL
+    assert _gemm(a=A + 8) == ERR_ALIGN
+    assert _gemm(c=C + 2) == ERR_ALIGN
+    assert _gemm(ldc=516) == ERR_ALIGN          # rows of C not 16-byte aligned
+    assert _gemm(sfa=S + 2) == ERR_ALIGN
+    assert _gemm(M=0) == OK and _gemm(N=0) == OK  # empty problems are a no-op
+    assert _gemm(M=0, a=None) == OK
+
+
+def _masked(a=A, sfa=S, b=B, sfb=T, c=C, mm=S + 4096, E=4, M_max=64, N=256, K=256):
+    return F._lib.fp8_block_gemm_grouped_masked(a, sfa, b, sfb, c, mm, E, M_max, N, K, None)
+
+
+def test_masked_validation():
+    assert _masked(K=200) == ERR_SHAPE
+    assert _masked(N=100) == ERR_SHAPE
+    assert _masked(E=-2) == ERR_SHAPE
+    assert _masked(mm=None) == ERR_NULL
+    assert _masked(b=B + 4) == ERR_ALIGN
+    assert _masked(mm=S + 4098) == ERR_ALIGN
+    assert _masked(E=0) == OK and _masked(M_max=0) == OK
+
+
+def test_quant_validation():
+    f = F._lib.fp8_quant_group_pack
+    assert f(A, 512, 8, 500, B, 512, S, 8, None) == ERR_SHAPE          # K % 128
+    assert f(A, 256, 8, 512, B, 512, S, 8, None) == ERR_SHAPE          # ldx < K
+    assert f(A, 512, 8, 512, B, 512, S, 7, None) == ERR_SHAPE          # ld_sf < M
+    assert f(None, 512, 8, 512, B, 512, S, 8, None) == ERR_NULL
+    assert f(A + 4, 512, 8, 512, B, 512, S, 8, None) == ERR_ALIGN
+    assert f(A, 516, 8, 512, B, 512, S, 8, None) == ERR_ALIGN          # bf16 rows not 16B aligned
+    assert f(A, 512, 8, 512, B, 520, S, 8, None) == ERR_ALIGN          # e4m3 rows not 16B aligned
+    assert f(A, 512, 0, 512, None, 512, None, 8, None) == OK
+    g = F._lib.silu_mul_quant_group_pack
+    assert g(A, S, 2, 8, 100, B, T, None) == ERR_SHAPE
+    assert g(A, None, 2, 8, 128, B, T, None) == ERR_NULL
+    assert g(A, S, 0, 8, 128, None, None, None) == OK
+    h = F._lib.fp8_block_quant_128x128
+    assert h(A, 128, 100, B, T, None) == ERR_SHAPE
+    assert h(A, 128, 128, None, T, None) == ERR_NULL
+    assert h(A + 1, 128, 128, B, T, None) == ERR_ALIGN
+
+
+def test_config_table_choices():
+    n = F.gemm_config_count()
+    assert n >= 2
+    d = F.gemm_config(False, 64, 7168, 18432)
+    assert 0 <= d["kernel"] < n and d["splits"] >= 1
+    assert d["splits"] * 0 == 0
+    p = F.gemm_config(False, 4096, 4096, 7168)
+    assert p["splits"] == 1
+    m = F.gemm_config(True, 256, 4096, 7168)
+    assert m["splits"] == 1
+    with pytest.raises(F.Fp8bsError):
+        F.gemm_config(False, 64, 100, 512)

@@ -1,0 +1,157 @@
+"""GPU parity of the dense block-scaled GEMM against the CPU oracle.
+
+Operands are quantized by the oracle on the host (never by the GPU), uploaded,
+multiplied on the GPU, and compared element by element with the oracle's double
+result: |C_gpu - ref| <= 1e-2 |ref| + 1e-2 rms(ref).  Exactly representable
+integer problems must match exactly.
+"""
+import numpy as np
+import pytest
+import torch
+
+import block_scaled_fp8_token_amd as F
+import oracle as O
+import workloads as W
+from gpu_helpers import DEV, gemm_tolerance_check, sync, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+def _operands(M, N, K, seed=0, outliers=False, b_std=0.02, varied_blocks=False):
+    if outliers:
+        a = W.normal_bf16_outliers((M, K), seed=seed)
+    else:
+        a = W.normal_bf16((M, K), seed=seed)
+    b = W.normal_bf16((N, K), std=b_std, seed=seed, tensor_id=W.T_B)
+    if varied_blocks:  # give every 128x128 block its own magnitude so sfb indexing matters
+        rng = np.random.default_rng(seed + 17)
+        f = W.bf16_bits_to_f32(b)
+        mult = 2.0 ** rng.integers(-8, 9, ((N + 127) // 128, K // 128))
+        f = f * np.repeat(np.repeat(mult, 128, 0)[:N], 128, 1).astype(np.float32)
+        b = W.f32_to_bf16_bits(f.astype(np.float32))
+    qa, sfa = O.quant_group_pack(a)
+    qb, sfb = O.block_quant_128x128(b)
+    return qa, sfa, qb, sfb
+
+
+def _run(qa, sfa, qb, sfb, kernel=None, splits=None, c=None):
+    out = F.fp8_block_gemm_nt(to_dev(qa), to_dev(sfa), to_dev(qb), to_dev(sfb), c=c, kernel=kernel,
+                              splits=splits)
+    sync()
+    return to_host(out)
+
+
+def _int_codes(vals):
+    """e4m3 codes of -1, 0, 1."""
+    return np.where(vals > 0, 0x38, np.where(vals < 0, 0xB8, 0x00)).astype(np.uint8)
+
+
+@pytest.mark.parametrize("kernel", range(4))
+@pytest.mark.parametrize("splits", [1, 2])
+def test_gemm_integer_identity_exact(kernel, splits):
+    rng = np.random.default_rng(kernel * 10 + splits)
+    M, N, K = 37, 320, 256
+    ai = rng.integers(-1, 2, (M, K))
+    bi = rng.integers(-1, 2, (N, K))
+    sfa = np.full((1, 40), 127 | (127 << 8), np.uint32)
+    sfb = np.ones((3, 2), np.float32)
+    c = _run(_int_codes(ai), sfa, _int_codes(bi), sfb, kernel=kernel, splits=splits)
+    want = (ai @ bi.T).astype(np.float32)
+    got = (c.astype(np.uint32) << 16).view(np.float32)
+    assert np.array_equal(got, want)
+
+
+SMALL = [(1, 64, 128), (17, 192, 384), (64, 512, 1024), (100, 640, 640), (130, 256, 512), (257, 384, 1152)]
+
+
+@pytest.mark.parametrize("M,N,K", SMALL)
+def test_gemm_parity_every_tile_config(M, N, K):
+    print("gemm parity %dx%dx%d" % (M, N, K), flush=True)
+    qa, sfa, qb, sfb = _operands(M, N, K, seed=M + N, b_std=1.0, varied_blocks=True)
+    ref = O.gemm_nt(qa, sfa, qb, sfb)
+    for kernel in range(F.gemm_config_count()):
+        for splits in (1, 3):
+            c = _run(qa, sfa, qb, sfb, kernel=kernel, splits=splits)
+            gemm_tolerance_check(c, ref, "kernel %d splits %d %dx%dx%d" % (kernel, splits, M, N, K))
+    c = _run(qa, sfa, qb, sfb)
+    gemm_tolerance_check(c, ref, "auto")
+
+
+def test_gemm_padded_ldc_and_ld_sfa():
+    M, N, K = 20, 128, 512
+    qa, sfa, qb, sfb = _operands(M, N, K, seed=3)
+    ref = O.gemm_nt(qa, sfa, qb, sfb)
+    sfa_pad = np.zeros((sfa.shape[0], 40), np.uint32)
+    sfa_pad[:, :M] = sfa[:, :M]
+    cbuf = torch.full((M, N + 64), -7.0, dtype=torch.bfloat16, device=DEV)
+    out = F.fp8_block_gemm_nt(to_dev(qa), to_dev(sfa_pad), to_dev(qb), to_dev(sfb), c=cbuf[:, :N])
+    sync()
+    full = to_host(cbuf)
+    gemm_tolerance_check(full[:, :N], ref, "padded ldc")
+    assert np.all(full[:, N:] == 0xC0E0)  # -7.0 canary untouched
+    del out
+
+
+def test_gemm_small_dense_case():
+    """8 x 512 x 512, A ~ N(0,1), B ~ N(0, 0.02), seed 0, automatic launch configuration."""
+    s = W.DENSE_SMALL
+    a, b = W.dense_inputs(s)
+    qa, sfa = O.quant_group_pack(a)
+    qb, sfb = O.block_quant_128x128(b)
+    ref = O.gemm_nt(qa, sfa, qb, sfb)
+    gemm_tolerance_check(_run(qa, sfa, qb, sfb), ref, s.name)
+
+
+def test_gemm_decode_full_and_deterministic():
+    """64 x 7168 x 18432 with 1% x50 outliers in A: every output element, automatic
+    (split-K) configuration; two runs give identical bits."""
+    s = W.DENSE_DECODE
+    a, b = W.dense_inputs(s)
+    qa, sfa = O.quant_group_pack(a)
+    qb, sfb = O.block_quant_128x128(b)
+    ref = O.gemm_nt(qa, sfa, qb, sfb)
+    print("decode cfg", F.gemm_config(False, s.M, s.N, s.K), flush=True)
+    da, dsa, db, dsb = to_dev(qa), to_dev(sfa), to_dev(qb), to_dev(sfb)
+    c1 = F.fp8_block_gemm_nt(da, dsa, db, dsb)
+    c2 = F.fp8_block_gemm_nt(da, dsa, db, dsb)
+    sync()
+    c1, c2 = to_host(c1), to_host(c2)
+    gemm_tolerance_check(c1, ref, s.name)
+    assert np.array_equal(c1, c2)
+    ref_bf16 = O.bf16_rne_array(ref)
+    assert O.calc_diff(W.bf16_bits_to_f32(c1).astype(np.float64), ref) < 1e-5
+    assert np.mean(c1 == ref_bf16) > 0.9
+
+
+@pytest.mark.parametrize("shape", W.DENSE_PREFILL, ids=lambda s: s.name)
+def test_gemm_prefill_sampled_rows(shape):
+    """Prefill sweep at full size in the automatic configuration; the oracle checks
+    24 rows spread over M (every column)."""
+    M, N, K = shape.M, shape.N, shape.K
+    print("prefill", shape.name, F.gemm_config(False, M, N, K), flush=True)
+    qa, sfa, qb, sfb = _operands(M, N, K, seed=0)
+    c = _run(qa, sfa, qb, sfb)
+    rows = np.unique(np.linspace(0, M - 1, 24).astype(np.int64))
+    ref = O.gemm_nt(qa, sfa, qb, sfb, rows=rows)
+    gemm_tolerance_check(c[rows], ref, shape.name)
+
+
+def test_gemm_varied_block_scales_and_outliers():
+    M, N, K = 96, 384, 2048
+    qa, sfa, qb, sfb = _operands(M, N, K, seed=5, outliers=True, b_std=1.0, varied_blocks=True)
+    assert len(np.unique(sfb)) > 5
+    ref = O.gemm_nt(qa, sfa, qb, sfb)
+    gemm_tolerance_check(_run(qa, sfa, qb, sfb), ref, "varied")
+
+
+def test_splitk_workspace_reuse_across_shapes():
+    """Split-K calls of different shapes on one stream share the library workspace; a
+    call with small partials after one with large partials must still find zeroed tile
+    counters (regression: counters used to sit right after the partials)."""
+    big = _operands(64, 2048, 4096, seed=8)
+    small = _operands(96, 384, 2048, seed=9, outliers=True)
+    refs = [O.gemm_nt(*big), O.gemm_nt(*small)]
+    for rep in range(2):
+        for ops, ref, sp in ((big, refs[0], 8), (small, refs[1], 2)):
+            c = _run(*ops, kernel=0 if ops is big else 1, splits=sp)
+            gemm_tolerance_check(c, ref, "reuse rep %d splits %d" % (rep, sp))

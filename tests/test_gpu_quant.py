@@ -1,0 +1,201 @@
+"""GPU parity of the quantization kernels against the CPU oracle.
+
+Quantized bytes and packed scale words must match bit for bit.  For the fused
+SiLU kernel y is computed in fp32 on both sides, but exp differs between the GPU
+math library and the host; an element may differ only where the oracle's y sits
+within a relative 2^-19 of an e4m3 rounding midpoint (or a group amax within
+2^-19 of a 448 * 2^k exponent boundary), and such elements must be rare.
+"""
+import numpy as np
+import pytest
+import torch
+
+import block_scaled_fp8_token_amd as F
+import oracle as O
+import workloads as W
+from gpu_helpers import DEV, sync, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+def _gpu_quant(x_bits, ld_sf, ldx_pad=0):
+    M, K = x_bits.shape
+    if ldx_pad:
+        xp = np.zeros((M, K + ldx_pad), np.uint16)
+        xp[:, :K] = x_bits
+        xd = to_dev(xp)[:, :K]
+    else:
+        xd = to_dev(x_bits)
+    Wd = (K // 128 + 3) // 4
+    sf = torch.full((Wd, ld_sf), 0x5A5A5A5A, dtype=torch.int32, device=DEV)  # canary
+    q, sf = F.fp8_quant_group_pack(xd, sf=sf)
+    sync()
+    return to_host(q), to_host(sf)
+
+
+def test_quant_every_bf16_pattern_under_several_exponents():
+    """Every finite bf16 pattern, 127 to a group next to a planted amax 448 * 2^t."""
+    pats = np.arange(65536, dtype=np.uint32)
+    pats = pats[((pats >> 7) & 0xFF) != 0xFF].astype(np.uint16)  # drop inf/nan
+    per = 127
+    ngroups = (pats.size + per - 1) // per
+    pats = np.concatenate([pats, np.zeros(ngroups * per - pats.size, np.uint16)])
+    rows = []
+    for t in (-45, -20, -9, 0, 5, 30, 100, 119):
+        plant = W.f32_to_bf16_bits(np.array([448.0 * 2.0 ** t], np.float32))[0]
+        g = np.concatenate([pats.reshape(ngroups, per), np.full((ngroups, 1), plant, np.uint16)], axis=1)
+        rows.append(g)
+    allg = np.concatenate(rows)                     # [groups, 128]
+    K = 1024
+    allg = np.concatenate([allg, np.zeros(((-allg.shape[0]) % 8, 128), np.uint16)])
+    x = allg.reshape(-1, K)
+    M = x.shape[0]
+    q_ref, sf_ref = O.quant_group_pack(x, ld_sf=M)
+    q, sf = _gpu_quant(x, ld_sf=M)
+    assert np.array_equal(q, q_ref)
+    assert np.array_equal(sf, sf_ref)
+
+
+@pytest.mark.parametrize("M,K,ldx_pad,ld_sf,outliers", [
+    (1, 128, 0, 4, False),
+    (5, 640, 0, 8, False),          # partial last word (5 groups)
+    (3, 1664, 64, 3, False),        # strided rows, 13 groups
+    (8, 512, 0, 8, False),          # the 8x512 dense case
+    (64, 18432, 0, 64, True),       # decode activations with 1% x50 outliers
+    (300, 2048, 0, 304, False),
+    (1024, 7168, 0, 1024, False),   # prefill activations
+])
+def test_quant_parity(M, K, ldx_pad, ld_sf, outliers):
+    print("quant parity M=%d K=%d" % (M, K), flush=True)
+    if outliers:
+        x = W.normal_bf16_outliers((M, K), seed=0)
+    else:
+        x = W.normal_bf16((M, K), seed=0)
+    q_ref, sf_ref = O.quant_group_pack(x, ld_sf=ld_sf)
+    q, sf = _gpu_quant(x, ld_sf, ldx_pad)
+    assert np.array_equal(q, q_ref)
+    assert np.array_equal(sf[:, :M], sf_ref[:, :M])
+    assert np.all(sf[:, M:] == 0x5A5A5A5A)  # rows past M untouched
+
+
+def test_quant_moe_activation_sampled_rows():
+    """[32*256, 7168] activations (the masked gate_up input): GPU quantizes all rows,
+    the oracle checks 96 spread rows bit for bit."""
+    M, K = 32 * 256, 7168
+    x = W.normal_bf16((M, K), seed=0)
+    q, sf = _gpu_quant(x, ld_sf=M)
+    rows = np.unique(np.concatenate([np.arange(0, M, 97), [M - 1]]))
+    q_ref, sf_ref = O.quant_group_pack(np.ascontiguousarray(x[rows]), ld_sf=len(rows))
+    assert np.array_equal(q[rows], q_ref)
+    assert np.array_equal(sf[:, rows], sf_ref[:, :len(rows)])
+
+
+def test_quant_zero_and_tiny_groups():
+    x = np.zeros((2, 256), np.uint16)
+    x[0, 3] = 0x8000                    # -0
+    x[1, 128:] = 0x0001                 # bf16 subnormals: amax below the 1e-10 floor
+    x[1, 200] = 0x8001
+    q_ref, sf_ref = O.quant_group_pack(x, ld_sf=4)
+    q, sf = _gpu_quant(x, 4)
+    assert np.array_equal(q, q_ref)
+    assert np.array_equal(sf[:, :2], sf_ref[:, :2])
+    assert sf[0, 0] & 0xFF == 85
+
+
+def test_block_quant_weight_ragged():
+    w = W.normal_bf16((200, 384), std=0.02, seed=1, tensor_id=W.T_B)
+    w[37, 300] = W.f32_to_bf16_bits(np.array([5.0], np.float32))[0]
+    q_ref, s_ref = O.block_quant_128x128(w)
+    q, s = F.fp8_block_quant_128x128(to_dev(w))
+    sync()
+    assert np.array_equal(to_host(q), q_ref)
+    assert np.array_equal(to_host(s), s_ref)
+
+
+def test_block_quant_weight_decode_shape_sampled_blocks():
+    N, K = 7168, 18432
+    w = W.normal_bf16((N, K), std=0.02, seed=0, tensor_id=W.T_B)
+    q, s = F.fp8_block_quant_128x128(to_dev(w))
+    sync()
+    q, s = to_host(q), to_host(s)
+    for nb in (0, 27, 55):
+        rows = slice(128 * nb, 128 * nb + 128)
+        q_ref, s_ref = O.block_quant_128x128(np.ascontiguousarray(w[rows]))
+        assert np.array_equal(q[rows], q_ref)
+        assert np.array_equal(s[nb], s_ref[0])
+
+
+# ---------------------------------------------------------------- fused SiLU-mul-quant
+
+def _silu_compare(x, counts, q, sf):
+    E, M_max, H2 = x.shape
+    H = H2 // 2
+    q_ref, sf_ref, y = O.silu_mul_quant_group_pack(x, counts, want_y=True)
+    tab = O.e4m3_table()
+    pos = np.sort(tab[:0x7F])
+    mids = (pos[:-1] + pos[1:]) / 2
+    n_amb = n_el = 0
+    for e in range(E):
+        c = int(min(max(counts[e], 0), M_max))
+        if c == 0:
+            continue
+        n_el += c * H
+        qe, qr = q[e, :c], q_ref[e, :c]
+        se, sr = sf[e, :, :c], sf_ref[e, :, :c]
+        if np.array_equal(qe, qr) and np.array_equal(se, sr):
+            continue
+        G = H // 128
+        for r in range(c):
+            for g in range(G):
+                be = (int(se[g // 4, r]) >> (8 * (g % 4))) & 0xFF
+                br = (int(sr[g // 4, r]) >> (8 * (g % 4))) & 0xFF
+                yg = y[e, r, 128 * g:128 * g + 128]
+                if be != br:
+                    amax = np.max(np.abs(yg)) / 448.0
+                    k = np.round(np.log2(amax))
+                    assert abs(be - br) == 1 and abs(amax / 2.0 ** k - 1) < 2.0 ** -19, (e, r, g)
+                    n_amb += 128
+                    continue
+                d = np.nonzero(qe[r, 128 * g:128 * g + 128] != qr[r, 128 * g:128 * g + 128])[0]
+                for j in d:
+                    v = abs(yg[j]) * 2.0 ** -(br - 127)
+                    m = mids[np.argmin(np.abs(mids - v))]
+                    assert abs(v - m) <= m * 2.0 ** -19, (e, r, g, j, v, m)
+                    a, b = int(qe[r, 128 * g + j]), int(qr[r, 128 * g + j])
+                    assert (a ^ b) & 0x80 == 0 and abs((a & 0x7F) - (b & 0x7F)) == 1
+                    n_amb += 1
+    assert n_amb <= max(8, 1e-4 * n_el), n_amb
+    return n_amb
+
+
+def test_silu_mul_quant_moe_down_input():
+    """[32, 256, 2*2048] bf16 with Zipf(1.1) counts over 4096 tokens (2780 valid rows)."""
+    E, M_max, H = W.MOE_E, W.MOE_M_MAX, W.MOE_DOWN["H"]
+    x = W.normal_bf16((E, M_max, 2 * H), seed=0, tensor_id=W.T_X)
+    counts = W.zipf_counts()
+    qd = torch.full((E, M_max, H), 0xA5, dtype=torch.uint8, device=DEV)
+    sfd = torch.full((E, (H // 128 + 3) // 4, M_max), 0x3C3C3C3C, dtype=torch.int32, device=DEV)
+    q, sf = F.silu_mul_quant_group_pack(to_dev(x), to_dev(counts), q=qd, sf=sfd)
+    sync()
+    q, sf = to_host(q), to_host(sf)
+    _silu_compare(x, counts, q, sf)
+    for e in range(E):  # padded rows untouched
+        assert np.all(q[e, counts[e]:] == 0xA5)
+        assert np.all(sf[e, :, counts[e]:] == 0x3C3C3C3C)
+
+
+def test_silu_mul_quant_edge_counts():
+    E, M_max, H = 5, 12, 640   # H: 5 groups -> partial word
+    x = W.normal_bf16((E, M_max, 2 * H), seed=2, tensor_id=W.T_X)
+    x[1, :, :H] = 0                       # zero gate -> zero groups
+    x[2, 0, 7] = W.f32_to_bf16_bits(np.array([-200.0], np.float32))[0]  # silu underflows
+    counts = np.array([0, 12, 99, -3, 7], np.int32)
+    qd = torch.full((E, M_max, H), 0xA5, dtype=torch.uint8, device=DEV)
+    sfd = torch.full((E, 2, M_max), 0x3C3C3C3C, dtype=torch.int32, device=DEV)
+    q, sf = F.silu_mul_quant_group_pack(to_dev(x), to_dev(counts), q=qd, sf=sfd)
+    sync()
+    q, sf = to_host(q), to_host(sf)
+    _silu_compare(x, counts, q, sf)
+    assert np.all(q[0] == 0xA5) and np.all(q[3] == 0xA5)
+    assert np.all(q[4, 7:] == 0xA5)
+    assert np.all(sf[1, 0, :] & 0xFF == 85)
