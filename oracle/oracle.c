@@ -141,6 +141,7 @@ void orc_quant_group_pack(const uint16_t* x, int64_t ldx, int64_t M, int64_t K,
                           uint8_t* q, int64_t ldq, uint32_t* sf, int64_t ld_sf) {
   init_tables();
   int64_t G = K / 128, W = (G + 3) / 4;
+#pragma omp parallel for schedule(dynamic, 16)
   for (int64_t r = 0; r < M; ++r) {
     for (int64_t w = 0; w < W; ++w) sf[w * ld_sf + r] = 0;
     for (int64_t g = 0; g < G; ++g) {
@@ -176,6 +177,7 @@ void orc_silu_mul_quant_group_pack(const uint16_t* x, const int32_t* masked_m, i
     int64_t c = masked_m[e];
     if (c < 0) c = 0;
     if (c > M_max) c = M_max;
+#pragma omp parallel for schedule(dynamic, 4)
     for (int64_t r = 0; r < c; ++r) {
       const uint16_t* row = x + (e * M_max + r) * 2 * H;
       uint8_t* qrow = q + (e * M_max + r) * H;
@@ -209,6 +211,7 @@ void orc_silu_mul_quant_group_pack(const uint16_t* x, const int32_t* masked_m, i
 void orc_block_quant_128x128(const uint16_t* w, int64_t N, int64_t K, uint8_t* q, float* sfb) {
   init_tables();
   int64_t NB = (N + 127) / 128, KB = K / 128;
+#pragma omp parallel for schedule(dynamic, 1)
   for (int64_t nb = 0; nb < NB; ++nb) {
     int64_t n1 = (nb + 1) * 128 < N ? (nb + 1) * 128 : N;
     for (int64_t kb = 0; kb < KB; ++kb) {
