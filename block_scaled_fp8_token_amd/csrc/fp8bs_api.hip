@@ -42,9 +42,9 @@ int check_device() {
   return it->second ? FP8BS_OK : FP8BS_ERR_DEVICE;
 }
 
-// Split-K workspace: one buffer per (device, stream), grown on demand.  Freshly
-// allocated memory is zeroed on the same stream (the tile counters must start at
-// zero; the GEMM returns every counter it uses to zero).
+// Split-K workspace: one buffer per (device, stream), grown on demand.  It holds
+// only the fp32 partials of the call in flight on that stream, which every split
+// overwrites before the reduction reads them, so it needs no initialisation.
 struct Workspace {
   void* ptr = nullptr;
   size_t bytes = 0;
@@ -83,11 +83,6 @@ int get_workspace(size_t need, hipStream_t stream, void** out) {
   if (e != hipSuccess) {
     g_last_hip_error = (int)e;
     return FP8BS_ERR_ALLOC;
-  }
-  e = hipMemsetAsync(p, 0, sz, stream);
-  if (e != hipSuccess) {
-    (void)hipFree(p);
-    return fail_hip(e);
   }
   w.ptr = p;
   w.bytes = sz;

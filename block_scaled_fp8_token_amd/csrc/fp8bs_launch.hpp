@@ -38,8 +38,8 @@ struct GemmConfig {
 
 GemmConfig choose_gemm_config(const GemmProblem& p);
 size_t gemm_workspace_bytes(const GemmProblem& p, const GemmConfig& cfg);
-// ws: a fixed 64 KiB region of 32-bit tile counters (zero on entry, returned to
-// zero by the kernel) followed by the fp32 split partials.
+// ws: the fp32 split partials [splits][M][N] (gemm_workspace_bytes); a split-K
+// launch runs the GEMM kernel and then the reduction kernel on `stream`.
 hipError_t launch_gemm(const GemmProblem& p, const GemmConfig& cfg, void* ws, hipStream_t stream);
 int gemm_config_count();
 bool gemm_config_by_index(int idx, const GemmProblem& p, int splits, GemmConfig* out);

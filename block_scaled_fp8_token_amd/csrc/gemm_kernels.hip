@@ -25,6 +25,8 @@
 // past the mask issue no MFMA.  Decode-sized M splits K across workgroups; the
 // last workgroup of a tile to finish sums the fp32 partials in split order
 // (deterministic) and writes bf16.
+#include <atomic>
+
 #include "fp8bs_device.hpp"
 #include "fp8bs_launch.hpp"
 
@@ -33,6 +35,25 @@ namespace fp8bs {
 namespace {
 
 constexpr int LDS_ROW = 144;  // 128 data bytes + 16 pad bytes per row of a K-block tile
+constexpr uint32_t kOOB = 0x80000000u;  // buffer offset past every descriptor range: loads return 0
+
+// Raw buffer resource over [base, base + bytes); gfx9 descriptor word 3 (raw, 32-bit format).
+// The fields are passed through readfirstlane: they are wave-uniform, and saying so
+// keeps the compiler from wrapping every load in a per-lane descriptor loop.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  void* u = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(u, (short)0, (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000);
+}
+__device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+  return make_uint4((uint32_t)v[0], (uint32_t)v[1], (uint32_t)v[2], (uint32_t)v[3]);
+}
+__device__ __forceinline__ uint32_t bload4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
+}
 
 struct KArgs {
   const uint8_t* a;
@@ -44,8 +65,8 @@ struct KArgs {
   int64_t M, N, K, ld_sfa, ldc;
   int64_t sa_e, ssfa_e, sb_e, ssfb_e, sc_e;  // per-group strides (elements)
   int tiles_m, tiles_n, splits, kb_per_split;
-  float* ws;
-  uint32_t* counters;
+  int sa_words;  // activation-scale words per row a split can touch (LDS table height)
+  float* ws;  // split-K partials [splits][M][N]
 };
 
 __device__ __forceinline__ v8i frag(const uint8_t* p) {
@@ -57,6 +78,89 @@ __device__ __forceinline__ v8i frag(const uint8_t* p) {
   return r;
 }
 
+// Epilogue shared by the kernels.  Lane l holds, for sub-tile (i, j), output row
+// row0 + 16i + (l & 15) and the four columns col0 + 16j + 4(l >> 4) + 0..3.
+// Without a K split the values go straight to bf16.  With a split every workgroup
+// stores its fp32 partial to the workspace and splitk_reduce_kernel finishes.
+template <int SM, int SN>
+__device__ __forceinline__ void store_tile(const float (&acc)[SM][SN][4], const KArgs& p, uint16_t* __restrict__ C,
+                                           int64_t row0, int64_t col0, int64_t m_limit, int split, int tile,
+                                           int lane, int tid) {
+  if (p.splits == 1) {
+#pragma unroll
+    for (int i = 0; i < SM; ++i) {
+      const int64_t m = row0 + 16 * i + (lane & 15);
+      if (m >= m_limit) continue;
+#pragma unroll
+      for (int j = 0; j < SN; ++j) {
+        const int64_t n = col0 + 16 * j + 4 * (lane >> 4);
+        if (n < p.N) {
+          uint2 o;
+          o.x = bf16_rne(acc[i][j][0]) | (bf16_rne(acc[i][j][1]) << 16);
+          o.y = bf16_rne(acc[i][j][2]) | (bf16_rne(acc[i][j][3]) << 16);
+          *reinterpret_cast<uint2*>(C + m * p.ldc + n) = o;
+        }
+      }
+    }
+    return;
+  }
+  // Split K: publish this split's scaled fp32 partial; a second kernel on the same
+  // stream adds the partials in split order and writes bf16 (the kernel boundary
+  // makes the partials visible, so no fence, atomic or counter is needed here).
+  const size_t slice = (size_t)p.M * (size_t)p.N;
+  float* __restrict__ ws = p.ws;
+#pragma unroll
+  for (int i = 0; i < SM; ++i) {
+    const int64_t m = row0 + 16 * i + (lane & 15);
+    if (m >= m_limit) continue;
+#pragma unroll
+    for (int j = 0; j < SN; ++j) {
+      const int64_t n = col0 + 16 * j + 4 * (lane >> 4);
+      if (n < p.N)
+        *reinterpret_cast<float4*>(ws + (size_t)split * slice + (size_t)m * p.N + n) =
+            make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
+    }
+  }
+  (void)tile;
+  (void)tid;
+}
+
+// Split-K reduction: thread t owns 8 consecutive columns of one row, adds the
+// partials of every split in split order (deterministic), and stores 8 bf16.
+// The loads of four splits are issued before any is added.
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ ws, int splits, int64_t M,
+                                                            int64_t N, uint16_t* __restrict__ C, int64_t ldc) {
+  const int64_t per_row = N / 8;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= M * per_row) return;
+  const int64_t m = idx / per_row, n = (idx - m * per_row) * 8;
+  const size_t slice = (size_t)M * (size_t)N;
+  const float* src = ws + (size_t)m * N + n;
+  float t[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int sp0 = 0; sp0 < splits; sp0 += 4) {
+    float4 v[4][2];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int sp = (sp0 + u < splits) ? sp0 + u : sp0;
+      v[u][0] = *reinterpret_cast<const float4*>(src + (size_t)sp * slice);
+      v[u][1] = *reinterpret_cast<const float4*>(src + (size_t)sp * slice + 4);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (sp0 + u < splits) {
+        t[0] += v[u][0].x; t[1] += v[u][0].y; t[2] += v[u][0].z; t[3] += v[u][0].w;
+        t[4] += v[u][1].x; t[5] += v[u][1].y; t[6] += v[u][1].z; t[7] += v[u][1].w;
+      }
+    }
+  }
+  uint4 o;
+  o.x = bf16_rne(t[0]) | (bf16_rne(t[1]) << 16);
+  o.y = bf16_rne(t[2]) | (bf16_rne(t[3]) << 16);
+  o.z = bf16_rne(t[4]) | (bf16_rne(t[5]) << 16);
+  o.w = bf16_rne(t[6]) | (bf16_rne(t[7]) << 16);
+  *reinterpret_cast<uint4*>(C + m * ldc + n) = o;
+}
+
 template <int BM, int BN, int WM, int WN>
 __global__ __launch_bounds__(256) void gemm_kernel(const KArgs p) {
   constexpr int NWN = BN / WN;
@@ -66,7 +170,8 @@ __global__ __launch_bounds__(256) void gemm_kernel(const KArgs p) {
   static_assert((BM * 8) % 256 == 0 && (BN * 8) % 256 == 0, "tile rows must fill the loaders");
   __shared__ __attribute__((aligned(16))) uint8_t lds[2][(BM + BN) * LDS_ROW];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wavefront
   const int wm = wave / NWN, wn = wave % NWN;
   const int64_t e = blockIdx.z;
   const int split = blockIdx.y;
@@ -184,75 +289,174 @@ __global__ __launch_bounds__(256) void gemm_kernel(const KArgs p) {
     buf ^= 1;
   }
 
-  if (p.splits == 1) {
+  store_tile<SM, SN>(acc, p, C, wrow0, n0 + wn * WN, m_limit, split, tile, lane, tid);
+}
+
+// ---------------------------------------------------------------------------
+// Weight-streaming kernel for few rows per group (decode-sized M, masked MoE
+// experts).  Every weight byte is used by exactly one wavefront, so B skips LDS:
+// each lane loads its MFMA operand bytes straight from global memory into
+// registers, DEPTH K-blocks ahead of use (a register ring), which keeps enough
+// bytes in flight to stream HBM.  The few activation rows are shared by the four
+// wavefronts through an LDS double buffer, fed from the same ring.  Wavefront w
+// owns WSN 16-column sub-tiles; all MS 16-row sub-tiles of the tile are computed
+// by every wavefront (sub-tiles past the mask are skipped).
+//
+// All global loads are buffer loads whose descriptor covers exactly the valid
+// rows of the tile (and of the wavefront's columns): rows past the mask, columns
+// past N and K-blocks past the split are given an offset outside the range, so
+// the hardware returns zeros without touching memory and without a branch.  With
+// no divergent branches around loads, the compiler's wait counts track the ring
+// exactly instead of draining it.  The activation-scale words and weight block
+// scales a workgroup needs for its K range are copied into LDS once, up front.
+//
+// Operand byte order: lane l carries bytes [16(l>>4), +16) and [64 + 16(l>>4), +16)
+// of its row's K-block, for A and B alike (the MFMA pairs A and B bytes by
+// position, so any order shared by both operands gives the same dot product);
+// each 16-lane row of a load then touches 64 contiguous bytes of one matrix row.
+template <int MS, int WSN, int DEPTH>
+__global__ __launch_bounds__(256) void stream_kernel(const KArgs p) {
+  constexpr int BM = MS * 16, BN = 4 * WSN * 16;
+  constexpr int ACH = BM * 8;                 // 16-byte chunks in one A K-block tile
+  constexpr int CA = (ACH + 255) / 256;       // chunks per thread
+  constexpr int NBW = (BN + 127) / 128;       // weight-scale blocks a tile can span
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wavefront
+  const int64_t e = blockIdx.z;
+  const int split = blockIdx.y;
+  const int tile = blockIdx.x;
+  const int tm = tile / p.tiles_n, tn = tile - tm * p.tiles_n;
+
+  int64_t m_limit = p.M;
+  if (p.masked_m) {
+    const int64_t cnt = p.masked_m[e];
+    m_limit = cnt < 0 ? 0 : (cnt > p.M ? p.M : cnt);
+  }
+  const int64_t m0 = (int64_t)tm * BM;
+  if (m0 >= m_limit) return;  // whole tile past the mask: no loads, no MFMA
+  const int64_t n0 = (int64_t)tn * BN;
+  const int64_t nw0 = n0 + wave * (WSN * 16);  // this wavefront's first column
+
+  const int KB = (int)(p.K / 128);
+  const int per = p.kb_per_split;
+  const int kb0 = split * per;
+  const int kb1 = (kb0 + per < KB) ? kb0 + per : KB;
+  const int w0 = kb0 >> 2;
+  const int nwords = (kb1 > kb0) ? ((kb1 - 1) >> 2) - w0 + 1 : 0;
+  const int nb0 = (int)(n0 >> 7);
+  const int NB = (int)((p.N + 127) / 128);
+  const int Wd = (KB + 3) / 4;
+
+  uint8_t* lds_a = smem;                                              // [2][BM * LDS_ROW]
+  uint32_t* lds_sa = reinterpret_cast<uint32_t*>(smem + 2 * BM * LDS_ROW);  // [sa_words][BM]
+  float* lds_sb = reinterpret_cast<float*>(lds_sa + p.sa_words * BM);       // [NBW][per]
+
+  const int64_t rows_valid = (m_limit - m0 < BM) ? m_limit - m0 : BM;
+  int64_t cols_valid = p.N - nw0;
+  cols_valid = cols_valid < 0 ? 0 : (cols_valid > WSN * 16 ? WSN * 16 : cols_valid);
+  const auto rA = make_rsrc(p.a + e * p.sa_e + m0 * p.K, (uint32_t)(rows_valid * p.K));
+  const auto rB = make_rsrc(p.b + e * p.sb_e + (cols_valid > 0 ? nw0 : 0) * p.K, (uint32_t)(cols_valid * p.K));
+  const auto rSA = make_rsrc(p.sfa + e * p.ssfa_e, (uint32_t)(Wd * p.ld_sfa * 4));
+  const auto rSB = make_rsrc(p.sfb + e * p.ssfb_e, (uint32_t)(NB * KB * 4));
+  uint16_t* __restrict__ C = p.c + e * p.sc_e;
+
+  uint4 ar[DEPTH][CA];
+  v8i br[DEPTH][WSN];
+  auto issue = [&](int d, int kb) {
+    const bool in = kb < kb1;
 #pragma unroll
-    for (int i = 0; i < SM; ++i) {
-      const int64_t m = wrow0 + 16 * i + (lane & 15);
-      if (m >= m_limit) continue;
+    for (int c = 0; c < CA; ++c) {
+      const int cidx = tid + 256 * c;
+      const uint32_t off = (in && cidx < ACH) ? (uint32_t)((cidx >> 3) * p.K + kb * 128 + (cidx & 7) * 16) : kOOB;
+      ar[d][c] = bload16(rA, off);
+    }
 #pragma unroll
-      for (int j = 0; j < SN; ++j) {
-        const int64_t n = n0 + wn * WN + 16 * j + 4 * (lane >> 4);
-        if (n < p.N) {
-          uint2 o;
-          o.x = bf16_rne(acc[i][j][0]) | (bf16_rne(acc[i][j][1]) << 16);
-          o.y = bf16_rne(acc[i][j][2]) | (bf16_rne(acc[i][j][3]) << 16);
-          *reinterpret_cast<uint2*>(C + m * p.ldc + n) = o;
+    for (int j = 0; j < WSN; ++j) {
+      const uint32_t off = in ? (uint32_t)((16 * j + (lane & 15)) * p.K + kb * 128 + (lane >> 4) * 16) : kOOB;
+      const uint4 lo = bload16(rB, off);
+      const uint4 hi = bload16(rB, off + 64);
+      br[d][j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    }
+  };
+  auto astore = [&](int d, int stage) {
+#pragma unroll
+    for (int c = 0; c < CA; ++c) {
+      const int cidx = tid + 256 * c;
+      if (cidx < ACH)
+        *reinterpret_cast<uint4*>(&lds_a[stage * BM * LDS_ROW + (cidx >> 3) * LDS_ROW + (cidx & 7) * 16]) = ar[d][c];
+    }
+  };
+
+  // prologue: fill the ring, then the scale tables (one latency for both)
+#pragma unroll
+  for (int d = 0; d < DEPTH; ++d) issue(d, kb0 + d);
+  for (int idx = tid; idx < nwords * BM; idx += 256) {
+    const int wl = idx / BM, row = idx - wl * BM;
+    const int64_t m = m0 + row;
+    const uint32_t off = (m < m_limit) ? (uint32_t)(((int64_t)(w0 + wl) * p.ld_sfa + m) * 4) : kOOB;
+    lds_sa[wl * BM + row] = bload4(rSA, off);
+  }
+  for (int idx = tid; idx < NBW * per; idx += 256) {
+    const int b = idx / per, kk = idx - b * per;
+    const int k = kb0 + kk, nb = nb0 + b;
+    const uint32_t off = (k < kb1 && nb < NB) ? (uint32_t)((nb * KB + k) * 4) : kOOB;
+    lds_sb[b * per + kk] = __uint_as_float(bload4(rSB, off));
+  }
+  astore(0, 0);
+  __syncthreads();
+
+  float acc[MS][WSN][4];
+#pragma unroll
+  for (int i = 0; i < MS; ++i)
+#pragma unroll
+    for (int j = 0; j < WSN; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[i][j][r] = 0.0f;
+
+  // Straight-line body: whole groups of DEPTH K-blocks.  Steps past kb1 multiply
+  // zeros (their loads were out of range) and get a zero scale, so they add nothing.
+  const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int kb = kb0; kb < kb1; kb += DEPTH) {
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) {
+      const int k = kb + d;
+      const bool live = k < kb1;
+      const int kk = live ? k - kb0 : 0;
+      const int stage = (k - kb0) & 1;
+      const uint8_t* As = lds_a + stage * BM * LDS_ROW;
+      float sb[WSN];
+#pragma unroll
+      for (int j = 0; j < WSN; ++j) {
+        const float v = lds_sb[(int)(((nw0 + 16 * j) >> 7) - nb0) * per + kk];
+        sb[j] = live ? v : 0.0f;
+      }
+      const uint32_t* saw = lds_sa + (((kb0 + kk) >> 2) - w0) * BM + (lane & 15);
+      const int sh = 8 * ((kb0 + kk) & 3);
+#pragma unroll
+      for (int i = 0; i < MS; ++i) {
+        const uint8_t* pa = As + (16 * i + (lane & 15)) * LDS_ROW + (lane >> 4) * 16;
+        const uint4 lo = *reinterpret_cast<const uint4*>(pa);
+        const uint4 hi = *reinterpret_cast<const uint4*>(pa + 64);
+        const v8i af = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        const float sa = __uint_as_float(((saw[16 * i] >> sh) & 0xFFu) << 23);
+#pragma unroll
+        for (int j = 0; j < WSN; ++j) {
+          const v4f r = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(br[d][j], af, zero, 0, 0, 0, 0, 0, 0);
+          const float sc = sa * sb[j];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) acc[i][j][q] = __builtin_fmaf(r[q], sc, acc[i][j][q]);
         }
       }
+      // stage the next K-block's activations, then refill this ring slot
+      astore((d + 1) % DEPTH, stage ^ 1);
+      issue(d, k + DEPTH);
+      __syncthreads();
     }
-    return;
   }
 
-  // split-K: publish this split's scaled partial, then the last arriver reduces
-  const size_t slice = (size_t)p.M * (size_t)p.N;
-  float* __restrict__ ws = p.ws;
-#pragma unroll
-  for (int i = 0; i < SM; ++i) {
-    const int64_t m = wrow0 + 16 * i + (lane & 15);
-    if (m >= m_limit) continue;
-#pragma unroll
-    for (int j = 0; j < SN; ++j) {
-      const int64_t n = n0 + wn * WN + 16 * j + 4 * (lane >> 4);
-      if (n < p.N)
-        *reinterpret_cast<float4*>(ws + (size_t)split * slice + (size_t)m * p.N + n) =
-            make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
-    }
-  }
-  __threadfence();
-  __syncthreads();
-  __shared__ int is_last;
-  if (tid == 0) {
-    const unsigned old = atomicAdd(&p.counters[tile], 1u);
-    is_last = (old == (unsigned)(p.splits - 1)) ? 1 : 0;
-  }
-  __syncthreads();
-  if (!is_last) return;
-  __threadfence();
-#pragma unroll
-  for (int i = 0; i < SM; ++i) {
-    const int64_t m = wrow0 + 16 * i + (lane & 15);
-    if (m >= m_limit) continue;
-#pragma unroll
-    for (int j = 0; j < SN; ++j) {
-      const int64_t n = n0 + wn * WN + 16 * j + 4 * (lane >> 4);
-      if (n >= p.N) continue;
-      float s0 = 0.0f, s1 = 0.0f, s2 = 0.0f, s3 = 0.0f;
-      for (int sp = 0; sp < p.splits; ++sp) {
-        float4 v;
-        if (sp == split) {
-          v = make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
-        } else {
-          v = *reinterpret_cast<const float4*>(ws + (size_t)sp * slice + (size_t)m * p.N + n);
-        }
-        s0 += v.x; s1 += v.y; s2 += v.z; s3 += v.w;
-      }
-      uint2 o;
-      o.x = bf16_rne(s0) | (bf16_rne(s1) << 16);
-      o.y = bf16_rne(s2) | (bf16_rne(s3) << 16);
-      *reinterpret_cast<uint2*>(C + m * p.ldc + n) = o;
-    }
-  }
-  if (tid == 0) p.counters[tile] = 0u;  // ready for the next call on this workspace
+  store_tile<MS, WSN>(acc, p, C, m0, nw0, m_limit, split, tile, lane, tid);
 }
 
 // ---------------------------------------------------------------------------
@@ -263,24 +467,35 @@ typedef void (*KernelFn)(const KArgs);
 struct TileEntry {
   KernelFn fn;
   int bm, bn;
+  bool stream;  // weight-streaming family (dynamic LDS: A stages + scale tables)
 };
 
+// 0-3: LDS-tiled kernels (both operands staged through LDS); 4+: weight-streaming.
 const TileEntry kTiles[] = {
-    {gemm_kernel<64, 128, 64, 32>, 64, 128},
-    {gemm_kernel<128, 128, 64, 64>, 128, 128},
-    {gemm_kernel<64, 256, 64, 64>, 64, 256},
-    {gemm_kernel<128, 256, 64, 128>, 128, 256},
+    {gemm_kernel<64, 128, 64, 32>, 64, 128, false},
+    {gemm_kernel<128, 128, 64, 64>, 128, 128, false},
+    {gemm_kernel<64, 256, 64, 64>, 64, 256, false},
+    {gemm_kernel<128, 256, 64, 128>, 128, 256, false},
+    {stream_kernel<4, 2, 4>, 64, 128, true},
+    {stream_kernel<4, 1, 4>, 64, 64, true},
+    {stream_kernel<1, 2, 4>, 16, 128, true},
+    {stream_kernel<2, 2, 4>, 32, 128, true},
+    {stream_kernel<4, 1, 8>, 64, 64, true},
+    {stream_kernel<4, 2, 6>, 64, 128, true},
 };
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Workspace layout: a fixed region of tile counters at offset 0 (only ever written
-// by the split-K protocol, which leaves every counter at zero), then the fp32
-// partials.  Keeping the counters at a fixed place means a later call with other
-// shapes never finds partial data where it expects a zero counter.
-constexpr size_t kCounterBytes = 64 * 1024;
-constexpr int64_t kMaxSplitTiles = (int64_t)(kCounterBytes / sizeof(uint32_t));
+constexpr size_t kMaxLds = 160 * 1024 - 1024;  // gfx950 LDS per workgroup, less room for static LDS
+
+// Dynamic LDS of a weight-streaming launch: two A stages, the activation-scale
+// word table [sa_words][bm] and the weight-scale table [ceil(bn/128)][per].
+inline size_t stream_lds_bytes(int bm, int bn, int per) {
+  const int sa_words = (per + 3) / 4 + 1;
+  return (size_t)2 * bm * LDS_ROW + (size_t)sa_words * bm * 4 + (size_t)((bn + 127) / 128) * per * 4;
+}
+
 
 }  // namespace
 
@@ -291,7 +506,13 @@ bool gemm_config_by_index(int idx, const GemmProblem& p, int splits, GemmConfig*
   const int KB = (int)(p.K / 128);
   if (splits > KB) splits = KB > 0 ? KB : 1;
   if (p.masked_m && splits != 1) return false;
-  if (splits > 1 && cdiv(p.M, kTiles[idx].bm) * cdiv(p.N, kTiles[idx].bn) > kMaxSplitTiles) splits = 1;
+  if (kTiles[idx].stream) {
+    // split K further if the scale tables would not fit next to the A stages
+    while (splits < KB && stream_lds_bytes(kTiles[idx].bm, kTiles[idx].bn, (int)cdiv(KB, splits)) > kMaxLds) {
+      if (p.masked_m) return false;
+      ++splits;
+    }
+  }
   out->kernel = idx;
   out->bm = kTiles[idx].bm;
   out->bn = kTiles[idx].bn;
@@ -306,10 +527,22 @@ GemmConfig choose_gemm_config(const GemmProblem& p) {
   GemmConfig cfg;
   const int KB = (int)(p.K / 128);
   if (p.masked_m) {
-    gemm_config_by_index(0, p, 1, &cfg);
+    // weight streaming, 64-row M tiles: tiles past an expert's count exit at once
+    gemm_config_by_index(4, p, 1, &cfg);
     return cfg;
   }
-  const int idx = (p.M <= 64) ? 0 : 1;
+  if (p.M <= 64) {
+    // decode: weight streaming over 128-column tiles, K split until about 224 workgroups
+    const int idx = 4;
+    const int64_t tiles = cdiv(p.N, kTiles[idx].bn);
+    int splits = (int)(224 / (tiles > 0 ? tiles : 1));
+    const int max_splits = KB / 8 > 1 ? KB / 8 : 1;
+    if (splits > max_splits) splits = max_splits;
+    if (splits < 1) splits = 1;
+    gemm_config_by_index(idx, p, splits, &cfg);
+    return cfg;
+  }
+  const int idx = 1;
   const int64_t tiles = cdiv(p.M, kTiles[idx].bm) * cdiv(p.N, kTiles[idx].bn);
   int splits = 1;
   if (tiles < 256) {
@@ -324,8 +557,7 @@ GemmConfig choose_gemm_config(const GemmProblem& p) {
 
 size_t gemm_workspace_bytes(const GemmProblem& p, const GemmConfig& cfg) {
   if (cfg.splits <= 1) return 0;
-  const size_t part = (size_t)cfg.splits * (size_t)p.M * (size_t)p.N * sizeof(float);
-  return kCounterBytes + part;
+  return (size_t)cfg.splits * (size_t)p.M * (size_t)p.N * sizeof(float);
 }
 
 hipError_t launch_gemm(const GemmProblem& p, const GemmConfig& cfg, void* ws, hipStream_t stream) {
@@ -342,15 +574,34 @@ hipError_t launch_gemm(const GemmProblem& p, const GemmConfig& cfg, void* ws, hi
   k.kb_per_split = cfg.kb_per_split;
   if ((int64_t)cfg.kb_per_split * (cfg.splits - 1) >= KB) return hipErrorInvalidValue;
   k.ws = nullptr;
-  k.counters = nullptr;
   if (cfg.splits > 1) {
-    if ((int64_t)k.tiles_m * k.tiles_n > kMaxSplitTiles || ws == nullptr) return hipErrorInvalidValue;
-    k.counters = static_cast<uint32_t*>(ws);
-    k.ws = reinterpret_cast<float*>(static_cast<char*>(ws) + kCounterBytes);
+    if (ws == nullptr) return hipErrorInvalidValue;
+    k.ws = static_cast<float*>(ws);
   }
+  k.sa_words = (cfg.kb_per_split + 3) / 4 + 1;
   const int64_t tiles = (int64_t)k.tiles_m * k.tiles_n;
   if (tiles < 1 || p.E < 1 || KB < 1) return hipSuccess;
-  hipLaunchKernelGGL(t.fn, dim3((unsigned)tiles, (unsigned)cfg.splits, (unsigned)p.E), dim3(256), 0, stream, k);
+  size_t dyn = 0;
+  if (t.stream) {
+    dyn = stream_lds_bytes(t.bm, t.bn, cfg.kb_per_split);
+    if (dyn > kMaxLds) return hipErrorInvalidValue;
+    // raise the kernel's dynamic-LDS limit to what this launch needs (never lowered)
+    static std::atomic<int> attr_bytes[kNumTiles];
+    if ((int)dyn > attr_bytes[cfg.kernel].load()) {
+      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(t.fn),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
+      if (e != hipSuccess) return e;
+      int cur = attr_bytes[cfg.kernel].load();
+      while ((int)dyn > cur && !attr_bytes[cfg.kernel].compare_exchange_weak(cur, (int)dyn)) {
+      }
+    }
+  }
+  hipLaunchKernelGGL(t.fn, dim3((unsigned)tiles, (unsigned)cfg.splits, (unsigned)p.E), dim3(256), dyn, stream, k);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || cfg.splits == 1) return e;
+  const int64_t threads = p.M * (p.N / 8);
+  hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)cdiv(threads, 256)), dim3(256), 0, stream,
+                     static_cast<const float*>(ws), cfg.splits, p.M, p.N, p.c, p.ldc);
   return hipGetLastError();
 }
 
