@@ -113,20 +113,23 @@ def n_copies_for(bytes_per_copy, cache_bytes=256 << 20, floor=1):
 # ----------------------------------------------------------------------------- timing
 
 def kernel_times(stream, launches, steps):
-    """Average GPU duration of each launch in a step, from HIP events recorded on the
-    launch stream around every launch.  A spin kernel first keeps the GPU busy while
-    the host enqueues, so the events bracket back-to-back kernels, not host gaps."""
-    n = len(launches)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(n + 1)] for _ in range(steps)]
-    with torch.cuda.stream(stream):
-        torch.cuda._sleep(int(2e7))
-        for s in range(steps):
-            ev[s][0].record(stream)
-            for j, fn in enumerate(launches):
+    """Average GPU duration of each launch type, in ms: `steps` back-to-back calls of
+    one launch between two HIP events recorded on the launch stream (a spin kernel
+    first keeps the GPU busy while the host enqueues, so the calls run back to back
+    and the per-event cost is spread over the batch)."""
+    out = []
+    for fn in launches:
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
+            torch.cuda._sleep(int(2e7))
+            e0.record(stream)
+            for s in range(steps):
                 fn(s)
-                ev[s][j + 1].record(stream)
-    stream.synchronize()
-    return [float(np.mean([ev[s][j].elapsed_time(ev[s][j + 1]) for s in range(steps)])) for j in range(n)]
+            e1.record(stream)
+        stream.synchronize()
+        out.append(e0.elapsed_time(e1) / steps)
+    return out
 
 
 def graph_step_time(stream, step_fn, n_variants, steps, warmup):
@@ -311,6 +314,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic_decode_gemm.json"),
                     help="HBM traffic per GEMM launch measured with rocprofv3 counters")
+    ap.add_argument("--counters", action="store_true",
+                    help="workload for rocprofv3 --pmc passes: a 256 MiB torch copy (counter calibration), "
+                         "then --steps eager decode steps; no timing")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -326,6 +332,9 @@ def main():
     torch.cuda.set_device(0)
     stream = torch.cuda.Stream()
     shape = W.DENSE_DECODE
+    if args.counters:
+        counters_workload(F, shape, args.steps)
+        return
     r = bench_dense(F, stream, shape, args.steps, args.warmup)
     print("[bench] %s" % json.dumps(r), file=sys.stderr, flush=True)
 
@@ -388,6 +397,23 @@ def main():
                 for x in rows:
                     f.write(json.dumps(x) + "\n")
     print(json.dumps(line), flush=True)
+
+
+def counters_workload(F, shape, steps):
+    """Kernels for the counter passes: three copies of 256 MiB (a plain copy kernel of
+    known size, to calibrate FETCH_SIZE / WRITE_SIZE), then eager decode steps."""
+    x = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+    y = torch.empty_like(x)
+    for _ in range(3):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    a, copies, qa, sfa, c = setup_dense(F, shape.M, shape.N, shape.K, shape.outliers)
+    for i in range(steps):
+        F.fp8_quant_group_pack(a, q=qa, sf=sfa)
+        qb, sfb = copies[i % len(copies)]
+        F.fp8_block_gemm_nt(qa, sfa, qb, sfb, c=c)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_each_way": 256 << 20, "steps": steps, "config": F.gemm_config(False, shape.M, shape.N, shape.K)}))
 
 
 def _kernel_hash():

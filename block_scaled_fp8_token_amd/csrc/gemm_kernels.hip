@@ -460,28 +460,272 @@ __global__ __launch_bounds__(256) void stream_kernel(const KArgs p) {
 }
 
 // ---------------------------------------------------------------------------
+// Scaled-MFMA tile kernel (prefill-sized M).
+//
+// gfx950's v_mfma_scale_f32_16x16x128_f8f6f4 computes C + 2^(ea + eb) * sum(a*b)
+// with E8M0 exponents ea, eb taken from a byte of a scale register (selected by an
+// immediate), which is exactly the per-K-block scale-then-accumulate of the
+// method: one instruction covers one 128-wide K-block, the packed activation word
+// (four groups per uint32) is the scale register of the activation operand with
+// the byte picked by kb % 4, and the weight block's exponent (the UE8M0 value of
+// its power-of-two scale) is the other.  The fp32 accumulator therefore stays in
+// the MFMA C operand and no VALU work is spent on scales.
+//
+// Tiles move global -> LDS by LDS-DMA (buffer loads with the lds flag): each
+// wavefront instruction writes 1 KiB = 8 rows of a K-block tile, lane l to byte
+// 16 l, so the tile is stored row-major without padding and the 16-byte chunks of
+// row r are XOR-swizzled (chunk c in slot c ^ swz(r)) for conflict-free operand
+// reads.  STAGES LDS buffers form a ring; the loads for K-block kb + STAGES - 1
+// are issued right after the barrier of step kb.  Rows past M (or past an
+// expert's count) and K-blocks past the range fall outside the buffer
+// descriptors and arrive as zeros.  Workgroups are mapped to tiles XCD by XCD
+// (a workgroup's XCD is its linear id mod 8), each XCD taking a compact block of
+// tiles so that its L2 serves the shared A and B panels.
+__device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
+
+template <int V>
+struct IntC {
+  static constexpr int value = V;
+};
+
+template <int BM, int BN, int WGM, int WGN, int STAGES>
+__global__ __launch_bounds__(256) void scaled_tile_kernel(const KArgs p) {
+  constexpr int WM = BM / WGM, WN = BN / WGN;
+  constexpr int SM = WM / 16, SN = WN / 16;
+  constexpr int A_INST = BM / 8, B_INST = BN / 8;          // 1 KiB DMA instructions per stage
+  constexpr int IPW = (A_INST + B_INST) / 4;               // per wavefront
+  constexpr int STAGE = (BM + BN) * 128;
+  static_assert(WGM * WGN == 4 && (A_INST + B_INST) % 4 == 0, "tile shape");
+  static_assert(STAGES == 2 || STAGES == 4, "the ring period must divide the 4-step unroll");
+  // One LDS array per ring stage, indexed with compile-time stage numbers, so the
+  // compiler can tell operand reads of one stage from DMA writes into another and
+  // does not make every read wait for all loads in flight.
+  __shared__ __attribute__((aligned(1024))) uint8_t st0[STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t st1[STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t st2[STAGES > 2 ? STAGE : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t st3[STAGES > 2 ? STAGE : 16];
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];  // scale tables
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WGN, wn = wave % WGN;
+  const int64_t e = blockIdx.z;
+
+  // XCD-aware tile order: workgroup id -> (XCD, slot) -> a compact run of tiles per
+  // XCD, walked in groups of GM tile rows.
+  const int T = p.tiles_m * p.tiles_n;
+  const int bid = blockIdx.x;
+  const int per_xcd = (T + 7) / 8;
+  int lin = (bid & 7) * per_xcd + (bid >> 3);
+  if ((T & 7) != 0) lin = bid;  // uneven split: plain order
+  constexpr int GM = 4;
+  const int group = lin / (GM * p.tiles_n);
+  const int first_m = group * GM;
+  const int gsz = (p.tiles_m - first_m) < GM ? (p.tiles_m - first_m) : GM;
+  const int in_g = lin - group * GM * p.tiles_n;
+  const int tm = first_m + in_g % gsz, tn = in_g / gsz;
+
+  int64_t m_limit = p.M;
+  if (p.masked_m) {
+    const int64_t cnt = p.masked_m[e];
+    m_limit = cnt < 0 ? 0 : (cnt > p.M ? p.M : cnt);
+  }
+  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+  if (m0 >= m_limit) return;
+
+  const int KB = (int)(p.K / 128);
+  const int Wd = (KB + 3) / 4;
+  const int NB = (int)((p.N + 127) / 128);
+  constexpr int NBT = (BN + 127) / 128;
+  uint32_t* lds_sa = reinterpret_cast<uint32_t*>(smem);  // [Wd][BM] activation words
+  uint32_t* lds_sb = lds_sa + Wd * BM;                  // [NBT][Wd] packed weight exponents
+
+  const int64_t rows_valid = (m_limit - m0 < BM) ? m_limit - m0 : BM;
+  int64_t cols_valid = p.N - n0;
+  cols_valid = cols_valid > BN ? BN : cols_valid;
+  const auto rA = make_rsrc(p.a + e * p.sa_e + m0 * p.K, (uint32_t)(rows_valid * p.K));
+  const auto rB = make_rsrc(p.b + e * p.sb_e + n0 * p.K, (uint32_t)(cols_valid * p.K));
+  const auto rSA = make_rsrc(p.sfa + e * p.ssfa_e, (uint32_t)(Wd * p.ld_sfa * 4));
+  const auto rSB = make_rsrc(p.sfb + e * p.ssfb_e, (uint32_t)(NB * KB * 4));
+
+  auto stage_ptr = [&](auto st_tag) -> uint8_t* {
+    constexpr int S = decltype(st_tag)::value;
+    if constexpr (S == 0) return st0;
+    else if constexpr (S == 1) return st1;
+    else if constexpr (S == 2) return st2;
+    else return st3;
+  };
+  // DMA of K-block kb into a stage: instruction t of wavefront w covers rows
+  // 8*i..8*i+7 of A (i < A_INST) or of B (i - A_INST), lane l -> row 8i + l/8,
+  // LDS slot l % 8 holding chunk (l % 8) ^ swz(row).
+  auto issue = [&](int kb, auto st_tag) {
+    uint8_t* base = stage_ptr(st_tag);
+#pragma unroll
+    for (int t = 0; t < IPW; ++t) {
+      const int inst = wave * IPW + t;
+      const bool isA = inst < A_INST;
+      const int ri = isA ? inst : inst - A_INST;
+      const int r = ri * 8 + (lane >> 3);
+      const int chunk = (lane & 7) ^ swz(r);
+      const uint32_t off = (kb < KB) ? (uint32_t)(r * p.K + kb * 128 + chunk * 16) : kOOB;
+      uint8_t* dst = base + (isA ? 0 : BM * 128) + ri * 1024;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(isA ? rA : rB, (__attribute__((address_space(3))) void*)dst, 16,
+                                               (int)off, 0, 0, 0);
+    }
+  };
+
+  // scale tables: activation words for this tile's rows, weight exponents packed
+  // four K-blocks to a word (byte kb % 4), matching the MFMA's byte select
+  for (int idx = tid; idx < Wd * BM; idx += 256) {
+    const int w = idx / BM, row = idx - w * BM;
+    const int64_t m = m0 + row;
+    const uint32_t off = (m < m_limit) ? (uint32_t)(((int64_t)w * p.ld_sfa + m) * 4) : kOOB;
+    lds_sa[idx] = bload4(rSA, off);
+  }
+  for (int idx = tid; idx < NBT * Wd; idx += 256) {
+    const int b = idx / Wd, w = idx - b * Wd;
+    const int nb = (int)(n0 >> 7) + b;
+    uint32_t word = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int k = 4 * w + q;
+      const uint32_t off = (nb < NB && k < KB) ? (uint32_t)((nb * KB + k) * 4) : kOOB;
+      word |= ((bload4(rSB, off) >> 23) & 0xFFu) << (8 * q);
+    }
+    lds_sb[idx] = word;
+  }
+  issue(0, IntC<0>{});
+  if constexpr (STAGES == 4) {
+    issue(1, IntC<1>{});
+    issue(2, IntC<2>{});
+  }
+
+  // accumulators: [SM][SN] 16x16 sub-tiles, lane holds row 16i + (l & 15) and
+  // columns 16j + 4(l >> 4) + 0..3 (the weight tile is the MFMA's first operand)
+  v4f acc[SM][SN];
+#pragma unroll
+  for (int i = 0; i < SM; ++i)
+#pragma unroll
+    for (int j = 0; j < SN; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+
+  // one K-block: OPS = kb % 4 (scale byte), ST = its ring stage
+  auto step = [&](int kb, auto ops_tag, auto st_tag) {
+    constexpr int OPS = decltype(ops_tag)::value;
+    constexpr int ST = decltype(st_tag)::value;
+    constexpr int NXT = (ST + STAGES - 1) % STAGES;
+    // own DMA for this stage done (later stages may still be in flight), then barrier
+    if constexpr (STAGES == 2) {
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), lgkm/exp unconstrained
+    } else {
+      constexpr int N = 2 * IPW;  // two younger stages may still be in flight
+      __builtin_amdgcn_s_waitcnt((N & 0xF) | 0x0F70 | ((N >> 4) << 14));
+    }
+    __syncthreads();
+    // Read every operand of this step from LDS first, then start the DMA of a
+    // later K-block: reads that precede the DMA in program order need no wait on it.
+    const uint8_t* As = stage_ptr(st_tag);
+    const uint8_t* Bs = As + BM * 128;
+    const int w = kb >> 2;
+    uint32_t sa[SM];
+#pragma unroll
+    for (int i = 0; i < SM; ++i) sa[i] = lds_sa[w * BM + wm * WM + 16 * i + (lane & 15)];
+    uint32_t sbw[SN];
+#pragma unroll
+    for (int j = 0; j < SN; ++j) sbw[j] = lds_sb[((wn * WN + 16 * j) >> 7) * Wd + w];
+    v8i af[SM], bf[SN];
+    const int c0 = (lane >> 4), c1 = 4 + (lane >> 4);
+#pragma unroll
+    for (int i = 0; i < SM; ++i) {
+      const int r = wm * WM + 16 * i + (lane & 15);
+      const uint4 lo = *reinterpret_cast<const uint4*>(As + r * 128 + ((c0 ^ swz(r)) << 4));
+      const uint4 hi = *reinterpret_cast<const uint4*>(As + r * 128 + ((c1 ^ swz(r)) << 4));
+      af[i] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    }
+#pragma unroll
+    for (int j = 0; j < SN; ++j) {
+      const int r = wn * WN + 16 * j + (lane & 15);
+      const uint4 lo = *reinterpret_cast<const uint4*>(Bs + r * 128 + ((c0 ^ swz(r)) << 4));
+      const uint4 hi = *reinterpret_cast<const uint4*>(Bs + r * 128 + ((c1 ^ swz(r)) << 4));
+      bf[j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    }
+    issue(kb + STAGES - 1, IntC<NXT>{});
+#pragma unroll
+    for (int j = 0; j < SN; ++j)
+#pragma unroll
+      for (int i = 0; i < SM; ++i)
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[j], af[i], acc[i][j], 0, 0, OPS, (int)sbw[j],
+                                                                     OPS, (int)sa[i]);
+  };
+
+  // K loop unrolled by four: the scale byte (kb % 4) and the ring stage are static
+  for (int kb = 0; kb < KB; kb += 4) {
+    step(kb, IntC<0>{}, IntC<0>{});
+    if (kb + 1 < KB) step(kb + 1, IntC<1>{}, IntC<1 % STAGES>{});
+    if (kb + 2 < KB) step(kb + 2, IntC<2>{}, IntC<2 % STAGES>{});
+    if (kb + 3 < KB) step(kb + 3, IntC<3>{}, IntC<3 % STAGES>{});
+  }
+
+  // epilogue straight from the accumulators (this kernel never splits K)
+  uint16_t* __restrict__ C = p.c + e * p.sc_e;
+#pragma unroll
+  for (int i = 0; i < SM; ++i) {
+    const int64_t m = m0 + wm * WM + 16 * i + (lane & 15);
+    if (m >= m_limit) continue;
+#pragma unroll
+    for (int j = 0; j < SN; ++j) {
+      const int64_t n = n0 + wn * WN + 16 * j + 4 * (lane >> 4);
+      if (n < p.N) {
+        uint2 o;
+        o.x = bf16_rne(acc[i][j][0]) | (bf16_rne(acc[i][j][1]) << 16);
+        o.y = bf16_rne(acc[i][j][2]) | (bf16_rne(acc[i][j][3]) << 16);
+        *reinterpret_cast<uint2*>(C + m * p.ldc + n) = o;
+      }
+    }
+  }
+}
+
+inline size_t scaled_tile_lds_bytes(int bm, int bn, int stages, int K) {
+  // dynamic part only (the stage buffers are static): the two scale tables
+  (void)stages;
+  const int KB = K / 128, Wd = (KB + 3) / 4;
+  return (size_t)Wd * bm * 4 + (size_t)((bn + 127) / 128) * Wd * 4;
+}
+
+inline size_t scaled_tile_static_bytes(int bm, int bn, int stages) {
+  return (size_t)(stages > 2 ? 4 : 2) * (bm + bn) * 128 + (stages > 2 ? 0 : 32);
+}
+
+// ---------------------------------------------------------------------------
 // compiled tile table
 
 typedef void (*KernelFn)(const KArgs);
 
+enum Kind { kTile = 0, kStream = 1, kScaled = 2 };
+
 struct TileEntry {
   KernelFn fn;
   int bm, bn;
-  bool stream;  // weight-streaming family (dynamic LDS: A stages + scale tables)
+  int kind;    // kTile: both operands via LDS (VALU scale FMA); kStream: weight streaming;
+               // kScaled: LDS-DMA tiles + scaled MFMA (no K split)
+  int stages;  // LDS ring depth of kScaled
 };
 
-// 0-3: LDS-tiled kernels (both operands staged through LDS); 4+: weight-streaming.
 const TileEntry kTiles[] = {
-    {gemm_kernel<64, 128, 64, 32>, 64, 128, false},
-    {gemm_kernel<128, 128, 64, 64>, 128, 128, false},
-    {gemm_kernel<64, 256, 64, 64>, 64, 256, false},
-    {gemm_kernel<128, 256, 64, 128>, 128, 256, false},
-    {stream_kernel<4, 2, 4>, 64, 128, true},
-    {stream_kernel<4, 1, 4>, 64, 64, true},
-    {stream_kernel<1, 2, 4>, 16, 128, true},
-    {stream_kernel<2, 2, 4>, 32, 128, true},
-    {stream_kernel<4, 1, 8>, 64, 64, true},
-    {stream_kernel<4, 2, 6>, 64, 128, true},
+    {gemm_kernel<64, 128, 64, 32>, 64, 128, kTile, 2},
+    {gemm_kernel<128, 128, 64, 64>, 128, 128, kTile, 2},
+    {gemm_kernel<64, 256, 64, 64>, 64, 256, kTile, 2},
+    {gemm_kernel<128, 256, 64, 128>, 128, 256, kTile, 2},
+    {stream_kernel<4, 2, 4>, 64, 128, kStream, 0},
+    {stream_kernel<4, 1, 4>, 64, 64, kStream, 0},
+    {stream_kernel<1, 2, 4>, 16, 128, kStream, 0},
+    {stream_kernel<2, 2, 4>, 32, 128, kStream, 0},
+    {stream_kernel<4, 1, 8>, 64, 64, kStream, 0},
+    {stream_kernel<4, 2, 6>, 64, 128, kStream, 0},
+    {scaled_tile_kernel<256, 256, 2, 2, 2>, 256, 256, kScaled, 2},
+    {scaled_tile_kernel<128, 256, 2, 2, 2>, 128, 256, kScaled, 2},
+    {scaled_tile_kernel<256, 128, 2, 2, 2>, 256, 128, kScaled, 2},
+    {scaled_tile_kernel<128, 128, 2, 2, 4>, 128, 128, kScaled, 4},
+    {scaled_tile_kernel<128, 128, 2, 2, 2>, 128, 128, kScaled, 2},
 };
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 
@@ -506,7 +750,14 @@ bool gemm_config_by_index(int idx, const GemmProblem& p, int splits, GemmConfig*
   const int KB = (int)(p.K / 128);
   if (splits > KB) splits = KB > 0 ? KB : 1;
   if (p.masked_m && splits != 1) return false;
-  if (kTiles[idx].stream) {
+  if (kTiles[idx].kind == kScaled) {
+    splits = 1;  // this family never splits K
+    if (scaled_tile_lds_bytes(kTiles[idx].bm, kTiles[idx].bn, kTiles[idx].stages, (int)p.K) +
+            scaled_tile_static_bytes(kTiles[idx].bm, kTiles[idx].bn, kTiles[idx].stages) >
+        kMaxLds)
+      return false;
+  }
+  if ((kTiles[idx].kind == kStream)) {
     // split K further if the scale tables would not fit next to the A stages
     while (splits < KB && stream_lds_bytes(kTiles[idx].bm, kTiles[idx].bn, (int)cdiv(KB, splits)) > kMaxLds) {
       if (p.masked_m) return false;
@@ -542,11 +793,13 @@ GemmConfig choose_gemm_config(const GemmProblem& p) {
     gemm_config_by_index(idx, p, splits, &cfg);
     return cfg;
   }
+  // prefill: LDS-DMA tiles + scaled MFMA, 128x128 workgroup tiles (two per compute
+  // unit); fall back to the VALU-scaled tile kernel when the scale tables do not fit
+  if (gemm_config_by_index(14, p, 1, &cfg)) return cfg;
   const int idx = 1;
   const int64_t tiles = cdiv(p.M, kTiles[idx].bm) * cdiv(p.N, kTiles[idx].bn);
   int splits = 1;
   if (tiles < 256) {
-    // fill about two workgroups per compute unit, keeping at least 8 K-blocks per split
     splits = (int)cdiv(512, tiles);
     const int max_splits = KB / 8 > 1 ? KB / 8 : 1;
     if (splits > max_splits) splits = max_splits;
@@ -582,8 +835,9 @@ hipError_t launch_gemm(const GemmProblem& p, const GemmConfig& cfg, void* ws, hi
   const int64_t tiles = (int64_t)k.tiles_m * k.tiles_n;
   if (tiles < 1 || p.E < 1 || KB < 1) return hipSuccess;
   size_t dyn = 0;
-  if (t.stream) {
-    dyn = stream_lds_bytes(t.bm, t.bn, cfg.kb_per_split);
+  if (t.kind != kTile) {
+    dyn = (t.kind == kStream) ? stream_lds_bytes(t.bm, t.bn, cfg.kb_per_split)
+                              : scaled_tile_lds_bytes(t.bm, t.bn, t.stages, (int)p.K);
     if (dyn > kMaxLds) return hipErrorInvalidValue;
     // raise the kernel's dynamic-LDS limit to what this launch needs (never lowered)
     static std::atomic<int> attr_bytes[kNumTiles];
