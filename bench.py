@@ -316,7 +316,9 @@ def main():
                     help="HBM traffic per GEMM launch measured with rocprofv3 counters")
     ap.add_argument("--counters", action="store_true",
                     help="workload for rocprofv3 --pmc passes: a 256 MiB torch copy (counter calibration), "
-                         "then --steps eager decode steps; no timing")
+                         "then --steps eager steps of --counters-shape; no timing")
+    ap.add_argument("--counters-shape", default="decode", choices=["decode", "prefill"],
+                    help="decode: M=64 N=7168 K=18432; prefill: M=4096 N=4096 K=7168")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -333,7 +335,7 @@ def main():
     stream = torch.cuda.Stream()
     shape = W.DENSE_DECODE
     if args.counters:
-        counters_workload(F, shape, args.steps)
+        counters_workload(F, shape if args.counters_shape == "decode" else W.DENSE_PREFILL[2], args.steps)
         return
     r = bench_dense(F, stream, shape, args.steps, args.warmup)
     print("[bench] %s" % json.dumps(r), file=sys.stderr, flush=True)

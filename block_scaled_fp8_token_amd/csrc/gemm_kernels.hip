@@ -474,14 +474,18 @@ __global__ __launch_bounds__(256) void stream_kernel(const KArgs p) {
 // Tiles move global -> LDS by LDS-DMA (buffer loads with the lds flag): each
 // wavefront instruction writes 1 KiB = 8 rows of a K-block tile, lane l to byte
 // 16 l, so the tile is stored row-major without padding and the 16-byte chunks of
-// row r are XOR-swizzled (chunk c in slot c ^ swz(r)) for conflict-free operand
-// reads.  STAGES LDS buffers form a ring; the loads for K-block kb + STAGES - 1
-// are issued right after the barrier of step kb.  Rows past M (or past an
+// row r are XOR-swizzled (chunk c in slot c ^ (r & 7)) for conflict-free operand
+// reads.  Two LDS stages: after the barrier that opens step kb, the DMA of kb + 1
+// goes into the stage kb - 1 used.  Rows past M (or past an
 // expert's count) and K-blocks past the range fall outside the buffer
 // descriptors and arrive as zeros.  Workgroups are mapped to tiles XCD by XCD
 // (a workgroup's XCD is its linear id mod 8), each XCD taking a compact block of
 // tiles so that its L2 serves the shared A and B panels.
-__device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
+// Chunk swizzle of a 128-byte tile row: slot = chunk ^ (row & 7).  Measured on
+// gfx950 with SQ_LDS_BANK_CONFLICT for the MFMA operand read pattern (lane l: row
+// l & 15, chunks l >> 4 and 4 + (l >> 4)): no conflicts, where unswizzled rows or
+// 144-byte padded rows cost 4-12 conflict cycles per ds_read_b128.
+__device__ __forceinline__ int swz(int r) { return r & 7; }
 
 template <int V>
 struct IntC {
@@ -489,21 +493,21 @@ struct IntC {
 };
 
 template <int BM, int BN, int WGM, int WGN, int STAGES>
-__global__ __launch_bounds__(256) void scaled_tile_kernel(const KArgs p) {
+__global__ __launch_bounds__(WGM * WGN * 64) void scaled_tile_kernel(const KArgs p) {
+  constexpr int NW = WGM * WGN;  // wavefronts per workgroup (4 or 8)
+  constexpr int NT = NW * 64;
   constexpr int WM = BM / WGM, WN = BN / WGN;
   constexpr int SM = WM / 16, SN = WN / 16;
   constexpr int A_INST = BM / 8, B_INST = BN / 8;          // 1 KiB DMA instructions per stage
-  constexpr int IPW = (A_INST + B_INST) / 4;               // per wavefront
+  constexpr int IPW = (A_INST + B_INST) / NW;              // per wavefront
   constexpr int STAGE = (BM + BN) * 128;
-  static_assert(WGM * WGN == 4 && (A_INST + B_INST) % 4 == 0, "tile shape");
-  static_assert(STAGES == 2 || STAGES == 4, "the ring period must divide the 4-step unroll");
+  static_assert((NW == 4 || NW == 8) && (A_INST + B_INST) % NW == 0, "tile shape");
+  static_assert(STAGES == 2, "two LDS stages; see the step schedule below");
   // One LDS array per ring stage, indexed with compile-time stage numbers, so the
   // compiler can tell operand reads of one stage from DMA writes into another and
   // does not make every read wait for all loads in flight.
   __shared__ __attribute__((aligned(1024))) uint8_t st0[STAGE];
   __shared__ __attribute__((aligned(1024))) uint8_t st1[STAGE];
-  __shared__ __attribute__((aligned(1024))) uint8_t st2[STAGES > 2 ? STAGE : 16];
-  __shared__ __attribute__((aligned(1024))) uint8_t st3[STAGES > 2 ? STAGE : 16];
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];  // scale tables
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -551,9 +555,7 @@ __global__ __launch_bounds__(256) void scaled_tile_kernel(const KArgs p) {
   auto stage_ptr = [&](auto st_tag) -> uint8_t* {
     constexpr int S = decltype(st_tag)::value;
     if constexpr (S == 0) return st0;
-    else if constexpr (S == 1) return st1;
-    else if constexpr (S == 2) return st2;
-    else return st3;
+    else return st1;
   };
   // DMA of K-block kb into a stage: instruction t of wavefront w covers rows
   // 8*i..8*i+7 of A (i < A_INST) or of B (i - A_INST), lane l -> row 8i + l/8,
@@ -576,13 +578,13 @@ __global__ __launch_bounds__(256) void scaled_tile_kernel(const KArgs p) {
 
   // scale tables: activation words for this tile's rows, weight exponents packed
   // four K-blocks to a word (byte kb % 4), matching the MFMA's byte select
-  for (int idx = tid; idx < Wd * BM; idx += 256) {
+  for (int idx = tid; idx < Wd * BM; idx += NT) {
     const int w = idx / BM, row = idx - w * BM;
     const int64_t m = m0 + row;
     const uint32_t off = (m < m_limit) ? (uint32_t)(((int64_t)w * p.ld_sfa + m) * 4) : kOOB;
     lds_sa[idx] = bload4(rSA, off);
   }
-  for (int idx = tid; idx < NBT * Wd; idx += 256) {
+  for (int idx = tid; idx < NBT * Wd; idx += NT) {
     const int b = idx / Wd, w = idx - b * Wd;
     const int nb = (int)(n0 >> 7) + b;
     uint32_t word = 0;
@@ -595,10 +597,6 @@ __global__ __launch_bounds__(256) void scaled_tile_kernel(const KArgs p) {
     lds_sb[idx] = word;
   }
   issue(0, IntC<0>{});
-  if constexpr (STAGES == 4) {
-    issue(1, IntC<1>{});
-    issue(2, IntC<2>{});
-  }
 
   // accumulators: [SM][SN] 16x16 sub-tiles, lane holds row 16i + (l & 15) and
   // columns 16j + 4(l >> 4) + 0..3 (the weight tile is the MFMA's first operand)
@@ -608,21 +606,12 @@ __global__ __launch_bounds__(256) void scaled_tile_kernel(const KArgs p) {
 #pragma unroll
     for (int j = 0; j < SN; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
-  // one K-block: OPS = kb % 4 (scale byte), ST = its ring stage
+  // One K-block: OPS = kb % 4 (scale byte), ST = kb % 2 (its stage).
   auto step = [&](int kb, auto ops_tag, auto st_tag) {
     constexpr int OPS = decltype(ops_tag)::value;
     constexpr int ST = decltype(st_tag)::value;
-    constexpr int NXT = (ST + STAGES - 1) % STAGES;
-    // own DMA for this stage done (later stages may still be in flight), then barrier
-    if constexpr (STAGES == 2) {
-      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), lgkm/exp unconstrained
-    } else {
-      constexpr int N = 2 * IPW;  // two younger stages may still be in flight
-      __builtin_amdgcn_s_waitcnt((N & 0xF) | 0x0F70 | ((N >> 4) << 14));
-    }
-    __syncthreads();
-    // Read every operand of this step from LDS first, then start the DMA of a
-    // later K-block: reads that precede the DMA in program order need no wait on it.
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // this wavefront's DMA of kb has landed
+    __syncthreads();                     // ... and everyone's; kb - 1's stage is free
     const uint8_t* As = stage_ptr(st_tag);
     const uint8_t* Bs = As + BM * 128;
     const int w = kb >> 2;
@@ -648,7 +637,10 @@ __global__ __launch_bounds__(256) void scaled_tile_kernel(const KArgs p) {
       const uint4 hi = *reinterpret_cast<const uint4*>(Bs + r * 128 + ((c1 ^ swz(r)) << 4));
       bf[j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
     }
-    issue(kb + STAGES - 1, IntC<NXT>{});
+    // Keep the DMA below the operand reads: the compiler would hoist it above them
+    // (the buffers differ) and then make the reads wait for it.
+    __builtin_amdgcn_sched_barrier(0);
+    issue(kb + 1, IntC<1 - ST>{});
 #pragma unroll
     for (int j = 0; j < SN; ++j)
 #pragma unroll
@@ -666,6 +658,196 @@ __global__ __launch_bounds__(256) void scaled_tile_kernel(const KArgs p) {
   }
 
   // epilogue straight from the accumulators (this kernel never splits K)
+  uint16_t* __restrict__ C = p.c + e * p.sc_e;
+#pragma unroll
+  for (int i = 0; i < SM; ++i) {
+    const int64_t m = m0 + wm * WM + 16 * i + (lane & 15);
+    if (m >= m_limit) continue;
+#pragma unroll
+    for (int j = 0; j < SN; ++j) {
+      const int64_t n = n0 + wn * WN + 16 * j + 4 * (lane >> 4);
+      if (n < p.N) {
+        uint2 o;
+        o.x = bf16_rne(acc[i][j][0]) | (bf16_rne(acc[i][j][1]) << 16);
+        o.y = bf16_rne(acc[i][j][2]) | (bf16_rne(acc[i][j][3]) << 16);
+        *reinterpret_cast<uint2*>(C + m * p.ldc + n) = o;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Software-pipelined variant of the scaled-MFMA tile kernel.  Per K-block kb, with
+// the operands of kb already in registers (set X):
+//   wait for this wavefront's DMA of kb + 1, barrier (every wavefront's DMA of
+//   kb + 1 has landed and every wavefront has finished reading kb's stage),
+//   DMA kb + 2 into kb's stage, read the operands of kb + 1 into the other register
+//   set, and issue kb's MFMAs -- so the LDS reads of the next step run under this
+//   step's MFMAs and each DMA has a whole step to arrive.  NW wavefronts per
+//   workgroup (4 or 8) in a WGM x WGN grid.
+template <int BM, int BN, int WGM, int WGN>
+__global__ __launch_bounds__(WGM * WGN * 64) void scaled_pipe_kernel(const KArgs p) {
+  constexpr int NW = WGM * WGN;
+  constexpr int NT = NW * 64;
+  constexpr int WM = BM / WGM, WN = BN / WGN;
+  constexpr int SM = WM / 16, SN = WN / 16;
+  constexpr int A_INST = BM / 8, B_INST = BN / 8;
+  constexpr int IPW = (A_INST + B_INST) / NW;
+  constexpr int STAGE = (BM + BN) * 128;
+  static_assert((A_INST + B_INST) % NW == 0, "tile shape");
+  __shared__ __attribute__((aligned(1024))) uint8_t st0[STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t st1[STAGE];
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];  // scale tables
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WGN, wn = wave % WGN;
+  const int64_t e = blockIdx.z;
+
+  const int T = p.tiles_m * p.tiles_n;
+  const int bid = blockIdx.x;
+  const int per_xcd = (T + 7) / 8;
+  int lin = (bid & 7) * per_xcd + (bid >> 3);
+  if ((T & 7) != 0) lin = bid;
+  constexpr int GM = 4;
+  const int group = lin / (GM * p.tiles_n);
+  const int first_m = group * GM;
+  const int gsz = (p.tiles_m - first_m) < GM ? (p.tiles_m - first_m) : GM;
+  const int in_g = lin - group * GM * p.tiles_n;
+  const int tm = first_m + in_g % gsz, tn = in_g / gsz;
+
+  int64_t m_limit = p.M;
+  if (p.masked_m) {
+    const int64_t cnt = p.masked_m[e];
+    m_limit = cnt < 0 ? 0 : (cnt > p.M ? p.M : cnt);
+  }
+  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+  if (m0 >= m_limit) return;
+
+  const int KB = (int)(p.K / 128);
+  const int Wd = (KB + 3) / 4;
+  const int NB = (int)((p.N + 127) / 128);
+  constexpr int NBT = (BN + 127) / 128;
+  uint32_t* lds_sa = reinterpret_cast<uint32_t*>(smem);
+  uint32_t* lds_sb = lds_sa + Wd * BM;
+
+  const int64_t rows_valid = (m_limit - m0 < BM) ? m_limit - m0 : BM;
+  int64_t cols_valid = p.N - n0;
+  cols_valid = cols_valid > BN ? BN : cols_valid;
+  const auto rA = make_rsrc(p.a + e * p.sa_e + m0 * p.K, (uint32_t)(rows_valid * p.K));
+  const auto rB = make_rsrc(p.b + e * p.sb_e + n0 * p.K, (uint32_t)(cols_valid * p.K));
+  const auto rSA = make_rsrc(p.sfa + e * p.ssfa_e, (uint32_t)(Wd * p.ld_sfa * 4));
+  const auto rSB = make_rsrc(p.sfb + e * p.ssfb_e, (uint32_t)(NB * KB * 4));
+
+  auto stage_ptr = [&](auto st_tag) -> uint8_t* {
+    if constexpr (decltype(st_tag)::value == 0) return st0;
+    else return st1;
+  };
+  auto issue = [&](int kb, auto st_tag) {
+    uint8_t* base = stage_ptr(st_tag);
+#pragma unroll
+    for (int t = 0; t < IPW; ++t) {
+      const int inst = wave * IPW + t;
+      const bool isA = inst < A_INST;
+      const int ri = isA ? inst : inst - A_INST;
+      const int r = ri * 8 + (lane >> 3);
+      const int chunk = (lane & 7) ^ swz(r);
+      const uint32_t off = (kb < KB) ? (uint32_t)(r * p.K + kb * 128 + chunk * 16) : kOOB;
+      uint8_t* dst = base + (isA ? 0 : BM * 128) + ri * 1024;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(isA ? rA : rB, (__attribute__((address_space(3))) void*)dst, 16,
+                                               (int)off, 0, 0, 0);
+    }
+  };
+
+  for (int idx = tid; idx < Wd * BM; idx += NT) {
+    const int w = idx / BM, row = idx - w * BM;
+    const int64_t m = m0 + row;
+    const uint32_t off = (m < m_limit) ? (uint32_t)(((int64_t)w * p.ld_sfa + m) * 4) : kOOB;
+    lds_sa[idx] = bload4(rSA, off);
+  }
+  for (int idx = tid; idx < NBT * Wd; idx += NT) {
+    const int b = idx / Wd, w = idx - b * Wd;
+    const int nb = (int)(n0 >> 7) + b;
+    uint32_t word = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int k = 4 * w + q;
+      const uint32_t off = (nb < NB && k < KB) ? (uint32_t)((nb * KB + k) * 4) : kOOB;
+      word |= ((bload4(rSB, off) >> 23) & 0xFFu) << (8 * q);
+    }
+    lds_sb[idx] = word;
+  }
+
+  struct Frags {
+    v8i a[SM], b[SN];
+    uint32_t sa[SM], sb[SN];
+  };
+  const int c0 = (lane >> 4), c1 = 4 + (lane >> 4);
+  auto read_frags = [&](int kb, auto st_tag, Frags& f) {
+    const uint8_t* As = stage_ptr(st_tag);
+    const uint8_t* Bs = As + BM * 128;
+    const int w = (kb < KB ? kb : KB - 1) >> 2;
+#pragma unroll
+    for (int i = 0; i < SM; ++i) f.sa[i] = lds_sa[w * BM + wm * WM + 16 * i + (lane & 15)];
+#pragma unroll
+    for (int j = 0; j < SN; ++j) f.sb[j] = lds_sb[((wn * WN + 16 * j) >> 7) * Wd + w];
+#pragma unroll
+    for (int i = 0; i < SM; ++i) {
+      const int r = wm * WM + 16 * i + (lane & 15);
+      const uint4 lo = *reinterpret_cast<const uint4*>(As + r * 128 + ((c0 ^ swz(r)) << 4));
+      const uint4 hi = *reinterpret_cast<const uint4*>(As + r * 128 + ((c1 ^ swz(r)) << 4));
+      f.a[i] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    }
+#pragma unroll
+    for (int j = 0; j < SN; ++j) {
+      const int r = wn * WN + 16 * j + (lane & 15);
+      const uint4 lo = *reinterpret_cast<const uint4*>(Bs + r * 128 + ((c0 ^ swz(r)) << 4));
+      const uint4 hi = *reinterpret_cast<const uint4*>(Bs + r * 128 + ((c1 ^ swz(r)) << 4));
+      f.b[j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    }
+  };
+
+  v4f acc[SM][SN];
+#pragma unroll
+  for (int i = 0; i < SM; ++i)
+#pragma unroll
+    for (int j = 0; j < SN; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+
+  // prologue: DMA K-blocks 0 and 1, wait for 0, read its operands into set X
+  Frags fx, fy;
+  issue(0, IntC<0>{});
+  issue(1, IntC<1>{});
+  __builtin_amdgcn_s_waitcnt((IPW & 0xF) | 0x0F70 | ((IPW >> 4) << 14));  // K-block 1 may remain in flight
+  __syncthreads();
+  read_frags(0, IntC<0>{}, fx);
+
+  // step kb: operands of kb in `cur`; stage of kb is ST
+  auto step = [&](int kb, auto ops_tag, auto st_tag, Frags& cur, Frags& nxt) {
+    constexpr int OPS = decltype(ops_tag)::value;
+    constexpr int ST = decltype(st_tag)::value;
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // this wavefront's DMA of kb + 1 has landed
+    __syncthreads();
+    read_frags(kb + 1, IntC<1 - ST>{}, nxt);  // operands of kb + 1 stream in under the MFMAs
+    // Keep the DMA below the operand reads: the compiler would hoist it above them
+    // (the buffers differ) and then make the reads wait for it.
+    __builtin_amdgcn_sched_barrier(0);
+    issue(kb + 2, st_tag);                   // kb's stage is free: everyone has read it
+#pragma unroll
+    for (int j = 0; j < SN; ++j)
+#pragma unroll
+      for (int i = 0; i < SM; ++i)
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(cur.b[j], cur.a[i], acc[i][j], 0, 0, OPS,
+                                                                     (int)cur.sb[j], OPS, (int)cur.sa[i]);
+  };
+
+  // unrolled by four: scale byte kb % 4, stage kb % 2 and register set kb % 2 are static
+  for (int kb = 0; kb < KB; kb += 4) {
+    step(kb, IntC<0>{}, IntC<0>{}, fx, fy);
+    if (kb + 1 < KB) step(kb + 1, IntC<1>{}, IntC<1>{}, fy, fx);
+    if (kb + 2 < KB) step(kb + 2, IntC<2>{}, IntC<0>{}, fx, fy);
+    if (kb + 3 < KB) step(kb + 3, IntC<3>{}, IntC<1>{}, fy, fx);
+  }
+
   uint16_t* __restrict__ C = p.c + e * p.sc_e;
 #pragma unroll
   for (int i = 0; i < SM; ++i) {
@@ -708,26 +890,38 @@ struct TileEntry {
   int kind;    // kTile: both operands via LDS (VALU scale FMA); kStream: weight streaming;
                // kScaled: LDS-DMA tiles + scaled MFMA (no K split)
   int stages;  // LDS ring depth of kScaled
+  int threads;  // workgroup size
 };
 
 const TileEntry kTiles[] = {
-    {gemm_kernel<64, 128, 64, 32>, 64, 128, kTile, 2},
-    {gemm_kernel<128, 128, 64, 64>, 128, 128, kTile, 2},
-    {gemm_kernel<64, 256, 64, 64>, 64, 256, kTile, 2},
-    {gemm_kernel<128, 256, 64, 128>, 128, 256, kTile, 2},
-    {stream_kernel<4, 2, 4>, 64, 128, kStream, 0},
-    {stream_kernel<4, 1, 4>, 64, 64, kStream, 0},
-    {stream_kernel<1, 2, 4>, 16, 128, kStream, 0},
-    {stream_kernel<2, 2, 4>, 32, 128, kStream, 0},
-    {stream_kernel<4, 1, 8>, 64, 64, kStream, 0},
-    {stream_kernel<4, 2, 6>, 64, 128, kStream, 0},
-    {scaled_tile_kernel<256, 256, 2, 2, 2>, 256, 256, kScaled, 2},
-    {scaled_tile_kernel<128, 256, 2, 2, 2>, 128, 256, kScaled, 2},
-    {scaled_tile_kernel<256, 128, 2, 2, 2>, 256, 128, kScaled, 2},
-    {scaled_tile_kernel<128, 128, 2, 2, 4>, 128, 128, kScaled, 4},
-    {scaled_tile_kernel<128, 128, 2, 2, 2>, 128, 128, kScaled, 2},
+    {gemm_kernel<64, 128, 64, 32>, 64, 128, kTile, 2, 256},
+    {gemm_kernel<128, 128, 64, 64>, 128, 128, kTile, 2, 256},
+    {gemm_kernel<64, 256, 64, 64>, 64, 256, kTile, 2, 256},
+    {gemm_kernel<128, 256, 64, 128>, 128, 256, kTile, 2, 256},
+    {stream_kernel<4, 2, 4>, 64, 128, kStream, 0, 256},
+    {stream_kernel<4, 1, 4>, 64, 64, kStream, 0, 256},
+    {stream_kernel<1, 2, 4>, 16, 128, kStream, 0, 256},
+    {stream_kernel<2, 2, 4>, 32, 128, kStream, 0, 256},
+    {stream_kernel<4, 1, 8>, 64, 64, kStream, 0, 256},
+    {stream_kernel<4, 2, 6>, 64, 128, kStream, 0, 256},
+    {scaled_tile_kernel<256, 256, 2, 2, 2>, 256, 256, kScaled, 2, 256},
+    {scaled_tile_kernel<128, 256, 2, 2, 2>, 128, 256, kScaled, 2, 256},
+    {scaled_tile_kernel<256, 128, 2, 2, 2>, 256, 128, kScaled, 2, 256},
+    {scaled_tile_kernel<128, 128, 2, 2, 2>, 128, 128, kScaled, 2, 256},
+    {scaled_pipe_kernel<128, 128, 2, 2>, 128, 128, kScaled, 2, 256},
+    {scaled_pipe_kernel<256, 128, 2, 2>, 256, 128, kScaled, 2, 256},
+    {scaled_pipe_kernel<128, 256, 2, 2>, 128, 256, kScaled, 2, 256},
+    {scaled_pipe_kernel<256, 128, 4, 2>, 256, 128, kScaled, 2, 512},
+    {scaled_tile_kernel<256, 256, 2, 4, 2>, 256, 256, kScaled, 2, 512},
+    {scaled_tile_kernel<256, 256, 4, 2, 2>, 256, 256, kScaled, 2, 512},
+    {scaled_tile_kernel<256, 128, 4, 2, 2>, 256, 128, kScaled, 2, 512},
 };
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
+// table entries the automatic choice uses
+constexpr int kCfgStream64x128 = 4;
+constexpr int kCfgScaled128x128 = 13;
+constexpr int kCfgScaled256x256 = 19;
+static_assert(kCfgScaled256x256 < kNumTiles, "tile table");
 
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -779,12 +973,12 @@ GemmConfig choose_gemm_config(const GemmProblem& p) {
   const int KB = (int)(p.K / 128);
   if (p.masked_m) {
     // weight streaming, 64-row M tiles: tiles past an expert's count exit at once
-    gemm_config_by_index(4, p, 1, &cfg);
+    gemm_config_by_index(kCfgStream64x128, p, 1, &cfg);
     return cfg;
   }
   if (p.M <= 64) {
     // decode: weight streaming over 128-column tiles, K split until about 224 workgroups
-    const int idx = 4;
+    const int idx = kCfgStream64x128;
     const int64_t tiles = cdiv(p.N, kTiles[idx].bn);
     int splits = (int)(224 / (tiles > 0 ? tiles : 1));
     const int max_splits = KB / 8 > 1 ? KB / 8 : 1;
@@ -795,7 +989,11 @@ GemmConfig choose_gemm_config(const GemmProblem& p) {
   }
   // prefill: LDS-DMA tiles + scaled MFMA, 128x128 workgroup tiles (two per compute
   // unit); fall back to the VALU-scaled tile kernel when the scale tables do not fit
-  if (gemm_config_by_index(14, p, 1, &cfg)) return cfg;
+  // 256x256 tiles (8 wavefronts, 64x128 each) once they fill the compute units,
+  // 128x128 tiles (two workgroups per compute unit) below that
+  const int64_t big_tiles = cdiv(p.M, 256) * cdiv(p.N, 256);
+  if (big_tiles >= 256 && gemm_config_by_index(kCfgScaled256x256, p, 1, &cfg)) return cfg;
+  if (gemm_config_by_index(kCfgScaled128x128, p, 1, &cfg)) return cfg;
   const int idx = 1;
   const int64_t tiles = cdiv(p.M, kTiles[idx].bm) * cdiv(p.N, kTiles[idx].bn);
   int splits = 1;
@@ -850,7 +1048,7 @@ hipError_t launch_gemm(const GemmProblem& p, const GemmConfig& cfg, void* ws, hi
       }
     }
   }
-  hipLaunchKernelGGL(t.fn, dim3((unsigned)tiles, (unsigned)cfg.splits, (unsigned)p.E), dim3(256), dyn, stream, k);
+  hipLaunchKernelGGL(t.fn, dim3((unsigned)tiles, (unsigned)cfg.splits, (unsigned)p.E), dim3(t.threads), dyn, stream, k);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || cfg.splits == 1) return e;
   const int64_t threads = p.M * (p.N / 8);
