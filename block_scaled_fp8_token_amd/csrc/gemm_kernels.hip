@@ -878,19 +878,398 @@ inline size_t scaled_tile_static_bytes(int bm, int bn, int stages) {
 }
 
 // ---------------------------------------------------------------------------
+// Ring kernel.  Four wavefronts in a WGM x WGN grid, each owning a (BM/WGM) x
+// (BN/WGN) sub-tile accumulated with v_mfma_scale_f32_32x32x64_f8f6f4.  One such
+// MFMA covers half of a 128-wide K-block, so the LDS ring is kept in K-halves:
+// four slots of (BM + BN) rows x 64 bytes, filled by LDS-DMA three half-steps
+// before they are read.  Half-step h of every wavefront:
+//   s_waitcnt: its own DMA of h + 1 has landed and its reads of h have returned;
+//   barrier:   so has everyone's, and nobody reads slot h any more;
+//   the MFMAs of h from registers, interleaved with the LDS reads of the
+//   operands of h + 1 and with the DMA of h + 4 into slot h.
+// LDS reads and DMA thus run under the MFMAs.  The UE8M0 exponents are the
+// MFMA's scale operands (byte kb % 4 of the packed words), so the block scaling
+// costs no VALU work; the activation words of the tile's rows and the packed
+// weight exponents are staged in LDS tables once per tile.  The K loop runs in
+// groups of four K-blocks; a ragged last group reads zeros (out-of-range DMA)
+// with zero scale bytes.
+//
+// Valid rows: each wavefront runs a copy of the loop specialised to the number
+// IV of its 32-row groups that hold valid rows (all of them except in the last
+// M tile or a masked group's partial tile) and issues neither operand reads nor
+// MFMAs for the others; it still takes its share of the DMA and every barrier.
+// In the 1 x 4 grid all four wavefronts share the same rows, so a masked group
+// with few rows still spreads its MFMAs over the four SIMDs.
+//
+// LDS slot layout: A rows [0, BM) then B rows [BM, BM + BN), 64 bytes each
+// (one K-half); 16-byte chunk c of row r sits at position c ^ ((r >> 2) & 3).
+// Measured on gfx950 with SQ_LDS_BANK_CONFLICT for the operand reads (lane l:
+// row l & 31, chunks 2(l >> 5) and 2(l >> 5) + 1): no conflicts with this
+// swizzle or with (r >> 3) & 3, about 4 conflict cycles per ds_read_b128 with
+// (r >> 1) & 3 and 12 without a swizzle.
+__device__ __forceinline__ int swz64(int r) { return (r >> 2) & 3; }
+
+typedef float v16f __attribute__((ext_vector_type(16)));
+// one 16-byte LDS load per operand half: a vector type keeps it a single load
+// of the slot array (a struct would be split into four), which is what lets the
+// compiler see which slot it reads
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+// s_waitcnt immediate (gfx9 encoding): vmcnt split over bits 3:0 and 15:14,
+// expcnt (bits 6:4) left at its maximum.
+constexpr int waitcnt_imm(int vm, int lgkm) { return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | ((lgkm & 15) << 8); }
+
+constexpr int kRingSlots = 4;
+
+template <int BM, int BN, int WGM, int WGN>
+struct RingShape {
+  static constexpr int WM = BM / WGM, WN = BN / WGN;
+  static constexpr int SM = WM / 32, SN = WN / 32;
+  static constexpr int SLOT = (BM + BN) * 64;
+  static constexpr int A_INST = BM / 16, B_INST = BN / 16;  // 1 KiB DMA instructions per slot
+  static constexpr int IPA = A_INST / 4, IPB = B_INST / 4;  // ... per wavefront, of A and of B
+  static constexpr int IPW = IPA + IPB;
+  static constexpr int NBT = BN / 128;                      // weight blocks across the tile
+  static constexpr int FIT = (160 * 1024 - kRingSlots * SLOT - 256) / (BM * 4 + NBT * 4);
+  static constexpr int WD_MAX = FIT < 32 ? FIT : 32;        // scale words per row the tables hold
+};
+
+// XCD-aware tile order: workgroup id -> (XCD, slot) -> a compact run of tiles per
+// XCD (a workgroup's XCD is its linear id mod 8), walked in groups of four tile rows.
+__device__ __forceinline__ void xcd_tile(const KArgs& p, int bid, int& tm, int& tn) {
+  const int T = p.tiles_m * p.tiles_n;
+  const int per_xcd = (T + 7) / 8;
+  int lin = (bid & 7) * per_xcd + (bid >> 3);
+  if ((T & 7) != 0) lin = bid;  // uneven split: plain order
+  constexpr int GM = 4;
+  const int group = lin / (GM * p.tiles_n);
+  const int first_m = group * GM;
+  const int gsz = (p.tiles_m - first_m) < GM ? (p.tiles_m - first_m) : GM;
+  const int in_g = lin - group * GM * p.tiles_n;
+  tm = first_m + in_g % gsz;
+  tn = in_g / gsz;
+}
+
+// Scheduling pattern for one half-step: NM MFMAs, each followed by its share of the
+// NR operand reads and of the NV DMA instructions (spread evenly).
+template <int NM, int NR, int NV, int Q = 0>
+__device__ __forceinline__ void mfma_read_dma_pattern() {
+  if constexpr (Q < NM) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    constexpr int r = (Q + 1) * NR / NM - Q * NR / NM;
+    if constexpr (r > 0) __builtin_amdgcn_sched_group_barrier(0x100, r, 0);
+    constexpr int v = (Q + 1) * NV / NM - Q * NV / NM;
+    if constexpr (v > 0) __builtin_amdgcn_sched_group_barrier(0x010, v, 0);
+    mfma_read_dma_pattern<NM, NR, NV, Q + 1>();
+  }
+}
+
+template <int BM, int BN, int WGM, int WGN>
+__global__ __launch_bounds__(256) void scaled_ring_kernel(const KArgs p) {
+  using R = RingShape<BM, BN, WGM, WGN>;
+  constexpr int S = kRingSlots;
+  constexpr int WM = R::WM, WN = R::WN, SM = R::SM, SN = R::SN, IPW = R::IPW;
+  constexpr int IPA = R::IPA, WD_MAX = R::WD_MAX, NBT = R::NBT;
+  static_assert(WGM * WGN == 4 && WM % 32 == 0 && WN % 32 == 0 && BN % 128 == 0 && BM % 64 == 0, "ring tile shape");
+  static_assert(WD_MAX >= 1, "scale tables do not fit");
+  // one array per slot: the compiler's LDS-DMA tracking tells them apart, so an
+  // operand read waits only for the DMA into its own slot
+  __shared__ __attribute__((aligned(1024))) uint8_t sl0[R::SLOT];
+  __shared__ __attribute__((aligned(1024))) uint8_t sl1[R::SLOT];
+  __shared__ __attribute__((aligned(1024))) uint8_t sl2[R::SLOT];
+  __shared__ __attribute__((aligned(1024))) uint8_t sl3[R::SLOT];
+  __shared__ __attribute__((aligned(16))) uint32_t sa_tab[WD_MAX * BM];   // [w][row]
+  __shared__ __attribute__((aligned(16))) uint32_t sb_tab[NBT * WD_MAX];  // [block][w], byte kb % 4
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WGN, wn = wave % WGN;
+  const int64_t e = blockIdx.z;
+  int tm, tn;
+  xcd_tile(p, blockIdx.x, tm, tn);
+
+  int64_t m_limit = p.M;
+  if (p.masked_m) {
+    const int64_t cnt = p.masked_m[e];
+    m_limit = cnt < 0 ? 0 : (cnt > p.M ? p.M : cnt);
+  }
+  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+  if (m0 >= m_limit) return;
+
+  const int KB = (int)(p.K / 128);
+  const int Wd = (KB + 3) / 4;  // <= WD_MAX (checked by the host)
+  const int NB = (int)((p.N + 127) / 128);
+  const int H = 8 * Wd;         // half-steps, K padded to whole groups of four blocks
+  const int64_t rows_valid = (m_limit - m0 < BM) ? m_limit - m0 : BM;
+  int64_t cols_valid = p.N - n0;
+  cols_valid = cols_valid > BN ? BN : cols_valid;
+  const auto rA = make_rsrc(p.a + e * p.sa_e + m0 * p.K, (uint32_t)(rows_valid * p.K));
+  const auto rB = make_rsrc(p.b + e * p.sb_e + n0 * p.K, (uint32_t)(cols_valid * p.K));
+  const auto rSA = make_rsrc(p.sfa + e * p.ssfa_e, (uint32_t)(Wd * p.ld_sfa * 4));
+  const auto rSB = make_rsrc(p.sfb + e * p.ssfb_e, (uint32_t)(NB * KB * 4));
+
+  auto slot = [&](auto sl_tag) -> uint8_t* {
+    constexpr int I = decltype(sl_tag)::value;
+    if constexpr (I == 0) return sl0;
+    else if constexpr (I == 1) return sl1;
+    else if constexpr (I == 2) return sl2;
+    else return sl3;
+  };
+
+  // DMA: instruction t < IPA of this wavefront covers A rows 16 ri .. 16 ri + 15 with
+  // ri = wave * IPA + t, the others B rows likewise; lane l -> row 16 ri + (l >> 2),
+  // slot position l & 3 holding chunk (l & 3) ^ swz64(row) of the K-half.
+  uint32_t boff[IPW];
+#pragma unroll
+  for (int t = 0; t < IPW; ++t) {
+    const int ri = t < IPA ? wave * IPA + t : wave * R::IPB + (t - IPA);
+    const int r = ri * 16 + (lane >> 2);
+    boff[t] = (uint32_t)(r * p.K) + (uint32_t)((((lane & 3) ^ swz64(r)) << 4));
+  }
+  auto issue = [&](int h, auto sl_tag) {
+    uint8_t* base = slot(sl_tag);
+    // past the last K-half the offset gets the top bit: out of range, zero-filled
+    // (an OR rather than a select keeps the loop body free of branches)
+    const uint32_t hoff = (uint32_t)h * 64u, oob = h < 2 * KB ? 0u : kOOB;
+#pragma unroll
+    for (int t = 0; t < IPW; ++t) {
+      const bool isA = t < IPA;  // static after unrolling
+      const int ri = isA ? wave * IPA + t : wave * R::IPB + (t - IPA);
+      uint8_t* dst = base + (isA ? 0 : BM * 64) + ri * 1024;
+      const uint32_t off = (boff[t] + hoff) | oob;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(isA ? rA : rB, (__attribute__((address_space(3))) void*)dst, 16,
+                                               (int)off, 0, 0, 0);
+    }
+  };
+
+  // Scale tables.  Activation words: zero for rows past the mask and for the bytes
+  // of K-blocks past K in the last word.  Weight exponents: byte kb % 4 of word
+  // kb / 4, zero past N or K.  The global loads are issued before the first DMAs
+  // and written to LDS after them, so the DMAs are in flight meanwhile.
+  constexpr int SA_IT = (WD_MAX * BM + 255) / 256;
+  constexpr int SB_IT = (NBT * WD_MAX * 4 + 255) / 256;
+  uint32_t sav[SA_IT], sbv[SB_IT];
+#pragma unroll
+  for (int t = 0; t < SA_IT; ++t) {
+    const int idx = t * 256 + tid;
+    const int w = idx / BM, row = idx - w * BM;
+    const bool ok = idx < WD_MAX * BM && w < Wd && m0 + row < m_limit;
+    sav[t] = bload4(rSA, ok ? (uint32_t)(((int64_t)w * p.ld_sfa + m0 + row) * 4) : kOOB);
+  }
+#pragma unroll
+  for (int t = 0; t < SB_IT; ++t) {
+    const int idx = t * 256 + tid;
+    const int b = idx / (WD_MAX * 4), k = idx - b * (WD_MAX * 4);
+    const int nb = (int)(n0 >> 7) + b;
+    const bool ok = idx < NBT * WD_MAX * 4 && nb < NB && k < KB;
+    sbv[t] = bload4(rSB, ok ? (uint32_t)((nb * KB + k) * 4) : kOOB);
+  }
+  issue(0, IntC<0>{});
+  issue(1, IntC<1>{});
+  issue(2, IntC<2>{});
+  issue(3, IntC<3>{});
+#pragma unroll
+  for (int t = 0; t < SA_IT; ++t) {
+    const int idx = t * 256 + tid;
+    const int w = idx / BM;
+    uint32_t v = sav[t];
+    const int left = KB - 4 * w;  // K-blocks of this word that exist
+    if (left < 4) v &= left <= 0 ? 0u : ((1u << (8 * left)) - 1u);
+    if (idx < WD_MAX * BM) sa_tab[idx] = v;
+  }
+  uint8_t* sb_bytes = reinterpret_cast<uint8_t*>(sb_tab);
+#pragma unroll
+  for (int t = 0; t < SB_IT; ++t) {
+    const int idx = t * 256 + tid;
+    if (idx < NBT * WD_MAX * 4) sb_bytes[idx] = (uint8_t)((sbv[t] >> 23) & 0xFFu);
+  }
+
+  // first DMA and the tables in place everywhere
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm((S - 1) * IPW, 0));
+  __builtin_amdgcn_s_barrier();
+
+  // operand reads: lane l takes row l & 31 of a 32-row group and the 32 bytes of
+  // K-half chunks 2(l >> 5), 2(l >> 5) + 1 (the same k order for both operands)
+  const int lr = lane & 31, c0 = 2 * (lane >> 5);
+  const uint32_t rd0 = (uint32_t)(lr * 64 + ((c0 ^ swz64(lr)) << 4));
+  const uint32_t rd1 = (uint32_t)(lr * 64 + (((c0 + 1) ^ swz64(lr)) << 4));
+  const int sb_blk = (wn * WN) >> 7;  // this wavefront's weight block within the tile
+  uint16_t* __restrict__ C = p.c + e * p.sc_e;
+
+  // The loop and epilogue for IV valid 32-row groups of this wavefront.
+  auto body = [&](auto iv_tag) {
+    constexpr int IV = decltype(iv_tag)::value;
+    auto read_frags = [&](auto sl_tag, v8i (&xf)[SM], v8i (&wf)[SN]) {
+      const uint8_t* base = slot(sl_tag);
+#pragma unroll
+      for (int i = 0; i < IV; ++i) {
+        const uint8_t* q = base + (wm * WM + 32 * i) * 64;
+        const v4i lo = *reinterpret_cast<const v4i*>(q + rd0);
+        const v4i hi = *reinterpret_cast<const v4i*>(q + rd1);
+        xf[i] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      }
+      if constexpr (IV > 0) {
+#pragma unroll
+        for (int j = 0; j < SN; ++j) {
+          const uint8_t* q = base + (BM + wn * WN + 32 * j) * 64;
+          const v4i lo = *reinterpret_cast<const v4i*>(q + rd0);
+          const v4i hi = *reinterpret_cast<const v4i*>(q + rd1);
+          wf[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        }
+      }
+    };
+
+    uint32_t sa[SM], sa_n[SM];
+    uint32_t sb = sb_tab[sb_blk * WD_MAX], sb_n;
+#pragma unroll
+    for (int i = 0; i < SM; ++i) sa[i] = i < IV ? sa_tab[wm * WM + 32 * i + lr] : 0u;
+    v8i xf[SM], wf[SN];
+    read_frags(IntC<0>{}, xf, wf);
+
+    v16f acc[SM][SN];
+#pragma unroll
+    for (int i = 0; i < SM; ++i)
+#pragma unroll
+      for (int j = 0; j < SN; ++j)
+#pragma unroll
+        for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
+
+    // half-step hb + HS of a group of four K-blocks (hb a multiple of 8): K-block
+    // kb = hb / 2 + HS / 2, so the scale byte kb % 4 is HS / 2
+    auto half = [&](int hb, auto hs_tag) {
+      constexpr int HS = decltype(hs_tag)::value;
+      constexpr int OPS = HS / 2;
+      const int h = hb + HS;
+      // nothing moves across the half-step boundary: the MFMAs below use registers
+      // only, and would otherwise drift past later barriers
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_waitcnt(waitcnt_imm((S - 2) * IPW, 0));
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      issue(h + S, IntC<HS % S>{});
+      if constexpr (HS == 0) {
+#pragma unroll
+        for (int i = 0; i < SM; ++i) sa[i] = sa_n[i];
+        sb = sb_n;
+      }
+      if constexpr (HS == 4) {
+        // scale words of the next group (clamped to the table; unused past the end)
+        const int wnx = (hb >> 3) + 1 < WD_MAX ? (hb >> 3) + 1 : WD_MAX - 1;
+#pragma unroll
+        for (int i = 0; i < SM; ++i) sa_n[i] = i < IV ? sa_tab[wnx * BM + wm * WM + 32 * i + lr] : 0u;
+        sb_n = sb_tab[sb_blk * WD_MAX + wnx];
+      }
+      v8i xn[SM], wnf[SN];
+      read_frags(IntC<(HS + 1) % S>{}, xn, wnf);
+#pragma unroll
+      for (int i = 0; i < IV; ++i)
+#pragma unroll
+        for (int j = 0; j < SN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wf[j], xf[i], acc[i][j], 0, 0, OPS, (int)sb,
+                                                                      OPS, (int)sa[i]);
+      // one operand read after every MFMA (two at the start while there are more
+      // reads than MFMAs) and the DMA spread over the half-step: a DMA that waits
+      // for room in the memory queue then stalls this wavefront's issue while an
+      // MFMA runs, rather than holding back the first MFMA
+      mfma_read_dma_pattern<IV * SN, 2 * (IV > 0 ? IV + SN : 0), IPW>();
+#pragma unroll
+      for (int i = 0; i < IV; ++i) xf[i] = xn[i];
+#pragma unroll
+      for (int j = 0; j < SN; ++j) wf[j] = wnf[j];
+    };
+
+    // the first group's scale words were read above; sa_n / sb_n feed HS == 0
+#pragma unroll
+    for (int i = 0; i < SM; ++i) sa_n[i] = sa[i];
+    sb_n = sb;
+    for (int hb = 0; hb < H; hb += 8) {
+      half(hb, IntC<0>{});
+      half(hb, IntC<1>{});
+      half(hb, IntC<2>{});
+      half(hb, IntC<3>{});
+      half(hb, IntC<4>{});
+      half(hb, IntC<5>{});
+      half(hb, IntC<6>{});
+      half(hb, IntC<7>{});
+    }
+    // the DMAs issued past the end (out of range, zero-filled) must land, and every
+    // wavefront must be done with the slots, before they are reused below
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
+    __builtin_amdgcn_s_barrier();
+    if constexpr (IV == 0) return;
+
+    // Epilogue through LDS.  Lane l holds, for sub-tile (i, j), row 32 i + (l & 31)
+    // and the columns 32 j + 8 q + 4 (l >> 5) + 0..3, q = 0..3 (registers 4q..4q+3):
+    // 16-byte pieces scattered over 32 rows per store.  Each wavefront instead
+    // writes its bf16 sub-tile to its own LDS slot (rows of WN * 2 bytes, 16-byte
+    // chunk c of row r at position c ^ (r % CPR)) and stores it back row by row,
+    // 16 bytes per lane, so every store instruction writes whole contiguous rows.
+    constexpr int RB = WN * 2, CPR = RB / 16, RPI = 64 / CPR;  // row bytes, chunks per row, rows per store
+    static_assert(WM * RB <= R::SLOT, "staging needs one slot per wavefront");
+    uint8_t* stg = wave == 0 ? sl0 : wave == 1 ? sl1 : wave == 2 ? sl2 : sl3;
+#pragma unroll
+    for (int i = 0; i < IV; ++i) {
+      const int row = 32 * i + lr;
+#pragma unroll
+      for (int j = 0; j < SN; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int chunk = 4 * j + q;
+          uint2 o;
+          o.x = bf16_rne(acc[i][j][4 * q]) | (bf16_rne(acc[i][j][4 * q + 1]) << 16);
+          o.y = bf16_rne(acc[i][j][4 * q + 2]) | (bf16_rne(acc[i][j][4 * q + 3]) << 16);
+          *reinterpret_cast<uint2*>(stg + row * RB + ((chunk ^ (row % CPR)) << 4) + 8 * (lane >> 5)) = o;
+        }
+    }
+    // (a wavefront reads back only what it wrote itself: LDS operations of one
+    // wavefront complete in order, so no barrier is needed; rows of the groups
+    // past IV are past the valid rows and are not stored)
+    const int c = lane % CPR;
+    const int64_t n = n0 + wn * WN + 8 * c;
+#pragma unroll
+    for (int t = 0; t < (IV * 32) / RPI; ++t) {
+      const int row = t * RPI + lane / CPR;
+      const v4i v = *reinterpret_cast<const v4i*>(stg + row * RB + ((c ^ (row % CPR)) << 4));
+      const int64_t m = m0 + wm * WM + row;
+      if (m < m_limit && n < p.N) *reinterpret_cast<v4i*>(C + m * p.ldc + n) = v;
+    }
+  };
+
+  // valid 32-row groups of this wavefront (uniform across the wavefront)
+  int64_t mine = m_limit - (m0 + wm * WM);
+  mine = mine < 0 ? 0 : (mine > WM ? WM : mine);
+  const int iv = __builtin_amdgcn_readfirstlane((int)((mine + 31) / 32));
+  switch (iv) {
+    case 0: body(IntC<0>{}); break;
+    case 1: body(IntC<1>{}); break;
+    case 2: if constexpr (SM >= 2) body(IntC<2 <= SM ? 2 : SM>{}); break;
+    case 3: if constexpr (SM >= 3) body(IntC<3 <= SM ? 3 : SM>{}); break;
+    case 4: if constexpr (SM >= 4) body(IntC<4 <= SM ? 4 : SM>{}); break;
+    case 5: if constexpr (SM >= 5) body(IntC<5 <= SM ? 5 : SM>{}); break;
+    case 6: if constexpr (SM >= 6) body(IntC<6 <= SM ? 6 : SM>{}); break;
+    case 7: if constexpr (SM >= 7) body(IntC<7 <= SM ? 7 : SM>{}); break;
+    default: if constexpr (SM >= 8) body(IntC<8 <= SM ? 8 : SM>{}); break;
+  }
+}
+
+template <int BM, int BN, int WGM, int WGN>
+constexpr int ring_wd_max() { return RingShape<BM, BN, WGM, WGN>::WD_MAX; }
+
+// ---------------------------------------------------------------------------
 // compiled tile table
 
 typedef void (*KernelFn)(const KArgs);
 
-enum Kind { kTile = 0, kStream = 1, kScaled = 2 };
+enum Kind { kTile = 0, kStream = 1, kScaled = 2, kRing = 3 };
 
 struct TileEntry {
   KernelFn fn;
   int bm, bn;
   int kind;    // kTile: both operands via LDS (VALU scale FMA); kStream: weight streaming;
                // kScaled: LDS-DMA tiles + scaled MFMA (no K split)
-  int stages;  // LDS ring depth of kScaled
+  int stages;  // LDS ring depth of kScaled / kRing
   int threads;  // workgroup size
+  int max_wd;   // kRing: most activation-scale words per row (K-blocks / 4) its tables hold
 };
 
 const TileEntry kTiles[] = {
@@ -915,13 +1294,20 @@ const TileEntry kTiles[] = {
     {scaled_tile_kernel<256, 256, 2, 4, 2>, 256, 256, kScaled, 2, 512},
     {scaled_tile_kernel<256, 256, 4, 2, 2>, 256, 256, kScaled, 2, 512},
     {scaled_tile_kernel<256, 128, 4, 2, 2>, 256, 128, kScaled, 2, 512},
+    {scaled_ring_kernel<256, 256, 2, 2>, 256, 256, kRing, 4, 256, ring_wd_max<256, 256, 2, 2>()},
+    {scaled_ring_kernel<256, 128, 2, 2>, 256, 128, kRing, 4, 256, ring_wd_max<256, 128, 2, 2>()},
+    {scaled_ring_kernel<128, 256, 2, 2>, 128, 256, kRing, 4, 256, ring_wd_max<128, 256, 2, 2>()},
+    {scaled_ring_kernel<256, 256, 1, 4>, 256, 256, kRing, 4, 256, ring_wd_max<256, 256, 1, 4>()},
+    {scaled_ring_kernel<128, 256, 1, 4>, 128, 256, kRing, 4, 256, ring_wd_max<128, 256, 1, 4>()},
 };
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 // table entries the automatic choice uses
 constexpr int kCfgStream64x128 = 4;
 constexpr int kCfgScaled128x128 = 13;
 constexpr int kCfgScaled256x256 = 19;
-static_assert(kCfgScaled256x256 < kNumTiles, "tile table");
+constexpr int kCfgRing256x256 = 21;        // 2 x 2 wavefronts
+constexpr int kCfgRing256x256Rows = 24;    // 1 x 4 wavefronts (all share the rows)
+static_assert(kCfgRing256x256Rows < kNumTiles, "tile table");
 
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -944,6 +1330,10 @@ bool gemm_config_by_index(int idx, const GemmProblem& p, int splits, GemmConfig*
   const int KB = (int)(p.K / 128);
   if (splits > KB) splits = KB > 0 ? KB : 1;
   if (p.masked_m && splits != 1) return false;
+  if (kTiles[idx].kind == kRing) {
+    splits = 1;  // never splits K; the scale tables bound K
+    if ((KB + 3) / 4 > kTiles[idx].max_wd) return false;
+  }
   if (kTiles[idx].kind == kScaled) {
     splits = 1;  // this family never splits K
     if (scaled_tile_lds_bytes(kTiles[idx].bm, kTiles[idx].bn, kTiles[idx].stages, (int)p.K) +
@@ -972,7 +1362,11 @@ GemmConfig choose_gemm_config(const GemmProblem& p) {
   GemmConfig cfg;
   const int KB = (int)(p.K / 128);
   if (p.masked_m) {
-    // weight streaming, 64-row M tiles: tiles past an expert's count exit at once
+    // 256 x 256 ring tiles with the four wavefronts side by side in N: a group's
+    // weights are read once per column tile, and a group's valid rows are spread
+    // over all four SIMDs (no operand reads or MFMAs for 32-row groups past the
+    // count); weight streaming over 64-row tiles when K is past the scale tables
+    if (gemm_config_by_index(kCfgRing256x256Rows, p, 1, &cfg)) return cfg;
     gemm_config_by_index(kCfgStream64x128, p, 1, &cfg);
     return cfg;
   }
@@ -987,11 +1381,12 @@ GemmConfig choose_gemm_config(const GemmProblem& p) {
     gemm_config_by_index(idx, p, splits, &cfg);
     return cfg;
   }
-  // prefill: LDS-DMA tiles + scaled MFMA, 128x128 workgroup tiles (two per compute
-  // unit); fall back to the VALU-scaled tile kernel when the scale tables do not fit
-  // 256x256 tiles (8 wavefronts, 64x128 each) once they fill the compute units,
-  // 128x128 tiles (two workgroups per compute unit) below that
+  // prefill: LDS-DMA tiles + scaled MFMA.  256x256 ring tiles once they fill the
+  // compute units (the 8-wavefront two-stage kernel when K is past the ring's
+  // scale tables), 128x128 tiles (two workgroups per compute unit) below that;
+  // the VALU-scaled tile kernel when no scale table fits
   const int64_t big_tiles = cdiv(p.M, 256) * cdiv(p.N, 256);
+  if (big_tiles >= 256 && gemm_config_by_index(kCfgRing256x256, p, 1, &cfg)) return cfg;
   if (big_tiles >= 256 && gemm_config_by_index(kCfgScaled256x256, p, 1, &cfg)) return cfg;
   if (gemm_config_by_index(kCfgScaled128x128, p, 1, &cfg)) return cfg;
   const int idx = 1;
@@ -1033,7 +1428,7 @@ hipError_t launch_gemm(const GemmProblem& p, const GemmConfig& cfg, void* ws, hi
   const int64_t tiles = (int64_t)k.tiles_m * k.tiles_n;
   if (tiles < 1 || p.E < 1 || KB < 1) return hipSuccess;
   size_t dyn = 0;
-  if (t.kind != kTile) {
+  if (t.kind == kStream || t.kind == kScaled) {
     dyn = (t.kind == kStream) ? stream_lds_bytes(t.bm, t.bn, cfg.kb_per_split)
                               : scaled_tile_lds_bytes(t.bm, t.bn, t.stages, (int)p.K);
     if (dyn > kMaxLds) return hipErrorInvalidValue;

@@ -96,10 +96,11 @@ def test_config_table_choices():
     assert n >= 2
     d = F.gemm_config(False, 64, 7168, 18432)
     assert 0 <= d["kernel"] < n and d["splits"] >= 1
-    assert d["splits"] * 0 == 0
     p = F.gemm_config(False, 4096, 4096, 7168)
-    assert p["splits"] == 1
+    assert p["splits"] == 1 and (p["bm"], p["bn"]) == (256, 256)
     m = F.gemm_config(True, 256, 4096, 7168)
-    assert m["splits"] == 1
+    assert m["splits"] == 1 and (m["bm"], m["bn"]) == (256, 256)
+    s = F.gemm_config(False, 2048, 4096, 7168)  # 128 tiles of 256 x 256 would leave half the chip idle
+    assert (s["bm"], s["bn"]) == (128, 128)
     with pytest.raises(F.Fp8bsError):
         F.gemm_config(False, 64, 100, 512)
