@@ -133,27 +133,40 @@ def kernel_times(stream, launches, steps):
 
 
 def graph_step_time(stream, step_fn, n_variants, steps, warmup):
-    """Capture one graph per input variant, replay `steps` of them round-robin, and
-    return wall ms per step with synchronizations on both sides of the timed loop."""
-    graphs = []
+    """Wall ms per step over exactly `steps` steps, with synchronizations on both
+    sides of the timed loop.  Steps are replayed from HIP graphs that each hold a run
+    of consecutive steps over the rotating input variants (one graph of n_variants
+    steps, replayed steps // n_variants times, plus one graph holding the remaining
+    steps), so the host cost of a graph launch is paid once per run of steps rather
+    than once per step, as in a serving loop that queues many steps."""
     with torch.cuda.stream(stream):
         for _ in range(2):
             for v in range(n_variants):
                 step_fn(v)
     stream.synchronize()
-    for v in range(n_variants):
+
+    def capture(n):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=stream):
-            step_fn(v)
-        graphs.append(g)
+            for v in range(n):
+                step_fn(v)
+        return g
+
+    full = capture(n_variants)
+    rest = steps % n_variants
+    tail = capture(rest) if rest else None
     with torch.cuda.stream(stream):
-        for i in range(warmup):
-            graphs[i % n_variants].replay()
+        for i in range(max(1, warmup // n_variants)):
+            full.replay()
+        if tail is not None:
+            tail.replay()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     with torch.cuda.stream(stream):
-        for i in range(steps):
-            graphs[i % n_variants].replay()
+        for i in range(steps // n_variants):
+            full.replay()
+        if tail is not None:
+            tail.replay()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     return (t1 - t0) * 1e3 / steps

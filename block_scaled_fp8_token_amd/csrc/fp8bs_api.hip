@@ -43,8 +43,10 @@ int check_device() {
 }
 
 // Split-K workspace: one buffer per (device, stream), grown on demand.  It holds
-// only the fp32 partials of the call in flight on that stream, which every split
-// overwrites before the reduction reads them, so it needs no initialisation.
+// the per-tile arrival counters of the fused split-K reduction (zeroed once when
+// the buffer is allocated; every call leaves them at zero) and the fp32 partials
+// of the call in flight on that stream, which every split overwrites before they
+// are read.
 struct Workspace {
   void* ptr = nullptr;
   size_t bytes = 0;
@@ -83,6 +85,11 @@ int get_workspace(size_t need, hipStream_t stream, void** out) {
   if (e != hipSuccess) {
     g_last_hip_error = (int)e;
     return FP8BS_ERR_ALLOC;
+  }
+  e = hipMemset(p, 0, fp8bs::gemm_workspace_zeroed_prefix());
+  if (e != hipSuccess) {
+    (void)hipFree(p);
+    return fail_hip(e);
   }
   w.ptr = p;
   w.bytes = sz;

@@ -38,6 +38,9 @@ struct GemmConfig {
 
 GemmConfig choose_gemm_config(const GemmProblem& p);
 size_t gemm_workspace_bytes(const GemmProblem& p, const GemmConfig& cfg);
+// Bytes at the front of every workspace that must be zero when it is first used
+// (split-K arrival counters; every call leaves them at zero again).
+size_t gemm_workspace_zeroed_prefix();
 // ws: the fp32 split partials [splits][M][N] (gemm_workspace_bytes); a split-K
 // launch runs the GEMM kernel and then the reduction kernel on `stream`.
 hipError_t launch_gemm(const GemmProblem& p, const GemmConfig& cfg, void* ws, hipStream_t stream);

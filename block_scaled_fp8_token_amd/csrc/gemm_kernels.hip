@@ -67,6 +67,7 @@ struct KArgs {
   int tiles_m, tiles_n, splits, kb_per_split;
   int sa_words;  // activation-scale words per row a split can touch (LDS table height)
   float* ws;  // split-K partials [splits][M][N]
+  uint32_t* counters;  // per-tile arrival counters of the fused split-K (zero between calls)
 };
 
 __device__ __forceinline__ v8i frag(const uint8_t* p) {
@@ -1256,11 +1257,348 @@ template <int BM, int BN, int WGM, int WGN>
 constexpr int ring_wd_max() { return RingShape<BM, BN, WGM, WGN>::WD_MAX; }
 
 // ---------------------------------------------------------------------------
+// Decode kernel: weight streaming for small M.  NW wavefronts, each owning 32
+// output columns of a 64 x (32 NW) tile; K is split across workgroups (grid y).
+// Per K-block kb of the workgroup's range:
+//   * weights: each lane loads its two 32-byte pieces of the block straight from
+//     HBM into registers in the 32x32x64 MFMA layout (lane l: row l & 31, bytes
+//     32 (l >> 5) + 64 h .. + 31 for K-half h), DB K-blocks ahead of use (measured
+//     on MI355X under back-to-back launches: three K-blocks of 4 KiB per wavefront
+//     in flight stream at 5.5 TB/s, four at 4.6 TB/s);
+//   * activations: the 64 x 128-byte block goes to LDS by DMA (DB - 1 blocks
+//     ahead, one stage per block in flight, K-half rows of 64 bytes with chunk c
+//     of row r at c ^ ((r >> 2) & 3)) and every wavefront reads it from there;
+//   * scales: UE8M0 exponent bytes from LDS tables filled once per workgroup
+//     go to the MFMA's scale operands.
+// Iteration kb waits for its own DMA of kb (and, in order, its loads of kb), meets
+// the other wavefronts at a barrier, DMAs kb + DB - 1 into the stage kb - 1 used,
+// reads the activation operands of kb, issues the weight loads of kb + DB and the
+// four MFMAs of kb.  The epilogue stages the tile through LDS: with a K split the
+// fp32 partial of every split goes to the workspace (splitk_reduce_kernel adds
+// them in split order), without one the bf16 result goes to C.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+constexpr int kSC1 = 16;              // cache-policy bit sc1 of buffer loads/stores (gfx940 family)
+constexpr int kDecodeMaxSplits = 8;   // K splits the decode kernel reduces itself
+constexpr int kCounterBytes = 65536;  // split-K arrival counters at the front of the workspace
+
+template <int NW, int DB_>
+struct DecodeShape {
+  static constexpr int DB = DB_;               // K-blocks of weights in flight per wavefront
+  static constexpr int UN = DB == 3 ? 12 : 4;  // unrolled iterations: stage/register ring and scale byte static
+  static constexpr int IA = 8 / NW;            // activation DMA instructions per wavefront per K-block
+  static constexpr int WMAX = 40;              // scale words per row the table holds (K <= 20480 per split)
+  static constexpr int NBT = (32 * NW + 127) / 128;
+};
+
+template <int NW, int DB_>
+__global__ __launch_bounds__(NW * 64) void decode_kernel(const KArgs p) {
+  using D = DecodeShape<NW, DB_>;
+  constexpr int DB = D::DB, UN = D::UN, IA = D::IA, WMAX = D::WMAX, NBT = D::NBT;
+  constexpr int NT = NW * 64, BN = 32 * NW;
+  static_assert((NW == 4 || NW == 8) && IA >= 1, "decode shape");
+  // one array per stage (see the ring kernel: the compiler's LDS-DMA tracking then
+  // tells a stage's reads from the other stages' DMA)
+  __shared__ __attribute__((aligned(1024))) uint8_t st0[8192];
+  __shared__ __attribute__((aligned(1024))) uint8_t st1[8192];
+  __shared__ __attribute__((aligned(1024))) uint8_t st2[8192];
+  __shared__ __attribute__((aligned(1024))) uint8_t st3[8192];
+  __shared__ __attribute__((aligned(16))) uint32_t sa_tab[WMAX * 64];       // [w][row]
+  __shared__ __attribute__((aligned(16))) uint32_t sb_tab[NBT * WMAX];      // [block][w], byte kb % 4
+  __shared__ __attribute__((aligned(16))) uint8_t stage_out[NW * 64 * 32 * 4];  // epilogue: [wave][64][32] fp32
+  static_assert(DB >= 2 && DB <= 4, "two to four stages");
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t e = blockIdx.z;
+  const int split = blockIdx.y;
+  const int tm = blockIdx.x / p.tiles_n, tn = blockIdx.x - tm * p.tiles_n;
+  int64_t m_limit = p.M;
+  if (p.masked_m) {
+    const int64_t cnt = p.masked_m[e];
+    m_limit = cnt < 0 ? 0 : (cnt > p.M ? p.M : cnt);
+  }
+  const int64_t m0 = (int64_t)tm * 64, n0 = (int64_t)tn * BN;
+  if (m0 >= m_limit) return;
+
+  const int KB = (int)(p.K / 128);
+  const int kb0 = split * p.kb_per_split;
+  const int nk = (KB - kb0 < p.kb_per_split) ? KB - kb0 : p.kb_per_split;  // >= 1 (host)
+  const int nkp = (nk + UN - 1) / UN * UN;  // iterations, padded to whole unrolled groups
+  const int NB = (int)((p.N + 127) / 128);
+  const int64_t rows_valid = (m_limit - m0 < 64) ? m_limit - m0 : 64;
+  int64_t cols_valid = p.N - n0;
+  cols_valid = cols_valid > BN ? BN : cols_valid;
+  const auto rA = make_rsrc(p.a + e * p.sa_e + m0 * p.K, (uint32_t)(rows_valid * p.K));
+  const auto rB = make_rsrc(p.b + e * p.sb_e + n0 * p.K, (uint32_t)(cols_valid * p.K));
+  const int Wd = (KB + 3) / 4;
+  const auto rSA = make_rsrc(p.sfa + e * p.ssfa_e, (uint32_t)(Wd * p.ld_sfa * 4));
+  const auto rSB = make_rsrc(p.sfb + e * p.ssfb_e, (uint32_t)(NB * KB * 4));
+
+  auto stage = [&](auto tag) -> uint8_t* {
+    constexpr int I = decltype(tag)::value;
+    if constexpr (I == 0) return st0;
+    else if constexpr (I == 1) return st1;
+    else if constexpr (I == 2) return st2;
+    else return st3;
+  };
+
+  // activation DMA: instruction t of this wavefront covers K-half hh of rows
+  // 16 rq .. 16 rq + 15 (rq, hh from the instruction index i = wave * IA + t:
+  // hh = i >> 2, rq = i & 3); lane l -> row 16 rq + (l >> 2), position l & 3
+  uint32_t aoff[IA];
+#pragma unroll
+  for (int t = 0; t < IA; ++t) {
+    const int i = wave * IA + t;
+    const int r = (i & 3) * 16 + (lane >> 2);
+    aoff[t] = (uint32_t)(r * p.K) + (uint32_t)((i >> 2) * 64) + (uint32_t)((((lane & 3) ^ swz64(r)) << 4));
+  }
+  auto issue_a = [&](int j, auto tag) {  // j: iteration index of the K-block
+    uint8_t* base = stage(tag);
+    const uint32_t koff = (uint32_t)(kb0 + j) * 128u, oob = j < nk ? 0u : kOOB;
+#pragma unroll
+    for (int t = 0; t < IA; ++t) {
+      const int i = wave * IA + t;
+      uint8_t* dst = base + (i >> 2) * 4096 + (i & 3) * 1024;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, (__attribute__((address_space(3))) void*)dst, 16,
+                                               (int)((aoff[t] + koff) | oob), 0, 0, 0);
+    }
+  };
+  // weight loads: lane l, row n0 + 32 wave + (l & 31), bytes 32 (l >> 5) + 64 h .. + 31
+  const uint32_t boff = (uint32_t)((wave * 32 + (lane & 31)) * p.K) + (uint32_t)(32 * (lane >> 5));
+  auto load_b = [&](int j, v8i (&bh)[2]) {
+    const uint32_t off = (boff + (uint32_t)(kb0 + j) * 128u) | (j < nk ? 0u : kOOB);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const v4i lo = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rB, (int)(off + 64 * h), 0, 0));
+      const v4i hi = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rB, (int)(off + 64 * h + 16), 0, 0));
+      bh[h] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+  };
+
+  // scale tables for this split's K-blocks: activation words of the 64 rows (zero
+  // past the rows and for K-blocks past the split), weight exponent bytes.  The
+  // global loads go out first, then the prologue prefetch, then the LDS writes, so
+  // the table loads' latency overlaps the prefetch.
+  const int w0 = kb0 / 4;                   // kb0 is a multiple of UN, hence of 4 (host)
+  const int nw = nkp / 4;                   // words of this split, <= WMAX (host)
+  constexpr int SA_PT = (WMAX * 64 + NT - 1) / NT, SB_PT = (NBT * WMAX * 4 + NT - 1) / NT;
+  uint32_t sav[SA_PT], sbv[SB_PT];
+#pragma unroll
+  for (int t = 0; t < SA_PT; ++t) {
+    const int idx = t * NT + tid, w = idx >> 6, row = idx & 63;
+    const bool ok = idx < nw * 64 && m0 + row < m_limit && w0 + w < Wd;
+    sav[t] = bload4(rSA, ok ? (uint32_t)(((int64_t)(w0 + w) * p.ld_sfa + m0 + row) * 4) : kOOB);
+  }
+#pragma unroll
+  for (int t = 0; t < SB_PT; ++t) {
+    const int idx = t * NT + tid, b = idx / (WMAX * 4), j = idx - b * (WMAX * 4);
+    const int nb = (int)(n0 >> 7) + b;
+    const bool ok = idx < NBT * WMAX * 4 && nb < NB && j < nk;
+    sbv[t] = bload4(rSB, ok ? (uint32_t)((nb * KB + kb0 + j) * 4) : kOOB);
+  }
+
+  // prologue: weights of iterations 0 .. DB-1 and activations of 0 .. DB-2, in the
+  // order the loop keeps (activations of j + DB - 1, then weights of j + DB)
+  v8i b0[2], b1[2], b2[2], b3[2];
+  auto breg = [&](auto tag) -> v8i (&)[2] {
+    constexpr int I = decltype(tag)::value;
+    if constexpr (I == 0) return b0;
+    else if constexpr (I == 1) return b1;
+    else if constexpr (I == 2) return b2;
+    else return b3;
+  };
+  load_b(0, b0);
+  issue_a(0, IntC<0>{});
+  load_b(1, b1);
+  if constexpr (DB > 2) {
+    issue_a(1, IntC<1>{});
+    load_b(2, b2);
+  }
+  if constexpr (DB > 3) {
+    issue_a(2, IntC<2>{});
+    load_b(3, b3);
+  }
+
+#pragma unroll
+  for (int t = 0; t < SA_PT; ++t) {
+    const int idx = t * NT + tid, w = idx >> 6;
+    uint32_t v = sav[t];
+    const int left = kb0 + nk - 4 * (w0 + w);  // K-blocks of this word inside the split
+    if (left < 4) v &= left <= 0 ? 0u : ((1u << (8 * left)) - 1u);
+    if (idx < WMAX * 64) sa_tab[idx] = v;
+  }
+  uint8_t* sbb = reinterpret_cast<uint8_t*>(sb_tab);
+#pragma unroll
+  for (int t = 0; t < SB_PT; ++t) {
+    const int idx = t * NT + tid;
+    if (idx < NBT * WMAX * 4) sbb[idx] = (uint8_t)((sbv[t] >> 23) & 0xFFu);
+  }
+  // VMEM instructions younger than the activation DMA of the current iteration
+  constexpr int YOUNGER = 4 + (DB - 2) * (IA + 4);
+
+  const int lr = lane & 31, c0 = 2 * (lane >> 5);
+  const uint32_t rd0 = (uint32_t)(lr * 64 + ((c0 ^ swz64(lr)) << 4));
+  const uint32_t rd1 = (uint32_t)(lr * 64 + (((c0 + 1) ^ swz64(lr)) << 4));
+  const int sb_blk = (wave * 32) >> 7;
+
+  auto body = [&](auto iv_tag) {
+    constexpr int IV = decltype(iv_tag)::value;  // 32-row groups with valid rows (1 or 2)
+    v16f acc[IV];
+#pragma unroll
+    for (int i = 0; i < IV; ++i)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[i][q] = 0.0f;
+    uint32_t sa[IV], sb = 0;
+
+    // iteration j = jb + U (jb a multiple of UN): K-block kb0 + j, scale byte U % 4,
+    // LDS stage and weight registers U % DB
+    auto iter = [&](int jb, auto u_tag) {
+      constexpr int U = decltype(u_tag)::value;
+      constexpr int OPS = U % 4;
+      v8i(&bcur)[2] = breg(IntC<U % DB>{});
+      const int j = jb + U;
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_waitcnt(waitcnt_imm(YOUNGER, 15));
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      issue_a(j + DB - 1, IntC<(U + DB - 1) % DB>{});
+      if constexpr (OPS == 0) {
+#pragma unroll
+        for (int i = 0; i < IV; ++i) sa[i] = sa_tab[(j >> 2) * 64 + 32 * i + lr];
+        sb = sb_tab[sb_blk * WMAX + (j >> 2)];
+      }
+      const uint8_t* base = stage(IntC<U % DB>{});
+      v8i af[2][IV];
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int i = 0; i < IV; ++i) {
+          const uint8_t* q = base + h * 4096 + (32 * i) * 64;
+          const v4i lo = *reinterpret_cast<const v4i*>(q + rd0);
+          const v4i hi = *reinterpret_cast<const v4i*>(q + rd1);
+          af[h][i] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        }
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int i = 0; i < IV; ++i)
+          acc[i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bcur[h], af[h][i], acc[i], 0, 0, OPS, (int)sb,
+                                                                   OPS, (int)sa[i]);
+      load_b(j + DB, bcur);  // the registers of kb are free again: fetch kb + DB
+    };
+
+    for (int jb = 0; jb < nkp; jb += UN) {
+      iter(jb, IntC<0>{});
+      iter(jb, IntC<1>{});
+      iter(jb, IntC<2>{});
+      iter(jb, IntC<3>{});
+      if constexpr (UN == 12) {
+        iter(jb, IntC<4>{});
+        iter(jb, IntC<5>{});
+        iter(jb, IntC<6>{});
+        iter(jb, IntC<7>{});
+        iter(jb, IntC<8>{});
+        iter(jb, IntC<9>{});
+        iter(jb, IntC<10>{});
+        iter(jb, IntC<11>{});
+      }
+    }
+    // the prefetches past the range (out of range, zero-filled) must land before
+    // the LDS is reused or released
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
+
+    // epilogue: lane l holds, for row group i, row 32 i + (l & 31) and the columns
+    // 8 q + 4 (l >> 5) + 0..3 of the wavefront's 32 (registers 4q..4q+3).  Stage the
+    // wavefront's 64 x 32 fp32 block in LDS (16-byte chunk c of row r at c ^ (r & 7))
+    // and move it 8 rows of 128 bytes per instruction.
+    float* so = reinterpret_cast<float*>(stage_out + wave * 64 * 128);
+#pragma unroll
+    for (int i = 0; i < IV; ++i) {
+      const int row = 32 * i + lr;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int chunk = 2 * q + (lane >> 5);
+        *reinterpret_cast<v4f*>(reinterpret_cast<uint8_t*>(so) + row * 128 + ((chunk ^ (row & 7)) << 4)) =
+            v4f{acc[i][4 * q], acc[i][4 * q + 1], acc[i][4 * q + 2], acc[i][4 * q + 3]};
+      }
+    }
+    const int ch = lane & 7;
+    const int64_t n = n0 + wave * 32 + 4 * ch;
+    auto staged = [&](int t) -> v4f {
+      const int row = t * 8 + (lane >> 3);
+      return *reinterpret_cast<const v4f*>(reinterpret_cast<const uint8_t*>(so) + row * 128 + ((ch ^ (row & 7)) << 4));
+    };
+    uint16_t* __restrict__ C = p.c + e * p.sc_e;
+    auto store_c = [&](int t, v4f v) {
+      const int64_t m = m0 + t * 8 + (lane >> 3);
+      if (m >= m_limit || n >= p.N) return;
+      uint2 o;
+      o.x = bf16_rne(v[0]) | (bf16_rne(v[1]) << 16);
+      o.y = bf16_rne(v[2]) | (bf16_rne(v[3]) << 16);
+      *reinterpret_cast<uint2*>(C + m * p.ldc + n) = o;
+    };
+    if (p.splits == 1) {
+#pragma unroll
+      for (int t = 0; t < IV * 4; ++t) store_c(t, staged(t));
+      return;
+    }
+    // K split, reduced in this kernel by the last split of the tile to arrive.  The
+    // partials are written with sc1 (coherent across the XCDs' L2 caches: written
+    // through) and complete (s_waitcnt) before this split bumps the tile's arrival
+    // counter; the last arrival reads the other partials with sc1 loads, adds all of
+    // them in split order (deterministic) and writes bf16, and sets the counter back
+    // to zero for the next call.  No cache-wide fence is needed: only the partials
+    // cross workgroups, and they never sit dirty in an L2.
+    const size_t slice = (size_t)p.M * (size_t)p.N;
+    const auto rW = make_rsrc(p.ws, (uint32_t)(((size_t)p.splits * slice) * 4 > 0x7FFFFFFFull
+                                                   ? 0x7FFFFFFFu : (size_t)p.splits * slice * 4));
+    auto woff = [&](int sp, int t) -> uint32_t {
+      const int64_t m = m0 + t * 8 + (lane >> 3);
+      return (m < m_limit && n < p.N) ? (uint32_t)(((size_t)sp * slice + (size_t)m * p.N + n) * 4) : kOOB;
+    };
+#pragma unroll
+    for (int t = 0; t < IV * 4; ++t)
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, staged(t)), rW, (int)woff(split, t), 0, kSC1);
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
+    __builtin_amdgcn_s_barrier();
+    __shared__ int last_flag;
+    const int tile = blockIdx.x;
+    if (tid == 0) {
+      const uint32_t old = __hip_atomic_fetch_add(p.counters + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      last_flag = (old == (uint32_t)(p.splits - 1)) ? 1 : 0;
+    }
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
+    __builtin_amdgcn_s_barrier();
+    if (!last_flag) return;
+    if (tid == 0) __hip_atomic_store(p.counters + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+    for (int t = 0; t < IV * 4; ++t) {
+      v4f part[kDecodeMaxSplits];
+#pragma unroll
+      for (int sp = 0; sp < kDecodeMaxSplits; ++sp)
+        part[sp] = __builtin_bit_cast(
+            v4f, __builtin_amdgcn_raw_buffer_load_b128(rW, (int)(sp < p.splits && sp != split ? woff(sp, t) : kOOB), 0, kSC1));
+      v4f sum = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int sp = 0; sp < kDecodeMaxSplits; ++sp)
+        if (sp < p.splits) sum += sp == split ? staged(t) : part[sp];
+      store_c(t, sum);
+    }
+  };
+
+  // tables and the first DMA in place everywhere
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
+  __builtin_amdgcn_s_barrier();
+  if (rows_valid > 32) body(IntC<2>{});
+  else body(IntC<1>{});
+}
+
+// ---------------------------------------------------------------------------
 // compiled tile table
 
 typedef void (*KernelFn)(const KArgs);
 
-enum Kind { kTile = 0, kStream = 1, kScaled = 2, kRing = 3 };
+enum Kind { kTile = 0, kStream = 1, kScaled = 2, kRing = 3, kDecode = 4 };
 
 struct TileEntry {
   KernelFn fn;
@@ -1269,7 +1607,8 @@ struct TileEntry {
                // kScaled: LDS-DMA tiles + scaled MFMA (no K split)
   int stages;  // LDS ring depth of kScaled / kRing
   int threads;  // workgroup size
-  int max_wd;   // kRing: most activation-scale words per row (K-blocks / 4) its tables hold
+  int max_wd;   // kRing: most activation-scale words per row (K-blocks / 4) its tables hold;
+                // kDecode: the same per K split
 };
 
 const TileEntry kTiles[] = {
@@ -1299,6 +1638,10 @@ const TileEntry kTiles[] = {
     {scaled_ring_kernel<128, 256, 2, 2>, 128, 256, kRing, 4, 256, ring_wd_max<128, 256, 2, 2>()},
     {scaled_ring_kernel<256, 256, 1, 4>, 256, 256, kRing, 4, 256, ring_wd_max<256, 256, 1, 4>()},
     {scaled_ring_kernel<128, 256, 1, 4>, 128, 256, kRing, 4, 256, ring_wd_max<128, 256, 1, 4>()},
+    {decode_kernel<4, 3>, 64, 128, kDecode, 3, 256, DecodeShape<4, 3>::WMAX},
+    {decode_kernel<8, 2>, 64, 256, kDecode, 2, 512, DecodeShape<8, 2>::WMAX},
+    {decode_kernel<4, 2>, 64, 128, kDecode, 2, 256, DecodeShape<4, 2>::WMAX},
+    {decode_kernel<8, 3>, 64, 256, kDecode, 3, 512, DecodeShape<8, 3>::WMAX},
 };
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 // table entries the automatic choice uses
@@ -1307,7 +1650,8 @@ constexpr int kCfgScaled128x128 = 13;
 constexpr int kCfgScaled256x256 = 19;
 constexpr int kCfgRing256x256 = 21;        // 2 x 2 wavefronts
 constexpr int kCfgRing256x256Rows = 24;    // 1 x 4 wavefronts (all share the rows)
-static_assert(kCfgRing256x256Rows < kNumTiles, "tile table");
+constexpr int kCfgDecode64x128 = 26;       // decode kernel, 4 wavefronts, three K-blocks in flight
+static_assert(kCfgDecode64x128 < kNumTiles, "tile table");
 
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -1348,6 +1692,29 @@ bool gemm_config_by_index(int idx, const GemmProblem& p, int splits, GemmConfig*
       ++splits;
     }
   }
+  if (kTiles[idx].kind == kDecode) {
+    // K-blocks per split: a multiple of the unrolled loop (then the scale byte, LDS
+    // stage and weight registers of a K-block are static), at most four per word
+    // of the scale table
+    const int un = kTiles[idx].stages == 3 ? 12 : 4;
+    if (splits > kDecodeMaxSplits) splits = kDecodeMaxSplits;
+    int per = (int)cdiv(cdiv(KB, splits), un) * un;
+    if (per > 4 * kTiles[idx].max_wd) {
+      if (p.masked_m) return false;
+      per = 4 * kTiles[idx].max_wd / un * un;
+    }
+    const int64_t tiles = cdiv(p.M, kTiles[idx].bm) * cdiv(p.N, kTiles[idx].bn);
+    if (cdiv(KB, per) > 1 &&
+        (cdiv(KB, per) > kDecodeMaxSplits || tiles > kCounterBytes / 4 ||
+         cdiv(KB, per) * p.M * p.N * 4 > 0x7FFFFFFF))
+      return false;
+    out->kernel = idx;
+    out->bm = kTiles[idx].bm;
+    out->bn = kTiles[idx].bn;
+    out->kb_per_split = per;
+    out->splits = (int)cdiv(KB, per);
+    return true;
+  }
   out->kernel = idx;
   out->bm = kTiles[idx].bm;
   out->bn = kTiles[idx].bn;
@@ -1371,7 +1738,14 @@ GemmConfig choose_gemm_config(const GemmProblem& p) {
     return cfg;
   }
   if (p.M <= 64) {
-    // decode: weight streaming over 128-column tiles, K split until about 224 workgroups
+    // decode: weight streaming over 128-column tiles with the activations shared
+    // through LDS, K split (and reduced in the kernel) until about 224 workgroups
+    {
+      const int64_t tiles = cdiv(p.N, kTiles[kCfgDecode64x128].bn);
+      int splits = (int)(224 / (tiles > 0 ? tiles : 1));
+      if (splits < 1) splits = 1;
+      if (gemm_config_by_index(kCfgDecode64x128, p, splits, &cfg)) return cfg;
+    }
     const int idx = kCfgStream64x128;
     const int64_t tiles = cdiv(p.N, kTiles[idx].bn);
     int splits = (int)(224 / (tiles > 0 ? tiles : 1));
@@ -1403,8 +1777,10 @@ GemmConfig choose_gemm_config(const GemmProblem& p) {
 
 size_t gemm_workspace_bytes(const GemmProblem& p, const GemmConfig& cfg) {
   if (cfg.splits <= 1) return 0;
-  return (size_t)cfg.splits * (size_t)p.M * (size_t)p.N * sizeof(float);
+  return (size_t)kCounterBytes + (size_t)cfg.splits * (size_t)p.M * (size_t)p.N * sizeof(float);
 }
+
+size_t gemm_workspace_zeroed_prefix() { return (size_t)kCounterBytes; }
 
 hipError_t launch_gemm(const GemmProblem& p, const GemmConfig& cfg, void* ws, hipStream_t stream) {
   if (cfg.kernel < 0 || cfg.kernel >= kNumTiles) return hipErrorInvalidValue;
@@ -1420,9 +1796,12 @@ hipError_t launch_gemm(const GemmProblem& p, const GemmConfig& cfg, void* ws, hi
   k.kb_per_split = cfg.kb_per_split;
   if ((int64_t)cfg.kb_per_split * (cfg.splits - 1) >= KB) return hipErrorInvalidValue;
   k.ws = nullptr;
+  k.counters = nullptr;
   if (cfg.splits > 1) {
+    // workspace: the arrival counters (zero between calls), then the fp32 partials
     if (ws == nullptr) return hipErrorInvalidValue;
-    k.ws = static_cast<float*>(ws);
+    k.counters = static_cast<uint32_t*>(ws);
+    k.ws = reinterpret_cast<float*>(static_cast<char*>(ws) + kCounterBytes);
   }
   k.sa_words = (cfg.kb_per_split + 3) / 4 + 1;
   const int64_t tiles = (int64_t)k.tiles_m * k.tiles_n;
@@ -1445,10 +1824,10 @@ hipError_t launch_gemm(const GemmProblem& p, const GemmConfig& cfg, void* ws, hi
   }
   hipLaunchKernelGGL(t.fn, dim3((unsigned)tiles, (unsigned)cfg.splits, (unsigned)p.E), dim3(t.threads), dyn, stream, k);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || cfg.splits == 1) return e;
+  if (e != hipSuccess || cfg.splits == 1 || t.kind == kDecode) return e;  // the decode kernel reduces itself
   const int64_t threads = p.M * (p.N / 8);
   hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)cdiv(threads, 256)), dim3(256), 0, stream,
-                     static_cast<const float*>(ws), cfg.splits, p.M, p.N, p.c, p.ldc);
+                     static_cast<const float*>(k.ws), cfg.splits, p.M, p.N, p.c, p.ldc);
   return hipGetLastError();
 }
 
