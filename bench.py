@@ -330,7 +330,7 @@ def main():
     ap.add_argument("--counters", action="store_true",
                     help="workload for rocprofv3 --pmc passes: a 256 MiB torch copy (counter calibration), "
                          "then --steps eager steps of --counters-shape; no timing")
-    ap.add_argument("--counters-shape", default="decode", choices=["decode", "prefill"],
+    ap.add_argument("--counters-shape", default="decode", choices=["decode", "prefill", "masked"],
                     help="decode: M=64 N=7168 K=18432; prefill: M=4096 N=4096 K=7168")
     args = ap.parse_args()
 
@@ -348,7 +348,10 @@ def main():
     stream = torch.cuda.Stream()
     shape = W.DENSE_DECODE
     if args.counters:
-        counters_workload(F, shape if args.counters_shape == "decode" else W.DENSE_PREFILL[2], args.steps)
+        if args.counters_shape == "masked":
+            counters_masked_workload(F, W, args.steps)
+        else:
+            counters_workload(F, shape if args.counters_shape == "decode" else W.DENSE_PREFILL[2], args.steps)
         return
     r = bench_dense(F, stream, shape, args.steps, args.warmup)
     print("[bench] %s" % json.dumps(r), file=sys.stderr, flush=True)
@@ -429,6 +432,36 @@ def counters_workload(F, shape, steps):
         F.fp8_block_gemm_nt(qa, sfa, qb, sfb, c=c)
     torch.cuda.synchronize()
     print(json.dumps({"copy_bytes_each_way": 256 << 20, "steps": steps, "config": F.gemm_config(False, shape.M, shape.N, shape.K)}))
+
+
+def counters_masked_workload(F, W, steps):
+    """Kernels for counter passes on the masked gate_up GEMM: the calibration copies,
+    then --steps calls with the Zipf counts, --steps with every count halved and
+    --steps with all counts zero (HBM bytes should follow the valid rows)."""
+    x = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+    y = torch.empty_like(x)
+    for _ in range(3):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    del x, y
+    E, M_max, N, K = W.MOE_E, W.MOE_M_MAX, W.MOE_GATE_UP["N"], W.MOE_GATE_UP["K"]
+    zipf = torch.from_numpy(W.zipf_counts()).to("cuda")
+    xa = randn_bf16((E * M_max, K), seed=11)
+    qa, sfa_flat = F.fp8_quant_group_pack(xa, ld_sf=E * M_max)
+    Wd = (K // 128 + 3) // 4
+    a = qa.view(E, M_max, K)
+    sfa = sfa_flat.view(Wd, E, M_max).permute(1, 0, 2).contiguous()
+    del xa
+    (qb, sfb), = quantized_weights(F, 1, N, K, 21, experts=E)
+    c = torch.empty((E, M_max, N), dtype=torch.bfloat16, device="cuda")
+    sets = [("zipf", zipf), ("halved", (zipf + 1) // 2), ("zero", torch.zeros_like(zipf))]
+    for name, counts in sets:
+        for i in range(steps):
+            F.fp8_block_gemm_grouped_masked(a, sfa, qb, sfb, counts, c=c)
+        torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_each_way": 256 << 20, "steps_per_set": steps,
+                      "sets": {n: {"S": int(cn.sum()), "E_active": int((cn > 0).sum())} for n, cn in sets},
+                      "config": F.gemm_config(True, M_max, N, K)}))
 
 
 def _kernel_hash():
