@@ -22,7 +22,7 @@ import torch
 __all__ = [
     "Fp8bsError", "fp8_quant_group_pack", "silu_mul_quant_group_pack", "fp8_block_quant_128x128",
     "fp8_block_gemm_nt", "fp8_block_gemm_grouped_masked", "gemm_config", "gemm_config_count",
-    "library_path", "header_path", "declared_functions",
+    "library_path", "header_path", "declared_functions", "gemm_config_of",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -50,6 +50,7 @@ _SIGS = {
     "fp8_block_gemm_grouped_masked_cfg": [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I32, _P],
     "fp8bs_gemm_config_count": [],
     "fp8bs_gemm_config": [ctypes.c_int, _I64, _I64, _I64, _I32P, _I32P, _I32P, _I32P],
+    "fp8bs_gemm_config_of": [_I32, ctypes.c_int, _I64, _I64, _I64, _I32, _I32P, _I32P, _I32P],
     "fp8bs_status_string": [ctypes.c_int],
     "fp8bs_last_hip_error": [],
 }
@@ -263,6 +264,18 @@ def fp8_block_gemm_grouped_masked(a: torch.Tensor, sfa: torch.Tensor, b: torch.T
 
 def gemm_config_count() -> int:
     return int(_lib.fp8bs_gemm_config_count())
+
+
+def gemm_config_of(kernel: int, masked: bool, M: int, N: int, K: int, splits: int = 1):
+    """Workgroup tile and split count table entry `kernel` would use for this
+    problem, or None if the entry does not accept it."""
+    bm, bn, sp = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+    st = _lib.fp8bs_gemm_config_of(int(kernel), 1 if masked else 0, M, N, K, int(splits), ctypes.byref(bm),
+                                   ctypes.byref(bn), ctypes.byref(sp))
+    if st == -2:
+        return None
+    _check("fp8bs_gemm_config_of", st)
+    return {"kernel": int(kernel), "bm": bm.value, "bn": bn.value, "splits": sp.value}
 
 
 def gemm_config(masked: bool, M: int, N: int, K: int) -> dict:

@@ -276,6 +276,22 @@ int fp8bs_gemm_config(int masked, int64_t M, int64_t N, int64_t K, int32_t* kern
   return FP8BS_OK;
 }
 
+int fp8bs_gemm_config_of(int32_t kernel, int masked, int64_t M, int64_t N, int64_t K, int32_t splits, int32_t* bm,
+                         int32_t* bn, int32_t* splits_out) {
+  if (M < 0 || N < 0 || K < 128 || K % 128 != 0 || N % 64 != 0) return FP8BS_ERR_SHAPE;
+  if (!bm || !bn || !splits_out) return FP8BS_ERR_NULL;
+  static const int32_t dummy_count = 0;
+  fp8bs::GemmProblem p = masked ? masked_problem(nullptr, nullptr, nullptr, nullptr, nullptr, &dummy_count, 1,
+                                                 M, N, K)
+                                : dense_problem(nullptr, nullptr, M, nullptr, nullptr, nullptr, N, M, N, K);
+  fp8bs::GemmConfig cfg;
+  if (!fp8bs::gemm_config_by_index(kernel, p, splits < 1 ? 1 : splits, &cfg)) return FP8BS_ERR_SHAPE;
+  *bm = cfg.bm;
+  *bn = cfg.bn;
+  *splits_out = cfg.splits;
+  return FP8BS_OK;
+}
+
 const char* fp8bs_status_string(int status) {
   switch (status) {
     case FP8BS_OK: return "ok";

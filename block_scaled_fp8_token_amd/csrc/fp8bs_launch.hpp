@@ -30,10 +30,15 @@ struct GemmProblem {
 
 // Tile configuration chosen for a problem (exposed for reporting and tuning).
 struct GemmConfig {
-  int kernel;   // index into the compiled tile table
-  int bm, bn;   // workgroup tile
-  int splits;   // K splits (1 = no split)
-  int kb_per_split;  // K-blocks per split; every split owns at least one
+  int kernel = 0;   // index into the compiled tile table
+  int bm = 0, bn = 0;   // workgroup tile
+  int splits = 1;   // K splits (1 = no split)
+  int kb_per_split = 1;  // K-blocks per split; every split owns at least one
+  // Column split (dense only): columns [0, n_split) with this configuration and
+  // columns [n_split, N) with table entry tail_kernel (splits 1), so that the first
+  // launch runs whole rounds of its large tiles.  n_split == 0: no column split.
+  int64_t n_split = 0;
+  int tail_kernel = 0, tail_bm = 0, tail_bn = 0, tail_kb_per_split = 1;
 };
 
 GemmConfig choose_gemm_config(const GemmProblem& p);

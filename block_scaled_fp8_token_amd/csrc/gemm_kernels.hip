@@ -1019,14 +1019,11 @@ __global__ __launch_bounds__(256) void scaled_ring_kernel(const KArgs p) {
 
   // DMA: instruction t < IPA of this wavefront covers A rows 16 ri .. 16 ri + 15 with
   // ri = wave * IPA + t, the others B rows likewise; lane l -> row 16 ri + (l >> 2),
-  // slot position l & 3 holding chunk (l & 3) ^ swz64(row) of the K-half.
-  uint32_t boff[IPW];
-#pragma unroll
-  for (int t = 0; t < IPW; ++t) {
-    const int ri = t < IPA ? wave * IPA + t : wave * R::IPB + (t - IPA);
-    const int r = ri * 16 + (lane >> 2);
-    boff[t] = (uint32_t)(r * p.K) + (uint32_t)((((lane & 3) ^ swz64(r)) << 4));
-  }
+  // slot position l & 3 holding chunk (l & 3) ^ swz64(row) of the K-half.  The
+  // swizzle of row 16 ri + (l >> 2) is ((l >> 4) & 3) for every ri, so one per-lane
+  // offset serves all instructions (the row base is added per instruction, which
+  // keeps eight registers free for the loop).
+  const uint32_t lane_off = (uint32_t)((lane >> 2) * p.K) + (uint32_t)((((lane & 3) ^ ((lane >> 4) & 3)) << 4));
   auto issue = [&](int h, auto sl_tag) {
     uint8_t* base = slot(sl_tag);
     // past the last K-half the offset gets the top bit: out of range, zero-filled
@@ -1037,7 +1034,7 @@ __global__ __launch_bounds__(256) void scaled_ring_kernel(const KArgs p) {
       const bool isA = t < IPA;  // static after unrolling
       const int ri = isA ? wave * IPA + t : wave * R::IPB + (t - IPA);
       uint8_t* dst = base + (isA ? 0 : BM * 64) + ri * 1024;
-      const uint32_t off = (boff[t] + hoff) | oob;
+      const uint32_t off = (lane_off + (uint32_t)(ri * 16 * p.K) + hoff) | oob;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(isA ? rA : rB, (__attribute__((address_space(3))) void*)dst, 16,
                                                (int)off, 0, 0, 0);
     }
@@ -1759,8 +1756,29 @@ GemmConfig choose_gemm_config(const GemmProblem& p) {
   // compute units (the 8-wavefront two-stage kernel when K is past the ring's
   // scale tables), 128x128 tiles (two workgroups per compute unit) below that;
   // the VALU-scaled tile kernel when no scale table fits
-  const int64_t big_tiles = cdiv(p.M, 256) * cdiv(p.N, 256);
-  if (big_tiles >= 256 && gemm_config_by_index(kCfgRing256x256, p, 1, &cfg)) return cfg;
+  const int64_t tm256 = cdiv(p.M, 256), tn256 = cdiv(p.N, 256), big_tiles = tm256 * tn256;
+  if (big_tiles >= 256 && gemm_config_by_index(kCfgRing256x256, p, 1, &cfg)) {
+    // With 256x256 tiles, one per compute unit at a time, a last round of less than
+    // half the compute units would leave the rest idle for a whole tile time: run
+    // the leading columns in whole rounds and the remaining columns with 128x128
+    // tiles in a second launch.
+    const int64_t rem = big_tiles % 256;
+    if (rem != 0 && rem < 128 && p.E == 1 && !p.masked_m) {
+      const int64_t lead_tn = (big_tiles / 256) * 256 / tm256;
+      const int64_t n_split = lead_tn * 256;
+      GemmProblem tp = p;
+      tp.N = p.N - n_split;
+      GemmConfig tc;
+      if (n_split > 0 && n_split < p.N && gemm_config_by_index(kCfgScaled128x128, tp, 1, &tc)) {
+        cfg.n_split = n_split;
+        cfg.tail_kernel = tc.kernel;
+        cfg.tail_bm = tc.bm;
+        cfg.tail_bn = tc.bn;
+        cfg.tail_kb_per_split = tc.kb_per_split;
+      }
+    }
+    return cfg;
+  }
   if (big_tiles >= 256 && gemm_config_by_index(kCfgScaled256x256, p, 1, &cfg)) return cfg;
   if (gemm_config_by_index(kCfgScaled128x128, p, 1, &cfg)) return cfg;
   const int idx = 1;
@@ -1784,6 +1802,28 @@ size_t gemm_workspace_zeroed_prefix() { return (size_t)kCounterBytes; }
 
 hipError_t launch_gemm(const GemmProblem& p, const GemmConfig& cfg, void* ws, hipStream_t stream) {
   if (cfg.kernel < 0 || cfg.kernel >= kNumTiles) return hipErrorInvalidValue;
+  if (cfg.n_split > 0) {
+    // column split: [0, n_split) with cfg's kernel, [n_split, N) with the tail entry
+    if (p.E != 1 || p.masked_m || cfg.n_split % 128 != 0 || cfg.n_split >= p.N) return hipErrorInvalidValue;
+    GemmProblem lead = p;
+    lead.N = cfg.n_split;
+    GemmConfig lc = cfg;
+    lc.n_split = 0;
+    hipError_t e = launch_gemm(lead, lc, ws, stream);
+    if (e != hipSuccess) return e;
+    GemmProblem tail = p;
+    tail.N = p.N - cfg.n_split;
+    tail.b = p.b + cfg.n_split * p.K;
+    tail.sfb = p.sfb + (cfg.n_split / 128) * (p.K / 128);
+    tail.c = p.c + cfg.n_split;
+    GemmConfig tc;
+    tc.kernel = cfg.tail_kernel;
+    tc.bm = cfg.tail_bm;
+    tc.bn = cfg.tail_bn;
+    tc.splits = 1;
+    tc.kb_per_split = cfg.tail_kb_per_split;
+    return launch_gemm(tail, tc, ws, stream);
+  }
   const TileEntry& t = kTiles[cfg.kernel];
   KArgs k;
   k.a = p.a; k.sfa = p.sfa; k.b = p.b; k.sfb = p.sfb; k.c = p.c; k.masked_m = p.masked_m;

@@ -141,6 +141,13 @@ int fp8_block_gemm_grouped_masked(const void* a, const uint32_t* sfa, const void
 int fp8bs_gemm_config_count(void);
 int fp8bs_gemm_config(int masked, int64_t M, int64_t N, int64_t K, int32_t* kernel, int32_t* bm,
                       int32_t* bn, int32_t* splits);
+/* Whether table entry `kernel` accepts a dense (masked = 0) or masked (masked = 1)
+ * problem of this shape with `splits` K splits: FP8BS_OK with its workgroup tile and
+ * the split count it would use, FP8BS_ERR_SHAPE if it does not (for instance K past
+ * the entry's scale tables, or a masked problem that would need K splits).
+ * Host-only; launches nothing. */
+int fp8bs_gemm_config_of(int32_t kernel, int masked, int64_t M, int64_t N, int64_t K, int32_t splits,
+                         int32_t* bm, int32_t* bn, int32_t* splits_out);
 int fp8_block_gemm_nt_cfg(const void* a, const uint32_t* sfa, int64_t ld_sfa, const void* b,
                           const float* sfb, void* c, int64_t ldc, int64_t M, int64_t N, int64_t K,
                           int32_t kernel, int32_t splits, void* stream);

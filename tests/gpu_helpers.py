@@ -17,6 +17,16 @@ def to_dev(a: np.ndarray) -> torch.Tensor:
     return torch.from_numpy(a).to(DEV)
 
 
+BF16_NAN = 0x7FC0
+
+
+def poisoned_bf16(*shape) -> torch.Tensor:
+    """A bf16 output buffer filled with NaN, so that any element a kernel fails to
+    write fails the tolerance check (the caching allocator would otherwise hand
+    back a previous call's correct output)."""
+    return torch.full(shape, BF16_NAN, dtype=torch.int16, device=DEV).view(torch.bfloat16)
+
+
 def to_host(t: torch.Tensor) -> np.ndarray:
     t = t.detach()
     if t.dtype == torch.bfloat16:

@@ -104,3 +104,19 @@ def test_config_table_choices():
     assert (s["bm"], s["bn"]) == (128, 128)
     with pytest.raises(F.Fp8bsError):
         F.gemm_config(False, 64, 100, 512)
+
+
+def test_config_of_table_entries():
+    """fp8bs_gemm_config_of: the chosen configuration is one the table accepts; every
+    entry takes a small masked problem; entries with K-bounded scale tables refuse a
+    masked problem whose K is past them (a masked group never splits K)."""
+    n = F.gemm_config_count()
+    for masked, (M, N, K) in ((False, (64, 7168, 18432)), (False, (4096, 4096, 7168)), (True, (256, 4096, 7168))):
+        c = F.gemm_config(masked, M, N, K)
+        e = F.gemm_config_of(c["kernel"], masked, M, N, K, c["splits"])
+        assert e is not None and (e["bm"], e["bn"], e["splits"]) == (c["bm"], c["bn"], c["splits"])
+    assert all(F.gemm_config_of(k, True, 72, 192, 384) is not None for k in range(n))
+    long_k = [F.gemm_config_of(k, True, 256, 4096, 128 * 1024) for k in range(n)]
+    assert any(x is None for x in long_k) and any(x is not None for x in long_k)
+    assert all(x is None or x["splits"] == 1 for x in long_k)
+    assert F.gemm_config_of(n, False, 64, 128, 128) is None

@@ -12,7 +12,7 @@ import torch
 import block_scaled_fp8_token_amd as F
 import oracle as O
 import workloads as W
-from gpu_helpers import DEV, gemm_tolerance_check, sync, to_dev, to_host
+from gpu_helpers import DEV, gemm_tolerance_check, poisoned_bf16, sync, to_dev, to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -35,6 +35,8 @@ def _operands(M, N, K, seed=0, outliers=False, b_std=0.02, varied_blocks=False):
 
 
 def _run(qa, sfa, qb, sfb, kernel=None, splits=None, c=None):
+    if c is None:
+        c = poisoned_bf16(qa.shape[0], qb.shape[0])
     out = F.fp8_block_gemm_nt(to_dev(qa), to_dev(sfa), to_dev(qb), to_dev(sfb), c=c, kernel=kernel,
                               splits=splits)
     sync()
@@ -112,8 +114,8 @@ def test_gemm_decode_full_and_deterministic():
     ref = O.gemm_nt(qa, sfa, qb, sfb)
     print("decode cfg", F.gemm_config(False, s.M, s.N, s.K), flush=True)
     da, dsa, db, dsb = to_dev(qa), to_dev(sfa), to_dev(qb), to_dev(sfb)
-    c1 = F.fp8_block_gemm_nt(da, dsa, db, dsb)
-    c2 = F.fp8_block_gemm_nt(da, dsa, db, dsb)
+    c1 = F.fp8_block_gemm_nt(da, dsa, db, dsb, c=poisoned_bf16(s.M, s.N))
+    c2 = F.fp8_block_gemm_nt(da, dsa, db, dsb, c=poisoned_bf16(s.M, s.N))
     sync()
     c1, c2 = to_host(c1), to_host(c2)
     gemm_tolerance_check(c1, ref, s.name)

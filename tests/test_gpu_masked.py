@@ -8,7 +8,7 @@ import torch
 import block_scaled_fp8_token_amd as F
 import oracle as O
 import workloads as W
-from gpu_helpers import DEV, bf16_to_f64, gemm_tolerance_check, sync, to_dev, to_host
+from gpu_helpers import DEV, bf16_to_f64, gemm_tolerance_check, poisoned_bf16, sync, to_dev, to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -57,6 +57,7 @@ def test_masked_small_all_kernels_edge_counts():
     a, sfa, b, sfb = _moe_operands(E, M_max, N, K, seed=1)
     counts = np.array([0, 1, 72, 100, -2, 33], np.int32)
     for kernel in range(F.gemm_config_count()):
+        assert F.gemm_config_of(kernel, True, M_max, N, K) is not None, kernel
         c = _run_masked(a, sfa, b, sfb, counts, kernel=kernel)
         _check(c, a, sfa, b, sfb, counts, what="kernel %d" % kernel)
 
@@ -67,7 +68,7 @@ def test_masked_full_counts_equal_dense():
     counts = np.full(E, M_max, np.int32)
     c = _run_masked(a, sfa, b, sfb, counts)
     for e in range(E):
-        d = F.fp8_block_gemm_nt(to_dev(a[e]), to_dev(sfa[e]), to_dev(b[e]), to_dev(sfb[e]))
+        d = F.fp8_block_gemm_nt(to_dev(a[e]), to_dev(sfa[e]), to_dev(b[e]), to_dev(sfb[e]), c=poisoned_bf16(M_max, N))
         sync()
         ref = O.gemm_nt(a[e], sfa[e], b[e], sfb[e])
         gemm_tolerance_check(c[e], ref, "masked e%d" % e)
