@@ -1568,19 +1568,31 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const KArgs p) {
     __builtin_amdgcn_s_barrier();
     if (!last_flag) return;
     if (tid == 0) __hip_atomic_store(p.counters + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // the other splits' partials, four splits at a time: every load of a batch is
+    // issued before the first add (one memory round trip per batch, not one per
+    // row group), and the adds keep split order
+    v4f sum[IV * 4];
 #pragma unroll
-    for (int t = 0; t < IV * 4; ++t) {
-      v4f part[kDecodeMaxSplits];
+    for (int t = 0; t < IV * 4; ++t) sum[t] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int sb = 0; sb < p.splits; sb += 4) {
+      v4f part[4][IV * 4];
 #pragma unroll
-      for (int sp = 0; sp < kDecodeMaxSplits; ++sp)
-        part[sp] = __builtin_bit_cast(
-            v4f, __builtin_amdgcn_raw_buffer_load_b128(rW, (int)(sp < p.splits && sp != split ? woff(sp, t) : kOOB), 0, kSC1));
-      v4f sum = {0.f, 0.f, 0.f, 0.f};
+      for (int u = 0; u < 4; ++u)
 #pragma unroll
-      for (int sp = 0; sp < kDecodeMaxSplits; ++sp)
-        if (sp < p.splits) sum += sp == split ? staged(t) : part[sp];
-      store_c(t, sum);
+        for (int t = 0; t < IV * 4; ++t) {
+          const int sp = sb + u;
+          part[u][t] = __builtin_bit_cast(
+              v4f, __builtin_amdgcn_raw_buffer_load_b128(rW, (int)(sp < p.splits && sp != split ? woff(sp, t) : kOOB), 0, kSC1));
+        }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int t = 0; t < IV * 4; ++t)
+          if (sb + u < p.splits) sum[t] += sb + u == split ? staged(t) : part[u][t];
     }
+#pragma unroll
+    for (int t = 0; t < IV * 4; ++t) store_c(t, sum[t]);
   };
 
   // tables and the first DMA in place everywhere
