@@ -252,6 +252,41 @@ def bench_masked_gate_up(F, W, stream, steps, warmup):
     return r
 
 
+def bench_contiguous_gate_up(F, W, stream, steps, warmup):
+    """The gate_up workload in the contiguous grouped layout: the Zipf counts' rows in
+    128-row runs per expert (padding rows included in the launch, skipped blocks none)."""
+    E, N, K = W.MOE_E, W.MOE_GATE_UP["N"], W.MOE_GATE_UP["K"]
+    counts_np = W.zipf_counts()
+    S = int(counts_np.sum())
+    E_active = int((counts_np > 0).sum())
+    mi_np = W.contiguous_layout(counts_np)
+    M = len(mi_np)
+    m_indices = torch.from_numpy(mi_np).to("cuda")
+    x = randn_bf16((M, K), seed=13)
+    qa, sfa = F.fp8_quant_group_pack(x)
+    del x
+    copies = quantized_weights(F, n_copies_for(E * N * K, floor=1), N, K, 23, experts=E)
+    nv = len(copies)
+    c = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+
+    def gemm(s):
+        qb, sfb = copies[s % nv]
+        F.fp8_block_gemm_grouped_contiguous(qa, sfa, qb, sfb, m_indices, c=c, stream=stream)
+
+    with torch.cuda.stream(stream):
+        for i in range(warmup):
+            gemm(i)
+    (t,) = kernel_times(stream, [gemm], steps)
+    r = {"workload": "moe_gate_up_contiguous_E32_N4096_K7168", "S": S, "M_rows": M, "E_active": E_active,
+         "gemm_us": t * 1e3, "gemm_tflops": masked_flops(S, N, K) / (t * 1e-3) / 1e12,
+         "gemm_gbs": masked_bytes(S, E_active, N, K) / (t * 1e-3) / 1e9, "weight_copies": nv,
+         "config": F.gemm_config(2, M, N, K)}
+    r["frac_hbm"] = r["gemm_gbs"] / HBM_PEAK_GBS
+    r["frac_mfma"] = r["gemm_tflops"] / FP8_PEAK_TFLOPS
+    del copies, qa, sfa, c, m_indices
+    return r
+
+
 def bench_silu_down(F, W, stream, steps, warmup):
     E, M_max, H, N = W.MOE_E, W.MOE_M_MAX, W.MOE_DOWN["H"], W.MOE_DOWN["N"]
     K = H
@@ -403,6 +438,8 @@ def main():
         rows.append(bench_masked_gate_up(F, W, stream, max(10, args.steps // 4), args.warmup))
         print("[bench] %s" % json.dumps(rows[-1]), file=sys.stderr, flush=True)
         rows.append(bench_silu_down(F, W, stream, max(10, args.steps // 4), args.warmup))
+        print("[bench] %s" % json.dumps(rows[-1]), file=sys.stderr, flush=True)
+        rows.append(bench_contiguous_gate_up(F, W, stream, max(10, args.steps // 4), args.warmup))
         print("[bench] %s" % json.dumps(rows[-1]), file=sys.stderr, flush=True)
         print("%-58s %10s %10s %10s %8s %8s" % ("workload", "gemm_us", "TFLOPS", "GB/s", "%MFMA", "%HBM"),
               file=sys.stderr)

@@ -48,6 +48,9 @@ _SIGS = {
     "fp8_block_gemm_nt_cfg": [_P, _P, _I64, _P, _P, _P, _I64, _I64, _I64, _I64, _I32, _I32, _P],
     "fp8_block_gemm_grouped_masked": [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _P],
     "fp8_block_gemm_grouped_masked_cfg": [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I32, _P],
+    "fp8_block_gemm_grouped_contiguous": [_P, _P, _I64, _P, _P, _P, _I64, _P, _I64, _I64, _I64, _I64, _P],
+    "fp8_block_gemm_grouped_contiguous_cfg": [_P, _P, _I64, _P, _P, _P, _I64, _P, _I64, _I64, _I64, _I64, _I32,
+                                              _P],
     "fp8bs_gemm_config_count": [],
     "fp8bs_gemm_config": [ctypes.c_int, _I64, _I64, _I64, _I32P, _I32P, _I32P, _I32P],
     "fp8bs_gemm_config_of": [_I32, ctypes.c_int, _I64, _I64, _I64, _I32, _I32P, _I32P, _I32P],
@@ -262,15 +265,54 @@ def fp8_block_gemm_grouped_masked(a: torch.Tensor, sfa: torch.Tensor, b: torch.T
     return c
 
 
+def fp8_block_gemm_grouped_contiguous(a: torch.Tensor, sfa: torch.Tensor, b: torch.Tensor, sfb: torch.Tensor,
+                                      m_indices: torch.Tensor, c: torch.Tensor | None = None,
+                                      kernel: int | None = None, stream=None) -> torch.Tensor:
+    """Contiguous grouped GEMM -> bf16 [M, N].  a uint8 [M, K] (rows grouped by expert in runs
+    aligned to 128 rows), sfa int32 [ceil(K/512), ld_sfa], b uint8 [E, N, K],
+    sfb float32 [E, ceil(N/128), K/128], m_indices int32 [M] (-1: padding row)."""
+    _expect(a, "a", _E4M3, 2)
+    _contig(a, "a")
+    _expect(b, "b", _E4M3, 3)
+    _contig(b, "b")
+    _expect(sfa, "sfa", (torch.int32, torch.uint32), 2)
+    _expect(sfb, "sfb", (torch.float32,), 3)
+    _contig(sfb, "sfb")
+    _expect(m_indices, "m_indices", (torch.int32,), 1)
+    _contig(m_indices, "m_indices")
+    M, K = a.shape
+    E, N = b.shape[0], b.shape[1]
+    if b.shape[2] != K or sfb.shape[0] != E or m_indices.shape[0] != M:
+        raise ValueError("inconsistent shapes")
+    if c is None:
+        c = torch.empty((M, N), dtype=torch.bfloat16, device=a.device)
+    _expect(c, "c", _BF16, 2)
+    if tuple(c.shape) != (M, N):
+        raise ValueError("c must be [M, N]")
+    s = _stream(stream)
+    args = (a.data_ptr(), sfa.data_ptr(), sfa.stride(0), b.data_ptr(), sfb.data_ptr(), c.data_ptr(), c.stride(0),
+            m_indices.data_ptr(), E, M, N, K)
+    if kernel is None:
+        st = _lib.fp8_block_gemm_grouped_contiguous(*args, s)
+    else:
+        st = _lib.fp8_block_gemm_grouped_contiguous_cfg(*args, int(kernel), s)
+    _check("fp8_block_gemm_grouped_contiguous", st)
+    return c
+
+
+LAYOUT_DENSE, LAYOUT_MASKED, LAYOUT_CONTIGUOUS = 0, 1, 2
+
+
 def gemm_config_count() -> int:
     return int(_lib.fp8bs_gemm_config_count())
 
 
-def gemm_config_of(kernel: int, masked: bool, M: int, N: int, K: int, splits: int = 1):
+def gemm_config_of(kernel: int, masked, M: int, N: int, K: int, splits: int = 1):
     """Workgroup tile and split count table entry `kernel` would use for this
-    problem, or None if the entry does not accept it."""
+    problem, or None if the entry does not accept it.  masked: False/0 dense,
+    True/1 masked grouped, 2 contiguous grouped."""
     bm, bn, sp = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
-    st = _lib.fp8bs_gemm_config_of(int(kernel), 1 if masked else 0, M, N, K, int(splits), ctypes.byref(bm),
+    st = _lib.fp8bs_gemm_config_of(int(kernel), int(masked), M, N, K, int(splits), ctypes.byref(bm),
                                    ctypes.byref(bn), ctypes.byref(sp))
     if st == -2:
         return None
@@ -278,9 +320,10 @@ def gemm_config_of(kernel: int, masked: bool, M: int, N: int, K: int, splits: in
     return {"kernel": int(kernel), "bm": bm.value, "bn": bn.value, "splits": sp.value}
 
 
-def gemm_config(masked: bool, M: int, N: int, K: int) -> dict:
+def gemm_config(masked, M: int, N: int, K: int) -> dict:
+    """Automatic choice for a dense (False/0), masked (True/1) or contiguous grouped (2) problem."""
     k, bm, bn, sp = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
-    st = _lib.fp8bs_gemm_config(1 if masked else 0, M, N, K, ctypes.byref(k), ctypes.byref(bm),
+    st = _lib.fp8bs_gemm_config(int(masked), M, N, K, ctypes.byref(k), ctypes.byref(bm),
                                 ctypes.byref(bn), ctypes.byref(sp))
     _check("fp8bs_gemm_config", st)
     return {"kernel": k.value, "bm": bm.value, "bn": bn.value, "splits": sp.value}

@@ -166,6 +166,37 @@ fp8bs::GemmProblem masked_problem(const void* a, const uint32_t* sfa, const void
   return p;
 }
 
+int check_contiguous(const void* a, const uint32_t* sfa, int64_t ld_sfa, const void* b, const float* sfb,
+                     const void* c, int64_t ldc, const int32_t* m_indices, int64_t E, int64_t M, int64_t N,
+                     int64_t K) {
+  if (E < 0) return FP8BS_ERR_SHAPE;
+  const int st = check_dense(a, sfa, ld_sfa, b, sfb, c, ldc, M, N, K);
+  if (st != FP8BS_OK) return st;
+  if (E == 0) return 1;  // no expert: every row is padding
+  if (!m_indices) return FP8BS_ERR_NULL;
+  if (!aligned(m_indices, 4)) return FP8BS_ERR_ALIGN;
+  return FP8BS_OK;
+}
+
+fp8bs::GemmProblem contiguous_problem(const void* a, const uint32_t* sfa, int64_t ld_sfa, const void* b,
+                                      const float* sfb, void* c, int64_t ldc, const int32_t* m_indices,
+                                      int64_t E, int64_t M, int64_t N, int64_t K) {
+  fp8bs::GemmProblem p = dense_problem(a, sfa, ld_sfa, b, sfb, c, ldc, M, N, K);
+  p.m_indices = m_indices;
+  p.groups = E;
+  return p;
+}
+
+// A problem of the given layout (0 dense, 1 masked, 2 contiguous) for host-side
+// configuration queries only: its pointers are placeholders that are never read.
+fp8bs::GemmProblem host_problem(int layout, int64_t M, int64_t N, int64_t K) {
+  static const int32_t placeholder = 0;
+  if (layout == 1) return masked_problem(nullptr, nullptr, nullptr, nullptr, nullptr, &placeholder, 1, M, N, K);
+  if (layout == 2)
+    return contiguous_problem(nullptr, nullptr, M, nullptr, nullptr, nullptr, N, &placeholder, 1, M, N, K);
+  return dense_problem(nullptr, nullptr, M, nullptr, nullptr, nullptr, N, M, N, K);
+}
+
 }  // namespace
 
 extern "C" {
@@ -258,16 +289,39 @@ int fp8_block_gemm_grouped_masked_cfg(const void* a, const uint32_t* sfa, const 
   return run_gemm(p, cfg, static_cast<hipStream_t>(stream));
 }
 
+int fp8_block_gemm_grouped_contiguous(const void* a, const uint32_t* sfa, int64_t ld_sfa, const void* b,
+                                      const float* sfb, void* c, int64_t ldc, const int32_t* m_indices, int64_t E,
+                                      int64_t M, int64_t N, int64_t K, void* stream) {
+  int st = check_contiguous(a, sfa, ld_sfa, b, sfb, c, ldc, m_indices, E, M, N, K);
+  if (st != FP8BS_OK) return st > 0 ? FP8BS_OK : st;
+  st = check_device();
+  if (st != FP8BS_OK) return st;
+  const fp8bs::GemmProblem p = contiguous_problem(a, sfa, ld_sfa, b, sfb, c, ldc, m_indices, E, M, N, K);
+  return run_gemm(p, fp8bs::choose_gemm_config(p), static_cast<hipStream_t>(stream));
+}
+
+int fp8_block_gemm_grouped_contiguous_cfg(const void* a, const uint32_t* sfa, int64_t ld_sfa, const void* b,
+                                          const float* sfb, void* c, int64_t ldc, const int32_t* m_indices,
+                                          int64_t E, int64_t M, int64_t N, int64_t K, int32_t kernel,
+                                          void* stream) {
+  int st = check_contiguous(a, sfa, ld_sfa, b, sfb, c, ldc, m_indices, E, M, N, K);
+  if (st != FP8BS_OK) return st > 0 ? FP8BS_OK : st;
+  st = check_device();
+  if (st != FP8BS_OK) return st;
+  const fp8bs::GemmProblem p = contiguous_problem(a, sfa, ld_sfa, b, sfb, c, ldc, m_indices, E, M, N, K);
+  fp8bs::GemmConfig cfg;
+  if (!fp8bs::gemm_config_by_index(kernel, p, 1, &cfg)) return FP8BS_ERR_SHAPE;
+  return run_gemm(p, cfg, static_cast<hipStream_t>(stream));
+}
+
 int fp8bs_gemm_config_count(void) { return fp8bs::gemm_config_count(); }
 
 int fp8bs_gemm_config(int masked, int64_t M, int64_t N, int64_t K, int32_t* kernel, int32_t* bm, int32_t* bn,
                       int32_t* splits) {
   if (M < 0 || N < 0 || K < 128 || K % 128 != 0 || N % 64 != 0) return FP8BS_ERR_SHAPE;
   if (!kernel || !bm || !bn || !splits) return FP8BS_ERR_NULL;
-  static const int32_t dummy_count = 0;
-  fp8bs::GemmProblem p = masked ? masked_problem(nullptr, nullptr, nullptr, nullptr, nullptr, &dummy_count, 1,
-                                                 M, N, K)
-                                : dense_problem(nullptr, nullptr, M, nullptr, nullptr, nullptr, N, M, N, K);
+  if (masked < 0 || masked > 2) return FP8BS_ERR_SHAPE;
+  const fp8bs::GemmProblem p = host_problem(masked, M, N, K);
   const fp8bs::GemmConfig cfg = fp8bs::choose_gemm_config(p);
   *kernel = cfg.kernel;
   *bm = cfg.bm;
@@ -280,10 +334,8 @@ int fp8bs_gemm_config_of(int32_t kernel, int masked, int64_t M, int64_t N, int64
                          int32_t* bn, int32_t* splits_out) {
   if (M < 0 || N < 0 || K < 128 || K % 128 != 0 || N % 64 != 0) return FP8BS_ERR_SHAPE;
   if (!bm || !bn || !splits_out) return FP8BS_ERR_NULL;
-  static const int32_t dummy_count = 0;
-  fp8bs::GemmProblem p = masked ? masked_problem(nullptr, nullptr, nullptr, nullptr, nullptr, &dummy_count, 1,
-                                                 M, N, K)
-                                : dense_problem(nullptr, nullptr, M, nullptr, nullptr, nullptr, N, M, N, K);
+  if (masked < 0 || masked > 2) return FP8BS_ERR_SHAPE;
+  const fp8bs::GemmProblem p = host_problem(masked, M, N, K);
   fp8bs::GemmConfig cfg;
   if (!fp8bs::gemm_config_by_index(kernel, p, splits < 1 ? 1 : splits, &cfg)) return FP8BS_ERR_SHAPE;
   *bm = cfg.bm;

@@ -16,17 +16,24 @@ hipError_t launch_silu_mul_quant(const uint16_t* x, const int32_t* masked_m, int
 hipError_t launch_block_quant(const uint16_t* w, int64_t N, int64_t K, uint8_t* q, float* sfb,
                               hipStream_t stream);
 
-// One GEMM problem: dense (masked_m == nullptr, E == 1) or masked grouped.
+// One GEMM problem: dense (masked_m == nullptr, m_indices == nullptr, E == 1), masked
+// grouped (masked_m set), or contiguous grouped (m_indices set, E == 1: the rows of A
+// and C are grouped by weight group in aligned runs, B holds `groups` weight sets).
 struct GemmProblem {
   const uint8_t* a;          // e4m3 [E][M][K]
   const uint32_t* sfa;       // packed UE8M0 [E][W][ld_sfa]
-  const uint8_t* b;          // e4m3 [E][N][K]
-  const float* sfb;          // fp32 [E][ceil(N/128)][K/128]
+  const uint8_t* b;          // e4m3 [E][N][K] ([groups][N][K] for the contiguous layout)
+  const float* sfb;          // fp32 [E][ceil(N/128)][K/128] (likewise)
   uint16_t* c;               // bf16 [E][M][ldc]
   const int32_t* masked_m;   // [E] valid rows per group, or nullptr (all M rows valid)
   int64_t E, M, N, K;
   int64_t ld_sfa, ldc;
+  const int32_t* m_indices = nullptr;  // [M] weight group of every row (-1: padding), or nullptr
+  int64_t groups = 1;                  // weight groups of the contiguous layout
 };
+
+// Rows per aligned run of one weight group in the contiguous grouped layout.
+constexpr int64_t kContiguousAlign = 128;
 
 // Tile configuration chosen for a problem (exposed for reporting and tuning).
 struct GemmConfig {

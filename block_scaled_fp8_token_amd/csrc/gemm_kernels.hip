@@ -68,7 +68,19 @@ struct KArgs {
   int sa_words;  // activation-scale words per row a split can touch (LDS table height)
   float* ws;  // split-K partials [splits][M][N]
   uint32_t* counters;  // per-tile arrival counters of the fused split-K (zero between calls)
+  const int32_t* m_indices;  // contiguous grouped layout: weight group of every row, or nullptr
+  int64_t groups;            // weight groups m_indices may name
 };
+
+// Weight group of the tile whose first row is m0: the grid's group e (dense and
+// masked calls), or in the contiguous grouped layout the group of row m0, where
+// every aligned tile holds rows of one group followed by padding; -1 (tile
+// skipped) when that row is padding or names no group.
+__device__ __forceinline__ int64_t weight_group(const KArgs& p, int64_t e, int64_t m0) {
+  if (!p.m_indices) return e;
+  const int64_t g = p.m_indices[m0];
+  return (g < 0 || g >= p.groups) ? -1 : g;
+}
 
 __device__ __forceinline__ v8i frag(const uint8_t* p) {
   const uint4 lo = *reinterpret_cast<const uint4*>(p);
@@ -186,11 +198,13 @@ __global__ __launch_bounds__(256) void gemm_kernel(const KArgs p) {
   }
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
   if (m0 >= m_limit) return;  // whole tile past the mask: no loads, no MFMA
+  const int64_t eb = weight_group(p, e, m0);
+  if (eb < 0) return;
 
   const uint8_t* __restrict__ A = p.a + e * p.sa_e;
   const uint32_t* __restrict__ SA = p.sfa + e * p.ssfa_e;
-  const uint8_t* __restrict__ B = p.b + e * p.sb_e;
-  const float* __restrict__ SB = p.sfb + e * p.ssfb_e;
+  const uint8_t* __restrict__ B = p.b + eb * p.sb_e;
+  const float* __restrict__ SB = p.sfb + eb * p.ssfb_e;
   uint16_t* __restrict__ C = p.c + e * p.sc_e;
   const int KB = (int)(p.K / 128);
   const int kb0 = split * p.kb_per_split;
@@ -337,6 +351,8 @@ __global__ __launch_bounds__(256) void stream_kernel(const KArgs p) {
   }
   const int64_t m0 = (int64_t)tm * BM;
   if (m0 >= m_limit) return;  // whole tile past the mask: no loads, no MFMA
+  const int64_t eb = weight_group(p, e, m0);
+  if (eb < 0) return;
   const int64_t n0 = (int64_t)tn * BN;
   const int64_t nw0 = n0 + wave * (WSN * 16);  // this wavefront's first column
 
@@ -358,9 +374,9 @@ __global__ __launch_bounds__(256) void stream_kernel(const KArgs p) {
   int64_t cols_valid = p.N - nw0;
   cols_valid = cols_valid < 0 ? 0 : (cols_valid > WSN * 16 ? WSN * 16 : cols_valid);
   const auto rA = make_rsrc(p.a + e * p.sa_e + m0 * p.K, (uint32_t)(rows_valid * p.K));
-  const auto rB = make_rsrc(p.b + e * p.sb_e + (cols_valid > 0 ? nw0 : 0) * p.K, (uint32_t)(cols_valid * p.K));
+  const auto rB = make_rsrc(p.b + eb * p.sb_e + (cols_valid > 0 ? nw0 : 0) * p.K, (uint32_t)(cols_valid * p.K));
   const auto rSA = make_rsrc(p.sfa + e * p.ssfa_e, (uint32_t)(Wd * p.ld_sfa * 4));
-  const auto rSB = make_rsrc(p.sfb + e * p.ssfb_e, (uint32_t)(NB * KB * 4));
+  const auto rSB = make_rsrc(p.sfb + eb * p.ssfb_e, (uint32_t)(NB * KB * 4));
   uint16_t* __restrict__ C = p.c + e * p.sc_e;
 
   uint4 ar[DEPTH][CA];
@@ -537,6 +553,8 @@ __global__ __launch_bounds__(WGM * WGN * 64) void scaled_tile_kernel(const KArgs
   }
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
   if (m0 >= m_limit) return;
+  const int64_t eb = weight_group(p, e, m0);
+  if (eb < 0) return;
 
   const int KB = (int)(p.K / 128);
   const int Wd = (KB + 3) / 4;
@@ -549,9 +567,9 @@ __global__ __launch_bounds__(WGM * WGN * 64) void scaled_tile_kernel(const KArgs
   int64_t cols_valid = p.N - n0;
   cols_valid = cols_valid > BN ? BN : cols_valid;
   const auto rA = make_rsrc(p.a + e * p.sa_e + m0 * p.K, (uint32_t)(rows_valid * p.K));
-  const auto rB = make_rsrc(p.b + e * p.sb_e + n0 * p.K, (uint32_t)(cols_valid * p.K));
+  const auto rB = make_rsrc(p.b + eb * p.sb_e + n0 * p.K, (uint32_t)(cols_valid * p.K));
   const auto rSA = make_rsrc(p.sfa + e * p.ssfa_e, (uint32_t)(Wd * p.ld_sfa * 4));
-  const auto rSB = make_rsrc(p.sfb + e * p.ssfb_e, (uint32_t)(NB * KB * 4));
+  const auto rSB = make_rsrc(p.sfb + eb * p.ssfb_e, (uint32_t)(NB * KB * 4));
 
   auto stage_ptr = [&](auto st_tag) -> uint8_t* {
     constexpr int S = decltype(st_tag)::value;
@@ -724,6 +742,8 @@ __global__ __launch_bounds__(WGM * WGN * 64) void scaled_pipe_kernel(const KArgs
   }
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
   if (m0 >= m_limit) return;
+  const int64_t eb = weight_group(p, e, m0);
+  if (eb < 0) return;
 
   const int KB = (int)(p.K / 128);
   const int Wd = (KB + 3) / 4;
@@ -736,9 +756,9 @@ __global__ __launch_bounds__(WGM * WGN * 64) void scaled_pipe_kernel(const KArgs
   int64_t cols_valid = p.N - n0;
   cols_valid = cols_valid > BN ? BN : cols_valid;
   const auto rA = make_rsrc(p.a + e * p.sa_e + m0 * p.K, (uint32_t)(rows_valid * p.K));
-  const auto rB = make_rsrc(p.b + e * p.sb_e + n0 * p.K, (uint32_t)(cols_valid * p.K));
+  const auto rB = make_rsrc(p.b + eb * p.sb_e + n0 * p.K, (uint32_t)(cols_valid * p.K));
   const auto rSA = make_rsrc(p.sfa + e * p.ssfa_e, (uint32_t)(Wd * p.ld_sfa * 4));
-  const auto rSB = make_rsrc(p.sfb + e * p.ssfb_e, (uint32_t)(NB * KB * 4));
+  const auto rSB = make_rsrc(p.sfb + eb * p.ssfb_e, (uint32_t)(NB * KB * 4));
 
   auto stage_ptr = [&](auto st_tag) -> uint8_t* {
     if constexpr (decltype(st_tag)::value == 0) return st0;
@@ -996,6 +1016,8 @@ __global__ __launch_bounds__(256) void scaled_ring_kernel(const KArgs p) {
   }
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
   if (m0 >= m_limit) return;
+  const int64_t eb = weight_group(p, e, m0);
+  if (eb < 0) return;
 
   const int KB = (int)(p.K / 128);
   const int Wd = (KB + 3) / 4;  // <= WD_MAX (checked by the host)
@@ -1005,9 +1027,9 @@ __global__ __launch_bounds__(256) void scaled_ring_kernel(const KArgs p) {
   int64_t cols_valid = p.N - n0;
   cols_valid = cols_valid > BN ? BN : cols_valid;
   const auto rA = make_rsrc(p.a + e * p.sa_e + m0 * p.K, (uint32_t)(rows_valid * p.K));
-  const auto rB = make_rsrc(p.b + e * p.sb_e + n0 * p.K, (uint32_t)(cols_valid * p.K));
+  const auto rB = make_rsrc(p.b + eb * p.sb_e + n0 * p.K, (uint32_t)(cols_valid * p.K));
   const auto rSA = make_rsrc(p.sfa + e * p.ssfa_e, (uint32_t)(Wd * p.ld_sfa * 4));
-  const auto rSB = make_rsrc(p.sfb + e * p.ssfb_e, (uint32_t)(NB * KB * 4));
+  const auto rSB = make_rsrc(p.sfb + eb * p.ssfb_e, (uint32_t)(NB * KB * 4));
 
   auto slot = [&](auto sl_tag) -> uint8_t* {
     constexpr int I = decltype(sl_tag)::value;
@@ -1316,6 +1338,8 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const KArgs p) {
   }
   const int64_t m0 = (int64_t)tm * 64, n0 = (int64_t)tn * BN;
   if (m0 >= m_limit) return;
+  const int64_t eb = weight_group(p, e, m0);
+  if (eb < 0) return;
 
   const int KB = (int)(p.K / 128);
   const int kb0 = split * p.kb_per_split;
@@ -1326,10 +1350,10 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const KArgs p) {
   int64_t cols_valid = p.N - n0;
   cols_valid = cols_valid > BN ? BN : cols_valid;
   const auto rA = make_rsrc(p.a + e * p.sa_e + m0 * p.K, (uint32_t)(rows_valid * p.K));
-  const auto rB = make_rsrc(p.b + e * p.sb_e + n0 * p.K, (uint32_t)(cols_valid * p.K));
+  const auto rB = make_rsrc(p.b + eb * p.sb_e + n0 * p.K, (uint32_t)(cols_valid * p.K));
   const int Wd = (KB + 3) / 4;
   const auto rSA = make_rsrc(p.sfa + e * p.ssfa_e, (uint32_t)(Wd * p.ld_sfa * 4));
-  const auto rSB = make_rsrc(p.sfb + e * p.ssfb_e, (uint32_t)(NB * KB * 4));
+  const auto rSB = make_rsrc(p.sfb + eb * p.ssfb_e, (uint32_t)(NB * KB * 4));
 
   auto stage = [&](auto tag) -> uint8_t* {
     constexpr int I = decltype(tag)::value;
@@ -1659,6 +1683,7 @@ constexpr int kCfgScaled128x128 = 13;
 constexpr int kCfgScaled256x256 = 19;
 constexpr int kCfgRing256x256 = 21;        // 2 x 2 wavefronts
 constexpr int kCfgRing256x256Rows = 24;    // 1 x 4 wavefronts (all share the rows)
+constexpr int kCfgRing128x256 = 23;        // 2 x 2 wavefronts, 128-row tiles
 constexpr int kCfgDecode64x128 = 26;       // decode kernel, 4 wavefronts, three K-blocks in flight
 static_assert(kCfgDecode64x128 < kNumTiles, "tile table");
 
@@ -1682,7 +1707,9 @@ bool gemm_config_by_index(int idx, const GemmProblem& p, int splits, GemmConfig*
   if (idx < 0 || idx >= kNumTiles || splits < 1) return false;
   const int KB = (int)(p.K / 128);
   if (splits > KB) splits = KB > 0 ? KB : 1;
-  if (p.masked_m && splits != 1) return false;
+  if ((p.masked_m || p.m_indices) && splits != 1) return false;
+  // contiguous grouped layout: a tile must not straddle two aligned runs
+  if (p.m_indices && kContiguousAlign % kTiles[idx].bm != 0) return false;
   if (kTiles[idx].kind == kRing) {
     splits = 1;  // never splits K; the scale tables bound K
     if ((KB + 3) / 4 > kTiles[idx].max_wd) return false;
@@ -1737,6 +1764,15 @@ bool gemm_config_by_index(int idx, const GemmProblem& p, int splits, GemmConfig*
 GemmConfig choose_gemm_config(const GemmProblem& p) {
   GemmConfig cfg;
   const int KB = (int)(p.K / 128);
+  if (p.m_indices) {
+    // contiguous grouped layout: 128-row tiles (one aligned run each); 128 x 256 ring
+    // tiles when the scale tables hold K, else the 128 x 128 scaled tiles
+    if (gemm_config_by_index(kCfgRing128x256, p, 1, &cfg)) return cfg;
+    if (gemm_config_by_index(kCfgScaled128x128, p, 1, &cfg)) return cfg;
+    if (gemm_config_by_index(kCfgStream64x128, p, 1, &cfg)) return cfg;
+    gemm_config_by_index(1, p, 1, &cfg);
+    return cfg;
+  }
   if (p.masked_m) {
     // 256 x 256 ring tiles with the four wavefronts side by side in N: a group's
     // weights are read once per column tile, and a group's valid rows are spread
@@ -1775,7 +1811,7 @@ GemmConfig choose_gemm_config(const GemmProblem& p) {
     // the leading columns in whole rounds and the remaining columns with 128x128
     // tiles in a second launch.
     const int64_t rem = big_tiles % 256;
-    if (rem != 0 && rem < 128 && p.E == 1 && !p.masked_m) {
+    if (rem != 0 && rem < 128 && p.E == 1 && !p.masked_m && !p.m_indices) {
       const int64_t lead_tn = (big_tiles / 256) * 256 / tm256;
       const int64_t n_split = lead_tn * 256;
       GemmProblem tp = p;
@@ -1816,7 +1852,8 @@ hipError_t launch_gemm(const GemmProblem& p, const GemmConfig& cfg, void* ws, hi
   if (cfg.kernel < 0 || cfg.kernel >= kNumTiles) return hipErrorInvalidValue;
   if (cfg.n_split > 0) {
     // column split: [0, n_split) with cfg's kernel, [n_split, N) with the tail entry
-    if (p.E != 1 || p.masked_m || cfg.n_split % 128 != 0 || cfg.n_split >= p.N) return hipErrorInvalidValue;
+    if (p.E != 1 || p.masked_m || p.m_indices || cfg.n_split % 128 != 0 || cfg.n_split >= p.N)
+      return hipErrorInvalidValue;
     GemmProblem lead = p;
     lead.N = cfg.n_split;
     GemmConfig lc = cfg;
@@ -1839,6 +1876,10 @@ hipError_t launch_gemm(const GemmProblem& p, const GemmConfig& cfg, void* ws, hi
   const TileEntry& t = kTiles[cfg.kernel];
   KArgs k;
   k.a = p.a; k.sfa = p.sfa; k.b = p.b; k.sfb = p.sfb; k.c = p.c; k.masked_m = p.masked_m;
+  k.m_indices = p.m_indices;
+  k.groups = p.groups;
+  if (p.m_indices && (p.E != 1 || p.masked_m || cfg.splits != 1 || kContiguousAlign % t.bm != 0))
+    return hipErrorInvalidValue;
   k.M = p.M; k.N = p.N; k.K = p.K; k.ld_sfa = p.ld_sfa; k.ldc = p.ldc;
   const int64_t W = (p.K / 128 + 3) / 4, NB = cdiv(p.N, 128), KB = p.K / 128;
   k.sa_e = p.M * p.K; k.ssfa_e = W * p.ld_sfa; k.sb_e = p.N * p.K; k.ssfb_e = NB * KB; k.sc_e = p.M * p.ldc;

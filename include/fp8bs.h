@@ -131,18 +131,42 @@ int fp8_block_gemm_grouped_masked(const void* a, const uint32_t* sfa, const void
                                   int64_t M_max, int64_t N, int64_t K, void* stream);
 
 /*
+ * Contiguous grouped GEMM, the layout of the high-throughput MoE path (PR #19111
+ * page, changelog: the "High-Throughput" DeepEP + DeepGEMM test).  The pages name
+ * that path only; the layout is read plainly: the rows of A and C are grouped by
+ * expert in runs aligned to 128 rows, and m_indices[m] names the expert of row m
+ * (-1 for padding).  Every aligned 128-row block holds rows of one expert followed
+ * by padding rows, or padding only.  For every row m with 0 <= m_indices[m] < E,
+ * row m of C is the dense NT result of a[m], sfa, b[m_indices[m]],
+ * sfb[m_indices[m]].  A block whose first row is padding or names no expert in
+ * [0, E) is skipped (no loads, no MFMA, C untouched); padding rows inside a block
+ * of an expert are written with that expert's result (unspecified values).
+ *   a         : e4m3 [M][K];            sfa : uint32 [ceil(K/512)][ld_sfa], ld_sfa >= M
+ *   b         : e4m3 [E][N][K];         sfb : fp32 [E][ceil(N/128)][K/128]
+ *   c         : bf16 [M][ldc], ldc >= N, ldc % 8 == 0
+ *   m_indices : int32 [M] on the device (values outside [0, E) mean padding)
+ *   K >= 128, K % 128 == 0, N % 64 == 0.
+ */
+int fp8_block_gemm_grouped_contiguous(const void* a, const uint32_t* sfa, int64_t ld_sfa,
+                                      const void* b, const float* sfb, void* c, int64_t ldc,
+                                      const int32_t* m_indices, int64_t E, int64_t M, int64_t N,
+                                      int64_t K, void* stream);
+
+/*
  * Tile-table access, for tuning and for tests that cover every compiled tile
  * shape.  fp8bs_gemm_config reports what the automatic choice would be for a
- * dense (masked = 0) or masked (masked = 1) problem: kernel index into the tile
+ * dense (masked = 0), masked (masked = 1) or contiguous grouped (masked = 2)
+ * problem: kernel index into the tile
  * table, workgroup tile bm x bn, and the number of K splits.  The _cfg variants
  * run the same GEMMs with an explicit kernel index and split count (splits is
- * clamped to [1, K/128]; the masked form accepts splits == 1 only).
+ * clamped to [1, K/128]; the masked and contiguous forms use splits == 1 only, and
+ * the contiguous form only tiles of at most 128 rows).
  */
 int fp8bs_gemm_config_count(void);
 int fp8bs_gemm_config(int masked, int64_t M, int64_t N, int64_t K, int32_t* kernel, int32_t* bm,
                       int32_t* bn, int32_t* splits);
-/* Whether table entry `kernel` accepts a dense (masked = 0) or masked (masked = 1)
- * problem of this shape with `splits` K splits: FP8BS_OK with its workgroup tile and
+/* Whether table entry `kernel` accepts a dense (masked = 0), masked (masked = 1) or
+ * contiguous grouped (masked = 2) problem of this shape with `splits` K splits: FP8BS_OK with its workgroup tile and
  * the split count it would use, FP8BS_ERR_SHAPE if it does not (for instance K past
  * the entry's scale tables, or a masked problem that would need K splits).
  * Host-only; launches nothing. */
@@ -155,6 +179,10 @@ int fp8_block_gemm_grouped_masked_cfg(const void* a, const uint32_t* sfa, const 
                                       const float* sfb, void* c, const int32_t* masked_m, int64_t E,
                                       int64_t M_max, int64_t N, int64_t K, int32_t kernel,
                                       void* stream);
+int fp8_block_gemm_grouped_contiguous_cfg(const void* a, const uint32_t* sfa, int64_t ld_sfa,
+                                          const void* b, const float* sfb, void* c, int64_t ldc,
+                                          const int32_t* m_indices, int64_t E, int64_t M,
+                                          int64_t N, int64_t K, int32_t kernel, void* stream);
 
 /* Status helpers. */
 const char* fp8bs_status_string(int status);

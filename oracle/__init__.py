@@ -63,6 +63,8 @@ def _load():
     lib.orc_gemm_nt.restype = None
     lib.orc_gemm_grouped_masked.argtypes = [P, P, P, P, P, I, I, I, I, P, I, P]
     lib.orc_gemm_grouped_masked.restype = None
+    lib.orc_gemm_grouped_contiguous.argtypes = [P, P, I, P, P, P, I, I, I, I, P, I, P]
+    lib.orc_gemm_grouped_contiguous.restype = None
     lib.orc_calc_diff.argtypes = [P, P, I]
     lib.orc_calc_diff.restype = ctypes.c_double
     lib.orc_num_threads.argtypes = []
@@ -210,6 +212,25 @@ def gemm_grouped_masked(a, sfa, b, sfb, masked_m, rows=None):
     out = np.full((E, M_max, N), np.nan)
     _load().orc_gemm_grouped_masked(_ptr(a), _ptr(sfa), _ptr(b), _ptr(sfb), _ptr(mm), E, M_max, N, K,
                                     _ptr(r), 0 if r is None else len(r), _ptr(out))
+    return out
+
+
+def gemm_grouped_contiguous(a, sfa, b, sfb, m_indices, rows=None):
+    """Contiguous grouped GEMM in double.  a uint8 [M, K], sfa uint32 [W, ld_sfa],
+    b uint8 [E, N, K], sfb float32 [E, ceil(N/128), K/128], m_indices int32 [M]
+    (group of every row; values outside [0, E) are padding).
+    Returns double [M, N]; rows not computed (padding, or not selected) are NaN."""
+    a = _req(a, np.uint8)
+    b = _req(b, np.uint8)
+    sfa = _req(sfa, np.uint32)
+    sfb = _req(sfb, np.float32)
+    mi = _req(m_indices, np.int32)
+    M, K = a.shape
+    E, N = b.shape[0], b.shape[1]
+    r = None if rows is None else _req(np.asarray(rows, np.int64), np.int64)
+    out = np.full((M, N), np.nan)
+    _load().orc_gemm_grouped_contiguous(_ptr(a), _ptr(sfa), sfa.shape[1], _ptr(b), _ptr(sfb), _ptr(mi), E, M, N,
+                                        K, _ptr(r), 0 if r is None else len(r), _ptr(out))
     return out
 
 

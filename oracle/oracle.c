@@ -299,6 +299,35 @@ void orc_gemm_grouped_masked(const uint8_t* a, const uint32_t* sfa, const uint8_
   free(sel);
 }
 
+/* Contiguous grouped GEMM (the high-throughput MoE layout; the PR #19111 page names
+ * that path, the layout is read plainly): row m of A is multiplied with the weights
+ * of group g = m_indices[m] when 0 <= g < E; rows with any other value are padding
+ * and are not computed.  a: e4m3 [M][K], sfa: uint32 [W][ld_sfa], b: e4m3 [E][N][K],
+ * sfb: fp32 [E][ceil(N/128)][K/128], out: double [M][N] (padding rows untouched).
+ * rows (optional) restricts the rows computed. */
+void orc_gemm_grouped_contiguous(const uint8_t* a, const uint32_t* sfa, int64_t ld_sfa, const uint8_t* b,
+                                 const float* sfb, const int32_t* m_indices, int64_t E, int64_t M,
+                                 int64_t N, int64_t K, const int64_t* rows, int64_t nrows, double* out) {
+  int64_t NB = (N + 127) / 128, KB = K / 128;
+  int64_t n_sel = rows ? nrows : M;
+  int64_t* sel = (int64_t*)malloc(sizeof(int64_t) * (size_t)(n_sel > 0 ? n_sel : 1));
+  for (int64_t g = 0; g < E; ++g) {
+    int64_t ns = 0;
+    for (int64_t i = 0; i < n_sel; ++i) {
+      int64_t m = rows ? rows[i] : i;
+      if (m >= 0 && m < M && m_indices[m] == g) sel[ns++] = m;
+    }
+    if (ns == 0) continue;
+    double* tmp = (double*)malloc(sizeof(double) * (size_t)(ns * N));
+    orc_gemm_nt(a, K, sfa, ld_sfa, b + g * N * K, K, sfb + g * NB * KB, M, N, K,
+                sel, ns, (const int64_t*)0, N, tmp);
+    for (int64_t i = 0; i < ns; ++i)
+      memcpy(out + sel[i] * N, tmp + i * N, sizeof(double) * (size_t)N);
+    free(tmp);
+  }
+  free(sel);
+}
+
 /* calc_diff of the benchmark post (section 4.4): 1 - 2*sum(x*y) / sum(x*x + y*y), in double. */
 double orc_calc_diff(const double* x, const double* y, int64_t n) {
   double num = 0.0, den = 0.0;

@@ -343,6 +343,53 @@ def test_masked_counts_clamped_and_rows_untouched():
     assert np.array_equal(out[1, :3], O.gemm_nt(a[1], sfa[1], b[1], sfb[1])[:3])
 
 
+# ---------------------------------------------------------------- contiguous grouped GEMM
+
+def test_contiguous_integer_brute_force_with_varied_scales():
+    """Integer operands (exact in e4m3), power-of-two activation and weight scales that
+    differ per row, group, column block and K-block: the exact result is an integer
+    matmul per row against that row's group, scaled per K-block (numpy int64 sums)."""
+    rng = np.random.default_rng(11)
+    E, N, K = 3, 192, 640
+    G, NB = K // 128, (N + 127) // 128
+    Wd = (G + 3) // 4
+    mi = W.contiguous_layout([130, 0, 5], tail_blocks=1)
+    mi[-3] = 7  # a row naming no group (past E): padding
+    M = len(mi)
+    ai = rng.integers(-16, 17, (M, K))
+    bi = rng.integers(-16, 17, (E, N, K))
+    qa, qb = _int_e4m3_codes(ai), _int_e4m3_codes(bi)
+    ea = rng.integers(-3, 4, (M, G))
+    sfa = np.zeros((Wd, M), np.uint32)
+    for m in range(M):
+        for g in range(G):
+            sfa[g // 4, m] |= np.uint32((ea[m, g] + 127) << (8 * (g % 4)))
+    eb = rng.integers(-3, 4, (E, NB, G))
+    sfb = np.ldexp(1.0, eb).astype(np.float32)
+    out = O.gemm_grouped_contiguous(qa, sfa, qb, sfb, mi)
+    for m in range(M):
+        g = mi[m]
+        if not (0 <= g < E):
+            assert np.all(np.isnan(out[m]))
+            continue
+        ref = np.zeros(N)
+        for kb in range(G):
+            dots = bi[g][:, kb * 128:(kb + 1) * 128] @ ai[m, kb * 128:(kb + 1) * 128]
+            ref += np.ldexp(1.0, ea[m, kb]) * np.ldexp(1.0, eb[g][np.arange(N) // 128, kb]) * dots
+        assert np.array_equal(out[m], ref), m
+
+
+def test_contiguous_single_group_equals_dense_and_rows_select():
+    E, N, K = 1, 128, 256
+    a, sfa, b, sfb = _moe_inputs(1, 256, N, K, seed=5)
+    mi = np.zeros(256, np.int32)
+    out = O.gemm_grouped_contiguous(a[0], sfa[0], b, sfb, mi)
+    assert np.array_equal(out, O.gemm_nt(a[0], sfa[0], b[0], sfb[0]))
+    part = O.gemm_grouped_contiguous(a[0], sfa[0], b, sfb, mi, rows=[3, 200])
+    assert np.array_equal(part[[3, 200]], out[[3, 200]])
+    assert np.all(np.isnan(np.delete(part, [3, 200], axis=0)))
+
+
 # ---------------------------------------------------------------- SiLU-mul-quant
 
 def test_silu_mul_matches_logistic_closed_form():

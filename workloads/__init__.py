@@ -1,7 +1,8 @@
 """Seeded synthetic inputs shared by the tests, the smoke check and the benchmark.
 
 This module holds input generation only: normal draws rounded to bf16, the
-outlier mask, and the per-expert token counts.  It contains none of the
+outlier mask, the per-expert token counts and the row -> group map of the
+contiguous grouped layout.  It contains none of the
 method's arithmetic (no quantization, no scales, no GEMM), and it imports
 neither the oracle nor the HIP library.
 
@@ -59,6 +60,18 @@ def zipf_counts(E: int = 32, tokens: int = 4096, s: float = 1.1, cap: int = 256,
     p /= p.sum()
     draw = np.random.default_rng(seed).multinomial(tokens, p)
     return np.minimum(draw, cap).astype(np.int32)
+
+
+def contiguous_layout(counts, align: int = 128, tail_blocks: int = 0) -> np.ndarray:
+    """Row -> group map of the contiguous grouped layout: group g's rows in a run of
+    round_up(counts[g], align) rows (the first counts[g] name g, the rest are padding,
+    -1), then tail_blocks runs of padding only."""
+    parts = []
+    for g, c in enumerate(np.asarray(counts, np.int64)):
+        run = -(-int(c) // align) * align
+        parts.append(np.concatenate([np.full(int(c), g, np.int32), np.full(run - int(c), -1, np.int32)]))
+    parts.append(np.full(tail_blocks * align, -1, np.int32))
+    return np.concatenate(parts).astype(np.int32)
 
 
 @dataclasses.dataclass(frozen=True)
