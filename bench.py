@@ -287,6 +287,39 @@ def bench_contiguous_gate_up(F, W, stream, steps, warmup):
     return r
 
 
+def bench_dispatch_quant(F, W, stream, steps, warmup):
+    """Per-token quant into the masked expert layout of routed tokens: 512 tokens x
+    top-8 of 32 experts (Zipf(1.1) weights), capacity 256, K = 7168."""
+    E, M_max, K = W.MOE_E, W.MOE_M_MAX, W.MOE_GATE_UP["K"]
+    ids_np = W.topk_routing()
+    T, topk = ids_np.shape
+    ids = torch.from_numpy(ids_np).to("cuda")
+    x = randn_bf16((T, K), seed=17)
+    Wd = (K // 128 + 3) // 4
+    q = torch.empty((E, M_max, K), dtype=torch.uint8, device="cuda")
+    sf = torch.empty((E, Wd, M_max), dtype=torch.int32, device="cuda")
+    mm = torch.empty((E,), dtype=torch.int32, device="cuda")
+    slot = torch.empty((T, topk), dtype=torch.int32, device="cuda")
+
+    def op(s):
+        F.fp8_quant_group_pack_to_experts(x, ids, E, M_max, q=q, sf=sf, masked_m=mm, slot_of=slot, stream=stream)
+
+    with torch.cuda.stream(stream):
+        for i in range(warmup):
+            op(i)
+    (t,) = kernel_times(stream, [op], steps)
+    rows = int(mm.clamp(0, M_max).sum())
+    # algorithmic bytes: bf16 tokens read once, e4m3 rows + scale words written per routed
+    # pair, ids read and slots written
+    nbytes = 2 * T * K + rows * (K + 4 * Wd) + 8 * T * topk + 4 * E
+    r = {"workload": "moe_dispatch_quant_T512_top8_E32_Mmax256_K7168", "rows_written": rows,
+         "op_us": t * 1e3, "op_gbs": nbytes / (t * 1e-3) / 1e9}
+    r["frac_hbm"] = r["op_gbs"] / HBM_PEAK_GBS
+    r["frac_mfma"] = 0.0
+    del x, q, sf, mm, slot, ids
+    return r
+
+
 def bench_silu_down(F, W, stream, steps, warmup):
     E, M_max, H, N = W.MOE_E, W.MOE_M_MAX, W.MOE_DOWN["H"], W.MOE_DOWN["N"]
     K = H
@@ -441,12 +474,16 @@ def main():
         print("[bench] %s" % json.dumps(rows[-1]), file=sys.stderr, flush=True)
         rows.append(bench_contiguous_gate_up(F, W, stream, max(10, args.steps // 4), args.warmup))
         print("[bench] %s" % json.dumps(rows[-1]), file=sys.stderr, flush=True)
-        print("%-58s %10s %10s %10s %8s %8s" % ("workload", "gemm_us", "TFLOPS", "GB/s", "%MFMA", "%HBM"),
+        rows.append(bench_dispatch_quant(F, W, stream, args.steps, args.warmup))
+        print("[bench] %s" % json.dumps(rows[-1]), file=sys.stderr, flush=True)
+        print("%-58s %10s %10s %10s %8s %8s" % ("workload", "us", "TFLOPS", "GB/s", "%MFMA", "%HBM"),
               file=sys.stderr)
         for x in rows:
-            print("%-58s %10.2f %10.1f %10.1f %8.1f %8.1f" % (x["workload"], x["gemm_us"], x["gemm_tflops"],
-                                                             x["gemm_gbs"], 100 * x["frac_mfma"],
-                                                             100 * x["frac_hbm"]), file=sys.stderr)
+            print("%-58s %10.2f %10.1f %10.1f %8.1f %8.1f" % (x["workload"], x.get("gemm_us", x.get("op_us")),
+                                                             x.get("gemm_tflops", 0.0),
+                                                             x.get("gemm_gbs", x.get("op_gbs")),
+                                                             100 * x["frac_mfma"], 100 * x["frac_hbm"]),
+                  file=sys.stderr)
         if args.sweep_out:
             with open(args.sweep_out, "w") as f:
                 for x in rows:

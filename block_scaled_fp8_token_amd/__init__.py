@@ -23,6 +23,7 @@ __all__ = [
     "Fp8bsError", "fp8_quant_group_pack", "silu_mul_quant_group_pack", "fp8_block_quant_128x128",
     "fp8_block_gemm_nt", "fp8_block_gemm_grouped_masked", "gemm_config", "gemm_config_count",
     "library_path", "header_path", "declared_functions", "gemm_config_of",
+    "fp8_quant_group_pack_to_experts", "fp8_block_gemm_grouped_contiguous",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -44,6 +45,7 @@ _SIGS = {
     "fp8_quant_group_pack": [_P, _I64, _I64, _I64, _P, _I64, _P, _I64, _P],
     "silu_mul_quant_group_pack": [_P, _P, _I64, _I64, _I64, _P, _P, _P],
     "fp8_block_quant_128x128": [_P, _I64, _I64, _P, _P, _P],
+    "fp8_quant_group_pack_to_experts": [_P, _I64, _I64, _I64, _P, _I32, _I64, _I64, _P, _P, _P, _P, _P],
     "fp8_block_gemm_nt": [_P, _P, _I64, _P, _P, _P, _I64, _I64, _I64, _I64, _P],
     "fp8_block_gemm_nt_cfg": [_P, _P, _I64, _P, _P, _P, _I64, _I64, _I64, _I64, _I32, _I32, _P],
     "fp8_block_gemm_grouped_masked": [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _P],
@@ -195,6 +197,46 @@ def fp8_block_quant_128x128(w: torch.Tensor, q: torch.Tensor | None = None, sfb:
     st = _lib.fp8_block_quant_128x128(w.data_ptr(), N, K, q.data_ptr(), sfb.data_ptr(), _stream(stream))
     _check("fp8_block_quant_128x128", st)
     return q, sfb
+
+
+def fp8_quant_group_pack_to_experts(x: torch.Tensor, topk_ids: torch.Tensor, E: int, M_max: int,
+                                    q: torch.Tensor | None = None, sf: torch.Tensor | None = None,
+                                    masked_m: torch.Tensor | None = None, slot_of: torch.Tensor | None = None,
+                                    stream=None):
+    """Per-token group quant into the masked expert layout of the routed tokens.
+    x bf16 [T, K], topk_ids int32 [T, topk] -> (q uint8 [E, M_max, K],
+    sf int32 [E, ceil(K/512), M_max], masked_m int32 [E], slot_of int32 [T, topk])."""
+    _expect(x, "x", _BF16, 2)
+    _expect(topk_ids, "topk_ids", (torch.int32,), 2)
+    _contig(topk_ids, "topk_ids")
+    T, K = x.shape
+    topk = topk_ids.shape[1]
+    if topk_ids.shape[0] != T:
+        raise ValueError("topk_ids must be [T, topk]")
+    Wd = (K // 128 + 3) // 4
+    dev = x.device
+    if q is None:
+        q = torch.empty((E, M_max, K), dtype=torch.uint8, device=dev)
+    if sf is None:
+        sf = torch.empty((E, Wd, M_max), dtype=torch.int32, device=dev)
+    if masked_m is None:
+        masked_m = torch.empty((E,), dtype=torch.int32, device=dev)
+    if slot_of is None:
+        slot_of = torch.empty((T, topk), dtype=torch.int32, device=dev)
+    _expect(q, "q", _E4M3, 3)
+    _contig(q, "q")
+    _expect(sf, "sf", (torch.int32, torch.uint32), 3)
+    _contig(sf, "sf")
+    _expect(masked_m, "masked_m", (torch.int32,), 1)
+    _expect(slot_of, "slot_of", (torch.int32,), 2)
+    _contig(slot_of, "slot_of")
+    if tuple(q.shape) != (E, M_max, K) or tuple(sf.shape) != (E, Wd, M_max) or tuple(slot_of.shape) != (T, topk):
+        raise ValueError("output shapes do not match E, M_max, K, T, topk")
+    st = _lib.fp8_quant_group_pack_to_experts(x.data_ptr(), x.stride(0), T, K, topk_ids.data_ptr(), topk, E, M_max,
+                                              q.data_ptr(), sf.data_ptr(), masked_m.data_ptr(), slot_of.data_ptr(),
+                                              _stream(stream))
+    _check("fp8_quant_group_pack_to_experts", st)
+    return q, sf, masked_m, slot_of
 
 
 def fp8_block_gemm_nt(a: torch.Tensor, sfa: torch.Tensor, b: torch.Tensor, sfb: torch.Tensor,

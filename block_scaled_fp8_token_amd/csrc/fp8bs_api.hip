@@ -3,6 +3,7 @@
 // The operations and their preconditions are stated in include/fp8bs.h.
 #include <hip/hip_runtime.h>
 
+#include <climits>
 #include <cstdint>
 #include <cstring>
 #include <map>
@@ -227,6 +228,34 @@ int silu_mul_quant_group_pack(const void* x, const int32_t* masked_m, int64_t E,
   if (st != FP8BS_OK) return st;
   hipError_t e = fp8bs::launch_silu_mul_quant(static_cast<const uint16_t*>(x), masked_m, E, M_max, H,
                                               static_cast<uint8_t*>(q), sf, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FP8BS_OK : fail_hip(e);
+}
+
+int fp8_quant_group_pack_to_experts(const void* x, int64_t ldx, int64_t T, int64_t K, const int32_t* topk_ids,
+                                    int32_t topk, int64_t E, int64_t M_max, void* q, uint32_t* sf,
+                                    int32_t* masked_m, int32_t* slot_of, void* stream) {
+  if (T < 0 || K < 0 || K % 128 != 0 || E < 0 || M_max < 0) return FP8BS_ERR_SHAPE;
+  if (topk < 1 || topk > 64 || E > fp8bs::kQuantToExpertsMaxExperts || T * (int64_t)topk > INT32_MAX)
+    return FP8BS_ERR_SHAPE;
+  if (E == 0) return FP8BS_OK;
+  if (!masked_m || (T > 0 && (!x || !topk_ids || !slot_of)) || (M_max > 0 && K > 0 && (!q || !sf)))
+    return FP8BS_ERR_NULL;
+  if (T > 0 && ldx < K) return FP8BS_ERR_SHAPE;
+  if ((x && !aligned(x, 16)) || (q && !aligned(q, 16)) || ldx % 8 != 0 || (sf && !aligned(sf, 4)) ||
+      !aligned(masked_m, 4) || (topk_ids && !aligned(topk_ids, 4)) || (slot_of && !aligned(slot_of, 4)))
+    return FP8BS_ERR_ALIGN;
+  int st = check_device();
+  if (st != FP8BS_OK) return st;
+  // pair ranks and per-chunk counts live in the stream's workspace past the counters
+  const size_t off = fp8bs::gemm_workspace_zeroed_prefix();
+  void* ws = nullptr;
+  st = get_workspace(off + fp8bs::quant_to_experts_scratch_bytes(T, topk, E), static_cast<hipStream_t>(stream),
+                     &ws);
+  if (st != FP8BS_OK) return st;
+  hipError_t e = fp8bs::launch_quant_to_experts(static_cast<const uint16_t*>(x), ldx, T, K, topk_ids, topk, E,
+                                                M_max, static_cast<uint8_t*>(q), sf, masked_m, slot_of,
+                                                reinterpret_cast<int32_t*>(static_cast<char*>(ws) + off),
+                                                static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FP8BS_OK : fail_hip(e);
 }
 

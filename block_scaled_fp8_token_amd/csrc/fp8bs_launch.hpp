@@ -16,6 +16,15 @@ hipError_t launch_silu_mul_quant(const uint16_t* x, const int32_t* masked_m, int
 hipError_t launch_block_quant(const uint16_t* w, int64_t N, int64_t K, uint8_t* q, float* sfb,
                               hipStream_t stream);
 
+// Routing ranks (one workgroup per 1024 pairs) then the quantization into the masked
+// expert layout; scratch: quant_to_experts_scratch_bytes() of device memory (pair
+// ranks and per-chunk expert counts), free for other use once the launches are done.
+hipError_t launch_quant_to_experts(const uint16_t* x, int64_t ldx, int64_t T, int64_t K, const int32_t* ids,
+                                  int topk, int64_t E, int64_t M_max, uint8_t* q, uint32_t* sf,
+                                  int32_t* masked_m, int32_t* slot_of, int32_t* scratch, hipStream_t stream);
+size_t quant_to_experts_scratch_bytes(int64_t T, int topk, int64_t E);
+constexpr int64_t kQuantToExpertsMaxExperts = 1024;
+
 // One GEMM problem: dense (masked_m == nullptr, m_indices == nullptr, E == 1), masked
 // grouped (masked_m set), or contiguous grouped (m_indices set, E == 1: the rows of A
 // and C are grouped by weight group in aligned runs, B holds `groups` weight sets).

@@ -6,7 +6,11 @@
 //     padded rows (vLLM PR #19885 "Optimize the little operations in the
 //     DeepGEMM + DeepEP low latency case", Summary item 2);
 //   * 128x128 weight block quant (the offline weight step of the vLLM DeepGEMM
-//     FP8 block GEMM benchmark post, section 4.1).
+//     FP8 block GEMM benchmark post, section 4.1);
+//   * the same per-token quant written straight into the masked expert layout of
+//     the routed tokens (the quantization half of FP8 dispatch: PR #19885,
+//     Summary item 1, DeepEP puts the scales in DeepGEMM's layout; PR #19111 review,
+//     the TODO asking for a batched quant).
 //
 // All three are HBM-bound streams.  The activation kernels give one wavefront
 // one (row, packed word) unit: 64 lanes x 8 bf16 = 512 columns = the four
@@ -148,6 +152,116 @@ __global__ __launch_bounds__(256) void block_quant_kernel(
   if (t == 0) sfb[nb * KB + kb] = exp2i(e);
 }
 
+// Expert slots of routed tokens (the dispatch half of FP8 dispatch on one GPU): pair
+// p = t * topk + j of token t's choice j goes to expert ids[p]; its slot is the
+// number of earlier pairs (in p order) routed to the same expert, and pairs whose
+// slot reaches M_max, or whose id names no expert, get slot -1.  Two parallel
+// passes, fully deterministic:
+//   * route_rank_kernel: one workgroup per chunk of 1024 pairs ranks every pair
+//     among the chunk's earlier pairs of its expert (inside a wavefront with
+//     ballots, across wavefronts with per-wavefront counts in LDS) and writes the
+//     chunk's per-expert counts;
+//   * quant_to_experts_kernel adds the counts of the earlier chunks to a pair's
+//     rank when it needs the slot.
+constexpr int kRouteThreads = 1024;
+constexpr int kRouteMaxExperts = 1024;
+
+__global__ __launch_bounds__(kRouteThreads) void route_rank_kernel(
+    const int32_t* __restrict__ ids, int64_t P, int64_t E, int32_t* __restrict__ rank_of,
+    int32_t* __restrict__ chunk_counts) {
+  constexpr int NW = kRouteThreads / 64;
+  __shared__ int wcnt[NW][kRouteMaxExperts];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int e = tid; e < E; e += kRouteThreads)
+#pragma unroll
+    for (int w = 0; w < NW; ++w) wcnt[w][e] = 0;
+  const int64_t p = (int64_t)blockIdx.x * kRouteThreads + tid;
+  const int e = p < P ? ids[p] : -1;
+  const bool valid = e >= 0 && e < E;
+  __syncthreads();
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  int rank = 0;
+  uint64_t pending = __ballot(valid);
+  while (pending) {  // one pass per distinct expert of this wavefront (uniform)
+    const int leader = __builtin_ctzll(pending);
+    const int el = __builtin_amdgcn_readlane(e, leader);
+    const uint64_t m = __ballot(valid && e == el);
+    if (valid && e == el) rank = __builtin_popcountll(m & below);
+    if (lane == leader) wcnt[wave][el] = __builtin_popcountll(m);
+    pending &= ~m;
+  }
+  __syncthreads();
+  if (p < P) {
+    int r = -1;
+    if (valid) {
+      r = rank;
+      for (int w = 0; w < wave; ++w) r += wcnt[w][e];
+    }
+    rank_of[p] = r;
+  }
+  for (int e2 = tid; e2 < E; e2 += kRouteThreads) {
+    int tot = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) tot += wcnt[w][e2];
+    chunk_counts[blockIdx.x * E + e2] = tot;
+  }
+}
+
+// Quantize every token once (the per-token group quant above, one wavefront per
+// (token, packed word)) and write its e4m3 row and scale word to the slot of each
+// of its routed choices in the masked expert layout q [E][M_max][K],
+// sf [E][W][M_max].  Pairs with slot -1 write nothing.  The wavefronts of word 0
+// also store the slots; workgroup 0 stores the per-expert row counts.
+__global__ __launch_bounds__(256) void quant_to_experts_kernel(
+    const uint16_t* __restrict__ x, int64_t ldx, int64_t T, int64_t K, const int32_t* __restrict__ ids,
+    const int32_t* __restrict__ rank_of, const int32_t* __restrict__ chunk_counts, int64_t nchunks, int topk,
+    int64_t E, int64_t M_max, uint8_t* __restrict__ q, uint32_t* __restrict__ sf, int64_t W,
+    int32_t* __restrict__ masked_m, int32_t* __restrict__ slot_of) {
+  const int lane = threadIdx.x & 63;
+  if (blockIdx.x == 0)
+    for (int64_t e = threadIdx.x; e < E; e += 256) {
+      int64_t tot = 0;
+      for (int64_t c = 0; c < nchunks; ++c) tot += chunk_counts[c * E + e];
+      masked_m[e] = (int32_t)(tot < M_max ? tot : M_max);
+    }
+  const int64_t units = T * W;
+  const int64_t nwaves = (int64_t)gridDim.x * 4;
+  for (int64_t u = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); u < units; u += nwaves) {
+    const int64_t t = u / W, w = u - t * W;
+    const int64_t col = w * 512 + lane * 8;
+    const bool valid = col < K;
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (valid) v = *reinterpret_cast<const uint4*>(x + t * ldx + col);
+    // lane j < topk resolves choice j's slot: its rank in its chunk plus the counts
+    // of its expert in the earlier chunks
+    const int64_t pj = t * topk + lane;
+    int32_t my_slot = -1, my_e = 0;
+    if (lane < topk) {
+      const int32_t r = rank_of[pj];
+      my_e = ids[pj];
+      if (r >= 0) {
+        int64_t sl = r;
+        const int64_t cj = pj / kRouteThreads;
+        for (int64_t c = 0; c < cj; ++c) sl += chunk_counts[c * E + my_e];
+        my_slot = sl < M_max ? (int32_t)sl : -1;
+      }
+      if (w == 0) slot_of[pj] = my_slot;
+    }
+    float f[8];
+    unpack8(v, f);
+    uint32_t eb;
+    const uint2 o = quant8(f, valid, &eb);
+    const uint32_t word = gather_word(eb);
+    for (int j = 0; j < topk; ++j) {
+      const int32_t s = __builtin_amdgcn_readlane(my_slot, j);
+      if (s < 0) continue;  // uniform per wavefront
+      const int64_t e = __builtin_amdgcn_readlane(my_e, j);
+      if (valid) *reinterpret_cast<uint2*>(q + (e * M_max + s) * K + col) = o;
+      if (lane == 0) sf[(e * W + w) * M_max + s] = word;
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_quant_group_pack(const uint16_t* x, int64_t ldx, int64_t M, int64_t K, uint8_t* q,
@@ -173,6 +287,35 @@ hipError_t launch_silu_mul_quant(const uint16_t* x, const int32_t* masked_m, int
   hipLaunchKernelGGL(silu_mul_quant_kernel, dim3((unsigned)bx, (unsigned)E), dim3(256), 0, stream, x,
                      masked_m, M_max, H, q, sf, W, rows_per_block);
   return hipGetLastError();
+}
+
+hipError_t launch_quant_to_experts(const uint16_t* x, int64_t ldx, int64_t T, int64_t K, const int32_t* ids,
+                                  int topk, int64_t E, int64_t M_max, uint8_t* q, uint32_t* sf,
+                                  int32_t* masked_m, int32_t* slot_of, int32_t* scratch, hipStream_t stream) {
+  if (E < 1 || E > kRouteMaxExperts) return hipErrorInvalidValue;
+  const int64_t P = T * topk;
+  const int64_t nchunks = (P + kRouteThreads - 1) / kRouteThreads;
+  int32_t* rank_of = scratch;
+  int32_t* chunk_counts = scratch + P;
+  if (nchunks > 0) {
+    hipLaunchKernelGGL(route_rank_kernel, dim3((unsigned)nchunks), dim3(kRouteThreads), 0, stream, ids, P, E,
+                       rank_of, chunk_counts);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const int64_t W = (K / 128 + 3) / 4;
+  int64_t blocks = (T * W + 3) / 4;
+  if (blocks > 4096) blocks = 4096;
+  if (blocks < 1) blocks = 1;  // workgroup 0 still stores the counts
+  hipLaunchKernelGGL(quant_to_experts_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, x, ldx, T, K, ids,
+                     rank_of, chunk_counts, nchunks, topk, E, M_max, q, sf, W, masked_m, slot_of);
+  return hipGetLastError();
+}
+
+size_t quant_to_experts_scratch_bytes(int64_t T, int topk, int64_t E) {
+  const int64_t P = T * topk;
+  const int64_t nchunks = (P + kRouteThreads - 1) / kRouteThreads;
+  return (size_t)(P + nchunks * E) * sizeof(int32_t);
 }
 
 hipError_t launch_block_quant(const uint16_t* w, int64_t N, int64_t K, uint8_t* q, float* sfb,

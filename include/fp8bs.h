@@ -87,6 +87,33 @@ int silu_mul_quant_group_pack(const void* x, const int32_t* masked_m, int64_t E,
                               int64_t H, void* q, uint32_t* sf, void* stream);
 
 /*
+ * Per-token group quant written into the masked expert layout of the routed
+ * tokens: the quantization half of FP8 dispatch on one GPU (PR #19885, Summary
+ * item 1: DeepEP quantizes and puts the scales in DeepGEMM's layout; PR #19111
+ * review: the TODO asking for a batched quant).  Token t's choice j routes pair
+ * p = t * topk + j to expert topk_ids[p]; its slot is the number of earlier pairs
+ * (in p order) routed to the same expert.  Pairs whose id is outside [0, E) or
+ * whose slot reaches M_max get slot -1 and are not written.  Every token is
+ * quantized once, exactly as fp8_quant_group_pack quantizes a row, and its e4m3
+ * row and scale words are written to row `slot` of its expert.
+ *   x        : bf16 [T][ldx], ldx >= K, ldx % 8 == 0;  K % 128 == 0
+ *   topk_ids : int32 [T][topk] on the device, 1 <= topk <= 64
+ *   q        : e4m3 [E][M_max][K];   sf : uint32 [E][ceil(K/512)][M_max]
+ *   masked_m : int32 [E] out: min(pairs routed to e, M_max)
+ *   slot_of  : int32 [T][topk] out: the slot of every pair, or -1
+ *   1 <= E <= 1024.  Rows at or past masked_m[e] of q and sf are left untouched.
+ * Two launches on `stream`: one workgroup per 1024 pairs ranks the pairs, then the
+ * quantization resolves the slots (deterministic) and reads every token once.  The
+ * ranks and per-chunk counts (4 * (T * topk + ceil(T * topk / 1024) * E) bytes) go
+ * to the library's per-(device, stream) workspace, allocated on the first call
+ * that needs it (FP8BS_ERR_ALLOC during HIP graph capture, as for the GEMMs).
+ */
+int fp8_quant_group_pack_to_experts(const void* x, int64_t ldx, int64_t T, int64_t K,
+                                    const int32_t* topk_ids, int32_t topk, int64_t E, int64_t M_max,
+                                    void* q, uint32_t* sf, int32_t* masked_m, int32_t* slot_of,
+                                    void* stream);
+
+/*
  * 128x128 weight block quant (benchmark post section 4.1, per_block_cast with
  * UE8M0: scale = block amax / 448 rounded up to a power of two).
  *   w   : bf16 [N][K] contiguous;  q : e4m3 [N][K] contiguous

@@ -57,6 +57,8 @@ def _load():
     lib.orc_quant_group_pack.restype = None
     lib.orc_silu_mul_quant_group_pack.argtypes = [P, P, I, I, I, P, P, P]
     lib.orc_silu_mul_quant_group_pack.restype = None
+    lib.orc_quant_group_pack_to_experts.argtypes = [P, I, I, I, P, I, I, I, P, P, P, P]
+    lib.orc_quant_group_pack_to_experts.restype = None
     lib.orc_block_quant_128x128.argtypes = [P, I, I, P, P]
     lib.orc_block_quant_128x128.restype = None
     lib.orc_gemm_nt.argtypes = [P, I, P, I, P, I, P, I, I, I, P, I, P, I, P]
@@ -163,6 +165,27 @@ def silu_mul_quant_group_pack(x: np.ndarray, masked_m: np.ndarray, want_y: bool 
     y = np.full((E, M_max, H), np.nan) if want_y else None
     _load().orc_silu_mul_quant_group_pack(_ptr(x), _ptr(mm), E, M_max, H, _ptr(q), _ptr(sf), _ptr(y))
     return (q, sf, y) if want_y else (q, sf)
+
+
+def quant_group_pack_to_experts(x: np.ndarray, topk_ids: np.ndarray, E: int, M_max: int):
+    """Per-token group quant of bf16 x [T, K] into the masked expert layout of the
+    routed tokens (topk_ids int32 [T, topk]).  Returns (q uint8 [E, M_max, K],
+    sf uint32 [E, W, M_max], masked_m int32 [E], slot_of int32 [T, topk]); rows at
+    or past masked_m[e] are zero here and are not part of the result."""
+    x = _req(x, np.uint16)
+    ids = _req(topk_ids, np.int32)
+    T, K = x.shape
+    topk = ids.shape[1]
+    if K % 128 or ids.shape[0] != T:
+        raise ValueError("bad shapes")
+    W = (K // 128 + 3) // 4
+    q = np.zeros((E, M_max, K), np.uint8)
+    sf = np.zeros((E, W, M_max), np.uint32)
+    mm = np.zeros(E, np.int32)
+    slot = np.zeros((T, topk), np.int32)
+    _load().orc_quant_group_pack_to_experts(_ptr(x), K, T, K, _ptr(ids), topk, E, M_max, _ptr(q), _ptr(sf),
+                                            _ptr(mm), _ptr(slot))
+    return q, sf, mm, slot
 
 
 def block_quant_128x128(w: np.ndarray):

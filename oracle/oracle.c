@@ -230,6 +230,44 @@ void orc_block_quant_128x128(const uint16_t* w, int64_t N, int64_t K, uint8_t* q
   }
 }
 
+/* Per-token group quant into the masked expert layout of routed tokens (the
+ * quantization of FP8 dispatch: PR #19885, Summary item 1; PR #19111 review, the
+ * TODO asking for a batched quant).  Pair p = t * topk + j goes to expert ids[p]
+ * when 0 <= ids[p] < E; its slot is the number of earlier pairs (in p order) routed
+ * to the same expert.  Invalid ids and slots >= M_max give slot -1 and write nothing.
+ * Every routed token is quantized as orc_quant_group_pack quantizes a row and copied
+ * to row `slot` of its expert.  q: e4m3 [E][M_max][K], sf: uint32 [E][W][M_max],
+ * masked_m: int32 [E] = min(pairs routed to e, M_max), slot_of: int32 [T * topk]. */
+void orc_quant_group_pack_to_experts(const uint16_t* x, int64_t ldx, int64_t T, int64_t K,
+                                     const int32_t* ids, int64_t topk, int64_t E, int64_t M_max,
+                                     uint8_t* q, uint32_t* sf, int32_t* masked_m, int32_t* slot_of) {
+  int64_t W = (K / 128 + 3) / 4;
+  int64_t* count = (int64_t*)calloc((size_t)(E > 0 ? E : 1), sizeof(int64_t));
+  uint8_t* qrow = (uint8_t*)malloc((size_t)(K > 0 ? K : 1));
+  uint32_t* sfrow = (uint32_t*)malloc(sizeof(uint32_t) * (size_t)(W > 0 ? W : 1));
+  for (int64_t t = 0; t < T; ++t) {
+    int quantized = 0;
+    for (int64_t j = 0; j < topk; ++j) {
+      int64_t pidx = t * topk + j;
+      int64_t e = ids[pidx];
+      if (e < 0 || e >= E) { slot_of[pidx] = -1; continue; }
+      int64_t slot = count[e]++;
+      if (slot >= M_max) { slot_of[pidx] = -1; continue; }
+      slot_of[pidx] = (int32_t)slot;
+      if (!quantized) {
+        orc_quant_group_pack(x + t * ldx, ldx, 1, K, qrow, K, sfrow, 1);
+        quantized = 1;
+      }
+      memcpy(q + (e * M_max + slot) * K, qrow, (size_t)K);
+      for (int64_t w = 0; w < W; ++w) sf[(e * W + w) * M_max + slot] = sfrow[w];
+    }
+  }
+  for (int64_t e = 0; e < E; ++e) masked_m[e] = (int32_t)(count[e] < M_max ? count[e] : M_max);
+  free(count);
+  free(qrow);
+  free(sfrow);
+}
+
 /* ------------------------------------------------------------------------ */
 /* Block-scaled GEMM, NT form: for each selected row m and column n,
  *   C[m][n] = sum over K-blocks kb of  2^(ea[m][kb]) * sfb[n/128][kb]

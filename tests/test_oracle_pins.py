@@ -343,6 +343,52 @@ def test_masked_counts_clamped_and_rows_untouched():
     assert np.array_equal(out[1, :3], O.gemm_nt(a[1], sfa[1], b[1], sfb[1])[:3])
 
 
+# ---------------------------------------------------------------- quant into the expert layout
+
+def _dispatch_case(seed=0):
+    rng = np.random.default_rng(seed)
+    T, topk, E, M_max, K = 41, 3, 5, 9, 640
+    ids = rng.integers(-1, E + 2, (T, topk)).astype(np.int32)  # -1 and >= E: not routed
+    ids[0] = [2, 2, 2]                                         # one token routed thrice to one expert
+    x = W.normal_bf16((T, K), seed=seed, tensor_id=W.T_X)
+    return x, ids, E, M_max
+
+
+def test_dispatch_slots_brute_force():
+    """Slots and counts against a dictionary walk over the pairs in token-major order."""
+    x, ids, E, M_max = _dispatch_case(1)
+    _, _, mm, slot = O.quant_group_pack_to_experts(x, ids, E, M_max)
+    seen = {}
+    for t in range(ids.shape[0]):
+        for j in range(ids.shape[1]):
+            e = int(ids[t, j])
+            if not 0 <= e < E:
+                assert slot[t, j] == -1
+                continue
+            k = seen.get(e, 0)
+            seen[e] = k + 1
+            assert slot[t, j] == (k if k < M_max else -1), (t, j)
+    assert [int(v) for v in mm] == [min(seen.get(e, 0), M_max) for e in range(E)]
+    assert any(seen.get(e, 0) > M_max for e in range(E))  # the case exercises the capacity
+
+
+def test_dispatch_rows_are_the_token_quant():
+    """Every written row equals the per-token quant of its token (the pinned a1 oracle);
+    rows at or past the count stay zero."""
+    x, ids, E, M_max = _dispatch_case(2)
+    q, sf, mm, slot = O.quant_group_pack_to_experts(x, ids, E, M_max)
+    qt, sft = O.quant_group_pack(x, ld_sf=x.shape[0])
+    written = np.zeros((E, M_max), bool)
+    for t, j in zip(*np.nonzero(slot >= 0)):
+        e, sl = ids[t, j], slot[t, j]
+        assert np.array_equal(q[e, sl], qt[t])
+        assert np.array_equal(sf[e, :, sl], sft[:, t])
+        written[e, sl] = True
+    for e in range(E):
+        assert written[e, :mm[e]].all() and not written[e, mm[e]:].any()
+        assert not q[e, mm[e]:].any()
+
+
 # ---------------------------------------------------------------- contiguous grouped GEMM
 
 def test_contiguous_integer_brute_force_with_varied_scales():

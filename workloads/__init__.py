@@ -62,6 +62,16 @@ def zipf_counts(E: int = 32, tokens: int = 4096, s: float = 1.1, cap: int = 256,
     return np.minimum(draw, cap).astype(np.int32)
 
 
+def topk_routing(T: int = 512, topk: int = 8, E: int = 32, s: float = 1.1, seed: int = 0) -> np.ndarray:
+    """Expert choices int32 [T, topk]: for every token, topk distinct experts drawn without
+    replacement with weights p_e ~ (e+1)^-s (the masked workload's Zipf skew), from
+    ``default_rng([seed, 7])``."""
+    p = (np.arange(1, E + 1, dtype=np.float64)) ** (-s)
+    p /= p.sum()
+    rng = np.random.default_rng([seed, 7])
+    return np.stack([rng.choice(E, size=topk, replace=False, p=p) for _ in range(T)]).astype(np.int32)
+
+
 def contiguous_layout(counts, align: int = 128, tail_blocks: int = 0) -> np.ndarray:
     """Row -> group map of the contiguous grouped layout: group g's rows in a run of
     round_up(counts[g], align) rows (the first counts[g] name g, the rest are padding,
