@@ -24,6 +24,7 @@ __all__ = [
     "fp8_block_gemm_nt", "fp8_block_gemm_grouped_masked", "gemm_config", "gemm_config_count",
     "library_path", "header_path", "declared_functions", "gemm_config_of",
     "fp8_quant_group_pack_to_experts", "fp8_block_gemm_grouped_contiguous",
+    "fp8_quant_group_float", "fp8_block_quant_128x128_float", "fp8_block_gemm_nt_float_scales",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -46,6 +47,10 @@ _SIGS = {
     "silu_mul_quant_group_pack": [_P, _P, _I64, _I64, _I64, _P, _P, _P],
     "fp8_block_quant_128x128": [_P, _I64, _I64, _P, _P, _P],
     "fp8_quant_group_pack_to_experts": [_P, _I64, _I64, _I64, _P, _I32, _I64, _I64, _P, _P, _P, _P, _P],
+    "fp8_quant_group_float": [_P, _I64, _I64, _I64, _P, _I64, _P, _I64, _P],
+    "fp8_block_quant_128x128_float": [_P, _I64, _I64, _P, _P, _P],
+    "fp8_block_gemm_nt_float_scales": [_P, _P, _I64, _P, _P, _P, _I64, _I64, _I64, _I64, _P],
+    "fp8_block_gemm_nt_float_scales_cfg": [_P, _P, _I64, _P, _P, _P, _I64, _I64, _I64, _I64, _I32, _I32, _P],
     "fp8_block_gemm_nt": [_P, _P, _I64, _P, _P, _P, _I64, _I64, _I64, _I64, _P],
     "fp8_block_gemm_nt_cfg": [_P, _P, _I64, _P, _P, _P, _I64, _I64, _I64, _I64, _I32, _I32, _P],
     "fp8_block_gemm_grouped_masked": [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _P],
@@ -342,7 +347,73 @@ def fp8_block_gemm_grouped_contiguous(a: torch.Tensor, sfa: torch.Tensor, b: tor
     return c
 
 
-LAYOUT_DENSE, LAYOUT_MASKED, LAYOUT_CONTIGUOUS = 0, 1, 2
+LAYOUT_DENSE, LAYOUT_MASKED, LAYOUT_CONTIGUOUS, LAYOUT_DENSE_FLOAT = 0, 1, 2, 3
+
+
+def fp8_quant_group_float(x: torch.Tensor, q: torch.Tensor | None = None, sf: torch.Tensor | None = None,
+                          ld_sf: int | None = None, stream=None):
+    """1x128 per-token group quant with float scales (amax / 448, unrounded).
+    x bf16 [M, K] -> (q uint8 [M, K], sf float32 [K/128, ld_sf]); ld_sf defaults to round_up(M, 4)."""
+    _expect(x, "x", _BF16, 2)
+    M, K = x.shape
+    if q is None:
+        q = torch.empty((M, K), dtype=torch.uint8, device=x.device)
+    if sf is None:
+        ld = ld_sf if ld_sf is not None else max(4, (M + 3) // 4 * 4)
+        sf = torch.empty((K // 128, ld), dtype=torch.float32, device=x.device)
+    _expect(q, "q", _E4M3, 2)
+    _expect(sf, "sf", (torch.float32,), 2)
+    st = _lib.fp8_quant_group_float(x.data_ptr(), x.stride(0), M, K, q.data_ptr(), q.stride(0), sf.data_ptr(),
+                                    sf.stride(0), _stream(stream))
+    _check("fp8_quant_group_float", st)
+    return q, sf
+
+
+def fp8_block_quant_128x128_float(w: torch.Tensor, stream=None):
+    """128x128 weight block quant with float scales: bf16 w [N, K] -> (q uint8 [N, K],
+    sfb float32 [ceil(N/128), K/128])."""
+    _expect(w, "w", _BF16, 2)
+    _contig(w, "w")
+    N, K = w.shape
+    q = torch.empty((N, K), dtype=torch.uint8, device=w.device)
+    sfb = torch.empty(((N + 127) // 128, K // 128), dtype=torch.float32, device=w.device)
+    st = _lib.fp8_block_quant_128x128_float(w.data_ptr(), N, K, q.data_ptr(), sfb.data_ptr(), _stream(stream))
+    _check("fp8_block_quant_128x128_float", st)
+    return q, sfb
+
+
+def fp8_block_gemm_nt_float_scales(a: torch.Tensor, sfa: torch.Tensor, b: torch.Tensor, sfb: torch.Tensor,
+                                   c: torch.Tensor | None = None, kernel: int | None = None,
+                                   splits: int | None = None, stream=None) -> torch.Tensor:
+    """Dense GEMM with float scales -> bf16 [M, N].  a uint8 [M, K], sfa float32 [K/128, ld_sfa],
+    b uint8 [N, K], sfb float32 [ceil(N/128), K/128]."""
+    _expect(a, "a", _E4M3, 2)
+    _contig(a, "a")
+    _expect(b, "b", _E4M3, 2)
+    _contig(b, "b")
+    _expect(sfa, "sfa", (torch.float32,), 2)
+    _expect(sfb, "sfb", (torch.float32,), 2)
+    _contig(sfb, "sfb")
+    M, K = a.shape
+    N = b.shape[0]
+    if b.shape[1] != K:
+        raise ValueError("a and b disagree on K")
+    if c is None:
+        c = torch.empty((M, N), dtype=torch.bfloat16, device=a.device)
+    _expect(c, "c", _BF16, 2)
+    if tuple(c.shape) != (M, N):
+        raise ValueError("c must be [M, N]")
+    s = _stream(stream)
+    args = (a.data_ptr(), sfa.data_ptr(), sfa.stride(0), b.data_ptr(), sfb.data_ptr(), c.data_ptr(), c.stride(0),
+            M, N, K)
+    if kernel is None and splits is None:
+        st = _lib.fp8_block_gemm_nt_float_scales(*args, s)
+    else:
+        if kernel is None:
+            kernel = gemm_config(LAYOUT_DENSE_FLOAT, M, N, K)["kernel"]
+        st = _lib.fp8_block_gemm_nt_float_scales_cfg(*args, int(kernel), int(splits or 1), s)
+    _check("fp8_block_gemm_nt_float_scales", st)
+    return c
 
 
 def gemm_config_count() -> int:
@@ -352,7 +423,7 @@ def gemm_config_count() -> int:
 def gemm_config_of(kernel: int, masked, M: int, N: int, K: int, splits: int = 1):
     """Workgroup tile and split count table entry `kernel` would use for this
     problem, or None if the entry does not accept it.  masked: False/0 dense,
-    True/1 masked grouped, 2 contiguous grouped."""
+    True/1 masked grouped, 2 contiguous grouped, 3 dense with float scales."""
     bm, bn, sp = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
     st = _lib.fp8bs_gemm_config_of(int(kernel), int(masked), M, N, K, int(splits), ctypes.byref(bm),
                                    ctypes.byref(bn), ctypes.byref(sp))
@@ -363,7 +434,8 @@ def gemm_config_of(kernel: int, masked, M: int, N: int, K: int, splits: int = 1)
 
 
 def gemm_config(masked, M: int, N: int, K: int) -> dict:
-    """Automatic choice for a dense (False/0), masked (True/1) or contiguous grouped (2) problem."""
+    """Automatic choice for a dense (False/0), masked (True/1), contiguous grouped (2) or
+    dense float-scale (3) problem."""
     k, bm, bn, sp = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
     st = _lib.fp8bs_gemm_config(int(masked), M, N, K, ctypes.byref(k), ctypes.byref(bm),
                                 ctypes.byref(bn), ctypes.byref(sp))

@@ -190,12 +190,15 @@ fp8bs::GemmProblem contiguous_problem(const void* a, const uint32_t* sfa, int64_
 
 // A problem of the given layout (0 dense, 1 masked, 2 contiguous) for host-side
 // configuration queries only: its pointers are placeholders that are never read.
+// (3: dense with float scales)
 fp8bs::GemmProblem host_problem(int layout, int64_t M, int64_t N, int64_t K) {
   static const int32_t placeholder = 0;
   if (layout == 1) return masked_problem(nullptr, nullptr, nullptr, nullptr, nullptr, &placeholder, 1, M, N, K);
   if (layout == 2)
     return contiguous_problem(nullptr, nullptr, M, nullptr, nullptr, nullptr, N, &placeholder, 1, M, N, K);
-  return dense_problem(nullptr, nullptr, M, nullptr, nullptr, nullptr, N, M, N, K);
+  fp8bs::GemmProblem p = dense_problem(nullptr, nullptr, M, nullptr, nullptr, nullptr, N, M, N, K);
+  p.float_scales = layout == 3;
+  return p;
 }
 
 }  // namespace
@@ -228,6 +231,34 @@ int silu_mul_quant_group_pack(const void* x, const int32_t* masked_m, int64_t E,
   if (st != FP8BS_OK) return st;
   hipError_t e = fp8bs::launch_silu_mul_quant(static_cast<const uint16_t*>(x), masked_m, E, M_max, H,
                                               static_cast<uint8_t*>(q), sf, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FP8BS_OK : fail_hip(e);
+}
+
+int fp8_quant_group_float(const void* x, int64_t ldx, int64_t M, int64_t K, void* q, int64_t ldq, float* sf,
+                          int64_t ld_sf, void* stream) {
+  if (M < 0 || K < 0 || K % 128 != 0) return FP8BS_ERR_SHAPE;
+  if (M == 0 || K == 0) return FP8BS_OK;
+  if (!x || !q || !sf) return FP8BS_ERR_NULL;
+  if (ldx < K || ldq < K || ld_sf < M) return FP8BS_ERR_SHAPE;
+  if (!aligned(x, 16) || !aligned(q, 16) || ldx % 8 != 0 || ldq % 16 != 0 || !aligned(sf, 4))
+    return FP8BS_ERR_ALIGN;
+  int st = check_device();
+  if (st != FP8BS_OK) return st;
+  hipError_t e = fp8bs::launch_quant_group_float(static_cast<const uint16_t*>(x), ldx, M, K,
+                                                 static_cast<uint8_t*>(q), ldq, sf, ld_sf,
+                                                 static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FP8BS_OK : fail_hip(e);
+}
+
+int fp8_block_quant_128x128_float(const void* w, int64_t N, int64_t K, void* q, float* sfb, void* stream) {
+  if (N < 0 || K < 0 || K % 128 != 0) return FP8BS_ERR_SHAPE;
+  if (N == 0 || K == 0) return FP8BS_OK;
+  if (!w || !q || !sfb) return FP8BS_ERR_NULL;
+  if (!aligned(w, 16) || !aligned(q, 16) || !aligned(sfb, 4)) return FP8BS_ERR_ALIGN;
+  int st = check_device();
+  if (st != FP8BS_OK) return st;
+  hipError_t e = fp8bs::launch_block_quant_float(static_cast<const uint16_t*>(w), N, K,
+                                                 static_cast<uint8_t*>(q), sfb, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FP8BS_OK : fail_hip(e);
 }
 
@@ -343,13 +374,38 @@ int fp8_block_gemm_grouped_contiguous_cfg(const void* a, const uint32_t* sfa, in
   return run_gemm(p, cfg, static_cast<hipStream_t>(stream));
 }
 
+int fp8_block_gemm_nt_float_scales(const void* a, const float* sfa, int64_t ld_sfa, const void* b, const float* sfb,
+                                   void* c, int64_t ldc, int64_t M, int64_t N, int64_t K, void* stream) {
+  int st = check_dense(a, reinterpret_cast<const uint32_t*>(sfa), ld_sfa, b, sfb, c, ldc, M, N, K);
+  if (st != FP8BS_OK) return st > 0 ? FP8BS_OK : st;
+  st = check_device();
+  if (st != FP8BS_OK) return st;
+  fp8bs::GemmProblem p = dense_problem(a, reinterpret_cast<const uint32_t*>(sfa), ld_sfa, b, sfb, c, ldc, M, N, K);
+  p.float_scales = true;
+  return run_gemm(p, fp8bs::choose_gemm_config(p), static_cast<hipStream_t>(stream));
+}
+
+int fp8_block_gemm_nt_float_scales_cfg(const void* a, const float* sfa, int64_t ld_sfa, const void* b,
+                                       const float* sfb, void* c, int64_t ldc, int64_t M, int64_t N, int64_t K,
+                                       int32_t kernel, int32_t splits, void* stream) {
+  int st = check_dense(a, reinterpret_cast<const uint32_t*>(sfa), ld_sfa, b, sfb, c, ldc, M, N, K);
+  if (st != FP8BS_OK) return st > 0 ? FP8BS_OK : st;
+  st = check_device();
+  if (st != FP8BS_OK) return st;
+  fp8bs::GemmProblem p = dense_problem(a, reinterpret_cast<const uint32_t*>(sfa), ld_sfa, b, sfb, c, ldc, M, N, K);
+  p.float_scales = true;
+  fp8bs::GemmConfig cfg;
+  if (!fp8bs::gemm_config_by_index(kernel, p, splits < 1 ? 1 : splits, &cfg)) return FP8BS_ERR_SHAPE;
+  return run_gemm(p, cfg, static_cast<hipStream_t>(stream));
+}
+
 int fp8bs_gemm_config_count(void) { return fp8bs::gemm_config_count(); }
 
 int fp8bs_gemm_config(int masked, int64_t M, int64_t N, int64_t K, int32_t* kernel, int32_t* bm, int32_t* bn,
                       int32_t* splits) {
   if (M < 0 || N < 0 || K < 128 || K % 128 != 0 || N % 64 != 0) return FP8BS_ERR_SHAPE;
   if (!kernel || !bm || !bn || !splits) return FP8BS_ERR_NULL;
-  if (masked < 0 || masked > 2) return FP8BS_ERR_SHAPE;
+  if (masked < 0 || masked > 3) return FP8BS_ERR_SHAPE;
   const fp8bs::GemmProblem p = host_problem(masked, M, N, K);
   const fp8bs::GemmConfig cfg = fp8bs::choose_gemm_config(p);
   *kernel = cfg.kernel;
@@ -363,7 +419,7 @@ int fp8bs_gemm_config_of(int32_t kernel, int masked, int64_t M, int64_t N, int64
                          int32_t* bn, int32_t* splits_out) {
   if (M < 0 || N < 0 || K < 128 || K % 128 != 0 || N % 64 != 0) return FP8BS_ERR_SHAPE;
   if (!bm || !bn || !splits_out) return FP8BS_ERR_NULL;
-  if (masked < 0 || masked > 2) return FP8BS_ERR_SHAPE;
+  if (masked < 0 || masked > 3) return FP8BS_ERR_SHAPE;
   const fp8bs::GemmProblem p = host_problem(masked, M, N, K);
   fp8bs::GemmConfig cfg;
   if (!fp8bs::gemm_config_by_index(kernel, p, splits < 1 ? 1 : splits, &cfg)) return FP8BS_ERR_SHAPE;

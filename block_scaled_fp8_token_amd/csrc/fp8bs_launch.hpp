@@ -16,6 +16,12 @@ hipError_t launch_silu_mul_quant(const uint16_t* x, const int32_t* masked_m, int
 hipError_t launch_block_quant(const uint16_t* w, int64_t N, int64_t K, uint8_t* q, float* sfb,
                               hipStream_t stream);
 
+// Float-scale (non-UE8M0) variants: scale = max(amax, 1e-10) / 448 in fp32.
+hipError_t launch_quant_group_float(const uint16_t* x, int64_t ldx, int64_t M, int64_t K, uint8_t* q,
+                                   int64_t ldq, float* sf, int64_t ld_sf, hipStream_t stream);
+hipError_t launch_block_quant_float(const uint16_t* w, int64_t N, int64_t K, uint8_t* q, float* sfb,
+                                   hipStream_t stream);
+
 // Routing ranks (one workgroup per 1024 pairs) then the quantization into the masked
 // expert layout; scratch: quant_to_experts_scratch_bytes() of device memory (pair
 // ranks and per-chunk expert counts), free for other use once the launches are done.
@@ -39,6 +45,9 @@ struct GemmProblem {
   int64_t ld_sfa, ldc;
   const int32_t* m_indices = nullptr;  // [M] weight group of every row (-1: padding), or nullptr
   int64_t groups = 1;                  // weight groups of the contiguous layout
+  // float-scale format (dense only): sfa points at fp32 [K/128][ld_sfa] scales and the
+  // weight scales are any fp32 values
+  bool float_scales = false;
 };
 
 // Rows per aligned run of one weight group in the contiguous grouped layout.

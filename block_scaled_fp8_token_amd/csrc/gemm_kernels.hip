@@ -70,6 +70,7 @@ struct KArgs {
   uint32_t* counters;  // per-tile arrival counters of the fused split-K (zero between calls)
   const int32_t* m_indices;  // contiguous grouped layout: weight group of every row, or nullptr
   int64_t groups;            // weight groups m_indices may name
+  const float* sfa_f;        // float activation scales [K/128][ld_sfa] (float-scale kernels), or nullptr
 };
 
 // Weight group of the tile whose first row is m0: the grid's group e (dense and
@@ -174,7 +175,9 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
   *reinterpret_cast<uint4*>(C + m * ldc + n) = o;
 }
 
-template <int BM, int BN, int WM, int WN>
+// FS: the float-scale format (activation scales fp32 [K/128][ld_sfa], weight scales
+// any fp32): the MFMA runs unscaled and the two scales multiply its result.
+template <int BM, int BN, int WM, int WN, bool FS = false>
 __global__ __launch_bounds__(256) void gemm_kernel(const KArgs p) {
   constexpr int NWN = BN / WN;
   constexpr int SM = WM / 16, SN = WN / 16;
@@ -272,8 +275,12 @@ __global__ __launch_bounds__(256) void gemm_kernel(const KArgs p) {
 #pragma unroll
     for (int i = 0; i < SM; ++i) {
       const int64_t m = wrow0 + 16 * i + (lane & 15);
-      const uint32_t wd = (m < m_limit) ? SA[(int64_t)(kb >> 2) * p.ld_sfa + m] : 0u;
-      sa[i] = __uint_as_float(((wd >> (8 * (kb & 3))) & 0xFFu) << 23);
+      if constexpr (FS) {
+        sa[i] = (m < m_limit) ? p.sfa_f[(int64_t)kb * p.ld_sfa + m] : 0.0f;
+      } else {
+        const uint32_t wd = (m < m_limit) ? SA[(int64_t)(kb >> 2) * p.ld_sfa + m] : 0u;
+        sa[i] = __uint_as_float(((wd >> (8 * (kb & 3))) & 0xFFu) << 23);
+      }
     }
 #pragma unroll
     for (int j = 0; j < SN; ++j) {
@@ -1631,7 +1638,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const KArgs p) {
 
 typedef void (*KernelFn)(const KArgs);
 
-enum Kind { kTile = 0, kStream = 1, kScaled = 2, kRing = 3, kDecode = 4 };
+enum Kind { kTile = 0, kStream = 1, kScaled = 2, kRing = 3, kDecode = 4, kTileFloat = 5 };
 
 struct TileEntry {
   KernelFn fn;
@@ -1675,6 +1682,10 @@ const TileEntry kTiles[] = {
     {decode_kernel<8, 2>, 64, 256, kDecode, 2, 512, DecodeShape<8, 2>::WMAX},
     {decode_kernel<4, 2>, 64, 128, kDecode, 2, 256, DecodeShape<4, 2>::WMAX},
     {decode_kernel<8, 3>, 64, 256, kDecode, 3, 512, DecodeShape<8, 3>::WMAX},
+    {gemm_kernel<64, 128, 64, 32, true>, 64, 128, kTileFloat, 2, 256},
+    {gemm_kernel<128, 128, 64, 64, true>, 128, 128, kTileFloat, 2, 256},
+    {gemm_kernel<64, 256, 64, 64, true>, 64, 256, kTileFloat, 2, 256},
+    {gemm_kernel<128, 256, 64, 128, true>, 128, 256, kTileFloat, 2, 256},
 };
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 // table entries the automatic choice uses
@@ -1684,8 +1695,11 @@ constexpr int kCfgScaled256x256 = 19;
 constexpr int kCfgRing256x256 = 21;        // 2 x 2 wavefronts
 constexpr int kCfgRing256x256Rows = 24;    // 1 x 4 wavefronts (all share the rows)
 constexpr int kCfgRing128x256 = 23;        // 2 x 2 wavefronts, 128-row tiles
+constexpr int kCfgFloat64x128 = 30;        // float-scale VALU-scaled tiles
+constexpr int kCfgFloat128x128 = 31;
+constexpr int kCfgFloat128x256 = 33;
 constexpr int kCfgDecode64x128 = 26;       // decode kernel, 4 wavefronts, three K-blocks in flight
-static_assert(kCfgDecode64x128 < kNumTiles, "tile table");
+static_assert(kCfgDecode64x128 < kNumTiles && kCfgFloat128x256 < kNumTiles, "tile table");
 
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -1708,6 +1722,9 @@ bool gemm_config_by_index(int idx, const GemmProblem& p, int splits, GemmConfig*
   const int KB = (int)(p.K / 128);
   if (splits > KB) splits = KB > 0 ? KB : 1;
   if ((p.masked_m || p.m_indices) && splits != 1) return false;
+  // the float-scale format runs on the float-scale entries only (dense calls)
+  if ((kTiles[idx].kind == kTileFloat) != p.float_scales) return false;
+  if (p.float_scales && (p.masked_m || p.m_indices || p.E != 1)) return false;
   // contiguous grouped layout: a tile must not straddle two aligned runs
   if (p.m_indices && kContiguousAlign % kTiles[idx].bm != 0) return false;
   if (kTiles[idx].kind == kRing) {
@@ -1764,6 +1781,22 @@ bool gemm_config_by_index(int idx, const GemmProblem& p, int splits, GemmConfig*
 GemmConfig choose_gemm_config(const GemmProblem& p) {
   GemmConfig cfg;
   const int KB = (int)(p.K / 128);
+  if (p.float_scales) {
+    // float-scale format: VALU-scaled tiles; small M splits K until about 224
+    // workgroups, large M takes 128 x 256 tiles once they fill the compute units
+    if (p.M <= 64) {
+      const int64_t tiles = cdiv(p.N, kTiles[kCfgFloat64x128].bn);
+      int splits = (int)(224 / (tiles > 0 ? tiles : 1));
+      const int max_splits = KB / 4 > 1 ? KB / 4 : 1;
+      if (splits > max_splits) splits = max_splits;
+      if (splits < 1) splits = 1;
+      gemm_config_by_index(kCfgFloat64x128, p, splits, &cfg);
+      return cfg;
+    }
+    const int64_t t256 = cdiv(p.M, 128) * cdiv(p.N, 256);
+    gemm_config_by_index(t256 >= 256 ? kCfgFloat128x256 : kCfgFloat128x128, p, 1, &cfg);
+    return cfg;
+  }
   if (p.m_indices) {
     // contiguous grouped layout: 128-row tiles (one aligned run each); 128 x 256 ring
     // tiles when the scale tables hold K, else the 128 x 128 scaled tiles
@@ -1878,6 +1911,8 @@ hipError_t launch_gemm(const GemmProblem& p, const GemmConfig& cfg, void* ws, hi
   k.a = p.a; k.sfa = p.sfa; k.b = p.b; k.sfb = p.sfb; k.c = p.c; k.masked_m = p.masked_m;
   k.m_indices = p.m_indices;
   k.groups = p.groups;
+  k.sfa_f = p.float_scales ? reinterpret_cast<const float*>(p.sfa) : nullptr;
+  if (p.float_scales != (t.kind == kTileFloat)) return hipErrorInvalidValue;
   if (p.m_indices && (p.E != 1 || p.masked_m || cfg.splits != 1 || kContiguousAlign % t.bm != 0))
     return hipErrorInvalidValue;
   k.M = p.M; k.N = p.N; k.K = p.K; k.ld_sfa = p.ld_sfa; k.ldc = p.ldc;

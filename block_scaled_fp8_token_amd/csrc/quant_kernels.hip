@@ -7,6 +7,8 @@
 //     DeepGEMM + DeepEP low latency case", Summary item 2);
 //   * 128x128 weight block quant (the offline weight step of the vLLM DeepGEMM
 //     FP8 block GEMM benchmark post, section 4.1);
+//   * float-scale variants of the activation and weight quant (scale = amax / 448
+//     unrounded: the non-UE8M0 format of the benchmark post, section 4.1);
 //   * the same per-token quant written straight into the masked expert layout of
 //     the routed tokens (the quantization half of FP8 dispatch: PR #19885,
 //     Summary item 1, DeepEP puts the scales in DeepGEMM's layout; PR #19111 review,
@@ -150,6 +152,85 @@ __global__ __launch_bounds__(256) void block_quant_kernel(
     if (n < N) *reinterpret_cast<uint2*>(q + n * K + kb * 128 + ch * 8) = e4m3x8(f);
   }
   if (t == 0) sfb[nb * KB + kb] = exp2i(e);
+}
+
+// Float-scale variants (the non-UE8M0 format of the benchmark post, section 4.1:
+// the scale of a group or block is amax / 448 itself, not rounded to a power of
+// two).  All in IEEE fp32 with correctly rounded division:
+//   s = max(amax, 1e-10f) / 448,  q = e4m3_rne(clamp(x / s, -448, 448)).
+__device__ __forceinline__ float float_scale(float amax) {
+  const float a = amax > 1e-10f ? amax : 1e-10f;
+  return a / 448.0f;
+}
+
+// One wavefront per (row, 512 columns): four groups, lanes 16g..16g+15 hold group g.
+// Scales fp32 [K/128][ld_sf] (one float per group, M-major).
+__global__ __launch_bounds__(256) void quant_group_float_kernel(
+    const uint16_t* __restrict__ x, int64_t ldx, int64_t M, int64_t K, uint8_t* __restrict__ q,
+    int64_t ldq, float* __restrict__ sf, int64_t ld_sf, int64_t W) {
+  const int lane = threadIdx.x & 63;
+  const int64_t units = M * W;
+  const int64_t nwaves = (int64_t)gridDim.x * 4;
+  for (int64_t u = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); u < units; u += nwaves) {
+    const int64_t r = u / W, w = u - r * W;
+    const int64_t col = w * 512 + lane * 8;
+    const bool valid = col < K;
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (valid) v = *reinterpret_cast<const uint4*>(x + r * ldx + col);
+    float f[8];
+    unpack8(v, f);
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = __builtin_fmaxf(amax, __builtin_fabsf(f[i]));
+    amax = max16(amax);
+    const float sc = float_scale(amax);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) f[i] = f[i] / sc;
+    if (valid) {
+      *reinterpret_cast<uint2*>(q + r * ldq + col) = e4m3x8(f);
+      if ((lane & 15) == 0) sf[(w * 4 + (lane >> 4)) * ld_sf + r] = sc;
+    }
+  }
+}
+
+// One workgroup per 128x128 block (as block_quant_kernel) with the float scale.
+__global__ __launch_bounds__(256) void block_quant_float_kernel(
+    const uint16_t* __restrict__ w, int64_t N, int64_t K, uint8_t* __restrict__ q,
+    float* __restrict__ sfb, int64_t KB) {
+  __shared__ float wmax[4];
+  const int64_t kb = blockIdx.x, nb = blockIdx.y;
+  const int t = threadIdx.x;
+  uint4 v[8];
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int cidx = t + 256 * i, row = cidx >> 4, ch = cidx & 15;
+    const int64_t n = nb * 128 + row;
+    v[i] = make_uint4(0u, 0u, 0u, 0u);
+    if (n < N) v[i] = *reinterpret_cast<const uint4*>(w + n * K + kb * 128 + ch * 8);
+    float f[8];
+    unpack8(v[i], f);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) amax = __builtin_fmaxf(amax, __builtin_fabsf(f[j]));
+  }
+  amax = max16(amax);
+  amax = __builtin_fmaxf(amax, __shfl_xor(amax, 16));
+  amax = __builtin_fmaxf(amax, __shfl_xor(amax, 32));
+  if ((t & 63) == 0) wmax[t >> 6] = amax;
+  __syncthreads();
+  amax = __builtin_fmaxf(__builtin_fmaxf(wmax[0], wmax[1]), __builtin_fmaxf(wmax[2], wmax[3]));
+  const float sc = float_scale(amax);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int cidx = t + 256 * i, row = cidx >> 4, ch = cidx & 15;
+    const int64_t n = nb * 128 + row;
+    float f[8];
+    unpack8(v[i], f);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) f[j] = f[j] / sc;
+    if (n < N) *reinterpret_cast<uint2*>(q + n * K + kb * 128 + ch * 8) = e4m3x8(f);
+  }
+  if (t == 0) sfb[nb * KB + kb] = sc;
 }
 
 // Expert slots of routed tokens (the dispatch half of FP8 dispatch on one GPU): pair
@@ -316,6 +397,26 @@ size_t quant_to_experts_scratch_bytes(int64_t T, int topk, int64_t E) {
   const int64_t P = T * topk;
   const int64_t nchunks = (P + kRouteThreads - 1) / kRouteThreads;
   return (size_t)(P + nchunks * E) * sizeof(int32_t);
+}
+
+hipError_t launch_quant_group_float(const uint16_t* x, int64_t ldx, int64_t M, int64_t K, uint8_t* q,
+                                   int64_t ldq, float* sf, int64_t ld_sf, hipStream_t stream) {
+  const int64_t W = (K / 128 + 3) / 4;
+  int64_t blocks = (M * W + 3) / 4;
+  if (blocks > 4096) blocks = 4096;
+  if (blocks < 1) return hipSuccess;
+  hipLaunchKernelGGL(quant_group_float_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, x, ldx, M, K, q,
+                     ldq, sf, ld_sf, W);
+  return hipGetLastError();
+}
+
+hipError_t launch_block_quant_float(const uint16_t* w, int64_t N, int64_t K, uint8_t* q, float* sfb,
+                                   hipStream_t stream) {
+  const int64_t KB = K / 128, NB = (N + 127) / 128;
+  if (KB < 1 || NB < 1) return hipSuccess;
+  hipLaunchKernelGGL(block_quant_float_kernel, dim3((unsigned)KB, (unsigned)NB), dim3(256), 0, stream, w, N, K,
+                     q, sfb, KB);
+  return hipGetLastError();
 }
 
 hipError_t launch_block_quant(const uint16_t* w, int64_t N, int64_t K, uint8_t* q, float* sfb,

@@ -87,6 +87,29 @@ int silu_mul_quant_group_pack(const void* x, const int32_t* masked_m, int64_t E,
                               int64_t H, void* q, uint32_t* sf, void* stream);
 
 /*
+ * Float-scale (non-UE8M0) format (benchmark post section 4.1: the scale of a
+ * group or block is amax / fp8_max, rounded up to a power of two only when UE8M0
+ * is asked for).  In IEEE fp32 with correctly rounded division:
+ *   s = max(amax, 1e-10f) / 448,  q = e4m3_rne(clamp(x / s, -448, 448)).
+ * fp8_quant_group_float: 1x128 groups of bf16 x [M][ldx] (ldx >= K, ldx % 8 == 0)
+ *   -> q e4m3 [M][ldq] (ldq % 16 == 0), sf fp32 [K/128][ld_sf], ld_sf >= M
+ *   (one float per group, M-major; entries of rows >= M untouched).
+ * fp8_block_quant_128x128_float: 128x128 blocks of bf16 w [N][K] -> q e4m3 [N][K],
+ *   sfb fp32 [ceil(N/128)][K/128].
+ * fp8_block_gemm_nt_float_scales: C[m][n] = bf16( sum over K-blocks kb of
+ *   sfa[kb][m] * sfb[n/128][kb] * (e4m3 dot product of the block) ), fp32
+ *   accumulation; sfa fp32 [K/128][ld_sfa], ld_sfa >= M; other arguments and
+ *   preconditions as fp8_block_gemm_nt (the scales may be any finite fp32).
+ */
+int fp8_quant_group_float(const void* x, int64_t ldx, int64_t M, int64_t K, void* q, int64_t ldq,
+                          float* sf, int64_t ld_sf, void* stream);
+int fp8_block_quant_128x128_float(const void* w, int64_t N, int64_t K, void* q, float* sfb,
+                                  void* stream);
+int fp8_block_gemm_nt_float_scales(const void* a, const float* sfa, int64_t ld_sfa, const void* b,
+                                   const float* sfb, void* c, int64_t ldc, int64_t M, int64_t N,
+                                   int64_t K, void* stream);
+
+/*
  * Per-token group quant written into the masked expert layout of the routed
  * tokens: the quantization half of FP8 dispatch on one GPU (PR #19885, Summary
  * item 1: DeepEP quantizes and puts the scales in DeepGEMM's layout; PR #19111
@@ -182,8 +205,8 @@ int fp8_block_gemm_grouped_contiguous(const void* a, const uint32_t* sfa, int64_
 /*
  * Tile-table access, for tuning and for tests that cover every compiled tile
  * shape.  fp8bs_gemm_config reports what the automatic choice would be for a
- * dense (masked = 0), masked (masked = 1) or contiguous grouped (masked = 2)
- * problem: kernel index into the tile
+ * dense (masked = 0), masked (masked = 1), contiguous grouped (masked = 2) or
+ * dense float-scale (masked = 3) problem: kernel index into the tile
  * table, workgroup tile bm x bn, and the number of K splits.  The _cfg variants
  * run the same GEMMs with an explicit kernel index and split count (splits is
  * clamped to [1, K/128]; the masked and contiguous forms use splits == 1 only, and
@@ -192,11 +215,12 @@ int fp8_block_gemm_grouped_contiguous(const void* a, const uint32_t* sfa, int64_
 int fp8bs_gemm_config_count(void);
 int fp8bs_gemm_config(int masked, int64_t M, int64_t N, int64_t K, int32_t* kernel, int32_t* bm,
                       int32_t* bn, int32_t* splits);
-/* Whether table entry `kernel` accepts a dense (masked = 0), masked (masked = 1) or
- * contiguous grouped (masked = 2) problem of this shape with `splits` K splits: FP8BS_OK with its workgroup tile and
- * the split count it would use, FP8BS_ERR_SHAPE if it does not (for instance K past
- * the entry's scale tables, or a masked problem that would need K splits).
- * Host-only; launches nothing. */
+/* Whether table entry `kernel` accepts a dense (masked = 0), masked (masked = 1),
+ * contiguous grouped (masked = 2) or dense float-scale (masked = 3) problem of this
+ * shape with `splits` K splits: FP8BS_OK with its workgroup tile and the split count
+ * it would use, FP8BS_ERR_SHAPE if it does not (for instance K past the entry's scale
+ * tables, a masked problem that would need K splits, or a scale format the entry does
+ * not read).  Host-only; launches nothing. */
 int fp8bs_gemm_config_of(int32_t kernel, int masked, int64_t M, int64_t N, int64_t K, int32_t splits,
                          int32_t* bm, int32_t* bn, int32_t* splits_out);
 int fp8_block_gemm_nt_cfg(const void* a, const uint32_t* sfa, int64_t ld_sfa, const void* b,
@@ -210,6 +234,9 @@ int fp8_block_gemm_grouped_contiguous_cfg(const void* a, const uint32_t* sfa, in
                                           const void* b, const float* sfb, void* c, int64_t ldc,
                                           const int32_t* m_indices, int64_t E, int64_t M,
                                           int64_t N, int64_t K, int32_t kernel, void* stream);
+int fp8_block_gemm_nt_float_scales_cfg(const void* a, const float* sfa, int64_t ld_sfa, const void* b,
+                                       const float* sfb, void* c, int64_t ldc, int64_t M, int64_t N,
+                                       int64_t K, int32_t kernel, int32_t splits, void* stream);
 
 /* Status helpers. */
 const char* fp8bs_status_string(int status);

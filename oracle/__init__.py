@@ -59,6 +59,12 @@ def _load():
     lib.orc_silu_mul_quant_group_pack.restype = None
     lib.orc_quant_group_pack_to_experts.argtypes = [P, I, I, I, P, I, I, I, P, P, P, P]
     lib.orc_quant_group_pack_to_experts.restype = None
+    lib.orc_quant_group_float.argtypes = [P, I, I, I, P, I, P, I]
+    lib.orc_quant_group_float.restype = None
+    lib.orc_block_quant_128x128_float.argtypes = [P, I, I, P, P]
+    lib.orc_block_quant_128x128_float.restype = None
+    lib.orc_gemm_nt_float_scales.argtypes = [P, I, P, I, P, I, P, I, I, I, P, I, P, I, P]
+    lib.orc_gemm_nt_float_scales.restype = None
     lib.orc_block_quant_128x128.argtypes = [P, I, I, P, P]
     lib.orc_block_quant_128x128.restype = None
     lib.orc_gemm_nt.argtypes = [P, I, P, I, P, I, P, I, I, I, P, I, P, I, P]
@@ -217,6 +223,53 @@ def gemm_nt(qa, sfa, qb, sfb, rows=None, cols=None):
     out = np.zeros((nr, nc), np.float64)
     _load().orc_gemm_nt(_ptr(qa), K, _ptr(sfa), sfa.shape[1], _ptr(qb), K, _ptr(sfb), M, N, K,
                         _ptr(r), nr, _ptr(c), nc, _ptr(out))
+    return out
+
+
+def quant_group_float(x: np.ndarray, ld_sf: int | None = None):
+    """1x128 per-token group quant with float scales (amax / 448 in fp32) of bf16 x [M, K].
+    Returns (q uint8 [M, K], sf float32 [K/128, ld_sf]); sf[:, M:] is zero here."""
+    x = _req(x, np.uint16)
+    M, K = x.shape
+    if K % 128:
+        raise ValueError("K must be a multiple of 128")
+    if ld_sf is None:
+        ld_sf = max(4, (M + 3) // 4 * 4)
+    q = np.zeros((M, K), np.uint8)
+    sf = np.zeros((K // 128, ld_sf), np.float32)
+    _load().orc_quant_group_float(_ptr(x), K, M, K, _ptr(q), K, _ptr(sf), ld_sf)
+    return q, sf
+
+
+def block_quant_128x128_float(w: np.ndarray):
+    """128x128 block quant with float scales of bf16 w [N, K] -> (q uint8 [N, K],
+    sfb float32 [ceil(N/128), K/128])."""
+    w = _req(w, np.uint16)
+    N, K = w.shape
+    if K % 128:
+        raise ValueError("K must be a multiple of 128")
+    q = np.zeros((N, K), np.uint8)
+    sfb = np.zeros(((N + 127) // 128, K // 128), np.float32)
+    _load().orc_block_quant_128x128_float(_ptr(w), N, K, _ptr(q), _ptr(sfb))
+    return q, sfb
+
+
+def gemm_nt_float_scales(qa, sfa, qb, sfb, rows=None, cols=None):
+    """Float-scale block GEMM C = A . B^T in double.  qa uint8 [M, K], sfa float32 [K/128, ld_sfa],
+    qb uint8 [N, K], sfb float32 [ceil(N/128), K/128]."""
+    qa = _req(qa, np.uint8)
+    qb = _req(qb, np.uint8)
+    sfa = _req(sfa, np.float32)
+    sfb = _req(sfb, np.float32)
+    M, K = qa.shape
+    N = qb.shape[0]
+    r = None if rows is None else _req(np.asarray(rows, np.int64), np.int64)
+    c = None if cols is None else _req(np.asarray(cols, np.int64), np.int64)
+    nr = M if r is None else len(r)
+    nc = N if c is None else len(c)
+    out = np.zeros((nr, nc), np.float64)
+    _load().orc_gemm_nt_float_scales(_ptr(qa), K, _ptr(sfa), sfa.shape[1], _ptr(qb), K, _ptr(sfb), M, N, K,
+                                     _ptr(r), nr, _ptr(c), nc, _ptr(out))
     return out
 
 

@@ -230,6 +230,69 @@ void orc_block_quant_128x128(const uint16_t* w, int64_t N, int64_t K, uint8_t* q
   }
 }
 
+/* ------------------------------------------------------------------------ */
+/* Float-scale (non-UE8M0) format, benchmark post section 4.1: the scale of a group
+ * or block is amax / fp8_max itself (rounding up to a power of two happens only for
+ * UE8M0).  The pages' implementations compute in fp32, so these steps are fp32 IEEE
+ * operations, each rounded to nearest even (C float arithmetic, no contraction):
+ *   s = max(amax, 1e-10f) / 448,  y = x / s,  y clamped to [-448, 448],
+ *   q = e4m3 RNE of y (exact decision: y is converted to double without rounding). */
+static float float_scale(float amax) {
+  float a = amax > 1e-10f ? amax : 1e-10f;
+  return a / 448.0f;
+}
+
+static uint8_t float_quant(float x, float s) {
+  float y = x / s;
+  if (y > 448.0f) y = 448.0f;
+  if (y < -448.0f) y = -448.0f;
+  return orc_e4m3_encode((double)y);
+}
+
+/* 1x128 groups of bf16 x [M][ldx] -> q e4m3 [M][ldq], sf fp32 [K/128][ld_sf] (M-major). */
+void orc_quant_group_float(const uint16_t* x, int64_t ldx, int64_t M, int64_t K, uint8_t* q, int64_t ldq,
+                           float* sf, int64_t ld_sf) {
+  init_tables();
+  int64_t G = K / 128;
+#pragma omp parallel for schedule(dynamic, 16)
+  for (int64_t r = 0; r < M; ++r) {
+    for (int64_t g = 0; g < G; ++g) {
+      float amax = 0.0f;
+      for (int64_t k = 128 * g; k < 128 * g + 128; ++k) {
+        float v = fabsf((float)bf16_to_double(x[r * ldx + k]));
+        if (v > amax) amax = v;
+      }
+      float s = float_scale(amax);
+      for (int64_t k = 128 * g; k < 128 * g + 128; ++k)
+        q[r * ldq + k] = float_quant((float)bf16_to_double(x[r * ldx + k]), s);
+      sf[g * ld_sf + r] = s;
+    }
+  }
+}
+
+/* 128x128 blocks of bf16 w [N][K] -> q e4m3 [N][K], sfb fp32 [ceil(N/128)][K/128]. */
+void orc_block_quant_128x128_float(const uint16_t* w, int64_t N, int64_t K, uint8_t* q, float* sfb) {
+  init_tables();
+  int64_t NB = (N + 127) / 128, KB = K / 128;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t nb = 0; nb < NB; ++nb) {
+    int64_t n1 = (nb + 1) * 128 < N ? (nb + 1) * 128 : N;
+    for (int64_t kb = 0; kb < KB; ++kb) {
+      float amax = 0.0f;
+      for (int64_t n = nb * 128; n < n1; ++n)
+        for (int64_t k = kb * 128; k < kb * 128 + 128; ++k) {
+          float v = fabsf((float)bf16_to_double(w[n * K + k]));
+          if (v > amax) amax = v;
+        }
+      float s = float_scale(amax);
+      for (int64_t n = nb * 128; n < n1; ++n)
+        for (int64_t k = kb * 128; k < kb * 128 + 128; ++k)
+          q[n * K + k] = float_quant((float)bf16_to_double(w[n * K + k]), s);
+      sfb[nb * KB + kb] = s;
+    }
+  }
+}
+
 /* Per-token group quant into the masked expert layout of routed tokens (the
  * quantization of FP8 dispatch: PR #19885, Summary item 1; PR #19111 review, the
  * TODO asking for a batched quant).  Pair p = t * topk + j goes to expert ids[p]
@@ -297,6 +360,38 @@ void orc_gemm_nt(const uint8_t* qa, int64_t lda, const uint32_t* sfa, int64_t ld
           dot += g_dec[qa[m * lda + k]] * g_dec[qb[n * ldb + k]];
         int ea = (int)((sfa[(kb / 4) * ld_sfa + m] >> (8 * (kb % 4))) & 0xFF) - 127;
         acc += ldexp(1.0, ea) * (double)sfb[(n / 128) * KB + kb] * dot;
+      }
+      out[i * ncols + j] = acc;
+    }
+  }
+}
+
+/* Block-scaled GEMM with float scales (benchmark post section 4.2, the accumulate
+ * rule read as acc += dot_kb * s_a[m] * s_b[n-block]): for each selected row m, column n
+ *   C[m][n] = sum over K-blocks kb of sfa[kb][m] * sfb[n/128][kb]
+ *             * sum_{k in block kb} dec(qa[m][k]) * dec(qb[n][k])
+ * in double (the products of the two fp32 scales and the block sums are exact or
+ * rounded once in double).  sfa: fp32 [K/128][ld_sfa]. */
+void orc_gemm_nt_float_scales(const uint8_t* qa, int64_t lda, const float* sfa, int64_t ld_sfa,
+                              const uint8_t* qb, int64_t ldb, const float* sfb,
+                              int64_t M, int64_t N, int64_t K,
+                              const int64_t* rows, int64_t nrows, const int64_t* cols, int64_t ncols,
+                              double* out) {
+  init_tables();
+  int64_t KB = K / 128;
+  if (!rows) nrows = M;
+  if (!cols) ncols = N;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t i = 0; i < nrows; ++i) {
+    int64_t m = rows ? rows[i] : i;
+    for (int64_t j = 0; j < ncols; ++j) {
+      int64_t n = cols ? cols[j] : j;
+      double acc = 0.0;
+      for (int64_t kb = 0; kb < KB; ++kb) {
+        double dot = 0.0;
+        for (int64_t k = kb * 128; k < kb * 128 + 128; ++k)
+          dot += g_dec[qa[m * lda + k]] * g_dec[qb[n * ldb + k]];
+        acc += (double)sfa[kb * ld_sfa + m] * (double)sfb[(n / 128) * KB + kb] * dot;
       }
       out[i * ncols + j] = acc;
     }

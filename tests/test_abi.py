@@ -115,7 +115,14 @@ def test_config_of_table_entries():
         c = F.gemm_config(masked, M, N, K)
         e = F.gemm_config_of(c["kernel"], masked, M, N, K, c["splits"])
         assert e is not None and (e["bm"], e["bn"], e["splits"]) == (c["bm"], c["bn"], c["splits"])
-    assert all(F.gemm_config_of(k, True, 72, 192, 384) is not None for k in range(n))
+    fl = [k for k in range(n) if F.gemm_config_of(k, F.LAYOUT_DENSE_FLOAT, 72, 192, 384) is not None]
+    assert fl and all(F.gemm_config_of(k, True, 72, 192, 384) is not None for k in range(n) if k not in fl)
+    # the float-scale entries read only the float format, the others only the packed one
+    assert all(F.gemm_config_of(k, False, 72, 192, 384) is None and F.gemm_config_of(k, True, 72, 192, 384) is None
+               for k in fl)
+    assert all(F.gemm_config_of(k, F.LAYOUT_DENSE_FLOAT, 72, 192, 384) is None for k in range(n) if k not in fl)
+    for M in (8, 64, 4096):
+        assert F.gemm_config(F.LAYOUT_DENSE_FLOAT, M, 7168, 7168)["kernel"] in fl
     long_k = [F.gemm_config_of(k, True, 256, 4096, 128 * 1024) for k in range(n)]
     assert any(x is None for x in long_k) and any(x is not None for x in long_k)
     assert all(x is None or x["splits"] == 1 for x in long_k)

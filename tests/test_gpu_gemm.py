@@ -55,9 +55,17 @@ def test_gemm_integer_identity_exact(kernel, splits):
     M, N, K = 37, 320, 256
     ai = rng.integers(-1, 2, (M, K))
     bi = rng.integers(-1, 2, (N, K))
-    sfa = np.full((1, 40), 127 | (127 << 8), np.uint32)
     sfb = np.ones((3, 2), np.float32)
-    c = _run(_int_codes(ai), sfa, _int_codes(bi), sfb, kernel=kernel, splits=splits)
+    if F.gemm_config_of(kernel, F.LAYOUT_DENSE_FLOAT, M, N, K) is not None:
+        # a float-scale entry: unit float scales
+        sfa_f = np.ones((K // 128, 40), np.float32)
+        c = F.fp8_block_gemm_nt_float_scales(to_dev(_int_codes(ai)), to_dev(sfa_f), to_dev(_int_codes(bi)),
+                                             to_dev(sfb), c=poisoned_bf16(M, N), kernel=kernel, splits=splits)
+        sync()
+        c = to_host(c)
+    else:
+        sfa = np.full((1, 40), 127 | (127 << 8), np.uint32)
+        c = _run(_int_codes(ai), sfa, _int_codes(bi), sfb, kernel=kernel, splits=splits)
     want = (ai @ bi.T).astype(np.float32)
     got = (c.astype(np.uint32) << 16).view(np.float32)
     assert np.array_equal(got, want)
@@ -72,6 +80,8 @@ def test_gemm_parity_every_tile_config(M, N, K):
     qa, sfa, qb, sfb = _operands(M, N, K, seed=M + N, b_std=1.0, varied_blocks=True)
     ref = O.gemm_nt(qa, sfa, qb, sfb)
     for kernel in range(F.gemm_config_count()):
+        if F.gemm_config_of(kernel, False, M, N, K) is None:
+            continue  # float-scale entries: covered by the float-scale tests
         for splits in (1, 3):
             c = _run(qa, sfa, qb, sfb, kernel=kernel, splits=splits)
             gemm_tolerance_check(c, ref, "kernel %d splits %d %dx%dx%d" % (kernel, splits, M, N, K))

@@ -57,6 +57,8 @@ def test_masked_small_all_kernels_edge_counts():
     a, sfa, b, sfb = _moe_operands(E, M_max, N, K, seed=1)
     counts = np.array([0, 1, 72, 100, -2, 33], np.int32)
     for kernel in range(F.gemm_config_count()):
+        if F.gemm_config_of(kernel, F.LAYOUT_DENSE_FLOAT, M_max, N, K) is not None:
+            continue  # float-scale entry: another scale format
         assert F.gemm_config_of(kernel, True, M_max, N, K) is not None, kernel
         c = _run_masked(a, sfa, b, sfb, counts, kernel=kernel)
         _check(c, a, sfa, b, sfb, counts, what="kernel %d" % kernel)

@@ -343,6 +343,86 @@ def test_masked_counts_clamped_and_rows_untouched():
     assert np.array_equal(out[1, :3], O.gemm_nt(a[1], sfa[1], b[1], sfb[1])[:3])
 
 
+# ---------------------------------------------------------------- float-scale format
+
+def _torch_e4m3(y32: np.ndarray) -> np.ndarray:
+    return torch.from_numpy(np.ascontiguousarray(y32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def test_float_quant_matches_fp32_formula_and_torch_cast():
+    """s = fp32(max(amax, 1e-10) / 448), q = RNE cast of clamp(fp32(x / s)): numpy fp32
+    arithmetic and torch's float8_e4m3fn cast, group by group; zero and tiny groups too."""
+    M, K = 6, 640
+    x = W.normal_bf16((M, K), seed=9)
+    x[1, 128:256] = 0                        # a zero group: s = 1e-10 / 448
+    x[2, :128] = W.f32_to_bf16_bits(np.full(128, 1e-20, np.float32))  # below the floor
+    q, sf = O.quant_group_float(x)
+    xf = W.bf16_bits_to_f32(x)
+    for r in range(M):
+        for g in range(K // 128):
+            blk = xf[r, g * 128:(g + 1) * 128]
+            amax = np.float32(np.abs(blk).max())
+            s = np.float32(max(amax, np.float32(1e-10))) / np.float32(448.0)
+            assert sf[g, r] == s, (r, g)
+            y = np.clip(blk / s, np.float32(-448), np.float32(448)).astype(np.float32)
+            assert np.array_equal(q[r, g * 128:(g + 1) * 128], _torch_e4m3(y)), (r, g)
+
+
+def test_float_block_quant_matches_fp32_formula():
+    N, K = 200, 256
+    w = W.normal_bf16((N, K), std=0.02, seed=10, tensor_id=W.T_B)
+    q, sfb = O.block_quant_128x128_float(w)
+    wf = W.bf16_bits_to_f32(w)
+    for nb in range(2):
+        for kb in range(2):
+            blk = wf[nb * 128:min(N, nb * 128 + 128), kb * 128:(kb + 1) * 128]
+            s = np.float32(max(np.float32(np.abs(blk).max()), np.float32(1e-10))) / np.float32(448.0)
+            assert sfb[nb, kb] == s
+            y = np.clip(blk / s, np.float32(-448), np.float32(448)).astype(np.float32)
+            assert np.array_equal(q[nb * 128:min(N, nb * 128 + 128), kb * 128:(kb + 1) * 128], _torch_e4m3(y))
+
+
+def test_float_gemm_exact_rational_small_case():
+    """Integer operands, arbitrary fp32 scales: every output in exact rational arithmetic."""
+    rng = np.random.default_rng(12)
+    M, N, K = 3, 130, 256
+    ai = rng.integers(-16, 17, (M, K))
+    bi = rng.integers(-16, 17, (N, K))
+    sfa = rng.uniform(0.001, 3.0, (K // 128, 4)).astype(np.float32)
+    sfb = rng.uniform(0.001, 3.0, (2, K // 128)).astype(np.float32)
+    out = O.gemm_nt_float_scales(_int_e4m3_codes(ai), sfa, _int_e4m3_codes(bi), sfb)
+    for m in range(M):
+        for n in range(N):
+            ref, mag = Fraction(0), Fraction(0)
+            for kb in range(K // 128):
+                dot = int(ai[m, kb * 128:(kb + 1) * 128] @ bi[n, kb * 128:(kb + 1) * 128])
+                term = Fraction(float(sfa[kb, m])) * Fraction(float(sfb[n // 128, kb])) * dot
+                ref += term
+                mag += abs(term)
+            # double rounding of each scaled block sum and of the running sum
+            assert abs(Fraction(out[m, n]) - ref) <= mag * Fraction(1, 2 ** 50), (m, n)
+
+
+def test_float_gemm_with_power_of_two_scales_equals_packed_gemm():
+    """Float scales that are powers of two give the packed-UE8M0 GEMM's result exactly."""
+    rng = np.random.default_rng(13)
+    M, N, K = 5, 256, 640
+    G = K // 128
+    qa = rng.integers(0, 256, (M, K), dtype=np.uint8)
+    qb = rng.integers(0, 256, (N, K), dtype=np.uint8)
+    qa[(qa & 0x7F) == 0x7F] = 0
+    qb[(qb & 0x7F) == 0x7F] = 0
+    ea = rng.integers(-10, 11, (M, G))
+    words = np.zeros(((G + 3) // 4, 8), np.uint32)
+    for m in range(M):
+        for g in range(G):
+            words[g // 4, m] |= np.uint32((ea[m, g] + 127) << (8 * (g % 4)))
+    sfa_f = np.zeros((G, 8), np.float32)
+    sfa_f[:, :M] = np.ldexp(1.0, ea.T)
+    sfb = np.ldexp(1.0, rng.integers(-10, 11, (2, G))).astype(np.float32)
+    assert np.array_equal(O.gemm_nt_float_scales(qa, sfa_f, qb, sfb), O.gemm_nt(qa, words, qb, sfb))
+
+
 # ---------------------------------------------------------------- quant into the expert layout
 
 def _dispatch_case(seed=0):
