@@ -581,12 +581,13 @@ def counters_masked_workload(F, W, steps):
 
 
 def _kernel_hash():
+    """Hash of the sources the decode GEMM kernel is built from (the GEMM kernels and the
+    two headers they include): stored traffic counters stay valid until these change."""
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "block_scaled_fp8_token_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        if name.endswith((".hip", ".hpp")):
-            h.update(open(os.path.join(csrc, name), "rb").read())
+    for name in ("fp8bs_device.hpp", "fp8bs_launch.hpp", "gemm_kernels.hip"):
+        h.update(open(os.path.join(csrc, name), "rb").read())
     return h.hexdigest()[:16]
 
 
