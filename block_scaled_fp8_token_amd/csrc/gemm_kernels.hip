@@ -516,7 +516,10 @@ struct IntC {
   static constexpr int value = V;
 };
 
-template <int BM, int BN, int WGM, int WGN, int STAGES>
+// FS: the float-scale format.  The tables then hold one fp32 per K-block (activations
+// [K-block][row], weights [column block][K-block]), each MFMA runs with unit scales on
+// zero, and acc += product * (s_a * s_b).
+template <int BM, int BN, int WGM, int WGN, int STAGES, bool FS = false>
 __global__ __launch_bounds__(WGM * WGN * 64) void scaled_tile_kernel(const KArgs p) {
   constexpr int NW = WGM * WGN;  // wavefronts per workgroup (4 or 8)
   constexpr int NT = NW * 64;
@@ -567,8 +570,9 @@ __global__ __launch_bounds__(WGM * WGN * 64) void scaled_tile_kernel(const KArgs
   const int Wd = (KB + 3) / 4;
   const int NB = (int)((p.N + 127) / 128);
   constexpr int NBT = (BN + 127) / 128;
-  uint32_t* lds_sa = reinterpret_cast<uint32_t*>(smem);  // [Wd][BM] activation words
-  uint32_t* lds_sb = lds_sa + Wd * BM;                  // [NBT][Wd] packed weight exponents
+  const int TW = FS ? KB : Wd;                          // table columns: K-blocks or words
+  uint32_t* lds_sa = reinterpret_cast<uint32_t*>(smem);  // [TW][BM] activation words / fp32 scales
+  uint32_t* lds_sb = lds_sa + TW * BM;                  // [NBT][TW] packed weight exponents / fp32 scales
 
   const int64_t rows_valid = (m_limit - m0 < BM) ? m_limit - m0 : BM;
   int64_t cols_valid = p.N - n0;
@@ -603,7 +607,21 @@ __global__ __launch_bounds__(WGM * WGN * 64) void scaled_tile_kernel(const KArgs
   };
 
   // scale tables: activation words for this tile's rows, weight exponents packed
-  // four K-blocks to a word (byte kb % 4), matching the MFMA's byte select
+  // four K-blocks to a word (byte kb % 4), matching the MFMA's byte select (float
+  // scales: the fp32 values per K-block)
+  if constexpr (FS) {
+    const auto rSAF = make_rsrc(p.sfa_f + e * p.ssfa_e, (uint32_t)(KB * p.ld_sfa * 4));
+    for (int idx = tid; idx < KB * BM; idx += NT) {
+      const int k = idx / BM, row = idx - k * BM;
+      const int64_t m = m0 + row;
+      lds_sa[idx] = bload4(rSAF, (m < m_limit) ? (uint32_t)(((int64_t)k * p.ld_sfa + m) * 4) : kOOB);
+    }
+    for (int idx = tid; idx < NBT * KB; idx += NT) {
+      const int b = idx / KB, k = idx - b * KB;
+      const int nb = (int)(n0 >> 7) + b;
+      lds_sb[idx] = bload4(rSB, nb < NB ? (uint32_t)((nb * KB + k) * 4) : kOOB);
+    }
+  } else {
   for (int idx = tid; idx < Wd * BM; idx += NT) {
     const int w = idx / BM, row = idx - w * BM;
     const int64_t m = m0 + row;
@@ -621,6 +639,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void scaled_tile_kernel(const KArgs
       word |= ((bload4(rSB, off) >> 23) & 0xFFu) << (8 * q);
     }
     lds_sb[idx] = word;
+  }
   }
   issue(0, IntC<0>{});
 
@@ -640,13 +659,13 @@ __global__ __launch_bounds__(WGM * WGN * 64) void scaled_tile_kernel(const KArgs
     __syncthreads();                     // ... and everyone's; kb - 1's stage is free
     const uint8_t* As = stage_ptr(st_tag);
     const uint8_t* Bs = As + BM * 128;
-    const int w = kb >> 2;
+    const int w = FS ? kb : kb >> 2;
     uint32_t sa[SM];
 #pragma unroll
     for (int i = 0; i < SM; ++i) sa[i] = lds_sa[w * BM + wm * WM + 16 * i + (lane & 15)];
     uint32_t sbw[SN];
 #pragma unroll
-    for (int j = 0; j < SN; ++j) sbw[j] = lds_sb[((wn * WN + 16 * j) >> 7) * Wd + w];
+    for (int j = 0; j < SN; ++j) sbw[j] = lds_sb[((wn * WN + 16 * j) >> 7) * TW + w];
     v8i af[SM], bf[SN];
     const int c0 = (lane >> 4), c1 = 4 + (lane >> 4);
 #pragma unroll
@@ -667,12 +686,25 @@ __global__ __launch_bounds__(WGM * WGN * 64) void scaled_tile_kernel(const KArgs
     // (the buffers differ) and then make the reads wait for it.
     __builtin_amdgcn_sched_barrier(0);
     issue(kb + 1, IntC<1 - ST>{});
+    if constexpr (FS) {
+      const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int j = 0; j < SN; ++j)
+      for (int j = 0; j < SN; ++j)
 #pragma unroll
-      for (int i = 0; i < SM; ++i)
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[j], af[i], acc[i][j], 0, 0, OPS, (int)sbw[j],
-                                                                     OPS, (int)sa[i]);
+        for (int i = 0; i < SM; ++i) {
+          const v4f d = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[j], af[i], zero, 0, 0, 0, 127, 0, 127);
+          const float sc = __uint_as_float(sa[i]) * __uint_as_float(sbw[j]);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[i][j][r] = __builtin_fmaf(d[r], sc, acc[i][j][r]);
+        }
+    } else {
+#pragma unroll
+      for (int j = 0; j < SN; ++j)
+#pragma unroll
+        for (int i = 0; i < SM; ++i)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[j], af[i], acc[i][j], 0, 0, OPS,
+                                                                       (int)sbw[j], OPS, (int)sa[i]);
+    }
   };
 
   // K loop unrolled by four: the scale byte (kb % 4) and the ring stage are static
@@ -894,10 +926,11 @@ __global__ __launch_bounds__(WGM * WGN * 64) void scaled_pipe_kernel(const KArgs
   }
 }
 
-inline size_t scaled_tile_lds_bytes(int bm, int bn, int stages, int K) {
-  // dynamic part only (the stage buffers are static): the two scale tables
+inline size_t scaled_tile_lds_bytes(int bm, int bn, int stages, int K, bool float_scales = false) {
+  // dynamic part only (the stage buffers are static): the two scale tables, one word
+  // per four K-blocks (packed UE8M0) or one fp32 per K-block (float scales)
   (void)stages;
-  const int KB = K / 128, Wd = (KB + 3) / 4;
+  const int KB = K / 128, Wd = float_scales ? KB : (KB + 3) / 4;
   return (size_t)Wd * bm * 4 + (size_t)((bn + 127) / 128) * Wd * 4;
 }
 
@@ -1316,7 +1349,11 @@ struct DecodeShape {
   static constexpr int NBT = (32 * NW + 127) / 128;
 };
 
-template <int NW, int DB_>
+// FS: the float-scale format.  The tables then hold fp32 scales per K-block of the
+// split (activations [K-block][row], weights [column block][K-block]; at most WMAX
+// K-blocks per split), the MFMAs run with unit scales into a per-K-block product,
+// and acc += product * (s_a * s_b) on the VALU.
+template <int NW, int DB_, bool FS = false>
 __global__ __launch_bounds__(NW * 64) void decode_kernel(const KArgs p) {
   using D = DecodeShape<NW, DB_>;
   constexpr int DB = D::DB, UN = D::UN, IA = D::IA, WMAX = D::WMAX, NBT = D::NBT;
@@ -1411,18 +1448,36 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const KArgs p) {
   const int nw = nkp / 4;                   // words of this split, <= WMAX (host)
   constexpr int SA_PT = (WMAX * 64 + NT - 1) / NT, SB_PT = (NBT * WMAX * 4 + NT - 1) / NT;
   uint32_t sav[SA_PT], sbv[SB_PT];
+  if constexpr (FS) {
+    // fp32 scales: activations [j][row], weights [block][j] for K-blocks j < nk
+    const auto rSAF = make_rsrc(p.sfa_f + e * p.ssfa_e, (uint32_t)(KB * p.ld_sfa * 4));
 #pragma unroll
-  for (int t = 0; t < SA_PT; ++t) {
-    const int idx = t * NT + tid, w = idx >> 6, row = idx & 63;
-    const bool ok = idx < nw * 64 && m0 + row < m_limit && w0 + w < Wd;
-    sav[t] = bload4(rSA, ok ? (uint32_t)(((int64_t)(w0 + w) * p.ld_sfa + m0 + row) * 4) : kOOB);
-  }
+    for (int t = 0; t < SA_PT; ++t) {
+      const int idx = t * NT + tid, j = idx >> 6, row = idx & 63;
+      const bool ok = idx < WMAX * 64 && j < nk && m0 + row < m_limit;
+      sav[t] = bload4(rSAF, ok ? (uint32_t)(((int64_t)(kb0 + j) * p.ld_sfa + m0 + row) * 4) : kOOB);
+    }
 #pragma unroll
-  for (int t = 0; t < SB_PT; ++t) {
-    const int idx = t * NT + tid, b = idx / (WMAX * 4), j = idx - b * (WMAX * 4);
-    const int nb = (int)(n0 >> 7) + b;
-    const bool ok = idx < NBT * WMAX * 4 && nb < NB && j < nk;
-    sbv[t] = bload4(rSB, ok ? (uint32_t)((nb * KB + kb0 + j) * 4) : kOOB);
+    for (int t = 0; t < SB_PT; ++t) {
+      const int idx = t * NT + tid, b = idx / WMAX, j = idx - b * WMAX;
+      const int nb = (int)(n0 >> 7) + b;
+      const bool ok = idx < NBT * WMAX && nb < NB && j < nk;
+      sbv[t] = bload4(rSB, ok ? (uint32_t)((nb * KB + kb0 + j) * 4) : kOOB);
+    }
+  } else {
+#pragma unroll
+    for (int t = 0; t < SA_PT; ++t) {
+      const int idx = t * NT + tid, w = idx >> 6, row = idx & 63;
+      const bool ok = idx < nw * 64 && m0 + row < m_limit && w0 + w < Wd;
+      sav[t] = bload4(rSA, ok ? (uint32_t)(((int64_t)(w0 + w) * p.ld_sfa + m0 + row) * 4) : kOOB);
+    }
+#pragma unroll
+    for (int t = 0; t < SB_PT; ++t) {
+      const int idx = t * NT + tid, b = idx / (WMAX * 4), j = idx - b * (WMAX * 4);
+      const int nb = (int)(n0 >> 7) + b;
+      const bool ok = idx < NBT * WMAX * 4 && nb < NB && j < nk;
+      sbv[t] = bload4(rSB, ok ? (uint32_t)((nb * KB + kb0 + j) * 4) : kOOB);
+    }
   }
 
   // prologue: weights of iterations 0 .. DB-1 and activations of 0 .. DB-2, in the
@@ -1447,19 +1502,32 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const KArgs p) {
     load_b(3, b3);
   }
 
+  if constexpr (FS) {
 #pragma unroll
-  for (int t = 0; t < SA_PT; ++t) {
-    const int idx = t * NT + tid, w = idx >> 6;
-    uint32_t v = sav[t];
-    const int left = kb0 + nk - 4 * (w0 + w);  // K-blocks of this word inside the split
-    if (left < 4) v &= left <= 0 ? 0u : ((1u << (8 * left)) - 1u);
-    if (idx < WMAX * 64) sa_tab[idx] = v;
-  }
-  uint8_t* sbb = reinterpret_cast<uint8_t*>(sb_tab);
+    for (int t = 0; t < SA_PT; ++t) {
+      const int idx = t * NT + tid;
+      if (idx < WMAX * 64) sa_tab[idx] = sav[t];
+    }
 #pragma unroll
-  for (int t = 0; t < SB_PT; ++t) {
-    const int idx = t * NT + tid;
-    if (idx < NBT * WMAX * 4) sbb[idx] = (uint8_t)((sbv[t] >> 23) & 0xFFu);
+    for (int t = 0; t < SB_PT; ++t) {
+      const int idx = t * NT + tid;
+      if (idx < NBT * WMAX) sb_tab[idx] = sbv[t];
+    }
+  } else {
+#pragma unroll
+    for (int t = 0; t < SA_PT; ++t) {
+      const int idx = t * NT + tid, w = idx >> 6;
+      uint32_t v = sav[t];
+      const int left = kb0 + nk - 4 * (w0 + w);  // K-blocks of this word inside the split
+      if (left < 4) v &= left <= 0 ? 0u : ((1u << (8 * left)) - 1u);
+      if (idx < WMAX * 64) sa_tab[idx] = v;
+    }
+    uint8_t* sbb = reinterpret_cast<uint8_t*>(sb_tab);
+#pragma unroll
+    for (int t = 0; t < SB_PT; ++t) {
+      const int idx = t * NT + tid;
+      if (idx < NBT * WMAX * 4) sbb[idx] = (uint8_t)((sbv[t] >> 23) & 0xFFu);
+    }
   }
   // VMEM instructions younger than the activation DMA of the current iteration
   constexpr int YOUNGER = 4 + (DB - 2) * (IA + 4);
@@ -1490,7 +1558,11 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const KArgs p) {
       __builtin_amdgcn_s_barrier();
       __builtin_amdgcn_sched_barrier(0);
       issue_a(j + DB - 1, IntC<(U + DB - 1) % DB>{});
-      if constexpr (OPS == 0) {
+      if constexpr (FS) {
+#pragma unroll
+        for (int i = 0; i < IV; ++i) sa[i] = sa_tab[j * 64 + 32 * i + lr];
+        sb = sb_tab[sb_blk * WMAX + j];
+      } else if constexpr (OPS == 0) {
 #pragma unroll
         for (int i = 0; i < IV; ++i) sa[i] = sa_tab[(j >> 2) * 64 + 32 * i + lr];
         sb = sb_tab[sb_blk * WMAX + (j >> 2)];
@@ -1506,12 +1578,26 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const KArgs p) {
           const v4i hi = *reinterpret_cast<const v4i*>(q + rd1);
           af[h][i] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
         }
+      if constexpr (FS) {
+        // unit scales (byte 127) into the K-block's product, then the two fp32 scales
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
+        for (int i = 0; i < IV; ++i) {
+          v16f d = {};
 #pragma unroll
-        for (int i = 0; i < IV; ++i)
-          acc[i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bcur[h], af[h][i], acc[i], 0, 0, OPS, (int)sb,
-                                                                   OPS, (int)sa[i]);
+          for (int h = 0; h < 2; ++h)
+            d = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bcur[h], af[h][i], d, 0, 0, 0, 127, 0, 127);
+          const float sc = __uint_as_float(sa[i]) * __uint_as_float(sb);
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[i][r] = __builtin_fmaf(d[r], sc, acc[i][r]);
+        }
+      } else {
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int i = 0; i < IV; ++i)
+            acc[i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bcur[h], af[h][i], acc[i], 0, 0, OPS, (int)sb,
+                                                                     OPS, (int)sa[i]);
+      }
       load_b(j + DB, bcur);  // the registers of kb are free again: fetch kb + DB
     };
 
@@ -1638,7 +1724,17 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const KArgs p) {
 
 typedef void (*KernelFn)(const KArgs);
 
-enum Kind { kTile = 0, kStream = 1, kScaled = 2, kRing = 3, kDecode = 4, kTileFloat = 5 };
+enum Kind { kTile = 0, kStream = 1, kScaled = 2, kRing = 3, kDecode = 4, kTileFloat = 5, kDecodeFloat = 6,
+            kScaledFloat = 7 };
+
+// Entries that read the float-scale format.
+inline bool reads_float_scales(int kind) {
+  return kind == kTileFloat || kind == kDecodeFloat || kind == kScaledFloat;
+}
+// LDS-DMA tile entries (dynamic LDS for the scale tables).
+inline bool is_scaled_tile(int kind) { return kind == kScaled || kind == kScaledFloat; }
+// Entries that reduce their own K split (arrival counters in the workspace).
+inline bool reduces_in_kernel(int kind) { return kind == kDecode || kind == kDecodeFloat; }
 
 struct TileEntry {
   KernelFn fn;
@@ -1686,6 +1782,10 @@ const TileEntry kTiles[] = {
     {gemm_kernel<128, 128, 64, 64, true>, 128, 128, kTileFloat, 2, 256},
     {gemm_kernel<64, 256, 64, 64, true>, 64, 256, kTileFloat, 2, 256},
     {gemm_kernel<128, 256, 64, 128, true>, 128, 256, kTileFloat, 2, 256},
+    // float scales: one fp32 per K-block in the tables, so WMAX K-blocks per split
+    {decode_kernel<4, 3, true>, 64, 128, kDecodeFloat, 3, 256, DecodeShape<4, 3>::WMAX / 4},
+    {scaled_tile_kernel<128, 128, 2, 2, 2, true>, 128, 128, kScaledFloat, 2, 256},
+    {scaled_tile_kernel<128, 256, 2, 2, 2, true>, 128, 256, kScaledFloat, 2, 256},
 };
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 // table entries the automatic choice uses
@@ -1698,8 +1798,11 @@ constexpr int kCfgRing128x256 = 23;        // 2 x 2 wavefronts, 128-row tiles
 constexpr int kCfgFloat64x128 = 30;        // float-scale VALU-scaled tiles
 constexpr int kCfgFloat128x128 = 31;
 constexpr int kCfgFloat128x256 = 33;
+constexpr int kCfgFloatDecode64x128 = 34;  // decode kernel, float scales
+constexpr int kCfgFloatScaled128x128 = 35; // LDS-DMA tiles, float scales
+constexpr int kCfgFloatScaled128x256 = 36;
 constexpr int kCfgDecode64x128 = 26;       // decode kernel, 4 wavefronts, three K-blocks in flight
-static_assert(kCfgDecode64x128 < kNumTiles && kCfgFloat128x256 < kNumTiles, "tile table");
+static_assert(kCfgDecode64x128 < kNumTiles && kCfgFloatScaled128x256 < kNumTiles, "tile table");
 
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -1723,7 +1826,7 @@ bool gemm_config_by_index(int idx, const GemmProblem& p, int splits, GemmConfig*
   if (splits > KB) splits = KB > 0 ? KB : 1;
   if ((p.masked_m || p.m_indices) && splits != 1) return false;
   // the float-scale format runs on the float-scale entries only (dense calls)
-  if ((kTiles[idx].kind == kTileFloat) != p.float_scales) return false;
+  if (reads_float_scales(kTiles[idx].kind) != p.float_scales) return false;
   if (p.float_scales && (p.masked_m || p.m_indices || p.E != 1)) return false;
   // contiguous grouped layout: a tile must not straddle two aligned runs
   if (p.m_indices && kContiguousAlign % kTiles[idx].bm != 0) return false;
@@ -1731,9 +1834,10 @@ bool gemm_config_by_index(int idx, const GemmProblem& p, int splits, GemmConfig*
     splits = 1;  // never splits K; the scale tables bound K
     if ((KB + 3) / 4 > kTiles[idx].max_wd) return false;
   }
-  if (kTiles[idx].kind == kScaled) {
+  if (is_scaled_tile(kTiles[idx].kind)) {
     splits = 1;  // this family never splits K
-    if (scaled_tile_lds_bytes(kTiles[idx].bm, kTiles[idx].bn, kTiles[idx].stages, (int)p.K) +
+    const bool fs = kTiles[idx].kind == kScaledFloat;
+    if (scaled_tile_lds_bytes(kTiles[idx].bm, kTiles[idx].bn, kTiles[idx].stages, (int)p.K, fs) +
             scaled_tile_static_bytes(kTiles[idx].bm, kTiles[idx].bn, kTiles[idx].stages) >
         kMaxLds)
       return false;
@@ -1745,7 +1849,7 @@ bool gemm_config_by_index(int idx, const GemmProblem& p, int splits, GemmConfig*
       ++splits;
     }
   }
-  if (kTiles[idx].kind == kDecode) {
+  if (reduces_in_kernel(kTiles[idx].kind)) {
     // K-blocks per split: a multiple of the unrolled loop (then the scale byte, LDS
     // stage and weight registers of a K-block are static), at most four per word
     // of the scale table
@@ -1785,6 +1889,12 @@ GemmConfig choose_gemm_config(const GemmProblem& p) {
     // float-scale format: VALU-scaled tiles; small M splits K until about 224
     // workgroups, large M takes 128 x 256 tiles once they fill the compute units
     if (p.M <= 64) {
+      {
+        const int64_t tiles = cdiv(p.N, kTiles[kCfgFloatDecode64x128].bn);
+        int splits = (int)(224 / (tiles > 0 ? tiles : 1));
+        if (splits < 1) splits = 1;
+        if (gemm_config_by_index(kCfgFloatDecode64x128, p, splits, &cfg)) return cfg;
+      }
       const int64_t tiles = cdiv(p.N, kTiles[kCfgFloat64x128].bn);
       int splits = (int)(224 / (tiles > 0 ? tiles : 1));
       const int max_splits = KB / 4 > 1 ? KB / 4 : 1;
@@ -1793,7 +1903,11 @@ GemmConfig choose_gemm_config(const GemmProblem& p) {
       gemm_config_by_index(kCfgFloat64x128, p, splits, &cfg);
       return cfg;
     }
+    // larger M: LDS-DMA tiles (128 x 256 once they fill the compute units), the
+    // VALU-scaled register-staged tiles when the scale tables do not fit
     const int64_t t256 = cdiv(p.M, 128) * cdiv(p.N, 256);
+    if (t256 >= 256 && gemm_config_by_index(kCfgFloatScaled128x256, p, 1, &cfg)) return cfg;
+    if (gemm_config_by_index(kCfgFloatScaled128x128, p, 1, &cfg)) return cfg;
     gemm_config_by_index(t256 >= 256 ? kCfgFloat128x256 : kCfgFloat128x128, p, 1, &cfg);
     return cfg;
   }
@@ -1912,7 +2026,7 @@ hipError_t launch_gemm(const GemmProblem& p, const GemmConfig& cfg, void* ws, hi
   k.m_indices = p.m_indices;
   k.groups = p.groups;
   k.sfa_f = p.float_scales ? reinterpret_cast<const float*>(p.sfa) : nullptr;
-  if (p.float_scales != (t.kind == kTileFloat)) return hipErrorInvalidValue;
+  if (p.float_scales != reads_float_scales(t.kind)) return hipErrorInvalidValue;
   if (p.m_indices && (p.E != 1 || p.masked_m || cfg.splits != 1 || kContiguousAlign % t.bm != 0))
     return hipErrorInvalidValue;
   k.M = p.M; k.N = p.N; k.K = p.K; k.ld_sfa = p.ld_sfa; k.ldc = p.ldc;
@@ -1935,9 +2049,9 @@ hipError_t launch_gemm(const GemmProblem& p, const GemmConfig& cfg, void* ws, hi
   const int64_t tiles = (int64_t)k.tiles_m * k.tiles_n;
   if (tiles < 1 || p.E < 1 || KB < 1) return hipSuccess;
   size_t dyn = 0;
-  if (t.kind == kStream || t.kind == kScaled) {
+  if (t.kind == kStream || is_scaled_tile(t.kind)) {
     dyn = (t.kind == kStream) ? stream_lds_bytes(t.bm, t.bn, cfg.kb_per_split)
-                              : scaled_tile_lds_bytes(t.bm, t.bn, t.stages, (int)p.K);
+                              : scaled_tile_lds_bytes(t.bm, t.bn, t.stages, (int)p.K, t.kind == kScaledFloat);
     if (dyn > kMaxLds) return hipErrorInvalidValue;
     // raise the kernel's dynamic-LDS limit to what this launch needs (never lowered)
     static std::atomic<int> attr_bytes[kNumTiles];
@@ -1952,7 +2066,7 @@ hipError_t launch_gemm(const GemmProblem& p, const GemmConfig& cfg, void* ws, hi
   }
   hipLaunchKernelGGL(t.fn, dim3((unsigned)tiles, (unsigned)cfg.splits, (unsigned)p.E), dim3(t.threads), dyn, stream, k);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || cfg.splits == 1 || t.kind == kDecode) return e;  // the decode kernel reduces itself
+  if (e != hipSuccess || cfg.splits == 1 || reduces_in_kernel(t.kind)) return e;  // the decode kernels reduce themselves
   const int64_t threads = p.M * (p.N / 8);
   hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)cdiv(threads, 256)), dim3(256), 0, stream,
                      static_cast<const float*>(k.ws), cfg.splits, p.M, p.N, p.c, p.ldc);
