@@ -1321,9 +1321,8 @@ constexpr int ring_wd_max() { return RingShape<BM, BN, WGM, WGN>::WD_MAX; }
 // Per K-block kb of the workgroup's range:
 //   * weights: each lane loads its two 32-byte pieces of the block straight from
 //     HBM into registers in the 32x32x64 MFMA layout (lane l: row l & 31, bytes
-//     32 (l >> 5) + 64 h .. + 31 for K-half h), DB K-blocks ahead of use (measured
-//     on MI355X under back-to-back launches: three K-blocks of 4 KiB per wavefront
-//     in flight stream at 5.5 TB/s, four at 4.6 TB/s);
+//     32 (l >> 5) + 64 h .. + 31 for K-half h), DB K-blocks ahead of use (three
+//     measured best on MI355X);
 //   * activations: the 64 x 128-byte block goes to LDS by DMA (DB - 1 blocks
 //     ahead, one stage per block in flight, K-half rows of 64 bytes with chunk c
 //     of row r at c ^ ((r >> 2) & 3)) and every wavefront reads it from there;
@@ -1332,9 +1331,10 @@ constexpr int ring_wd_max() { return RingShape<BM, BN, WGM, WGN>::WD_MAX; }
 // Iteration kb waits for its own DMA of kb (and, in order, its loads of kb), meets
 // the other wavefronts at a barrier, DMAs kb + DB - 1 into the stage kb - 1 used,
 // reads the activation operands of kb, issues the weight loads of kb + DB and the
-// four MFMAs of kb.  The epilogue stages the tile through LDS: with a K split the
-// fp32 partial of every split goes to the workspace (splitk_reduce_kernel adds
-// them in split order), without one the bf16 result goes to C.
+// four MFMAs of kb.  The epilogue stages the tile through LDS: without a K split
+// the bf16 result goes to C; with one, every split's fp32 partial goes to the
+// workspace and the last split of the tile to arrive adds them in split order and
+// writes C (see the reduction below).
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kSC1 = 16;              // cache-policy bit sc1 of buffer loads/stores (gfx940 family)
 constexpr int kDecodeMaxSplits = 8;   // K splits the decode kernel reduces itself

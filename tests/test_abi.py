@@ -19,7 +19,9 @@ A, B, C, S, T = 0x100000, 0x200000, 0x300000, 0x400000, 0x500000
 def test_header_declares_the_entry_points():
     names = F.declared_functions()
     for n in ("fp8_quant_group_pack", "silu_mul_quant_group_pack", "fp8_block_gemm_nt",
-              "fp8_block_gemm_grouped_masked", "fp8_block_quant_128x128", "fp8bs_status_string"):
+              "fp8_block_gemm_grouped_masked", "fp8_block_quant_128x128", "fp8bs_status_string",
+              "fp8_block_gemm_grouped_contiguous", "fp8_quant_group_pack_to_experts", "fp8_quant_group_float",
+              "fp8_block_quant_128x128_float", "fp8_block_gemm_nt_float_scales"):
         assert n in names
 
 
@@ -89,6 +91,58 @@ def test_quant_validation():
     assert h(A, 128, 100, B, T, None) == ERR_SHAPE
     assert h(A, 128, 128, None, T, None) == ERR_NULL
     assert h(A + 1, 128, 128, B, T, None) == ERR_ALIGN
+
+
+def test_contiguous_validation():
+    f = F._lib.fp8_block_gemm_grouped_contiguous
+
+    def call(a=A, sfa=S, ld_sfa=256, b=B, sfb=T, c=C, ldc=256, mi=S + 8192, E=4, M=256, N=256, K=256):
+        return f(a, sfa, ld_sfa, b, sfb, c, ldc, mi, E, M, N, K, None)
+
+    assert call(K=200) == ERR_SHAPE
+    assert call(N=96) == ERR_SHAPE
+    assert call(E=-1) == ERR_SHAPE
+    assert call(ld_sfa=255) == ERR_SHAPE
+    assert call(mi=None) == ERR_NULL
+    assert call(mi=S + 8194) == ERR_ALIGN
+    assert call(E=0) == OK and call(M=0) == OK and call(E=0, mi=None) == OK
+
+
+def test_quant_to_experts_validation():
+    f = F._lib.fp8_quant_group_pack_to_experts
+
+    def call(x=A, ldx=512, T_=8, K=512, ids=S, topk=2, E=4, M_max=16, q=B, sf=T, mm=C, slot=C + 4096):
+        return f(x, ldx, T_, K, ids, topk, E, M_max, q, sf, mm, slot, None)
+
+    assert call(K=500) == ERR_SHAPE
+    assert call(topk=0) == ERR_SHAPE and call(topk=65) == ERR_SHAPE
+    assert call(E=1025) == ERR_SHAPE
+    assert call(ldx=256) == ERR_SHAPE
+    assert call(ids=None) == ERR_NULL
+    assert call(mm=None) == ERR_NULL
+    assert call(slot=None) == ERR_NULL
+    assert call(q=None) == ERR_NULL
+    assert call(x=A + 4) == ERR_ALIGN
+    assert call(ids=S + 2) == ERR_ALIGN
+    assert call(E=0) == OK
+
+
+def test_float_scale_validation():
+    q = F._lib.fp8_quant_group_float
+    assert q(A, 512, 8, 500, B, 512, S, 8, None) == ERR_SHAPE
+    assert q(A, 512, 8, 512, B, 512, S, 7, None) == ERR_SHAPE
+    assert q(A, 512, 8, 512, B, 512, None, 8, None) == ERR_NULL
+    assert q(A, 512, 8, 512, B, 520, S, 8, None) == ERR_ALIGN
+    assert q(A, 512, 0, 512, None, 512, None, 8, None) == OK
+    h = F._lib.fp8_block_quant_128x128_float
+    assert h(A, 128, 100, B, T, None) == ERR_SHAPE
+    assert h(A, 128, 128, B, None, None) == ERR_NULL
+    g = F._lib.fp8_block_gemm_nt_float_scales
+    assert g(A, S, 64, B, T, C, 512, 64, 512, 100, None) == ERR_SHAPE
+    assert g(A, S, 63, B, T, C, 512, 64, 512, 512, None) == ERR_SHAPE
+    assert g(A, None, 64, B, T, C, 512, 64, 512, 512, None) == ERR_NULL
+    assert g(A, S, 64, B, T, C + 2, 512, 64, 512, 512, None) == ERR_ALIGN
+    assert g(A, S, 64, B, T, C, 512, 0, 512, 512, None) == OK
 
 
 def test_config_table_choices():
