@@ -9,6 +9,7 @@
 #include <map>
 #include <mutex>
 #include <utility>
+#include <vector>
 
 #include "../../include/fp8bs.h"
 #include "fp8bs_launch.hpp"
@@ -47,10 +48,12 @@ int check_device() {
 // the per-tile arrival counters of the fused split-K reduction (zeroed once when
 // the buffer is allocated; every call leaves them at zero) and the fp32 partials
 // of the call in flight on that stream, which every split overwrites before they
-// are read.
+// are read.  A buffer that is outgrown is kept, never freed: a HIP graph captured
+// earlier on the stream still launches kernels that use it.
 struct Workspace {
   void* ptr = nullptr;
   size_t bytes = 0;
+  std::vector<void*> retired;
 };
 
 int get_workspace(size_t need, hipStream_t stream, void** out) {
@@ -71,15 +74,10 @@ int get_workspace(size_t need, hipStream_t stream, void** out) {
   e = hipStreamIsCapturing(stream, &cap);
   if (e != hipSuccess) return fail_hip(e);
   if (cap != hipStreamCaptureStatusNone) return FP8BS_ERR_ALLOC;
-  if (w.ptr) {
-    // earlier work on this stream may still use the old buffer
-    e = hipStreamSynchronize(stream);
-    if (e != hipSuccess) return fail_hip(e);
-    (void)hipFree(w.ptr);
-    w.ptr = nullptr;
-    w.bytes = 0;
-  }
+  // at least double on growth, so that the retired buffers add up to less than the
+  // live one
   size_t sz = need < (size_t(1) << 20) ? (size_t(1) << 20) : need;
+  if (sz < 2 * w.bytes) sz = 2 * w.bytes;
   sz = (sz + (size_t(1) << 20) - 1) & ~((size_t(1) << 20) - 1);
   void* p = nullptr;
   e = hipMalloc(&p, sz);
@@ -92,6 +90,7 @@ int get_workspace(size_t need, hipStream_t stream, void** out) {
     (void)hipFree(p);
     return fail_hip(e);
   }
+  if (w.ptr) w.retired.push_back(w.ptr);  // earlier work or captured graphs may still use it
   w.ptr = p;
   w.bytes = sz;
   *out = p;

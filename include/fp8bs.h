@@ -159,7 +159,11 @@ int fp8_block_quant_128x128(const void* w, int64_t N, int64_t K, void* q, float*
  * library-owned device workspace kept per (device, stream), allocated on the
  * first call that needs it (make that call outside HIP graph capture: during
  * capture an allocation is refused with FP8BS_ERR_ALLOC).  Calls on different
- * streams never share a workspace.
+ * streams never share a workspace.  A workspace that a larger call outgrows is
+ * replaced but never freed, so graphs captured earlier stay valid.  A captured
+ * graph keeps the workspace of the stream it was captured on: replay it in
+ * stream order with the other calls on that stream (a replay running at the same
+ * time as calls on the capture stream would share the split-K counters with them).
  */
 int fp8_block_gemm_nt(const void* a, const uint32_t* sfa, int64_t ld_sfa, const void* b,
                       const float* sfb, void* c, int64_t ldc, int64_t M, int64_t N, int64_t K,
