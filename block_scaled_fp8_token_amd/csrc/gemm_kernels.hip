@@ -734,198 +734,6 @@ __global__ __launch_bounds__(WGM * WGN * 64) void scaled_tile_kernel(const KArgs
   }
 }
 
-// ---------------------------------------------------------------------------
-// Software-pipelined variant of the scaled-MFMA tile kernel.  Per K-block kb, with
-// the operands of kb already in registers (set X):
-//   wait for this wavefront's DMA of kb + 1, barrier (every wavefront's DMA of
-//   kb + 1 has landed and every wavefront has finished reading kb's stage),
-//   DMA kb + 2 into kb's stage, read the operands of kb + 1 into the other register
-//   set, and issue kb's MFMAs -- so the LDS reads of the next step run under this
-//   step's MFMAs and each DMA has a whole step to arrive.  NW wavefronts per
-//   workgroup (4 or 8) in a WGM x WGN grid.
-template <int BM, int BN, int WGM, int WGN>
-__global__ __launch_bounds__(WGM * WGN * 64) void scaled_pipe_kernel(const KArgs p) {
-  constexpr int NW = WGM * WGN;
-  constexpr int NT = NW * 64;
-  constexpr int WM = BM / WGM, WN = BN / WGN;
-  constexpr int SM = WM / 16, SN = WN / 16;
-  constexpr int A_INST = BM / 8, B_INST = BN / 8;
-  constexpr int IPW = (A_INST + B_INST) / NW;
-  constexpr int STAGE = (BM + BN) * 128;
-  static_assert((A_INST + B_INST) % NW == 0, "tile shape");
-  __shared__ __attribute__((aligned(1024))) uint8_t st0[STAGE];
-  __shared__ __attribute__((aligned(1024))) uint8_t st1[STAGE];
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];  // scale tables
-
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave / WGN, wn = wave % WGN;
-  const int64_t e = blockIdx.z;
-
-  const int T = p.tiles_m * p.tiles_n;
-  const int bid = blockIdx.x;
-  const int per_xcd = (T + 7) / 8;
-  int lin = (bid & 7) * per_xcd + (bid >> 3);
-  if ((T & 7) != 0) lin = bid;
-  constexpr int GM = 4;
-  const int group = lin / (GM * p.tiles_n);
-  const int first_m = group * GM;
-  const int gsz = (p.tiles_m - first_m) < GM ? (p.tiles_m - first_m) : GM;
-  const int in_g = lin - group * GM * p.tiles_n;
-  const int tm = first_m + in_g % gsz, tn = in_g / gsz;
-
-  int64_t m_limit = p.M;
-  if (p.masked_m) {
-    const int64_t cnt = p.masked_m[e];
-    m_limit = cnt < 0 ? 0 : (cnt > p.M ? p.M : cnt);
-  }
-  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
-  if (m0 >= m_limit) return;
-  const int64_t eb = weight_group(p, e, m0);
-  if (eb < 0) return;
-
-  const int KB = (int)(p.K / 128);
-  const int Wd = (KB + 3) / 4;
-  const int NB = (int)((p.N + 127) / 128);
-  constexpr int NBT = (BN + 127) / 128;
-  uint32_t* lds_sa = reinterpret_cast<uint32_t*>(smem);
-  uint32_t* lds_sb = lds_sa + Wd * BM;
-
-  const int64_t rows_valid = (m_limit - m0 < BM) ? m_limit - m0 : BM;
-  int64_t cols_valid = p.N - n0;
-  cols_valid = cols_valid > BN ? BN : cols_valid;
-  const auto rA = make_rsrc(p.a + e * p.sa_e + m0 * p.K, (uint32_t)(rows_valid * p.K));
-  const auto rB = make_rsrc(p.b + eb * p.sb_e + n0 * p.K, (uint32_t)(cols_valid * p.K));
-  const auto rSA = make_rsrc(p.sfa + e * p.ssfa_e, (uint32_t)(Wd * p.ld_sfa * 4));
-  const auto rSB = make_rsrc(p.sfb + eb * p.ssfb_e, (uint32_t)(NB * KB * 4));
-
-  auto stage_ptr = [&](auto st_tag) -> uint8_t* {
-    if constexpr (decltype(st_tag)::value == 0) return st0;
-    else return st1;
-  };
-  auto issue = [&](int kb, auto st_tag) {
-    uint8_t* base = stage_ptr(st_tag);
-#pragma unroll
-    for (int t = 0; t < IPW; ++t) {
-      const int inst = wave * IPW + t;
-      const bool isA = inst < A_INST;
-      const int ri = isA ? inst : inst - A_INST;
-      const int r = ri * 8 + (lane >> 3);
-      const int chunk = (lane & 7) ^ swz(r);
-      const uint32_t off = (kb < KB) ? (uint32_t)(r * p.K + kb * 128 + chunk * 16) : kOOB;
-      uint8_t* dst = base + (isA ? 0 : BM * 128) + ri * 1024;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(isA ? rA : rB, (__attribute__((address_space(3))) void*)dst, 16,
-                                               (int)off, 0, 0, 0);
-    }
-  };
-
-  for (int idx = tid; idx < Wd * BM; idx += NT) {
-    const int w = idx / BM, row = idx - w * BM;
-    const int64_t m = m0 + row;
-    const uint32_t off = (m < m_limit) ? (uint32_t)(((int64_t)w * p.ld_sfa + m) * 4) : kOOB;
-    lds_sa[idx] = bload4(rSA, off);
-  }
-  for (int idx = tid; idx < NBT * Wd; idx += NT) {
-    const int b = idx / Wd, w = idx - b * Wd;
-    const int nb = (int)(n0 >> 7) + b;
-    uint32_t word = 0;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int k = 4 * w + q;
-      const uint32_t off = (nb < NB && k < KB) ? (uint32_t)((nb * KB + k) * 4) : kOOB;
-      word |= ((bload4(rSB, off) >> 23) & 0xFFu) << (8 * q);
-    }
-    lds_sb[idx] = word;
-  }
-
-  struct Frags {
-    v8i a[SM], b[SN];
-    uint32_t sa[SM], sb[SN];
-  };
-  const int c0 = (lane >> 4), c1 = 4 + (lane >> 4);
-  auto read_frags = [&](int kb, auto st_tag, Frags& f) {
-    const uint8_t* As = stage_ptr(st_tag);
-    const uint8_t* Bs = As + BM * 128;
-    const int w = (kb < KB ? kb : KB - 1) >> 2;
-#pragma unroll
-    for (int i = 0; i < SM; ++i) f.sa[i] = lds_sa[w * BM + wm * WM + 16 * i + (lane & 15)];
-#pragma unroll
-    for (int j = 0; j < SN; ++j) f.sb[j] = lds_sb[((wn * WN + 16 * j) >> 7) * Wd + w];
-#pragma unroll
-    for (int i = 0; i < SM; ++i) {
-      const int r = wm * WM + 16 * i + (lane & 15);
-      const uint4 lo = *reinterpret_cast<const uint4*>(As + r * 128 + ((c0 ^ swz(r)) << 4));
-      const uint4 hi = *reinterpret_cast<const uint4*>(As + r * 128 + ((c1 ^ swz(r)) << 4));
-      f.a[i] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-    }
-#pragma unroll
-    for (int j = 0; j < SN; ++j) {
-      const int r = wn * WN + 16 * j + (lane & 15);
-      const uint4 lo = *reinterpret_cast<const uint4*>(Bs + r * 128 + ((c0 ^ swz(r)) << 4));
-      const uint4 hi = *reinterpret_cast<const uint4*>(Bs + r * 128 + ((c1 ^ swz(r)) << 4));
-      f.b[j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-    }
-  };
-
-  v4f acc[SM][SN];
-#pragma unroll
-  for (int i = 0; i < SM; ++i)
-#pragma unroll
-    for (int j = 0; j < SN; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-
-  // prologue: DMA K-blocks 0 and 1, wait for 0, read its operands into set X
-  Frags fx, fy;
-  issue(0, IntC<0>{});
-  issue(1, IntC<1>{});
-  __builtin_amdgcn_s_waitcnt((IPW & 0xF) | 0x0F70 | ((IPW >> 4) << 14));  // K-block 1 may remain in flight
-  __syncthreads();
-  read_frags(0, IntC<0>{}, fx);
-
-  // step kb: operands of kb in `cur`; stage of kb is ST
-  auto step = [&](int kb, auto ops_tag, auto st_tag, Frags& cur, Frags& nxt) {
-    constexpr int OPS = decltype(ops_tag)::value;
-    constexpr int ST = decltype(st_tag)::value;
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // this wavefront's DMA of kb + 1 has landed
-    __syncthreads();
-    read_frags(kb + 1, IntC<1 - ST>{}, nxt);  // operands of kb + 1 stream in under the MFMAs
-    // Keep the DMA below the operand reads: the compiler would hoist it above them
-    // (the buffers differ) and then make the reads wait for it.
-    __builtin_amdgcn_sched_barrier(0);
-    issue(kb + 2, st_tag);                   // kb's stage is free: everyone has read it
-#pragma unroll
-    for (int j = 0; j < SN; ++j)
-#pragma unroll
-      for (int i = 0; i < SM; ++i)
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(cur.b[j], cur.a[i], acc[i][j], 0, 0, OPS,
-                                                                     (int)cur.sb[j], OPS, (int)cur.sa[i]);
-  };
-
-  // unrolled by four: scale byte kb % 4, stage kb % 2 and register set kb % 2 are static
-  for (int kb = 0; kb < KB; kb += 4) {
-    step(kb, IntC<0>{}, IntC<0>{}, fx, fy);
-    if (kb + 1 < KB) step(kb + 1, IntC<1>{}, IntC<1>{}, fy, fx);
-    if (kb + 2 < KB) step(kb + 2, IntC<2>{}, IntC<0>{}, fx, fy);
-    if (kb + 3 < KB) step(kb + 3, IntC<3>{}, IntC<1>{}, fy, fx);
-  }
-
-  uint16_t* __restrict__ C = p.c + e * p.sc_e;
-#pragma unroll
-  for (int i = 0; i < SM; ++i) {
-    const int64_t m = m0 + wm * WM + 16 * i + (lane & 15);
-    if (m >= m_limit) continue;
-#pragma unroll
-    for (int j = 0; j < SN; ++j) {
-      const int64_t n = n0 + wn * WN + 16 * j + 4 * (lane >> 4);
-      if (n < p.N) {
-        uint2 o;
-        o.x = bf16_rne(acc[i][j][0]) | (bf16_rne(acc[i][j][1]) << 16);
-        o.y = bf16_rne(acc[i][j][2]) | (bf16_rne(acc[i][j][3]) << 16);
-        *reinterpret_cast<uint2*>(C + m * p.ldc + n) = o;
-      }
-    }
-  }
-}
-
 inline size_t scaled_tile_lds_bytes(int bm, int bn, int stages, int K, bool float_scales = false) {
   // dynamic part only (the stage buffers are static): the two scale tables, one word
   // per four K-blocks (packed UE8M0) or one fp32 per K-block (float scales)
@@ -1762,10 +1570,6 @@ const TileEntry kTiles[] = {
     {scaled_tile_kernel<128, 256, 2, 2, 2>, 128, 256, kScaled, 2, 256},
     {scaled_tile_kernel<256, 128, 2, 2, 2>, 256, 128, kScaled, 2, 256},
     {scaled_tile_kernel<128, 128, 2, 2, 2>, 128, 128, kScaled, 2, 256},
-    {scaled_pipe_kernel<128, 128, 2, 2>, 128, 128, kScaled, 2, 256},
-    {scaled_pipe_kernel<256, 128, 2, 2>, 256, 128, kScaled, 2, 256},
-    {scaled_pipe_kernel<128, 256, 2, 2>, 128, 256, kScaled, 2, 256},
-    {scaled_pipe_kernel<256, 128, 4, 2>, 256, 128, kScaled, 2, 512},
     {scaled_tile_kernel<256, 256, 2, 4, 2>, 256, 256, kScaled, 2, 512},
     {scaled_tile_kernel<256, 256, 4, 2, 2>, 256, 256, kScaled, 2, 512},
     {scaled_tile_kernel<256, 128, 4, 2, 2>, 256, 128, kScaled, 2, 512},
@@ -1791,17 +1595,17 @@ constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 // table entries the automatic choice uses
 constexpr int kCfgStream64x128 = 4;
 constexpr int kCfgScaled128x128 = 13;
-constexpr int kCfgScaled256x256 = 19;
-constexpr int kCfgRing256x256 = 21;        // 2 x 2 wavefronts
-constexpr int kCfgRing256x256Rows = 24;    // 1 x 4 wavefronts (all share the rows)
-constexpr int kCfgRing128x256 = 23;        // 2 x 2 wavefronts, 128-row tiles
-constexpr int kCfgFloat64x128 = 30;        // float-scale VALU-scaled tiles
-constexpr int kCfgFloat128x128 = 31;
-constexpr int kCfgFloat128x256 = 33;
-constexpr int kCfgFloatDecode64x128 = 34;  // decode kernel, float scales
-constexpr int kCfgFloatScaled128x128 = 35; // LDS-DMA tiles, float scales
-constexpr int kCfgFloatScaled128x256 = 36;
-constexpr int kCfgDecode64x128 = 26;       // decode kernel, 4 wavefronts, three K-blocks in flight
+constexpr int kCfgScaled256x256 = 15;
+constexpr int kCfgRing256x256 = 17;        // 2 x 2 wavefronts
+constexpr int kCfgRing256x256Rows = 20;    // 1 x 4 wavefronts (all share the rows)
+constexpr int kCfgRing128x256 = 19;        // 2 x 2 wavefronts, 128-row tiles
+constexpr int kCfgFloat64x128 = 26;        // float-scale VALU-scaled tiles
+constexpr int kCfgFloat128x128 = 27;
+constexpr int kCfgFloat128x256 = 29;
+constexpr int kCfgFloatDecode64x128 = 30;  // decode kernel, float scales
+constexpr int kCfgFloatScaled128x128 = 31; // LDS-DMA tiles, float scales
+constexpr int kCfgFloatScaled128x256 = 32;
+constexpr int kCfgDecode64x128 = 22;       // decode kernel, 4 wavefronts, three K-blocks in flight
 static_assert(kCfgDecode64x128 < kNumTiles && kCfgFloatScaled128x256 < kNumTiles, "tile table");
 
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
