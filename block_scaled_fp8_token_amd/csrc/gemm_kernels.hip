@@ -1757,12 +1757,13 @@ GemmConfig choose_gemm_config(const GemmProblem& p) {
   // the VALU-scaled tile kernel when no scale table fits
   const int64_t tm256 = cdiv(p.M, 256), tn256 = cdiv(p.N, 256), big_tiles = tm256 * tn256;
   if (big_tiles >= 256 && gemm_config_by_index(kCfgRing256x256, p, 1, &cfg)) {
-    // With 256x256 tiles, one per compute unit at a time, a last round of less than
+    // With 256x256 tiles, one per compute unit at a time, a last round of at most
     // half the compute units would leave the rest idle for a whole tile time: run
     // the leading columns in whole rounds and the remaining columns with 128x128
-    // tiles in a second launch.
+    // tiles in a second launch (up to 512 of them: two per compute unit, which
+    // finish well within one 256x256 tile time).
     const int64_t rem = big_tiles % 256;
-    if (rem != 0 && rem < 128 && p.E == 1 && !p.masked_m && !p.m_indices) {
+    if (rem != 0 && rem <= 128 && p.E == 1 && !p.masked_m && !p.m_indices) {
       const int64_t lead_tn = (big_tiles / 256) * 256 / tm256;
       const int64_t n_split = lead_tn * 256;
       GemmProblem tp = p;
