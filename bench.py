@@ -36,6 +36,10 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
 FP8_PEAK_TFLOPS = 5000.0     # MI355X dense FP8 MFMA, published
 H100_DEEPGEMM_DECODE_TFLOPS = 243.6  # benchmark post, section 3.2, m=64 n=7168 k=18432 (context)
+GRAPH_RUN_STEPS = 40          # steps per captured graph (rounded to whole weight rotations)
+SETTLE_MS = 40.0              # GPU time run before timing a long launch (clock settling)
+SHORT_LAUNCH_MS = 0.05        # launches shorter than this are timed behind a spin kernel
+SETTLE_MAX_LAUNCHES = 400
 
 
 # ----------------------------------------------------------------------------- metrics
@@ -112,17 +116,34 @@ def n_copies_for(bytes_per_copy, cache_bytes=256 << 20, floor=1):
 
 # ----------------------------------------------------------------------------- timing
 
-def kernel_times(stream, launches, steps):
+def kernel_times(stream, launches, steps, settle_ms=SETTLE_MS):
     """Average GPU duration of each launch type, in ms: `steps` back-to-back calls of
-    one launch between two HIP events recorded on the launch stream (a spin kernel
-    first keeps the GPU busy while the host enqueues, so the calls run back to back
-    and the per-event cost is spread over the batch)."""
+    one launch between two HIP events recorded on the launch stream.
+
+    Launches shorter than SHORT_LAUNCH_MS are queued behind a spin kernel, so that
+    they run back to back although the host enqueues them more slowly than they run.
+    Longer launches (the prefill and MoE GEMMs, which the host easily stays ahead of)
+    first run back to back for at least `settle_ms` of GPU time, queued together with
+    the timed calls: the clock of a GPU that starts from idle boosts, then drops under
+    the power limit for a few launches of an MFMA-bound kernel before it settles, and
+    the figure wanted is the settled one."""
     out = []
     for fn in launches:
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         with torch.cuda.stream(stream):
-            torch.cuda._sleep(int(2e7))
+            e0.record(stream)
+            for s in range(3):
+                fn(s)
+            e1.record(stream)
+        stream.synchronize()
+        t_est = e0.elapsed_time(e1) / 3
+        with torch.cuda.stream(stream):
+            if t_est < SHORT_LAUNCH_MS:
+                torch.cuda._sleep(int(2e7))
+            else:
+                for s in range(int(min(SETTLE_MAX_LAUNCHES, np.ceil(settle_ms / t_est)))):
+                    fn(s)
             e0.record(stream)
             for s in range(steps):
                 fn(s)
@@ -135,10 +156,12 @@ def kernel_times(stream, launches, steps):
 def graph_step_time(stream, step_fn, n_variants, steps, warmup):
     """Wall ms per step over exactly `steps` steps, with synchronizations on both
     sides of the timed loop.  Steps are replayed from HIP graphs that each hold a run
-    of consecutive steps over the rotating input variants (one graph of n_variants
-    steps, replayed steps // n_variants times, plus one graph holding the remaining
-    steps), so the host cost of a graph launch is paid once per run of steps rather
-    than once per step, as in a serving loop that queues many steps."""
+    of consecutive steps over the rotating input variants (one graph of `per_graph`
+    steps -- whole rotations, about 40 steps -- replayed steps // per_graph times, plus
+    one graph holding the remaining steps), so the host cost of a graph launch (about
+    13 us between two replays, measured) is paid once per run of steps rather than
+    once per step, as in a serving loop that queues many steps."""
+    per_graph = n_variants * max(1, GRAPH_RUN_STEPS // n_variants)
     with torch.cuda.stream(stream):
         for _ in range(2):
             for v in range(n_variants):
@@ -152,18 +175,26 @@ def graph_step_time(stream, step_fn, n_variants, steps, warmup):
                 step_fn(v)
         return g
 
-    full = capture(n_variants)
-    rest = steps % n_variants
+    full = capture(per_graph)
+    rest = steps % per_graph
     tail = capture(rest) if rest else None
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
     with torch.cuda.stream(stream):
-        for i in range(max(1, warmup // n_variants)):
+        e0.record(stream)
+        full.replay()
+        e1.record(stream)
+    stream.synchronize()
+    n_warm = max(1, warmup // per_graph, int(np.ceil(SETTLE_MS / max(e0.elapsed_time(e1), 1e-3))))
+    with torch.cuda.stream(stream):
+        for i in range(min(n_warm, SETTLE_MAX_LAUNCHES)):
             full.replay()
         if tail is not None:
             tail.replay()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     with torch.cuda.stream(stream):
-        for i in range(steps // n_variants):
+        for i in range(steps // per_graph):
             full.replay()
         if tail is not None:
             tail.replay()
