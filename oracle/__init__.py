@@ -73,6 +73,8 @@ def _load():
     lib.orc_gemm_grouped_masked.restype = None
     lib.orc_gemm_grouped_contiguous.argtypes = [P, P, I, P, P, P, I, I, I, I, P, I, P]
     lib.orc_gemm_grouped_contiguous.restype = None
+    lib.orc_weight_preshuffle.argtypes = [P, I, I, P]
+    lib.orc_weight_preshuffle.restype = None
     lib.orc_calc_diff.argtypes = [P, P, I]
     lib.orc_calc_diff.restype = ctypes.c_double
     lib.orc_num_threads.argtypes = []
@@ -204,6 +206,18 @@ def block_quant_128x128(w: np.ndarray):
     sfb = np.zeros(((N + 127) // 128, K // 128), np.float32)
     _load().orc_block_quant_128x128(_ptr(w), N, K, _ptr(q), _ptr(sfb))
     return q, sfb
+
+
+def weight_preshuffle(w: np.ndarray) -> np.ndarray:
+    """e4m3 weights [rows, K] (uint8, rows % 32 == 0, K % 128 == 0) -> the same bytes in the
+    pre-shuffled layout (a flat uint8 array of rows*K bytes, returned as [rows, K])."""
+    w = _req(w, np.uint8)
+    rows, K = w.shape
+    if rows % 32 or K % 128:
+        raise ValueError("rows must be a multiple of 32 and K of 128")
+    out = np.zeros((rows, K), np.uint8)
+    _load().orc_weight_preshuffle(_ptr(w), rows, K, _ptr(out))
+    return out
 
 
 def gemm_nt(qa, sfa, qb, sfb, rows=None, cols=None):

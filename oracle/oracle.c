@@ -462,6 +462,27 @@ void orc_gemm_grouped_contiguous(const uint8_t* a, const uint32_t* sfa, int64_t 
 }
 
 /* calc_diff of the benchmark post (section 4.4): 1 - 2*sum(x*y) / sum(x*x + y*y), in double. */
+/*
+ * Pre-shuffled weight layout.  Not a step of the method: a byte permutation of
+ * e4m3 weights [rows][K] that the GEMM library declares for its decode kernel
+ * (fp8_weight_preshuffle).  Byte i of 16-byte chunk l of load q of K-block kb of
+ * 32-row group g sits at ((g*KB + kb)*4 + q)*1024 + l*16 + i and holds weight
+ * row 32g + (l mod 32), column 128kb + 64*(q div 2) + 32*(l div 32) + 16*(q mod 2) + i.
+ * Written here as the plain loop over that definition; rows % 32 == 0, K % 128 == 0.
+ */
+void orc_weight_preshuffle(const uint8_t* w, int64_t rows, int64_t K, uint8_t* out) {
+  const int64_t KB = K / 128;
+  for (int64_t g = 0; g < rows / 32; ++g)
+    for (int64_t kb = 0; kb < KB; ++kb)
+      for (int q = 0; q < 4; ++q)
+        for (int l = 0; l < 64; ++l)
+          for (int i = 0; i < 16; ++i) {
+            const int64_t row = 32 * g + (l % 32);
+            const int64_t col = 128 * kb + 64 * (q / 2) + 32 * (l / 32) + 16 * (q % 2) + i;
+            out[(((g * KB + kb) * 4 + q) * 64 + l) * 16 + i] = w[row * K + col];
+          }
+}
+
 double orc_calc_diff(const double* x, const double* y, int64_t n) {
   double num = 0.0, den = 0.0;
   for (int64_t i = 0; i < n; ++i) {

@@ -566,3 +566,31 @@ def test_bf16_rne_matches_torch():
     got = O.bf16_rne_array(v.astype(np.float64))
     assert np.array_equal(got, want)
     assert np.array_equal(W.f32_to_bf16_bits(v), want)
+
+
+def test_weight_preshuffle_layout_properties():
+    """The pre-shuffled weight layout is a byte permutation whose every 1 KB load (g, kb, q)
+    gives lane l sixteen consecutive bytes of row 32g + (l mod 32), and whose two loads
+    q = 2h, 2h + 1 give that lane the 32 consecutive K-bytes 128kb + 64h + 32*(l div 32) ..
+    + 31: the operand of lane l for the h-th 64-wide MFMA of K-block kb (a 32-row x 64-K
+    operand, lane l holding row l mod 32 and the (l div 32)-th 32-byte half of the K range).
+    Checked with position-coded inputs (the source row and column of every output byte)."""
+    rows, K = 96, 640
+    r_idx, c_idx = np.meshgrid(np.arange(rows), np.arange(K), indexing="ij")
+    src_row = O.weight_preshuffle(r_idx.astype(np.uint8)).reshape(-1).astype(np.int64)
+    src_lo = O.weight_preshuffle((c_idx % 256).astype(np.uint8)).reshape(-1).astype(np.int64)
+    src_hi = O.weight_preshuffle((c_idx // 256).astype(np.uint8)).reshape(-1).astype(np.int64)
+    src_col = src_lo + 256 * src_hi
+    # a bijection: every (row, col) appears exactly once
+    flat = np.sort(src_row * K + src_col)
+    assert np.array_equal(flat, np.arange(rows * K))
+    KB = K // 128
+    loads = np.stack([src_row, src_col], 1).reshape(rows // 32, KB, 4, 64, 16, 2)
+    for g in range(rows // 32):
+        for kb in range(KB):
+            for l in range(64):
+                for h in range(2):
+                    chunk = np.concatenate([loads[g, kb, 2 * h, l], loads[g, kb, 2 * h + 1, l]])
+                    assert (chunk[:, 0] == 32 * g + l % 32).all()
+                    start = 128 * kb + 64 * h + 32 * (l // 32)
+                    assert np.array_equal(chunk[:, 1], np.arange(start, start + 32))
