@@ -25,6 +25,7 @@ __all__ = [
     "library_path", "header_path", "declared_functions", "gemm_config_of",
     "fp8_quant_group_pack_to_experts", "fp8_block_gemm_grouped_contiguous",
     "fp8_quant_group_float", "fp8_block_quant_128x128_float", "fp8_block_gemm_nt_float_scales",
+    "fp8_weight_preshuffle", "fp8_block_gemm_nt_preshuffled",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -53,6 +54,9 @@ _SIGS = {
     "fp8_block_gemm_nt_float_scales_cfg": [_P, _P, _I64, _P, _P, _P, _I64, _I64, _I64, _I64, _I32, _I32, _P],
     "fp8_block_gemm_nt": [_P, _P, _I64, _P, _P, _P, _I64, _I64, _I64, _I64, _P],
     "fp8_block_gemm_nt_cfg": [_P, _P, _I64, _P, _P, _P, _I64, _I64, _I64, _I64, _I32, _I32, _P],
+    "fp8_weight_preshuffle": [_P, _I64, _I64, _P, _P],
+    "fp8_block_gemm_nt_preshuffled": [_P, _P, _I64, _P, _P, _P, _I64, _I64, _I64, _I64, _P],
+    "fp8_block_gemm_nt_preshuffled_cfg": [_P, _P, _I64, _P, _P, _P, _I64, _I64, _I64, _I64, _I32, _I32, _P],
     "fp8_block_gemm_grouped_masked": [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _P],
     "fp8_block_gemm_grouped_masked_cfg": [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I32, _P],
     "fp8_block_gemm_grouped_contiguous": [_P, _P, _I64, _P, _P, _P, _I64, _P, _I64, _I64, _I64, _I64, _P],
@@ -279,6 +283,58 @@ def fp8_block_gemm_nt(a: torch.Tensor, sfa: torch.Tensor, b: torch.Tensor, sfb: 
     return c
 
 
+def fp8_weight_preshuffle(w: torch.Tensor, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """e4m3 weights [..., rows, K] (rows over all leading dims a multiple of 32) -> the same
+    bytes in the pre-shuffled layout of fp8_block_gemm_nt_preshuffled, same shape."""
+    _expect(w, "w", _E4M3, w.dim())
+    _contig(w, "w")
+    if w.dim() < 2:
+        raise ValueError("w must be [..., rows, K]")
+    K = w.shape[-1]
+    rows = w.numel() // K if K else 0
+    if out is None:
+        out = torch.empty_like(w)
+    _expect(out, "out", _E4M3, w.dim())
+    _contig(out, "out")
+    if tuple(out.shape) != tuple(w.shape):
+        raise ValueError("out must have the shape of w")
+    _check("fp8_weight_preshuffle", _lib.fp8_weight_preshuffle(w.data_ptr(), rows, K, out.data_ptr(), _stream(stream)))
+    return out
+
+
+def fp8_block_gemm_nt_preshuffled(a: torch.Tensor, sfa: torch.Tensor, b: torch.Tensor, sfb: torch.Tensor,
+                                  c: torch.Tensor | None = None, kernel: int | None = None,
+                                  splits: int | None = None, stream=None) -> torch.Tensor:
+    """fp8_block_gemm_nt with b [N, K] in the pre-shuffled layout (fp8_weight_preshuffle)."""
+    _expect(a, "a", _E4M3, 2)
+    _contig(a, "a")
+    _expect(b, "b", _E4M3, 2)
+    _contig(b, "b")
+    _expect(sfa, "sfa", (torch.int32, torch.uint32), 2)
+    _expect(sfb, "sfb", (torch.float32,), 2)
+    _contig(sfb, "sfb")
+    M, K = a.shape
+    N = b.shape[0]
+    if b.shape[1] != K:
+        raise ValueError("a and b disagree on K")
+    if c is None:
+        c = torch.empty((M, N), dtype=torch.bfloat16, device=a.device)
+    _expect(c, "c", _BF16, 2)
+    if tuple(c.shape) != (M, N):
+        raise ValueError("c must be [M, N]")
+    s = _stream(stream)
+    args = (a.data_ptr(), sfa.data_ptr(), sfa.stride(0), b.data_ptr(), sfb.data_ptr(), c.data_ptr(), c.stride(0),
+            M, N, K)
+    if kernel is None and splits is None:
+        st = _lib.fp8_block_gemm_nt_preshuffled(*args, s)
+    else:
+        if kernel is None:
+            kernel = gemm_config(LAYOUT_DENSE_PRESHUFFLED, M, N, K)["kernel"]
+        st = _lib.fp8_block_gemm_nt_preshuffled_cfg(*args, int(kernel), int(splits or 1), s)
+    _check("fp8_block_gemm_nt_preshuffled", st)
+    return c
+
+
 def fp8_block_gemm_grouped_masked(a: torch.Tensor, sfa: torch.Tensor, b: torch.Tensor, sfb: torch.Tensor,
                                   masked_m: torch.Tensor, c: torch.Tensor | None = None,
                                   kernel: int | None = None, stream=None) -> torch.Tensor:
@@ -347,7 +403,7 @@ def fp8_block_gemm_grouped_contiguous(a: torch.Tensor, sfa: torch.Tensor, b: tor
     return c
 
 
-LAYOUT_DENSE, LAYOUT_MASKED, LAYOUT_CONTIGUOUS, LAYOUT_DENSE_FLOAT = 0, 1, 2, 3
+LAYOUT_DENSE, LAYOUT_MASKED, LAYOUT_CONTIGUOUS, LAYOUT_DENSE_FLOAT, LAYOUT_DENSE_PRESHUFFLED = 0, 1, 2, 3, 4
 
 
 def fp8_quant_group_float(x: torch.Tensor, q: torch.Tensor | None = None, sf: torch.Tensor | None = None,
@@ -423,7 +479,8 @@ def gemm_config_count() -> int:
 def gemm_config_of(kernel: int, masked, M: int, N: int, K: int, splits: int = 1):
     """Workgroup tile and split count table entry `kernel` would use for this
     problem, or None if the entry does not accept it.  masked: False/0 dense,
-    True/1 masked grouped, 2 contiguous grouped, 3 dense with float scales."""
+    True/1 masked grouped, 2 contiguous grouped, 3 dense with float scales, 4 dense
+    with pre-shuffled weights."""
     bm, bn, sp = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
     st = _lib.fp8bs_gemm_config_of(int(kernel), int(masked), M, N, K, int(splits), ctypes.byref(bm),
                                    ctypes.byref(bn), ctypes.byref(sp))
@@ -434,8 +491,8 @@ def gemm_config_of(kernel: int, masked, M: int, N: int, K: int, splits: int = 1)
 
 
 def gemm_config(masked, M: int, N: int, K: int) -> dict:
-    """Automatic choice for a dense (False/0), masked (True/1), contiguous grouped (2) or
-    dense float-scale (3) problem."""
+    """Automatic choice for a dense (False/0), masked (True/1), contiguous grouped (2),
+    dense float-scale (3) or dense pre-shuffled-weight (4) problem."""
     k, bm, bn, sp = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
     st = _lib.fp8bs_gemm_config(int(masked), M, N, K, ctypes.byref(k), ctypes.byref(bm),
                                 ctypes.byref(bn), ctypes.byref(sp))

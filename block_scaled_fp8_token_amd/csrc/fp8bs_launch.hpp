@@ -16,6 +16,10 @@ hipError_t launch_silu_mul_quant(const uint16_t* x, const int32_t* masked_m, int
 hipError_t launch_block_quant(const uint16_t* w, int64_t N, int64_t K, uint8_t* q, float* sfb,
                               hipStream_t stream);
 
+// e4m3 weights [rows][K] -> the pre-shuffled layout read by the decode kernel
+// (rows % 32 == 0, K % 128 == 0).
+hipError_t launch_weight_preshuffle(const uint8_t* w, int64_t rows, int64_t K, uint8_t* out, hipStream_t stream);
+
 // Float-scale (non-UE8M0) variants: scale = max(amax, 1e-10) / 448 in fp32.
 hipError_t launch_quant_group_float(const uint16_t* x, int64_t ldx, int64_t M, int64_t K, uint8_t* q,
                                    int64_t ldq, float* sf, int64_t ld_sf, hipStream_t stream);
@@ -48,6 +52,8 @@ struct GemmProblem {
   // float-scale format (dense only): sfa points at fp32 [K/128][ld_sfa] scales and the
   // weight scales are any fp32 values
   bool float_scales = false;
+  // weights in the pre-shuffled layout of fp8_weight_preshuffle (dense only)
+  bool b_shuffled = false;
 };
 
 // Rows per aligned run of one weight group in the contiguous grouped layout.

@@ -141,7 +141,7 @@ __device__ __forceinline__ void store_tile(const float (&acc)[SM][SN][4], const 
 
 // Split-K reduction: thread t owns 8 consecutive columns of one row, adds the
 // partials of every split in split order (deterministic), and stores 8 bf16.
-// The loads of four splits are issued before any is added.
+// The loads of eight splits are issued before any is added.
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ ws, int splits, int64_t M,
                                                             int64_t N, uint16_t* __restrict__ C, int64_t ldc) {
   const int64_t per_row = N / 8;
@@ -151,16 +151,16 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
   const size_t slice = (size_t)M * (size_t)N;
   const float* src = ws + (size_t)m * N + n;
   float t[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int sp0 = 0; sp0 < splits; sp0 += 4) {
-    float4 v[4][2];
+  for (int sp0 = 0; sp0 < splits; sp0 += 8) {
+    float4 v[8][2];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < 8; ++u) {
       const int sp = (sp0 + u < splits) ? sp0 + u : sp0;
       v[u][0] = *reinterpret_cast<const float4*>(src + (size_t)sp * slice);
       v[u][1] = *reinterpret_cast<const float4*>(src + (size_t)sp * slice + 4);
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < 8; ++u) {
       if (sp0 + u < splits) {
         t[0] += v[u][0].x; t[1] += v[u][0].y; t[2] += v[u][0].z; t[3] += v[u][0].w;
         t[4] += v[u][1].x; t[5] += v[u][1].y; t[6] += v[u][1].z; t[7] += v[u][1].w;
@@ -1144,8 +1144,11 @@ constexpr int ring_wd_max() { return RingShape<BM, BN, WGM, WGN>::WD_MAX; }
 // workspace and the last split of the tile to arrive adds them in split order and
 // writes C (see the reduction below).
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+// An empty use of a register pair: the loads that wrote it must be issued.
+__device__ __forceinline__ void keep_issued(const v8i (&r)[2]) { asm volatile("" ::"v"(r[0]), "v"(r[1])); }
 constexpr int kSC1 = 16;              // cache-policy bit sc1 of buffer loads/stores (gfx940 family)
 constexpr int kDecodeMaxSplits = 8;   // K splits the decode kernel reduces itself
+constexpr int kDecodeSepMaxSplits = 16;  // K splits of the decode kernel left to splitk_reduce_kernel
 constexpr int kCounterBytes = 65536;  // split-K arrival counters at the front of the workspace
 
 template <int NW, int DB_>
@@ -1161,7 +1164,7 @@ struct DecodeShape {
 // split (activations [K-block][row], weights [column block][K-block]; at most WMAX
 // K-blocks per split), the MFMAs run with unit scales into a per-K-block product,
 // and acc += product * (s_a * s_b) on the VALU.
-template <int NW, int DB_, bool FS = false>
+template <int NW, int DB_, bool FS = false, bool SHUF = false>
 __global__ __launch_bounds__(NW * 64) void decode_kernel(const KArgs p) {
   using D = DecodeShape<NW, DB_>;
   constexpr int DB = D::DB, UN = D::UN, IA = D::IA, WMAX = D::WMAX, NBT = D::NBT;
@@ -1196,7 +1199,8 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const KArgs p) {
   const int KB = (int)(p.K / 128);
   const int kb0 = split * p.kb_per_split;
   const int nk = (KB - kb0 < p.kb_per_split) ? KB - kb0 : p.kb_per_split;  // >= 1 (host)
-  const int nkp = (nk + UN - 1) / UN * UN;  // iterations, padded to whole unrolled groups
+  const int nk4 = (nk + 3) & ~3;            // iterations: K-blocks padded to a whole scale word
+  const int nfull = nk4 / UN * UN;          // iterations in whole unrolled groups; a tail of 4 or 8 follows
   const int NB = (int)((p.N + 127) / 128);
   const int64_t rows_valid = (m_limit - m0 < 64) ? m_limit - m0 : 64;
   int64_t cols_valid = p.N - n0;
@@ -1236,14 +1240,18 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const KArgs p) {
                                                (int)((aoff[t] + koff) | oob), 0, 0, 0);
     }
   };
-  // weight loads: lane l, row n0 + 32 wave + (l & 31), bytes 32 (l >> 5) + 64 h .. + 31
-  const uint32_t boff = (uint32_t)((wave * 32 + (lane & 31)) * p.K) + (uint32_t)(32 * (lane >> 5));
+  // weight loads: lane l, row n0 + 32 wave + (l & 31), bytes 32 (l >> 5) + 64 h .. + 31.
+  // SHUF: the same bytes from the pre-shuffled layout, where every 32-row group's
+  // K-block is 4 KB in load order (one contiguous 1 KB per load instruction)
+  const uint32_t boff = SHUF ? (uint32_t)(wave * 32 * p.K) + (uint32_t)(16 * lane)
+                             : (uint32_t)((wave * 32 + (lane & 31)) * p.K) + (uint32_t)(32 * (lane >> 5));
+  constexpr uint32_t KB_STEP = SHUF ? 4096u : 128u, H_STEP = SHUF ? 2048u : 64u, P_STEP = SHUF ? 1024u : 16u;
   auto load_b = [&](int j, v8i (&bh)[2]) {
-    const uint32_t off = (boff + (uint32_t)(kb0 + j) * 128u) | (j < nk ? 0u : kOOB);
+    const uint32_t off = (boff + (uint32_t)(kb0 + j) * KB_STEP) | (j < nk ? 0u : kOOB);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const v4i lo = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rB, (int)(off + 64 * h), 0, 0));
-      const v4i hi = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rB, (int)(off + 64 * h + 16), 0, 0));
+      const v4i lo = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rB, (int)(off + H_STEP * h), 0, 0));
+      const v4i hi = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rB, (int)(off + H_STEP * h + P_STEP), 0, 0));
       bh[h] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
     }
   };
@@ -1252,8 +1260,8 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const KArgs p) {
   // past the rows and for K-blocks past the split), weight exponent bytes.  The
   // global loads go out first, then the prologue prefetch, then the LDS writes, so
   // the table loads' latency overlaps the prefetch.
-  const int w0 = kb0 / 4;                   // kb0 is a multiple of UN, hence of 4 (host)
-  const int nw = nkp / 4;                   // words of this split, <= WMAX (host)
+  const int w0 = kb0 / 4;                   // kb0 is a multiple of 4 (host)
+  const int nw = nk4 / 4;                   // words of this split, <= WMAX (host)
   constexpr int SA_PT = (WMAX * 64 + NT - 1) / NT, SB_PT = (NBT * WMAX * 4 + NT - 1) / NT;
   uint32_t sav[SA_PT], sbv[SB_PT];
   if constexpr (FS) {
@@ -1409,7 +1417,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const KArgs p) {
       load_b(j + DB, bcur);  // the registers of kb are free again: fetch kb + DB
     };
 
-    for (int jb = 0; jb < nkp; jb += UN) {
+    for (int jb = 0; jb < nfull; jb += UN) {
       iter(jb, IntC<0>{});
       iter(jb, IntC<1>{});
       iter(jb, IntC<2>{});
@@ -1425,6 +1433,30 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const KArgs p) {
         iter(jb, IntC<11>{});
       }
     }
+    if constexpr (UN == 12) {
+      // tail of 4 or 8 iterations: a multiple of three unrolled groups precede it, so
+      // the stage / register ring and the scale byte continue from U = 0
+      if (nk4 - nfull >= 4) {
+        iter(nfull, IntC<0>{});
+        iter(nfull, IntC<1>{});
+        iter(nfull, IntC<2>{});
+        iter(nfull, IntC<3>{});
+      }
+      if (nk4 - nfull >= 8) {
+        iter(nfull, IntC<4>{});
+        iter(nfull, IntC<5>{});
+        iter(nfull, IntC<6>{});
+        iter(nfull, IntC<7>{});
+      }
+    }
+    // The weight prefetches past the last K-block are never read, so in straight-line
+    // code after the loop the compiler would drop them; every iteration's vmcnt wait
+    // counts them as issued after its activation DMA, so without them the wait would
+    // no longer cover the DMA.  An empty use keeps them.
+    keep_issued(b0);
+    keep_issued(b1);
+    if constexpr (DB > 2) keep_issued(b2);
+    if constexpr (DB > 3) keep_issued(b3);
     // the prefetches past the range (out of range, zero-filled) must land before
     // the LDS is reused or released
     __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
@@ -1464,6 +1496,18 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const KArgs p) {
       for (int t = 0; t < IV * 4; ++t) store_c(t, staged(t));
       return;
     }
+    const size_t slice = (size_t)p.M * (size_t)p.N;
+    if (!p.counters) {
+      // K split finished by splitk_reduce_kernel on the same stream: publish this
+      // split's partial (the kernel boundary makes it visible to the reduction)
+#pragma unroll
+      for (int t = 0; t < IV * 4; ++t) {
+        const int64_t m = m0 + t * 8 + (lane >> 3);
+        if (m < m_limit && n < p.N)
+          *reinterpret_cast<v4f*>(p.ws + (size_t)split * slice + (size_t)m * p.N + n) = staged(t);
+      }
+      return;
+    }
     // K split, reduced in this kernel by the last split of the tile to arrive.  The
     // partials are written with sc1 (coherent across the XCDs' L2 caches: written
     // through) and complete (s_waitcnt) before this split bumps the tile's arrival
@@ -1471,7 +1515,6 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const KArgs p) {
     // them in split order (deterministic) and writes bf16, and sets the counter back
     // to zero for the next call.  No cache-wide fence is needed: only the partials
     // cross workgroups, and they never sit dirty in an L2.
-    const size_t slice = (size_t)p.M * (size_t)p.N;
     const auto rW = make_rsrc(p.ws, (uint32_t)(((size_t)p.splits * slice) * 4 > 0x7FFFFFFFull
                                                    ? 0x7FFFFFFFu : (size_t)p.splits * slice * 4));
     auto woff = [&](int sp, int t) -> uint32_t {
@@ -1533,7 +1576,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const KArgs p) {
 typedef void (*KernelFn)(const KArgs);
 
 enum Kind { kTile = 0, kStream = 1, kScaled = 2, kRing = 3, kDecode = 4, kTileFloat = 5, kDecodeFloat = 6,
-            kScaledFloat = 7 };
+            kScaledFloat = 7, kDecodeSep = 8, kDecodeShuf = 9, kDecodeShufSep = 10 };
 
 // Entries that read the float-scale format.
 inline bool reads_float_scales(int kind) {
@@ -1542,7 +1585,12 @@ inline bool reads_float_scales(int kind) {
 // LDS-DMA tile entries (dynamic LDS for the scale tables).
 inline bool is_scaled_tile(int kind) { return kind == kScaled || kind == kScaledFloat; }
 // Entries that reduce their own K split (arrival counters in the workspace).
-inline bool reduces_in_kernel(int kind) { return kind == kDecode || kind == kDecodeFloat; }
+inline bool reduces_in_kernel(int kind) { return kind == kDecode || kind == kDecodeFloat || kind == kDecodeShuf; }
+// Entries that read the weights in the pre-shuffled layout.
+inline bool reads_shuffled(int kind) { return kind == kDecodeShuf || kind == kDecodeShufSep; }
+// Decode-kernel entries (K split in whole scale words; kDecodeSep leaves the sum of
+// the partials to splitk_reduce_kernel).
+inline bool is_decode(int kind) { return reduces_in_kernel(kind) || kind == kDecodeSep || kind == kDecodeShufSep; }
 
 struct TileEntry {
   KernelFn fn;
@@ -1590,6 +1638,12 @@ const TileEntry kTiles[] = {
     {decode_kernel<4, 3, true>, 64, 128, kDecodeFloat, 3, 256, DecodeShape<4, 3>::WMAX / 4},
     {scaled_tile_kernel<128, 128, 2, 2, 2, true>, 128, 128, kScaledFloat, 2, 256},
     {scaled_tile_kernel<128, 256, 2, 2, 2, true>, 128, 256, kScaledFloat, 2, 256},
+    {decode_kernel<8, 3>, 64, 256, kDecodeSep, 3, 512, DecodeShape<8, 3>::WMAX},
+    {decode_kernel<4, 3>, 64, 128, kDecodeSep, 3, 256, DecodeShape<4, 3>::WMAX},
+    // pre-shuffled weights
+    {decode_kernel<4, 3, false, true>, 64, 128, kDecodeShuf, 3, 256, DecodeShape<4, 3>::WMAX},
+    {decode_kernel<4, 3, false, true>, 64, 128, kDecodeShufSep, 3, 256, DecodeShape<4, 3>::WMAX},
+    {decode_kernel<8, 3, false, true>, 64, 256, kDecodeShufSep, 3, 512, DecodeShape<8, 3>::WMAX},
 };
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 // table entries the automatic choice uses
@@ -1606,7 +1660,9 @@ constexpr int kCfgFloatDecode64x128 = 30;  // decode kernel, float scales
 constexpr int kCfgFloatScaled128x128 = 31; // LDS-DMA tiles, float scales
 constexpr int kCfgFloatScaled128x256 = 32;
 constexpr int kCfgDecode64x128 = 22;       // decode kernel, 4 wavefronts, three K-blocks in flight
+constexpr int kCfgShufDecode64x128 = 35;   // the same on pre-shuffled weights
 static_assert(kCfgDecode64x128 < kNumTiles && kCfgFloatScaled128x256 < kNumTiles, "tile table");
+static_assert(kCfgShufDecode64x128 < kNumTiles, "tile table");
 
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -1632,6 +1688,9 @@ bool gemm_config_by_index(int idx, const GemmProblem& p, int splits, GemmConfig*
   // the float-scale format runs on the float-scale entries only (dense calls)
   if (reads_float_scales(kTiles[idx].kind) != p.float_scales) return false;
   if (p.float_scales && (p.masked_m || p.m_indices || p.E != 1)) return false;
+  // pre-shuffled weights run on the entries that read that layout (dense calls)
+  if (reads_shuffled(kTiles[idx].kind) != p.b_shuffled) return false;
+  if (p.b_shuffled && (p.masked_m || p.m_indices || p.E != 1 || p.float_scales)) return false;
   // contiguous grouped layout: a tile must not straddle two aligned runs
   if (p.m_indices && kContiguousAlign % kTiles[idx].bm != 0) return false;
   if (kTiles[idx].kind == kRing) {
@@ -1653,20 +1712,21 @@ bool gemm_config_by_index(int idx, const GemmProblem& p, int splits, GemmConfig*
       ++splits;
     }
   }
-  if (reduces_in_kernel(kTiles[idx].kind)) {
-    // K-blocks per split: a multiple of the unrolled loop (then the scale byte, LDS
-    // stage and weight registers of a K-block are static), at most four per word
-    // of the scale table
-    const int un = kTiles[idx].stages == 3 ? 12 : 4;
-    if (splits > kDecodeMaxSplits) splits = kDecodeMaxSplits;
-    int per = (int)cdiv(cdiv(KB, splits), un) * un;
+  if (is_decode(kTiles[idx].kind)) {
+    // K-blocks per split: a multiple of four (whole words of packed scales, so the
+    // scale byte of every unrolled iteration is static), at most four per word of
+    // the scale table
+    const bool in_kernel = reduces_in_kernel(kTiles[idx].kind);
+    const int max_splits = in_kernel ? kDecodeMaxSplits : kDecodeSepMaxSplits;
+    if (splits > max_splits) splits = max_splits;
+    int per = (int)cdiv(cdiv(KB, splits), 4) * 4;
     if (per > 4 * kTiles[idx].max_wd) {
       if (p.masked_m) return false;
-      per = 4 * kTiles[idx].max_wd / un * un;
+      per = 4 * kTiles[idx].max_wd;
     }
     const int64_t tiles = cdiv(p.M, kTiles[idx].bm) * cdiv(p.N, kTiles[idx].bn);
     if (cdiv(KB, per) > 1 &&
-        (cdiv(KB, per) > kDecodeMaxSplits || tiles > kCounterBytes / 4 ||
+        (cdiv(KB, per) > max_splits || (in_kernel && tiles > kCounterBytes / 4) ||
          cdiv(KB, per) * p.M * p.N * 4 > 0x7FFFFFFF))
       return false;
     out->kernel = idx;
@@ -1689,6 +1749,16 @@ bool gemm_config_by_index(int idx, const GemmProblem& p, int splits, GemmConfig*
 GemmConfig choose_gemm_config(const GemmProblem& p) {
   GemmConfig cfg;
   const int KB = (int)(p.K / 128);
+  if (p.b_shuffled) {
+    // pre-shuffled weights: the decode kernel, K split until about 224 workgroups and
+    // reduced by the last split of each tile (a separate reduction kernel measured
+    // within run-to-run noise of it at the decode shape)
+    const int64_t tiles = cdiv(p.M, kTiles[kCfgShufDecode64x128].bm) * cdiv(p.N, kTiles[kCfgShufDecode64x128].bn);
+    int splits = (int)(224 / (tiles > 0 ? tiles : 1));
+    if (splits < 1) splits = 1;
+    if (!gemm_config_by_index(kCfgShufDecode64x128, p, splits, &cfg)) cfg.kernel = -1;
+    return cfg;
+  }
   if (p.float_scales) {
     // float-scale format: VALU-scaled tiles; small M splits K until about 224
     // workgroups, large M takes 128 x 256 tiles once they fill the compute units
@@ -1832,6 +1902,7 @@ hipError_t launch_gemm(const GemmProblem& p, const GemmConfig& cfg, void* ws, hi
   k.groups = p.groups;
   k.sfa_f = p.float_scales ? reinterpret_cast<const float*>(p.sfa) : nullptr;
   if (p.float_scales != reads_float_scales(t.kind)) return hipErrorInvalidValue;
+  if (p.b_shuffled != reads_shuffled(t.kind)) return hipErrorInvalidValue;
   if (p.m_indices && (p.E != 1 || p.masked_m || cfg.splits != 1 || kContiguousAlign % t.bm != 0))
     return hipErrorInvalidValue;
   k.M = p.M; k.N = p.N; k.K = p.K; k.ld_sfa = p.ld_sfa; k.ldc = p.ldc;
@@ -1845,9 +1916,10 @@ hipError_t launch_gemm(const GemmProblem& p, const GemmConfig& cfg, void* ws, hi
   k.ws = nullptr;
   k.counters = nullptr;
   if (cfg.splits > 1) {
-    // workspace: the arrival counters (zero between calls), then the fp32 partials
+    // workspace: the arrival counters (zero between calls), then the fp32 partials;
+    // only the kernels that reduce their own split use the counters
     if (ws == nullptr) return hipErrorInvalidValue;
-    k.counters = static_cast<uint32_t*>(ws);
+    k.counters = reduces_in_kernel(t.kind) ? static_cast<uint32_t*>(ws) : nullptr;
     k.ws = reinterpret_cast<float*>(static_cast<char*>(ws) + kCounterBytes);
   }
   k.sa_words = (cfg.kb_per_split + 3) / 4 + 1;

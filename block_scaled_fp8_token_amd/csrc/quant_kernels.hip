@@ -428,4 +428,32 @@ hipError_t launch_block_quant(const uint16_t* w, int64_t N, int64_t K, uint8_t* 
   return hipGetLastError();
 }
 
+// Pre-shuffled weight layout: thread t moves the 16 bytes of output chunk t.  With
+// t = ((g * KB + kb) * 4 + q) * 64 + l, the chunk holds row 32 g + (l & 31), bytes
+// 128 kb + 64 (q >> 1) + 32 (l >> 5) + 16 (q & 1) .. + 15: the bytes lane l of a
+// wavefront loads with its q-th 16-byte load of K-block kb for the 32 x 64 operands
+// of two scaled MFMAs, so that every such load reads 1 KB of contiguous memory.
+__global__ __launch_bounds__(256) void weight_preshuffle_kernel(const uint8_t* __restrict__ w,
+                                                                uint8_t* __restrict__ out, int64_t rows,
+                                                                int64_t K) {
+  const int64_t KB = K / 128;
+  const int64_t chunks = rows * (K / 16);
+  for (int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x; t < chunks; t += (int64_t)gridDim.x * 256) {
+    const int l = (int)(t & 63), q = (int)((t >> 6) & 3);
+    const int64_t gk = t >> 8, g = gk / KB, kb = gk - g * KB;
+    const int64_t row = 32 * g + (l & 31);
+    const int64_t col = 128 * kb + 64 * (q >> 1) + 32 * (l >> 5) + 16 * (q & 1);
+    *reinterpret_cast<uint4*>(out + 16 * t) = *reinterpret_cast<const uint4*>(w + row * K + col);
+  }
+}
+
+hipError_t launch_weight_preshuffle(const uint8_t* w, int64_t rows, int64_t K, uint8_t* out, hipStream_t stream) {
+  const int64_t chunks = rows * (K / 16);
+  if (chunks < 1) return hipSuccess;
+  int64_t blocks = (chunks + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(weight_preshuffle_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, w, out, rows, K);
+  return hipGetLastError();
+}
+
 }  // namespace fp8bs

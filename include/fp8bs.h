@@ -170,6 +170,30 @@ int fp8_block_gemm_nt(const void* a, const uint32_t* sfa, int64_t ld_sfa, const 
                       void* stream);
 
 /*
+ * Offline weight layout for the decode GEMM.  The weights of a block-scaled GEMM
+ * are prepared once, outside the timed step (benchmark post section 4.1 quantizes
+ * B before timing); this library's own pre-shuffled layout is a byte permutation
+ * of the e4m3 weights [rows][K] (same size) in which every 16-byte load of the
+ * decode kernel reads one contiguous kilobyte:
+ *   out[((g * KB + kb) * 4 + q) * 1024 + l * 16 + i]
+ *     = w[32 g + (l & 31)][128 kb + 64 (q >> 1) + 32 (l >> 5) + 16 (q & 1) + i]
+ * for g < rows/32, kb < KB = K/128, q < 4, l < 64, i < 16.  The block scales are
+ * unchanged.  Expert weights [E][N][K] are shuffled as rows = E*N.
+ *   w, out : device, 16-byte aligned, not overlapping;  rows % 32 == 0, K % 128 == 0.
+ */
+int fp8_weight_preshuffle(const void* w, int64_t rows, int64_t K, void* out, void* stream);
+
+/*
+ * fp8_block_gemm_nt with the weights b in the layout of fp8_weight_preshuffle
+ * (rows = N); every other argument, the result and the workspace rules are those
+ * of fp8_block_gemm_nt.  Meant for decode-sized M (each 64-row tile of A streams
+ * all the weights once).
+ */
+int fp8_block_gemm_nt_preshuffled(const void* a, const uint32_t* sfa, int64_t ld_sfa, const void* b,
+                                  const float* sfb, void* c, int64_t ldc, int64_t M, int64_t N,
+                                  int64_t K, void* stream);
+
+/*
  * Masked grouped GEMM (PR #19111: m_grouped GEMM, masked, over [E, max_tokens, K]
  * with per-expert valid counts; 128x128 blocks).  For each expert e and row
  * r < clamp(masked_m[e], 0, M_max), row r of C[e] is the dense NT result of
@@ -209,8 +233,9 @@ int fp8_block_gemm_grouped_contiguous(const void* a, const uint32_t* sfa, int64_
 /*
  * Tile-table access, for tuning and for tests that cover every compiled tile
  * shape.  fp8bs_gemm_config reports what the automatic choice would be for a
- * dense (masked = 0), masked (masked = 1), contiguous grouped (masked = 2) or
- * dense float-scale (masked = 3) problem: kernel index into the tile
+ * dense (masked = 0), masked (masked = 1), contiguous grouped (masked = 2),
+ * dense float-scale (masked = 3) or dense pre-shuffled-weight (masked = 4)
+ * problem: kernel index into the tile
  * table, workgroup tile bm x bn, and the number of K splits.  The _cfg variants
  * run the same GEMMs with an explicit kernel index and split count (splits is
  * clamped to [1, K/128]; the masked and contiguous forms use splits == 1 only, and
@@ -220,7 +245,8 @@ int fp8bs_gemm_config_count(void);
 int fp8bs_gemm_config(int masked, int64_t M, int64_t N, int64_t K, int32_t* kernel, int32_t* bm,
                       int32_t* bn, int32_t* splits);
 /* Whether table entry `kernel` accepts a dense (masked = 0), masked (masked = 1),
- * contiguous grouped (masked = 2) or dense float-scale (masked = 3) problem of this
+ * contiguous grouped (masked = 2), dense float-scale (masked = 3) or dense
+ * pre-shuffled-weight (masked = 4) problem of this
  * shape with `splits` K splits: FP8BS_OK with its workgroup tile and the split count
  * it would use, FP8BS_ERR_SHAPE if it does not (for instance K past the entry's scale
  * tables, a masked problem that would need K splits, or a scale format the entry does
@@ -241,6 +267,9 @@ int fp8_block_gemm_grouped_contiguous_cfg(const void* a, const uint32_t* sfa, in
 int fp8_block_gemm_nt_float_scales_cfg(const void* a, const float* sfa, int64_t ld_sfa, const void* b,
                                        const float* sfb, void* c, int64_t ldc, int64_t M, int64_t N,
                                        int64_t K, int32_t kernel, int32_t splits, void* stream);
+int fp8_block_gemm_nt_preshuffled_cfg(const void* a, const uint32_t* sfa, int64_t ld_sfa, const void* b,
+                                      const float* sfb, void* c, int64_t ldc, int64_t M, int64_t N,
+                                      int64_t K, int32_t kernel, int32_t splits, void* stream);
 
 /* Status helpers. */
 const char* fp8bs_status_string(int status);

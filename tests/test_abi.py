@@ -145,6 +145,34 @@ def test_float_scale_validation():
     assert g(A, S, 64, B, T, C, 512, 0, 512, 512, None) == OK
 
 
+def test_preshuffle_validation():
+    f = F._lib.fp8_weight_preshuffle
+    assert f(A, 48, 512, B, None) == ERR_SHAPE      # rows % 32
+    assert f(A, 64, 500, B, None) == ERR_SHAPE      # K % 128
+    assert f(A, -32, 512, B, None) == ERR_SHAPE
+    assert f(None, 64, 512, B, None) == ERR_NULL
+    assert f(A, 64, 512, None, None) == ERR_NULL
+    assert f(A + 8, 64, 512, B, None) == ERR_ALIGN
+    assert f(A, 0, 512, B, None) == OK and f(None, 0, 512, None, None) == OK
+    g = F._lib.fp8_block_gemm_nt_preshuffled
+    assert g(A, S, 64, B, T, C, 512, 64, 96, 512, None) == ERR_SHAPE   # N % 64
+    assert g(A, S, 64, B, T, C, 512, 64, 512, 500, None) == ERR_SHAPE  # K % 128
+    assert g(None, S, 64, B, T, C, 512, 64, 512, 512, None) == ERR_NULL
+    assert g(A, S, 64, B + 8, T, C, 512, 64, 512, 512, None) == ERR_ALIGN
+    assert g(A, S, 64, B, T, C, 512, 0, 512, 512, None) == OK
+
+
+def test_preshuffled_config_uses_shuffled_entries_only():
+    cfg = F.gemm_config(F.LAYOUT_DENSE_PRESHUFFLED, 64, 7168, 18432)
+    assert cfg["kernel"] >= 0 and cfg["splits"] >= 1
+    for k in range(F.gemm_config_count()):
+        plain = F.gemm_config_of(k, F.LAYOUT_DENSE, 64, 7168, 18432, 4)
+        shuf = F.gemm_config_of(k, F.LAYOUT_DENSE_PRESHUFFLED, 64, 7168, 18432, 4)
+        assert plain is None or shuf is None  # no entry reads both layouts
+    assert F.gemm_config_of(cfg["kernel"], F.LAYOUT_DENSE, 64, 7168, 18432, 4) is None
+    assert F.gemm_config_of(cfg["kernel"], F.LAYOUT_MASKED, 64, 7168, 18432, 1) is None
+
+
 def test_config_table_choices():
     n = F.gemm_config_count()
     assert n >= 2
@@ -170,11 +198,17 @@ def test_config_of_table_entries():
         e = F.gemm_config_of(c["kernel"], masked, M, N, K, c["splits"])
         assert e is not None and (e["bm"], e["bn"], e["splits"]) == (c["bm"], c["bn"], c["splits"])
     fl = [k for k in range(n) if F.gemm_config_of(k, F.LAYOUT_DENSE_FLOAT, 72, 192, 384) is not None]
-    assert fl and all(F.gemm_config_of(k, True, 72, 192, 384) is not None for k in range(n) if k not in fl)
+    sh = [k for k in range(n) if F.gemm_config_of(k, F.LAYOUT_DENSE_PRESHUFFLED, 72, 192, 384) is not None]
+    assert fl and sh and not set(fl) & set(sh)
+    assert all(F.gemm_config_of(k, True, 72, 192, 384) is not None for k in range(n) if k not in fl + sh)
+    # the pre-shuffled entries read only that layout (dense calls)
+    assert all(F.gemm_config_of(k, False, 72, 192, 384) is None and F.gemm_config_of(k, True, 72, 192, 384) is None
+               for k in sh)
     # the float-scale entries read only the float format, the others only the packed one
     assert all(F.gemm_config_of(k, False, 72, 192, 384) is None and F.gemm_config_of(k, True, 72, 192, 384) is None
                for k in fl)
     assert all(F.gemm_config_of(k, F.LAYOUT_DENSE_FLOAT, 72, 192, 384) is None for k in range(n) if k not in fl)
+    assert all(F.gemm_config_of(k, F.LAYOUT_DENSE_PRESHUFFLED, 72, 192, 384) is None for k in range(n) if k not in sh)
     for M in (8, 64, 4096):
         assert F.gemm_config(F.LAYOUT_DENSE_FLOAT, M, 7168, 7168)["kernel"] in fl
     long_k = [F.gemm_config_of(k, True, 256, 4096, 128 * 1024) for k in range(n)]
