@@ -298,7 +298,14 @@ def bench_dense_float(F, stream, shape, steps, warmup):
     return r
 
 
-def bench_masked_gate_up(F, W, stream, steps, warmup):
+def _preshuffle_copies(F, copies):
+    """Weight copies in the pre-shuffled layout (offline, outside timing)."""
+    out = [(F.fp8_weight_preshuffle(qb), sfb) for qb, sfb in copies]
+    torch.cuda.synchronize()
+    return out
+
+
+def bench_masked_gate_up(F, W, stream, steps, warmup, preshuffled=False):
     E, M_max, N, K = W.MOE_E, W.MOE_M_MAX, W.MOE_GATE_UP["N"], W.MOE_GATE_UP["K"]
     counts = torch.from_numpy(W.zipf_counts()).to("cuda")
     S = int(counts.clamp(0, M_max).sum())
@@ -310,21 +317,24 @@ def bench_masked_gate_up(F, W, stream, steps, warmup):
     sfa = sfa_flat.view(Wd, E, M_max).permute(1, 0, 2).contiguous()
     del x
     copies = quantized_weights(F, n_copies_for(E * N * K, floor=1), N, K, 21, experts=E)
+    if preshuffled:
+        copies = _preshuffle_copies(F, copies)
     nv = len(copies)
     c = torch.empty((E, M_max, N), dtype=torch.bfloat16, device="cuda")
 
     def gemm(s):
         qb, sfb = copies[s % nv]
-        F.fp8_block_gemm_grouped_masked(a, sfa, qb, sfb, counts, c=c, stream=stream)
+        F.fp8_block_gemm_grouped_masked(a, sfa, qb, sfb, counts, c=c, stream=stream, preshuffled=preshuffled)
 
     with torch.cuda.stream(stream):
         for i in range(warmup):
             gemm(i)
     (t,) = kernel_times(stream, [gemm], steps)
-    r = {"workload": "moe_gate_up_masked_E32_Mmax256_N4096_K7168", "S": S, "E_active": E_active,
+    r = {"workload": "moe_gate_up_masked_E32_Mmax256_N4096_K7168" + ("_preshuffled" if preshuffled else ""),
+         "S": S, "E_active": E_active,
          "gemm_us": t * 1e3, "gemm_tflops": masked_flops(S, N, K) / (t * 1e-3) / 1e12,
          "gemm_gbs": masked_bytes(S, E_active, N, K) / (t * 1e-3) / 1e9, "weight_copies": nv,
-         "config": F.gemm_config(True, M_max, N, K)}
+         "config": F.gemm_config(F.LAYOUT_MASKED_PRESHUFFLED if preshuffled else F.LAYOUT_MASKED, M_max, N, K)}
     r["frac_hbm"] = r["gemm_gbs"] / HBM_PEAK_GBS
     r["frac_mfma"] = r["gemm_tflops"] / FP8_PEAK_TFLOPS
     del copies, a, sfa, c
@@ -399,7 +409,7 @@ def bench_dispatch_quant(F, W, stream, steps, warmup):
     return r
 
 
-def bench_silu_down(F, W, stream, steps, warmup):
+def bench_silu_down(F, W, stream, steps, warmup, preshuffled=False):
     E, M_max, H, N = W.MOE_E, W.MOE_M_MAX, W.MOE_DOWN["H"], W.MOE_DOWN["N"]
     K = H
     counts = torch.from_numpy(W.zipf_counts()).to("cuda")
@@ -407,6 +417,8 @@ def bench_silu_down(F, W, stream, steps, warmup):
     E_active = int((counts > 0).sum())
     x = randn_bf16((E, M_max, 2 * H), seed=31)
     copies = quantized_weights(F, n_copies_for(E * N * K, floor=1), N, K, 41, experts=E)
+    if preshuffled:
+        copies = _preshuffle_copies(F, copies)
     nv = len(copies)
     q = torch.empty((E, M_max, H), dtype=torch.uint8, device="cuda")
     sf = torch.empty((E, (H // 128 + 3) // 4, M_max), dtype=torch.int32, device="cuda")
@@ -417,14 +429,15 @@ def bench_silu_down(F, W, stream, steps, warmup):
 
     def gemm(s):
         qb, sfb = copies[s % nv]
-        F.fp8_block_gemm_grouped_masked(q, sf, qb, sfb, counts, c=c, stream=stream)
+        F.fp8_block_gemm_grouped_masked(q, sf, qb, sfb, counts, c=c, stream=stream, preshuffled=preshuffled)
 
     with torch.cuda.stream(stream):
         for i in range(warmup):
             silu(i)
             gemm(i)
     t_silu, t_gemm = kernel_times(stream, [silu, gemm], steps)
-    r = {"workload": "moe_silu_quant_then_down_masked_E32_Mmax256_H2048_N7168", "S": S,
+    r = {"workload": "moe_silu_quant_then_down_masked_E32_Mmax256_H2048_N7168" + ("_preshuffled" if preshuffled else ""),
+         "S": S, "config": F.gemm_config(F.LAYOUT_MASKED_PRESHUFFLED if preshuffled else F.LAYOUT_MASKED, M_max, N, K),
          "silu_us": t_silu * 1e3, "silu_gbs": silu_bytes(S, H) / (t_silu * 1e-3) / 1e9,
          "gemm_us": t_gemm * 1e3, "gemm_tflops": masked_flops(S, N, K) / (t_gemm * 1e-3) / 1e12,
          "gemm_gbs": masked_bytes(S, E_active, N, K) / (t_gemm * 1e-3) / 1e9, "weight_copies": nv}
@@ -558,12 +571,14 @@ def main():
         rows = [r, plain]
         rows.append(bench_dense(F, stream, W.DENSE_SMALL, args.steps, args.warmup))
         for s in W.DENSE_PREFILL:
-            rows.append(bench_dense(F, stream, s, max(10, args.steps // 4), args.warmup))
+            for pre in (False, True):
+                rows.append(bench_dense(F, stream, s, max(10, args.steps // 4), args.warmup, preshuffled=pre))
+                print("[bench] %s" % json.dumps(rows[-1]), file=sys.stderr, flush=True)
+        for pre in (False, True):
+            rows.append(bench_masked_gate_up(F, W, stream, max(10, args.steps // 4), args.warmup, preshuffled=pre))
             print("[bench] %s" % json.dumps(rows[-1]), file=sys.stderr, flush=True)
-        rows.append(bench_masked_gate_up(F, W, stream, max(10, args.steps // 4), args.warmup))
-        print("[bench] %s" % json.dumps(rows[-1]), file=sys.stderr, flush=True)
-        rows.append(bench_silu_down(F, W, stream, max(10, args.steps // 4), args.warmup))
-        print("[bench] %s" % json.dumps(rows[-1]), file=sys.stderr, flush=True)
+            rows.append(bench_silu_down(F, W, stream, max(10, args.steps // 4), args.warmup, preshuffled=pre))
+            print("[bench] %s" % json.dumps(rows[-1]), file=sys.stderr, flush=True)
         rows.append(bench_contiguous_gate_up(F, W, stream, max(10, args.steps // 4), args.warmup))
         print("[bench] %s" % json.dumps(rows[-1]), file=sys.stderr, flush=True)
         rows.append(bench_dispatch_quant(F, W, stream, args.steps, args.warmup))

@@ -25,7 +25,7 @@ __all__ = [
     "library_path", "header_path", "declared_functions", "gemm_config_of",
     "fp8_quant_group_pack_to_experts", "fp8_block_gemm_grouped_contiguous",
     "fp8_quant_group_float", "fp8_block_quant_128x128_float", "fp8_block_gemm_nt_float_scales",
-    "fp8_weight_preshuffle", "fp8_block_gemm_nt_preshuffled",
+    "fp8_weight_preshuffle", "fp8_block_gemm_nt_preshuffled", "fp8_block_gemm_grouped_masked_preshuffled",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -57,6 +57,8 @@ _SIGS = {
     "fp8_weight_preshuffle": [_P, _I64, _I64, _P, _P],
     "fp8_block_gemm_nt_preshuffled": [_P, _P, _I64, _P, _P, _P, _I64, _I64, _I64, _I64, _P],
     "fp8_block_gemm_nt_preshuffled_cfg": [_P, _P, _I64, _P, _P, _P, _I64, _I64, _I64, _I64, _I32, _I32, _P],
+    "fp8_block_gemm_grouped_masked_preshuffled": [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _P],
+    "fp8_block_gemm_grouped_masked_preshuffled_cfg": [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I32, _P],
     "fp8_block_gemm_grouped_masked": [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _P],
     "fp8_block_gemm_grouped_masked_cfg": [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I32, _P],
     "fp8_block_gemm_grouped_contiguous": [_P, _P, _I64, _P, _P, _P, _I64, _P, _I64, _I64, _I64, _I64, _P],
@@ -337,9 +339,10 @@ def fp8_block_gemm_nt_preshuffled(a: torch.Tensor, sfa: torch.Tensor, b: torch.T
 
 def fp8_block_gemm_grouped_masked(a: torch.Tensor, sfa: torch.Tensor, b: torch.Tensor, sfb: torch.Tensor,
                                   masked_m: torch.Tensor, c: torch.Tensor | None = None,
-                                  kernel: int | None = None, stream=None) -> torch.Tensor:
+                                  kernel: int | None = None, stream=None, preshuffled: bool = False) -> torch.Tensor:
     """Masked grouped GEMM -> bf16 [E, M_max, N].  a uint8 [E, M_max, K], sfa int32 [E, ceil(K/512), M_max],
-    b uint8 [E, N, K], sfb float32 [E, ceil(N/128), K/128], masked_m int32 [E]."""
+    b uint8 [E, N, K], sfb float32 [E, ceil(N/128), K/128], masked_m int32 [E].  preshuffled: b is in the
+    layout of fp8_weight_preshuffle (fp8_block_gemm_grouped_masked_preshuffled)."""
     for t, n in ((a, "a"), (b, "b")):
         _expect(t, n, _E4M3, 3)
         _contig(t, n)
@@ -357,15 +360,21 @@ def fp8_block_gemm_grouped_masked(a: torch.Tensor, sfa: torch.Tensor, b: torch.T
     _expect(c, "c", _BF16, 3)
     _contig(c, "c")
     s = _stream(stream)
+    name = "fp8_block_gemm_grouped_masked" + ("_preshuffled" if preshuffled else "")
+    args = (a.data_ptr(), sfa.data_ptr(), b.data_ptr(), sfb.data_ptr(), c.data_ptr(), masked_m.data_ptr(),
+            E, M_max, N, K)
     if kernel is None:
-        st = _lib.fp8_block_gemm_grouped_masked(a.data_ptr(), sfa.data_ptr(), b.data_ptr(), sfb.data_ptr(),
-                                                c.data_ptr(), masked_m.data_ptr(), E, M_max, N, K, s)
+        st = getattr(_lib, name)(*args, s)
     else:
-        st = _lib.fp8_block_gemm_grouped_masked_cfg(a.data_ptr(), sfa.data_ptr(), b.data_ptr(), sfb.data_ptr(),
-                                                    c.data_ptr(), masked_m.data_ptr(), E, M_max, N, K,
-                                                    int(kernel), s)
-    _check("fp8_block_gemm_grouped_masked", st)
+        st = getattr(_lib, name + "_cfg")(*args, int(kernel), s)
+    _check(name, st)
     return c
+
+
+def fp8_block_gemm_grouped_masked_preshuffled(a, sfa, b, sfb, masked_m, c=None, kernel=None, stream=None):
+    """fp8_block_gemm_grouped_masked with b [E, N, K] in the pre-shuffled layout."""
+    return fp8_block_gemm_grouped_masked(a, sfa, b, sfb, masked_m, c=c, kernel=kernel, stream=stream,
+                                         preshuffled=True)
 
 
 def fp8_block_gemm_grouped_contiguous(a: torch.Tensor, sfa: torch.Tensor, b: torch.Tensor, sfb: torch.Tensor,
@@ -403,7 +412,8 @@ def fp8_block_gemm_grouped_contiguous(a: torch.Tensor, sfa: torch.Tensor, b: tor
     return c
 
 
-LAYOUT_DENSE, LAYOUT_MASKED, LAYOUT_CONTIGUOUS, LAYOUT_DENSE_FLOAT, LAYOUT_DENSE_PRESHUFFLED = 0, 1, 2, 3, 4
+(LAYOUT_DENSE, LAYOUT_MASKED, LAYOUT_CONTIGUOUS, LAYOUT_DENSE_FLOAT, LAYOUT_DENSE_PRESHUFFLED,
+ LAYOUT_MASKED_PRESHUFFLED) = 0, 1, 2, 3, 4, 5
 
 
 def fp8_quant_group_float(x: torch.Tensor, q: torch.Tensor | None = None, sf: torch.Tensor | None = None,

@@ -189,10 +189,15 @@ fp8bs::GemmProblem contiguous_problem(const void* a, const uint32_t* sfa, int64_
 
 // A problem of the given layout (0 dense, 1 masked, 2 contiguous) for host-side
 // configuration queries only: its pointers are placeholders that are never read.
-// (3: dense with float scales, 4: dense with pre-shuffled weights)
+// (3: dense with float scales, 4: dense with pre-shuffled weights, 5: masked with
+// pre-shuffled weights)
 fp8bs::GemmProblem host_problem(int layout, int64_t M, int64_t N, int64_t K) {
   static const int32_t placeholder = 0;
-  if (layout == 1) return masked_problem(nullptr, nullptr, nullptr, nullptr, nullptr, &placeholder, 1, M, N, K);
+  if (layout == 1 || layout == 5) {
+    fp8bs::GemmProblem p = masked_problem(nullptr, nullptr, nullptr, nullptr, nullptr, &placeholder, 1, M, N, K);
+    p.b_shuffled = layout == 5;
+    return p;
+  }
   if (layout == 2)
     return contiguous_problem(nullptr, nullptr, M, nullptr, nullptr, nullptr, N, &placeholder, 1, M, N, K);
   fp8bs::GemmProblem p = dense_problem(nullptr, nullptr, M, nullptr, nullptr, nullptr, N, M, N, K);
@@ -365,6 +370,35 @@ int fp8_block_gemm_nt_preshuffled_cfg(const void* a, const uint32_t* sfa, int64_
   return run_gemm(p, cfg, static_cast<hipStream_t>(stream));
 }
 
+int fp8_block_gemm_grouped_masked_preshuffled(const void* a, const uint32_t* sfa, const void* b, const float* sfb,
+                                              void* c, const int32_t* masked_m, int64_t E, int64_t M_max, int64_t N,
+                                              int64_t K, void* stream) {
+  int st = check_masked(a, sfa, b, sfb, c, masked_m, E, M_max, N, K);
+  if (st != FP8BS_OK) return st > 0 ? FP8BS_OK : st;
+  st = check_device();
+  if (st != FP8BS_OK) return st;
+  fp8bs::GemmProblem p = masked_problem(a, sfa, b, sfb, c, masked_m, E, M_max, N, K);
+  p.b_shuffled = true;
+  const fp8bs::GemmConfig cfg = fp8bs::choose_gemm_config(p);
+  if (cfg.kernel < 0) return FP8BS_ERR_SHAPE;
+  return run_gemm(p, cfg, static_cast<hipStream_t>(stream));
+}
+
+int fp8_block_gemm_grouped_masked_preshuffled_cfg(const void* a, const uint32_t* sfa, const void* b,
+                                                  const float* sfb, void* c, const int32_t* masked_m, int64_t E,
+                                                  int64_t M_max, int64_t N, int64_t K, int32_t kernel,
+                                                  void* stream) {
+  int st = check_masked(a, sfa, b, sfb, c, masked_m, E, M_max, N, K);
+  if (st != FP8BS_OK) return st > 0 ? FP8BS_OK : st;
+  st = check_device();
+  if (st != FP8BS_OK) return st;
+  fp8bs::GemmProblem p = masked_problem(a, sfa, b, sfb, c, masked_m, E, M_max, N, K);
+  p.b_shuffled = true;
+  fp8bs::GemmConfig cfg;
+  if (!fp8bs::gemm_config_by_index(kernel, p, 1, &cfg)) return FP8BS_ERR_SHAPE;
+  return run_gemm(p, cfg, static_cast<hipStream_t>(stream));
+}
+
 int fp8_block_gemm_grouped_masked(const void* a, const uint32_t* sfa, const void* b, const float* sfb, void* c,
                                   const int32_t* masked_m, int64_t E, int64_t M_max, int64_t N, int64_t K,
                                   void* stream) {
@@ -445,7 +479,7 @@ int fp8bs_gemm_config(int masked, int64_t M, int64_t N, int64_t K, int32_t* kern
                       int32_t* splits) {
   if (M < 0 || N < 0 || K < 128 || K % 128 != 0 || N % 64 != 0) return FP8BS_ERR_SHAPE;
   if (!kernel || !bm || !bn || !splits) return FP8BS_ERR_NULL;
-  if (masked < 0 || masked > 4) return FP8BS_ERR_SHAPE;
+  if (masked < 0 || masked > 5) return FP8BS_ERR_SHAPE;
   const fp8bs::GemmProblem p = host_problem(masked, M, N, K);
   const fp8bs::GemmConfig cfg = fp8bs::choose_gemm_config(p);
   *kernel = cfg.kernel;
@@ -459,7 +493,7 @@ int fp8bs_gemm_config_of(int32_t kernel, int masked, int64_t M, int64_t N, int64
                          int32_t* bn, int32_t* splits_out) {
   if (M < 0 || N < 0 || K < 128 || K % 128 != 0 || N % 64 != 0) return FP8BS_ERR_SHAPE;
   if (!bm || !bn || !splits_out) return FP8BS_ERR_NULL;
-  if (masked < 0 || masked > 4) return FP8BS_ERR_SHAPE;
+  if (masked < 0 || masked > 5) return FP8BS_ERR_SHAPE;
   const fp8bs::GemmProblem p = host_problem(masked, M, N, K);
   fp8bs::GemmConfig cfg;
   if (!fp8bs::gemm_config_by_index(kernel, p, splits < 1 ? 1 : splits, &cfg)) return FP8BS_ERR_SHAPE;

@@ -833,7 +833,7 @@ __device__ __forceinline__ void mfma_read_dma_pattern() {
   }
 }
 
-template <int BM, int BN, int WGM, int WGN>
+template <int BM, int BN, int WGM, int WGN, bool SHUF = false>
 __global__ __launch_bounds__(256) void scaled_ring_kernel(const KArgs p) {
   using R = RingShape<BM, BN, WGM, WGN>;
   constexpr int S = kRingSlots;
@@ -894,17 +894,27 @@ __global__ __launch_bounds__(256) void scaled_ring_kernel(const KArgs p) {
   // offset serves all instructions (the row base is added per instruction, which
   // keeps eight registers free for the loop).
   const uint32_t lane_off = (uint32_t)((lane >> 2) * p.K) + (uint32_t)((((lane & 3) ^ ((lane >> 4) & 3)) << 4));
+  // SHUF: weights in the pre-shuffled layout, where chunk c of a K-half of row r (of
+  // 32-row group g) is 16-byte chunk 32 (c >> 1) + (r & 31) of load 2 hh + (c & 1) of
+  // its K-block: the 16 rows x 4 chunks of one instruction are four contiguous 256-byte
+  // runs.  Per lane: chunk c = (l & 3) ^ swizzle, row 16 ri + (l >> 2); per instruction:
+  // group ri >> 1, half-group (ri & 1) * 256; per K-half h: K-block h >> 1, hh = h & 1.
+  const int cB = (lane & 3) ^ ((lane >> 4) & 3);
+  const uint32_t lane_off_b = SHUF ? (uint32_t)((cB & 1) * 1024 + (32 * (cB >> 1) + (lane >> 2)) * 16) : lane_off;
   auto issue = [&](int h, auto sl_tag) {
     uint8_t* base = slot(sl_tag);
     // past the last K-half the offset gets the top bit: out of range, zero-filled
     // (an OR rather than a select keeps the loop body free of branches)
     const uint32_t hoff = (uint32_t)h * 64u, oob = h < 2 * KB ? 0u : kOOB;
+    const uint32_t hoff_b = SHUF ? (uint32_t)(h >> 1) * 4096u + (uint32_t)(h & 1) * 2048u : hoff;
 #pragma unroll
     for (int t = 0; t < IPW; ++t) {
       const bool isA = t < IPA;  // static after unrolling
       const int ri = isA ? wave * IPA + t : wave * R::IPB + (t - IPA);
       uint8_t* dst = base + (isA ? 0 : BM * 64) + ri * 1024;
-      const uint32_t off = (lane_off + (uint32_t)(ri * 16 * p.K) + hoff) | oob;
+      const uint32_t off =
+          (isA || !SHUF) ? (lane_off + (uint32_t)(ri * 16 * p.K) + hoff) | oob
+                         : (lane_off_b + (uint32_t)((ri >> 1) * KB * 4096 + (ri & 1) * 256) + hoff_b) | oob;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(isA ? rA : rB, (__attribute__((address_space(3))) void*)dst, 16,
                                                (int)off, 0, 0, 0);
     }
@@ -1576,7 +1586,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const KArgs p) {
 typedef void (*KernelFn)(const KArgs);
 
 enum Kind { kTile = 0, kStream = 1, kScaled = 2, kRing = 3, kDecode = 4, kTileFloat = 5, kDecodeFloat = 6,
-            kScaledFloat = 7, kDecodeSep = 8, kDecodeShuf = 9, kDecodeShufSep = 10 };
+            kScaledFloat = 7, kDecodeSep = 8, kDecodeShuf = 9, kDecodeShufSep = 10, kRingShuf = 11 };
 
 // Entries that read the float-scale format.
 inline bool reads_float_scales(int kind) {
@@ -1587,7 +1597,9 @@ inline bool is_scaled_tile(int kind) { return kind == kScaled || kind == kScaled
 // Entries that reduce their own K split (arrival counters in the workspace).
 inline bool reduces_in_kernel(int kind) { return kind == kDecode || kind == kDecodeFloat || kind == kDecodeShuf; }
 // Entries that read the weights in the pre-shuffled layout.
-inline bool reads_shuffled(int kind) { return kind == kDecodeShuf || kind == kDecodeShufSep; }
+inline bool reads_shuffled(int kind) { return kind == kDecodeShuf || kind == kDecodeShufSep || kind == kRingShuf; }
+// Ring entries (K never split; the scale tables bound K).
+inline bool is_ring(int kind) { return kind == kRing || kind == kRingShuf; }
 // Decode-kernel entries (K split in whole scale words; kDecodeSep leaves the sum of
 // the partials to splitk_reduce_kernel).
 inline bool is_decode(int kind) { return reduces_in_kernel(kind) || kind == kDecodeSep || kind == kDecodeShufSep; }
@@ -1644,6 +1656,9 @@ const TileEntry kTiles[] = {
     {decode_kernel<4, 3, false, true>, 64, 128, kDecodeShuf, 3, 256, DecodeShape<4, 3>::WMAX},
     {decode_kernel<4, 3, false, true>, 64, 128, kDecodeShufSep, 3, 256, DecodeShape<4, 3>::WMAX},
     {decode_kernel<8, 3, false, true>, 64, 256, kDecodeShufSep, 3, 512, DecodeShape<8, 3>::WMAX},
+    {scaled_ring_kernel<256, 256, 1, 4, true>, 256, 256, kRingShuf, 4, 256, ring_wd_max<256, 256, 1, 4>()},
+    {scaled_ring_kernel<256, 256, 2, 2, true>, 256, 256, kRingShuf, 4, 256, ring_wd_max<256, 256, 2, 2>()},
+    {scaled_ring_kernel<128, 256, 2, 2, true>, 128, 256, kRingShuf, 4, 256, ring_wd_max<128, 256, 2, 2>()},
 };
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 // table entries the automatic choice uses
@@ -1661,8 +1676,11 @@ constexpr int kCfgFloatScaled128x128 = 31; // LDS-DMA tiles, float scales
 constexpr int kCfgFloatScaled128x256 = 32;
 constexpr int kCfgDecode64x128 = 22;       // decode kernel, 4 wavefronts, three K-blocks in flight
 constexpr int kCfgShufDecode64x128 = 35;   // the same on pre-shuffled weights
+constexpr int kCfgShufRing256x256Rows = 38;  // pre-shuffled weights: ring 256x256, 1 x 4 wavefronts
+constexpr int kCfgShufRing256x256 = 39;      // 2 x 2 wavefronts
+constexpr int kCfgShufRing128x256 = 40;
 static_assert(kCfgDecode64x128 < kNumTiles && kCfgFloatScaled128x256 < kNumTiles, "tile table");
-static_assert(kCfgShufDecode64x128 < kNumTiles, "tile table");
+static_assert(kCfgShufRing128x256 < kNumTiles, "tile table");
 
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -1690,10 +1708,10 @@ bool gemm_config_by_index(int idx, const GemmProblem& p, int splits, GemmConfig*
   if (p.float_scales && (p.masked_m || p.m_indices || p.E != 1)) return false;
   // pre-shuffled weights run on the entries that read that layout (dense calls)
   if (reads_shuffled(kTiles[idx].kind) != p.b_shuffled) return false;
-  if (p.b_shuffled && (p.masked_m || p.m_indices || p.E != 1 || p.float_scales)) return false;
+  if (p.b_shuffled && (p.m_indices || p.float_scales)) return false;
   // contiguous grouped layout: a tile must not straddle two aligned runs
   if (p.m_indices && kContiguousAlign % kTiles[idx].bm != 0) return false;
-  if (kTiles[idx].kind == kRing) {
+  if (is_ring(kTiles[idx].kind)) {
     splits = 1;  // never splits K; the scale tables bound K
     if ((KB + 3) / 4 > kTiles[idx].max_wd) return false;
   }
@@ -1750,11 +1768,21 @@ GemmConfig choose_gemm_config(const GemmProblem& p) {
   GemmConfig cfg;
   const int KB = (int)(p.K / 128);
   if (p.b_shuffled) {
-    // pre-shuffled weights: the decode kernel, K split until about 224 workgroups and
-    // reduced by the last split of each tile (a separate reduction kernel measured
-    // within run-to-run noise of it at the decode shape)
+    // pre-shuffled weights.  Masked: the 256 x 256 ring tiles with the wavefronts side
+    // by side in N, as for the plain layout.  Dense M <= 64: the decode kernel, K split
+    // until about 224 workgroups and reduced by the last split of each tile (a separate
+    // reduction kernel measured within run-to-run noise of it at the decode shape).
+    // Larger M: ring tiles, 256 x 256 once they fill the compute units, else 128 x 256.
+    // The decode kernel takes whatever the ring's scale tables cannot hold.
+    if (p.masked_m) {
+      if (gemm_config_by_index(kCfgShufRing256x256Rows, p, 1, &cfg)) return cfg;
+    } else if (p.M > 64) {
+      const int64_t big_tiles = cdiv(p.M, 256) * cdiv(p.N, 256);
+      if (gemm_config_by_index(big_tiles >= 256 ? kCfgShufRing256x256 : kCfgShufRing128x256, p, 1, &cfg))
+        return cfg;
+    }
     const int64_t tiles = cdiv(p.M, kTiles[kCfgShufDecode64x128].bm) * cdiv(p.N, kTiles[kCfgShufDecode64x128].bn);
-    int splits = (int)(224 / (tiles > 0 ? tiles : 1));
+    int splits = p.masked_m ? 1 : (int)(224 / (tiles > 0 ? tiles : 1));
     if (splits < 1) splits = 1;
     if (!gemm_config_by_index(kCfgShufDecode64x128, p, splits, &cfg)) cfg.kernel = -1;
     return cfg;

@@ -186,8 +186,10 @@ int fp8_weight_preshuffle(const void* w, int64_t rows, int64_t K, void* out, voi
 /*
  * fp8_block_gemm_nt with the weights b in the layout of fp8_weight_preshuffle
  * (rows = N); every other argument, the result and the workspace rules are those
- * of fp8_block_gemm_nt.  Meant for decode-sized M (each 64-row tile of A streams
- * all the weights once).
+ * of fp8_block_gemm_nt.  Meant for decode-sized M (M <= 64: the weight-streaming
+ * kernel, whose loads this layout makes contiguous).  Larger M runs 128- or 256-row
+ * tiles on the same layout, which measured slower than fp8_block_gemm_nt on the
+ * plain layout at prefill sizes.
  */
 int fp8_block_gemm_nt_preshuffled(const void* a, const uint32_t* sfa, int64_t ld_sfa, const void* b,
                                   const float* sfb, void* c, int64_t ldc, int64_t M, int64_t N,
@@ -207,6 +209,17 @@ int fp8_block_gemm_nt_preshuffled(const void* a, const uint32_t* sfa, int64_t ld
 int fp8_block_gemm_grouped_masked(const void* a, const uint32_t* sfa, const void* b,
                                   const float* sfb, void* c, const int32_t* masked_m, int64_t E,
                                   int64_t M_max, int64_t N, int64_t K, void* stream);
+
+/*
+ * fp8_block_gemm_grouped_masked with the expert weights b in the layout of
+ * fp8_weight_preshuffle (rows = E*N, so each expert's [N][K] block is shuffled on
+ * its own); every other argument and the result are those of
+ * fp8_block_gemm_grouped_masked.
+ */
+int fp8_block_gemm_grouped_masked_preshuffled(const void* a, const uint32_t* sfa, const void* b,
+                                              const float* sfb, void* c, const int32_t* masked_m,
+                                              int64_t E, int64_t M_max, int64_t N, int64_t K,
+                                              void* stream);
 
 /*
  * Contiguous grouped GEMM, the layout of the high-throughput MoE path (PR #19111
@@ -234,8 +247,8 @@ int fp8_block_gemm_grouped_contiguous(const void* a, const uint32_t* sfa, int64_
  * Tile-table access, for tuning and for tests that cover every compiled tile
  * shape.  fp8bs_gemm_config reports what the automatic choice would be for a
  * dense (masked = 0), masked (masked = 1), contiguous grouped (masked = 2),
- * dense float-scale (masked = 3) or dense pre-shuffled-weight (masked = 4)
- * problem: kernel index into the tile
+ * dense float-scale (masked = 3), dense pre-shuffled-weight (masked = 4) or
+ * masked pre-shuffled-weight (masked = 5) problem: kernel index into the tile
  * table, workgroup tile bm x bn, and the number of K splits.  The _cfg variants
  * run the same GEMMs with an explicit kernel index and split count (splits is
  * clamped to [1, K/128]; the masked and contiguous forms use splits == 1 only, and
@@ -245,8 +258,8 @@ int fp8bs_gemm_config_count(void);
 int fp8bs_gemm_config(int masked, int64_t M, int64_t N, int64_t K, int32_t* kernel, int32_t* bm,
                       int32_t* bn, int32_t* splits);
 /* Whether table entry `kernel` accepts a dense (masked = 0), masked (masked = 1),
- * contiguous grouped (masked = 2), dense float-scale (masked = 3) or dense
- * pre-shuffled-weight (masked = 4) problem of this
+ * contiguous grouped (masked = 2), dense float-scale (masked = 3), dense
+ * pre-shuffled-weight (masked = 4) or masked pre-shuffled-weight (masked = 5) problem of this
  * shape with `splits` K splits: FP8BS_OK with its workgroup tile and the split count
  * it would use, FP8BS_ERR_SHAPE if it does not (for instance K past the entry's scale
  * tables, a masked problem that would need K splits, or a scale format the entry does
@@ -270,6 +283,10 @@ int fp8_block_gemm_nt_float_scales_cfg(const void* a, const float* sfa, int64_t 
 int fp8_block_gemm_nt_preshuffled_cfg(const void* a, const uint32_t* sfa, int64_t ld_sfa, const void* b,
                                       const float* sfb, void* c, int64_t ldc, int64_t M, int64_t N,
                                       int64_t K, int32_t kernel, int32_t splits, void* stream);
+int fp8_block_gemm_grouped_masked_preshuffled_cfg(const void* a, const uint32_t* sfa, const void* b,
+                                                  const float* sfb, void* c, const int32_t* masked_m,
+                                                  int64_t E, int64_t M_max, int64_t N, int64_t K,
+                                                  int32_t kernel, void* stream);
 
 /* Status helpers. */
 const char* fp8bs_status_string(int status);

@@ -17,12 +17,16 @@ def _bits(t):
     return t.view(torch.int16).cpu().numpy() if t.dtype == torch.bfloat16 else t.cpu().numpy()
 
 
-def test_graph_replays_of_the_decode_step_match_eager():
+@pytest.mark.parametrize("preshuffled", [False, True], ids=["plain", "preshuffled"])
+def test_graph_replays_of_the_decode_step_match_eager(preshuffled):
     M, N, K = 64, 7168, 18432
     s = torch.cuda.Stream()
+    gemm = F.fp8_block_gemm_nt_preshuffled if preshuffled else F.fp8_block_gemm_nt
     x = to_dev(W.normal_bf16_outliers((M, K), seed=3))
     with torch.cuda.stream(s):
         qb, sfb = F.fp8_block_quant_128x128(to_dev(W.normal_bf16((N, K), std=0.02, seed=3, tensor_id=W.T_B)))
+        if preshuffled:
+            qb = F.fp8_weight_preshuffle(qb)
         q = torch.empty((M, K), dtype=torch.uint8, device=DEV)
         sf = torch.empty(((K // 128 + 3) // 4, M), dtype=torch.int32, device=DEV)
         c = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
@@ -32,11 +36,11 @@ def test_graph_replays_of_the_decode_step_match_eager():
 
         def step():
             F.fp8_quant_group_pack(x, q=q, sf=sf)
-            F.fp8_block_gemm_nt(q, sf, qb, sfb, c=c)
+            gemm(q, sf, qb, sfb, c=c)
 
         step()  # eager, also creates the stream's workspace before capture
     s.synchronize()
-    assert F.gemm_config(False, M, N, K)["splits"] > 1
+    assert F.gemm_config(F.LAYOUT_DENSE_PRESHUFFLED if preshuffled else F.LAYOUT_DENSE, M, N, K)["splits"] > 1
     eager = _bits(c).copy()
     other_eager = _bits(F.fp8_block_gemm_nt(oa, osa, ob, osb))
     g = torch.cuda.CUDAGraph()

@@ -100,3 +100,112 @@ def test_preshuffled_decode_shape_matches_plain_and_oracle():
     rows = np.unique(np.linspace(0, s.M - 1, 16).astype(np.int64))
     ref = O.gemm_nt(qa, sfa, qb, sfb, rows=rows)
     gemm_tolerance_check(c1[rows], ref, s.name)
+
+
+CANARY = 0x7E7E
+
+
+def _moe_operands(E, M_max, N, K, seed=0):
+    x = W.normal_bf16((E * M_max, K), seed=seed)
+    qa, sfa_flat = O.quant_group_pack(x, ld_sf=E * M_max)
+    Wd = (K // 128 + 3) // 4
+    a = qa.reshape(E, M_max, K)
+    sfa = np.ascontiguousarray(sfa_flat.reshape(Wd, E, M_max).transpose(1, 0, 2))
+    w = W.normal_bf16((E * N, K), std=0.02, seed=seed, tensor_id=W.T_B)
+    qb = np.empty((E, N, K), np.uint8)
+    sfb = np.empty((E, (N + 127) // 128, K // 128), np.float32)
+    for e in range(E):
+        qb[e], sfb[e] = O.block_quant_128x128(np.ascontiguousarray(w[e * N:(e + 1) * N]))
+    return a, sfa, qb, sfb
+
+
+def _masked(a, sfa, b_dev, sfb, counts, kernel=None, preshuffled=False):
+    E, M_max, K = a.shape
+    N = b_dev.shape[1]
+    c = torch.full((E, M_max, N), CANARY, dtype=torch.int16, device=DEV).view(torch.bfloat16)
+    F.fp8_block_gemm_grouped_masked(to_dev(a), to_dev(sfa), b_dev, to_dev(sfb), to_dev(counts), c=c, kernel=kernel,
+                                    preshuffled=preshuffled)
+    sync()
+    return to_host(c)
+
+
+def test_preshuffled_masked_every_entry_edge_counts():
+    """Every entry reading pre-shuffled weights in the masked form: valid rows within the
+    GEMM tolerance of the oracle, rows past the count untouched (canary), and bit-equal to
+    the plain-layout entry of the same tile where there is one."""
+    E, M_max, N, K = 4, 96, 256, 640
+    a, sfa, qb, sfb = _moe_operands(E, M_max, N, K, seed=4)
+    counts = np.array([0, 17, 96, 200], np.int32)  # empty, partial, full, clamped
+    ref = O.gemm_grouped_masked(a, sfa, qb, sfb, counts)
+    db, dbs = to_dev(qb), F.fp8_weight_preshuffle(to_dev(qb))
+    entries = [k for k in range(F.gemm_config_count())
+               if F.gemm_config_of(k, F.LAYOUT_MASKED_PRESHUFFLED, M_max, N, K) is not None]
+    assert entries
+    plain_by_tile = {}
+    for k in range(F.gemm_config_count()):
+        cfg = F.gemm_config_of(k, True, M_max, N, K)
+        if cfg is not None:
+            plain_by_tile.setdefault((cfg["bm"], cfg["bn"]), []).append(k)
+    for kernel in entries:
+        print("masked preshuffled kernel %d" % kernel, flush=True)
+        c = _masked(a, sfa, dbs, sfb, counts, kernel=kernel, preshuffled=True)
+        for e in range(E):
+            ce = int(min(max(counts[e], 0), M_max))
+            if ce:
+                gemm_tolerance_check(c[e, :ce], ref[e, :ce], "kernel %d expert %d" % (kernel, e))
+            assert np.all(c[e, ce:] == CANARY), "kernel %d expert %d: padded rows written" % (kernel, e)
+        cfg = F.gemm_config_of(kernel, F.LAYOUT_MASKED_PRESHUFFLED, M_max, N, K)
+        same = [_masked(a, sfa, db, sfb, counts, kernel=k) for k in plain_by_tile.get((cfg["bm"], cfg["bn"]), [])]
+        assert not same or any(np.array_equal(c, x) for x in same), "kernel %d differs from its plain tile" % kernel
+    c = _masked(a, sfa, dbs, sfb, counts, preshuffled=True)
+    for e in range(1, E):
+        ce = int(min(counts[e], M_max))
+        gemm_tolerance_check(c[e, :ce], ref[e, :ce], "auto expert %d" % e)
+
+
+def test_preshuffled_dense_ring_entries_match_plain():
+    """Prefill-sized dense calls on pre-shuffled weights (ring tiles) equal the plain-layout
+    ring tiles of the same shape bit for bit and meet the oracle's tolerance."""
+    M, N, K = 512, 512, 1152
+    a = W.normal_bf16((M, K), seed=21)
+    b = W.normal_bf16((N, K), std=1.0, seed=21, tensor_id=W.T_B)
+    qa, sfa = O.quant_group_pack(a)
+    qb, sfb = O.block_quant_128x128(b)
+    rows = np.arange(0, M, 7)
+    ref = O.gemm_nt(qa, sfa, qb, sfb, rows=rows)
+    da, dsa, db, dsb = to_dev(qa), to_dev(sfa), to_dev(qb), to_dev(sfb)
+    dbs = F.fp8_weight_preshuffle(db)
+    ring = [k for k in range(F.gemm_config_count())
+            if (F.gemm_config_of(k, SHUF, M, N, K) or {}).get("bm", 0) >= 128]
+    assert ring
+    for kernel in ring:
+        c = to_host(F.fp8_block_gemm_nt_preshuffled(da, dsa, dbs, dsb, c=poisoned_bf16(M, N), kernel=kernel))
+        sync()
+        gemm_tolerance_check(c[rows], ref, "ring kernel %d" % kernel)
+        cfg = F.gemm_config_of(kernel, SHUF, M, N, K)
+        plain = [k for k in range(F.gemm_config_count())
+                 if F.gemm_config_of(k, False, M, N, K) == {**cfg, "kernel": k}]
+        outs = [to_host(F.fp8_block_gemm_nt(da, dsa, db, dsb, c=poisoned_bf16(M, N), kernel=k)) for k in plain]
+        sync()
+        assert any(np.array_equal(c, x) for x in outs), "ring kernel %d differs from the plain ring tiles" % kernel
+
+
+def test_preshuffled_masked_gate_up_shape_matches_plain():
+    """The masked gate_up workload (32 experts x 256 padded rows, Zipf counts, N 4096, K 7168):
+    pre-shuffled equals the plain layout bit for bit on every valid row, and the oracle
+    agrees on sampled rows."""
+    E, M_max, N, K = W.MOE_E, W.MOE_M_MAX, W.MOE_GATE_UP["N"], W.MOE_GATE_UP["K"]
+    counts = W.zipf_counts()
+    a, sfa, qb, sfb = _moe_operands(E, M_max, N, K, seed=0)
+    db = to_dev(qb)
+    dbs = F.fp8_weight_preshuffle(db)
+    print("gate_up preshuffled cfg", F.gemm_config(F.LAYOUT_MASKED_PRESHUFFLED, M_max, N, K), flush=True)
+    cs = _masked(a, sfa, dbs, sfb, counts, preshuffled=True)
+    cp = _masked(a, sfa, db, sfb, counts)
+    assert np.array_equal(cs, cp)
+    rows = np.array([0, 1, 63, 64, 127, 200, 255])
+    ref = O.gemm_grouped_masked(a, sfa, qb, sfb, counts, rows=rows)
+    for e in (0, 1, 7, 31):
+        sel = np.array([r for r in rows if r < counts[e]], np.int64)
+        if sel.size:
+            gemm_tolerance_check(cs[e, sel], ref[e, sel], "gate_up expert %d" % e)
