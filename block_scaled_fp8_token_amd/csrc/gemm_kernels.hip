@@ -1770,8 +1770,10 @@ GemmConfig choose_gemm_config(const GemmProblem& p) {
   if (p.b_shuffled) {
     // pre-shuffled weights.  Masked: the 256 x 256 ring tiles with the wavefronts side
     // by side in N, as for the plain layout.  Dense M <= 64: the decode kernel, K split
-    // until about 224 workgroups and reduced by the last split of each tile (a separate
-    // reduction kernel measured within run-to-run noise of it at the decode shape).
+    // until about 224 workgroups and reduced by the last split of each tile.  Leaving
+    // the sum to splitk_reduce_kernel makes the call 0.9 us shorter back to back, but a
+    // quant + GEMM step replayed from a graph no faster (one more kernel boundary), so
+    // the single launch stays.
     // Larger M: ring tiles, 256 x 256 once they fill the compute units, else 128 x 256.
     // The decode kernel takes whatever the ring's scale tables cannot hold.
     if (p.masked_m) {
