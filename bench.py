@@ -259,7 +259,7 @@ def bench_dense(F, stream, shape, steps, warmup, preshuffled=False):
     return r
 
 
-def bench_dense_float(F, stream, shape, steps, warmup):
+def bench_dense_float(F, stream, shape, steps, warmup, preshuffled=False):
     """The dense step in the float-scale (non-UE8M0) format: activation quant with fp32
     group scales, weights block-quantized with fp32 scales, the float-scale GEMM."""
     M, N, K = shape.M, shape.N, shape.K
@@ -270,6 +270,9 @@ def bench_dense_float(F, stream, shape, steps, warmup):
         copies.append(F.fp8_block_quant_128x128_float(w))
         del w
     torch.cuda.synchronize()
+    if preshuffled:
+        copies = [(F.fp8_weight_preshuffle(qb), sfb) for qb, sfb in copies]
+        torch.cuda.synchronize()
     nv = len(copies)
     qa = torch.empty((M, K), dtype=torch.uint8, device="cuda")
     sfa = torch.empty((K // 128, max(4, (M + 3) // 4 * 4)), dtype=torch.float32, device="cuda")
@@ -280,18 +283,20 @@ def bench_dense_float(F, stream, shape, steps, warmup):
 
     def gemm(s):
         qb, sfb = copies[s % nv]
-        F.fp8_block_gemm_nt_float_scales(qa, sfa, qb, sfb, c=c, stream=stream)
+        F.fp8_block_gemm_nt_float_scales(qa, sfa, qb, sfb, c=c, stream=stream, preshuffled=preshuffled)
 
     with torch.cuda.stream(stream):
         for i in range(warmup):
             quant(i)
             gemm(i)
     t_quant, t_gemm = kernel_times(stream, [quant, gemm], steps)
-    r = {"workload": shape.name.replace("dense_", "dense_float_scales_"), "M": M, "N": N, "K": K,
+    r = {"workload": shape.name.replace("dense_", "dense_float_scales_") + ("_preshuffled" if preshuffled else ""),
+         "M": M, "N": N, "K": K,
          "quant_us": t_quant * 1e3, "gemm_us": t_gemm * 1e3,
          "gemm_tflops": gemm_flops(M, N, K) / (t_gemm * 1e-3) / 1e12,
          "gemm_gbs": gemm_bytes(M, N, K) / (t_gemm * 1e-3) / 1e9,
-         "config": F.gemm_config(F.LAYOUT_DENSE_FLOAT, M, N, K), "weight_copies": nv}
+         "config": F.gemm_config(F.LAYOUT_DENSE_FLOAT_PRESHUFFLED if preshuffled else F.LAYOUT_DENSE_FLOAT, M, N, K),
+         "weight_copies": nv}
     r["frac_hbm"] = r["gemm_gbs"] / HBM_PEAK_GBS
     r["frac_mfma"] = r["gemm_tflops"] / FP8_PEAK_TFLOPS
     del a, copies, qa, sfa, c
@@ -583,8 +588,8 @@ def main():
         print("[bench] %s" % json.dumps(rows[-1]), file=sys.stderr, flush=True)
         rows.append(bench_dispatch_quant(F, W, stream, args.steps, args.warmup))
         print("[bench] %s" % json.dumps(rows[-1]), file=sys.stderr, flush=True)
-        for fs in (W.DENSE_DECODE, W.DENSE_PREFILL[2]):
-            rows.append(bench_dense_float(F, stream, fs, max(10, args.steps // 4), args.warmup))
+        for fs, pre in ((W.DENSE_DECODE, False), (W.DENSE_DECODE, True), (W.DENSE_PREFILL[2], False)):
+            rows.append(bench_dense_float(F, stream, fs, max(10, args.steps // 4), args.warmup, preshuffled=pre))
             print("[bench] %s" % json.dumps(rows[-1]), file=sys.stderr, flush=True)
         print("%-58s %10s %10s %10s %8s %8s" % ("workload", "us", "TFLOPS", "GB/s", "%MFMA", "%HBM"),
               file=sys.stderr)

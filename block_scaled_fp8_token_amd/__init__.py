@@ -59,6 +59,9 @@ _SIGS = {
     "fp8_block_gemm_nt_preshuffled_cfg": [_P, _P, _I64, _P, _P, _P, _I64, _I64, _I64, _I64, _I32, _I32, _P],
     "fp8_block_gemm_grouped_masked_preshuffled": [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _P],
     "fp8_block_gemm_grouped_masked_preshuffled_cfg": [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I32, _P],
+    "fp8_block_gemm_nt_float_scales_preshuffled": [_P, _P, _I64, _P, _P, _P, _I64, _I64, _I64, _I64, _P],
+    "fp8_block_gemm_nt_float_scales_preshuffled_cfg": [_P, _P, _I64, _P, _P, _P, _I64, _I64, _I64, _I64, _I32,
+                                                       _I32, _P],
     "fp8_block_gemm_grouped_masked": [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _P],
     "fp8_block_gemm_grouped_masked_cfg": [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I32, _P],
     "fp8_block_gemm_grouped_contiguous": [_P, _P, _I64, _P, _P, _P, _I64, _P, _I64, _I64, _I64, _I64, _P],
@@ -413,7 +416,7 @@ def fp8_block_gemm_grouped_contiguous(a: torch.Tensor, sfa: torch.Tensor, b: tor
 
 
 (LAYOUT_DENSE, LAYOUT_MASKED, LAYOUT_CONTIGUOUS, LAYOUT_DENSE_FLOAT, LAYOUT_DENSE_PRESHUFFLED,
- LAYOUT_MASKED_PRESHUFFLED) = 0, 1, 2, 3, 4, 5
+ LAYOUT_MASKED_PRESHUFFLED, LAYOUT_DENSE_FLOAT_PRESHUFFLED) = 0, 1, 2, 3, 4, 5, 6
 
 
 def fp8_quant_group_float(x: torch.Tensor, q: torch.Tensor | None = None, sf: torch.Tensor | None = None,
@@ -450,9 +453,10 @@ def fp8_block_quant_128x128_float(w: torch.Tensor, stream=None):
 
 def fp8_block_gemm_nt_float_scales(a: torch.Tensor, sfa: torch.Tensor, b: torch.Tensor, sfb: torch.Tensor,
                                    c: torch.Tensor | None = None, kernel: int | None = None,
-                                   splits: int | None = None, stream=None) -> torch.Tensor:
+                                   splits: int | None = None, stream=None, preshuffled: bool = False) -> torch.Tensor:
     """Dense GEMM with float scales -> bf16 [M, N].  a uint8 [M, K], sfa float32 [K/128, ld_sfa],
-    b uint8 [N, K], sfb float32 [ceil(N/128), K/128]."""
+    b uint8 [N, K], sfb float32 [ceil(N/128), K/128].  preshuffled: b is in the layout of
+    fp8_weight_preshuffle (fp8_block_gemm_nt_float_scales_preshuffled)."""
     _expect(a, "a", _E4M3, 2)
     _contig(a, "a")
     _expect(b, "b", _E4M3, 2)
@@ -472,13 +476,14 @@ def fp8_block_gemm_nt_float_scales(a: torch.Tensor, sfa: torch.Tensor, b: torch.
     s = _stream(stream)
     args = (a.data_ptr(), sfa.data_ptr(), sfa.stride(0), b.data_ptr(), sfb.data_ptr(), c.data_ptr(), c.stride(0),
             M, N, K)
+    name = "fp8_block_gemm_nt_float_scales" + ("_preshuffled" if preshuffled else "")
     if kernel is None and splits is None:
-        st = _lib.fp8_block_gemm_nt_float_scales(*args, s)
+        st = getattr(_lib, name)(*args, s)
     else:
         if kernel is None:
-            kernel = gemm_config(LAYOUT_DENSE_FLOAT, M, N, K)["kernel"]
-        st = _lib.fp8_block_gemm_nt_float_scales_cfg(*args, int(kernel), int(splits or 1), s)
-    _check("fp8_block_gemm_nt_float_scales", st)
+            kernel = gemm_config(LAYOUT_DENSE_FLOAT_PRESHUFFLED if preshuffled else LAYOUT_DENSE_FLOAT, M, N, K)["kernel"]
+        st = getattr(_lib, name + "_cfg")(*args, int(kernel), int(splits or 1), s)
+    _check(name, st)
     return c
 
 

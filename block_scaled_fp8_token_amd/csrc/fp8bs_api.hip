@@ -190,7 +190,7 @@ fp8bs::GemmProblem contiguous_problem(const void* a, const uint32_t* sfa, int64_
 // A problem of the given layout (0 dense, 1 masked, 2 contiguous) for host-side
 // configuration queries only: its pointers are placeholders that are never read.
 // (3: dense with float scales, 4: dense with pre-shuffled weights, 5: masked with
-// pre-shuffled weights)
+// pre-shuffled weights, 6: dense with float scales and pre-shuffled weights)
 fp8bs::GemmProblem host_problem(int layout, int64_t M, int64_t N, int64_t K) {
   static const int32_t placeholder = 0;
   if (layout == 1 || layout == 5) {
@@ -201,8 +201,8 @@ fp8bs::GemmProblem host_problem(int layout, int64_t M, int64_t N, int64_t K) {
   if (layout == 2)
     return contiguous_problem(nullptr, nullptr, M, nullptr, nullptr, nullptr, N, &placeholder, 1, M, N, K);
   fp8bs::GemmProblem p = dense_problem(nullptr, nullptr, M, nullptr, nullptr, nullptr, N, M, N, K);
-  p.float_scales = layout == 3;
-  p.b_shuffled = layout == 4;
+  p.float_scales = layout == 3 || layout == 6;
+  p.b_shuffled = layout == 4 || layout == 6;
   return p;
 }
 
@@ -473,13 +473,43 @@ int fp8_block_gemm_nt_float_scales_cfg(const void* a, const float* sfa, int64_t 
   return run_gemm(p, cfg, static_cast<hipStream_t>(stream));
 }
 
+int fp8_block_gemm_nt_float_scales_preshuffled(const void* a, const float* sfa, int64_t ld_sfa, const void* b,
+                                                const float* sfb, void* c, int64_t ldc, int64_t M, int64_t N,
+                                                int64_t K, void* stream) {
+  int st = check_dense(a, reinterpret_cast<const uint32_t*>(sfa), ld_sfa, b, sfb, c, ldc, M, N, K);
+  if (st != FP8BS_OK) return st > 0 ? FP8BS_OK : st;
+  st = check_device();
+  if (st != FP8BS_OK) return st;
+  fp8bs::GemmProblem p = dense_problem(a, reinterpret_cast<const uint32_t*>(sfa), ld_sfa, b, sfb, c, ldc, M, N, K);
+  p.float_scales = true;
+  p.b_shuffled = true;
+  const fp8bs::GemmConfig cfg = fp8bs::choose_gemm_config(p);
+  if (cfg.kernel < 0) return FP8BS_ERR_SHAPE;
+  return run_gemm(p, cfg, static_cast<hipStream_t>(stream));
+}
+
+int fp8_block_gemm_nt_float_scales_preshuffled_cfg(const void* a, const float* sfa, int64_t ld_sfa, const void* b,
+                                                    const float* sfb, void* c, int64_t ldc, int64_t M, int64_t N,
+                                                    int64_t K, int32_t kernel, int32_t splits, void* stream) {
+  int st = check_dense(a, reinterpret_cast<const uint32_t*>(sfa), ld_sfa, b, sfb, c, ldc, M, N, K);
+  if (st != FP8BS_OK) return st > 0 ? FP8BS_OK : st;
+  st = check_device();
+  if (st != FP8BS_OK) return st;
+  fp8bs::GemmProblem p = dense_problem(a, reinterpret_cast<const uint32_t*>(sfa), ld_sfa, b, sfb, c, ldc, M, N, K);
+  p.float_scales = true;
+  p.b_shuffled = true;
+  fp8bs::GemmConfig cfg;
+  if (!fp8bs::gemm_config_by_index(kernel, p, splits < 1 ? 1 : splits, &cfg)) return FP8BS_ERR_SHAPE;
+  return run_gemm(p, cfg, static_cast<hipStream_t>(stream));
+}
+
 int fp8bs_gemm_config_count(void) { return fp8bs::gemm_config_count(); }
 
 int fp8bs_gemm_config(int masked, int64_t M, int64_t N, int64_t K, int32_t* kernel, int32_t* bm, int32_t* bn,
                       int32_t* splits) {
   if (M < 0 || N < 0 || K < 128 || K % 128 != 0 || N % 64 != 0) return FP8BS_ERR_SHAPE;
   if (!kernel || !bm || !bn || !splits) return FP8BS_ERR_NULL;
-  if (masked < 0 || masked > 5) return FP8BS_ERR_SHAPE;
+  if (masked < 0 || masked > 6) return FP8BS_ERR_SHAPE;
   const fp8bs::GemmProblem p = host_problem(masked, M, N, K);
   const fp8bs::GemmConfig cfg = fp8bs::choose_gemm_config(p);
   *kernel = cfg.kernel;
@@ -493,7 +523,7 @@ int fp8bs_gemm_config_of(int32_t kernel, int masked, int64_t M, int64_t N, int64
                          int32_t* bn, int32_t* splits_out) {
   if (M < 0 || N < 0 || K < 128 || K % 128 != 0 || N % 64 != 0) return FP8BS_ERR_SHAPE;
   if (!bm || !bn || !splits_out) return FP8BS_ERR_NULL;
-  if (masked < 0 || masked > 5) return FP8BS_ERR_SHAPE;
+  if (masked < 0 || masked > 6) return FP8BS_ERR_SHAPE;
   const fp8bs::GemmProblem p = host_problem(masked, M, N, K);
   fp8bs::GemmConfig cfg;
   if (!fp8bs::gemm_config_by_index(kernel, p, splits < 1 ? 1 : splits, &cfg)) return FP8BS_ERR_SHAPE;

@@ -1586,18 +1586,23 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const KArgs p) {
 typedef void (*KernelFn)(const KArgs);
 
 enum Kind { kTile = 0, kStream = 1, kScaled = 2, kRing = 3, kDecode = 4, kTileFloat = 5, kDecodeFloat = 6,
-            kScaledFloat = 7, kDecodeSep = 8, kDecodeShuf = 9, kDecodeShufSep = 10, kRingShuf = 11 };
+            kScaledFloat = 7, kDecodeSep = 8, kDecodeShuf = 9, kDecodeShufSep = 10, kRingShuf = 11,
+            kDecodeFloatShuf = 12 };
 
 // Entries that read the float-scale format.
 inline bool reads_float_scales(int kind) {
-  return kind == kTileFloat || kind == kDecodeFloat || kind == kScaledFloat;
+  return kind == kTileFloat || kind == kDecodeFloat || kind == kScaledFloat || kind == kDecodeFloatShuf;
 }
 // LDS-DMA tile entries (dynamic LDS for the scale tables).
 inline bool is_scaled_tile(int kind) { return kind == kScaled || kind == kScaledFloat; }
 // Entries that reduce their own K split (arrival counters in the workspace).
-inline bool reduces_in_kernel(int kind) { return kind == kDecode || kind == kDecodeFloat || kind == kDecodeShuf; }
+inline bool reduces_in_kernel(int kind) {
+  return kind == kDecode || kind == kDecodeFloat || kind == kDecodeShuf || kind == kDecodeFloatShuf;
+}
 // Entries that read the weights in the pre-shuffled layout.
-inline bool reads_shuffled(int kind) { return kind == kDecodeShuf || kind == kDecodeShufSep || kind == kRingShuf; }
+inline bool reads_shuffled(int kind) {
+  return kind == kDecodeShuf || kind == kDecodeShufSep || kind == kRingShuf || kind == kDecodeFloatShuf;
+}
 // Ring entries (K never split; the scale tables bound K).
 inline bool is_ring(int kind) { return kind == kRing || kind == kRingShuf; }
 // Decode-kernel entries (K split in whole scale words; kDecodeSep leaves the sum of
@@ -1659,6 +1664,7 @@ const TileEntry kTiles[] = {
     {scaled_ring_kernel<256, 256, 1, 4, true>, 256, 256, kRingShuf, 4, 256, ring_wd_max<256, 256, 1, 4>()},
     {scaled_ring_kernel<256, 256, 2, 2, true>, 256, 256, kRingShuf, 4, 256, ring_wd_max<256, 256, 2, 2>()},
     {scaled_ring_kernel<128, 256, 2, 2, true>, 128, 256, kRingShuf, 4, 256, ring_wd_max<128, 256, 2, 2>()},
+    {decode_kernel<4, 3, true, true>, 64, 128, kDecodeFloatShuf, 3, 256, DecodeShape<4, 3>::WMAX / 4},
 };
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 // table entries the automatic choice uses
@@ -1679,8 +1685,9 @@ constexpr int kCfgShufDecode64x128 = 35;   // the same on pre-shuffled weights
 constexpr int kCfgShufRing256x256Rows = 38;  // pre-shuffled weights: ring 256x256, 1 x 4 wavefronts
 constexpr int kCfgShufRing256x256 = 39;      // 2 x 2 wavefronts
 constexpr int kCfgShufRing128x256 = 40;
+constexpr int kCfgFloatShufDecode64x128 = 41;  // float scales, pre-shuffled weights
 static_assert(kCfgDecode64x128 < kNumTiles && kCfgFloatScaled128x256 < kNumTiles, "tile table");
-static_assert(kCfgShufRing128x256 < kNumTiles, "tile table");
+static_assert(kCfgFloatShufDecode64x128 < kNumTiles, "tile table");
 
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -1708,7 +1715,7 @@ bool gemm_config_by_index(int idx, const GemmProblem& p, int splits, GemmConfig*
   if (p.float_scales && (p.masked_m || p.m_indices || p.E != 1)) return false;
   // pre-shuffled weights run on the entries that read that layout (dense calls)
   if (reads_shuffled(kTiles[idx].kind) != p.b_shuffled) return false;
-  if (p.b_shuffled && (p.m_indices || p.float_scales)) return false;
+  if (p.b_shuffled && p.m_indices) return false;
   // contiguous grouped layout: a tile must not straddle two aligned runs
   if (p.m_indices && kContiguousAlign % kTiles[idx].bm != 0) return false;
   if (is_ring(kTiles[idx].kind)) {
@@ -1767,6 +1774,15 @@ bool gemm_config_by_index(int idx, const GemmProblem& p, int splits, GemmConfig*
 GemmConfig choose_gemm_config(const GemmProblem& p) {
   GemmConfig cfg;
   const int KB = (int)(p.K / 128);
+  if (p.b_shuffled && p.float_scales) {
+    // float scales on pre-shuffled weights: the float-scale decode kernel, K split
+    // until about 224 workgroups (the only entry reading both)
+    const int64_t tiles = cdiv(p.M, 64) * cdiv(p.N, kTiles[kCfgFloatShufDecode64x128].bn);
+    int splits = (int)(224 / (tiles > 0 ? tiles : 1));
+    if (splits < 1) splits = 1;
+    if (!gemm_config_by_index(kCfgFloatShufDecode64x128, p, splits, &cfg)) cfg.kernel = -1;
+    return cfg;
+  }
   if (p.b_shuffled) {
     // pre-shuffled weights.  Masked: the 256 x 256 ring tiles with the wavefronts side
     // by side in N, as for the plain layout.  Dense M <= 64: the decode kernel, K split

@@ -105,6 +105,15 @@ int fp8_quant_group_float(const void* x, int64_t ldx, int64_t M, int64_t K, void
                           float* sf, int64_t ld_sf, void* stream);
 int fp8_block_quant_128x128_float(const void* w, int64_t N, int64_t K, void* q, float* sfb,
                                   void* stream);
+/*
+ * fp8_block_gemm_nt_float_scales with the weights b in the layout of
+ * fp8_weight_preshuffle (rows = N); every other argument and the result are those of
+ * fp8_block_gemm_nt_float_scales.  Runs the float-scale decode kernel at every M:
+ * meant for decode-sized M (M <= 64).
+ */
+int fp8_block_gemm_nt_float_scales_preshuffled(const void* a, const float* sfa, int64_t ld_sfa,
+                                                const void* b, const float* sfb, void* c, int64_t ldc,
+                                                int64_t M, int64_t N, int64_t K, void* stream);
 int fp8_block_gemm_nt_float_scales(const void* a, const float* sfa, int64_t ld_sfa, const void* b,
                                    const float* sfb, void* c, int64_t ldc, int64_t M, int64_t N,
                                    int64_t K, void* stream);
@@ -247,8 +256,9 @@ int fp8_block_gemm_grouped_contiguous(const void* a, const uint32_t* sfa, int64_
  * Tile-table access, for tuning and for tests that cover every compiled tile
  * shape.  fp8bs_gemm_config reports what the automatic choice would be for a
  * dense (masked = 0), masked (masked = 1), contiguous grouped (masked = 2),
- * dense float-scale (masked = 3), dense pre-shuffled-weight (masked = 4) or
- * masked pre-shuffled-weight (masked = 5) problem: kernel index into the tile
+ * dense float-scale (masked = 3), dense pre-shuffled-weight (masked = 4),
+ * masked pre-shuffled-weight (masked = 5) or dense float-scale pre-shuffled-weight
+ * (masked = 6) problem: kernel index into the tile
  * table, workgroup tile bm x bn, and the number of K splits.  The _cfg variants
  * run the same GEMMs with an explicit kernel index and split count (splits is
  * clamped to [1, K/128]; the masked and contiguous forms use splits == 1 only, and
@@ -259,7 +269,8 @@ int fp8bs_gemm_config(int masked, int64_t M, int64_t N, int64_t K, int32_t* kern
                       int32_t* bn, int32_t* splits);
 /* Whether table entry `kernel` accepts a dense (masked = 0), masked (masked = 1),
  * contiguous grouped (masked = 2), dense float-scale (masked = 3), dense
- * pre-shuffled-weight (masked = 4) or masked pre-shuffled-weight (masked = 5) problem of this
+ * pre-shuffled-weight (masked = 4), masked pre-shuffled-weight (masked = 5) or dense
+ * float-scale pre-shuffled-weight (masked = 6) problem of this
  * shape with `splits` K splits: FP8BS_OK with its workgroup tile and the split count
  * it would use, FP8BS_ERR_SHAPE if it does not (for instance K past the entry's scale
  * tables, a masked problem that would need K splits, or a scale format the entry does
@@ -283,6 +294,10 @@ int fp8_block_gemm_nt_float_scales_cfg(const void* a, const float* sfa, int64_t 
 int fp8_block_gemm_nt_preshuffled_cfg(const void* a, const uint32_t* sfa, int64_t ld_sfa, const void* b,
                                       const float* sfb, void* c, int64_t ldc, int64_t M, int64_t N,
                                       int64_t K, int32_t kernel, int32_t splits, void* stream);
+int fp8_block_gemm_nt_float_scales_preshuffled_cfg(const void* a, const float* sfa, int64_t ld_sfa,
+                                                    const void* b, const float* sfb, void* c, int64_t ldc,
+                                                    int64_t M, int64_t N, int64_t K, int32_t kernel,
+                                                    int32_t splits, void* stream);
 int fp8_block_gemm_grouped_masked_preshuffled_cfg(const void* a, const uint32_t* sfa, const void* b,
                                                   const float* sfb, void* c, const int32_t* masked_m,
                                                   int64_t E, int64_t M_max, int64_t N, int64_t K,

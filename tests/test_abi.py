@@ -199,8 +199,11 @@ def test_config_of_table_entries():
         assert e is not None and (e["bm"], e["bn"], e["splits"]) == (c["bm"], c["bn"], c["splits"])
     fl = [k for k in range(n) if F.gemm_config_of(k, F.LAYOUT_DENSE_FLOAT, 72, 192, 384) is not None]
     sh = [k for k in range(n) if F.gemm_config_of(k, F.LAYOUT_DENSE_PRESHUFFLED, 72, 192, 384) is not None]
-    assert fl and sh and not set(fl) & set(sh)
-    assert all(F.gemm_config_of(k, True, 72, 192, 384) is not None for k in range(n) if k not in fl + sh)
+    fsh = [k for k in range(n) if F.gemm_config_of(k, F.LAYOUT_DENSE_FLOAT_PRESHUFFLED, 72, 192, 384) is not None]
+    assert fl and sh and fsh and not set(fl) & set(sh) and not set(fsh) & set(fl + sh)
+    assert all(F.gemm_config_of(k, True, 72, 192, 384) is not None for k in range(n) if k not in fl + sh + fsh)
+    assert all(F.gemm_config_of(k, True, 72, 192, 384) is None and F.gemm_config_of(k, False, 72, 192, 384) is None
+               for k in fsh)
     # the pre-shuffled entries read only that layout (dense calls)
     assert all(F.gemm_config_of(k, False, 72, 192, 384) is None and F.gemm_config_of(k, True, 72, 192, 384) is None
                for k in sh)

@@ -111,3 +111,33 @@ def test_float_chain_on_gpu_sampled_rows(M, N, K):
     assert np.array_equal(sfb.cpu().numpy().view(np.uint32), sfb_ref.view(np.uint32))
     ref = O.gemm_nt_float_scales(qa_ref, sfa_ref, qb_ref, sfb_ref)
     gemm_tolerance_check(c[rows], ref, "float chain %dx%dx%d" % (M, N, K))
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 64, 128), (17, 192, 384), (64, 512, 1024), (64, 128, 2560)])
+def test_float_gemm_preshuffled_every_entry(M, N, K):
+    """Float scales on pre-shuffled weights: every entry reading that combination, several
+    splits, within the tolerance of the oracle on the unshuffled weights, and bit-equal to
+    the float-scale decode kernel on the plain layout with the same tile and split."""
+    qa, sfa, qb, sfb = _float_operands(M, N, K, seed=M + N + K + 1)
+    ref = O.gemm_nt_float_scales(qa, sfa, qb, sfb)
+    da, dsa, db, dsb = to_dev(qa), to_dev(sfa), to_dev(qb), to_dev(sfb)
+    dbs = F.fp8_weight_preshuffle(db)
+    entries = [k for k in range(F.gemm_config_count())
+               if F.gemm_config_of(k, F.LAYOUT_DENSE_FLOAT_PRESHUFFLED, M, N, K) is not None]
+    assert entries
+    for kernel in entries:
+        for splits in (1, 2, 3):
+            cfg = F.gemm_config_of(kernel, F.LAYOUT_DENSE_FLOAT_PRESHUFFLED, M, N, K, splits)
+            c = to_host(F.fp8_block_gemm_nt_float_scales(da, dsa, dbs, dsb, c=poisoned_bf16(M, N), kernel=kernel,
+                                                         splits=splits, preshuffled=True))
+            sync()
+            gemm_tolerance_check(c, ref, "float preshuffled kernel %d splits %d %dx%dx%d" % (kernel, splits, M, N, K))
+            plain = [k for k in range(F.gemm_config_count())
+                     if F.gemm_config_of(k, FLOAT, M, N, K, splits) == {**cfg, "kernel": k}]
+            outs = [to_host(F.fp8_block_gemm_nt_float_scales(da, dsa, db, dsb, c=poisoned_bf16(M, N), kernel=k,
+                                                             splits=splits)) for k in plain]
+            sync()
+            assert any(np.array_equal(c, x) for x in outs), "kernel %d splits %d" % (kernel, splits)
+    c = to_host(F.fp8_block_gemm_nt_float_scales(da, dsa, dbs, dsb, c=poisoned_bf16(M, N), preshuffled=True))
+    sync()
+    gemm_tolerance_check(c, ref, "float preshuffled auto")
