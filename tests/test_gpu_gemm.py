@@ -63,6 +63,14 @@ def test_gemm_integer_identity_exact(kernel, splits):
                                              to_dev(sfb), c=poisoned_bf16(M, N), kernel=kernel, splits=splits)
         sync()
         c = to_host(c)
+    elif F.gemm_config_of(kernel, F.LAYOUT_DENSE_FLOAT_PRESHUFFLED, M, N, K) is not None:
+        # float scales on pre-shuffled weights: unit float scales, shuffled codes
+        sfa_f = np.ones((K // 128, 40), np.float32)
+        db = F.fp8_weight_preshuffle(to_dev(_int_codes(bi)))
+        c = F.fp8_block_gemm_nt_float_scales(to_dev(_int_codes(ai)), to_dev(sfa_f), db, to_dev(sfb),
+                                             c=poisoned_bf16(M, N), kernel=kernel, splits=splits, preshuffled=True)
+        sync()
+        c = to_host(c)
     elif F.gemm_config_of(kernel, F.LAYOUT_DENSE_PRESHUFFLED, M, N, K) is not None:
         # an entry reading pre-shuffled weights: the same integer problem on shuffled codes
         sfa = np.full((1, 40), 127 | (127 << 8), np.uint32)

@@ -61,6 +61,8 @@ def test_masked_small_all_kernels_edge_counts():
             continue  # float-scale entry: another scale format
         if F.gemm_config_of(kernel, F.LAYOUT_DENSE_PRESHUFFLED, M_max, N, K) is not None:
             continue  # dense entry on pre-shuffled weights
+        if F.gemm_config_of(kernel, F.LAYOUT_DENSE_FLOAT_PRESHUFFLED, M_max, N, K) is not None:
+            continue  # float scales on pre-shuffled weights
         assert F.gemm_config_of(kernel, True, M_max, N, K) is not None, kernel
         c = _run_masked(a, sfa, b, sfb, counts, kernel=kernel)
         _check(c, a, sfa, b, sfb, counts, what="kernel %d" % kernel)
