@@ -1174,12 +1174,20 @@ struct DecodeShape {
 // split (activations [K-block][row], weights [column block][K-block]; at most WMAX
 // K-blocks per split), the MFMAs run with unit scales into a per-K-block product,
 // and acc += product * (s_a * s_b) on the VALU.
-template <int NW, int DB_, bool FS = false, bool SHUF = false>
+//
+// WL: the weights go through LDS too.  Each wavefront DMAs its own 32 rows of the
+// K-block, 8 whole 128-byte rows per instruction (chunk c of row r stored at
+// c ^ (r & 7): the operand reads below are conflict-free), into a ring of DB stages
+// filled DB - 1 K-blocks ahead with the activations; the MFMA operands are then read
+// from LDS in the lane layout the register path loads directly.
+template <int NW, int DB_, bool FS = false, bool SHUF = false, bool WL = false>
 __global__ __launch_bounds__(NW * 64) void decode_kernel(const KArgs p) {
   using D = DecodeShape<NW, DB_>;
   constexpr int DB = D::DB, UN = D::UN, IA = D::IA, WMAX = D::WMAX, NBT = D::NBT;
   constexpr int NT = NW * 64, BN = 32 * NW;
   static_assert((NW == 4 || NW == 8) && IA >= 1, "decode shape");
+  static_assert(!(WL && SHUF), "one weight path");
+  constexpr int WST = WL ? BN * 128 : 16;  // bytes of one weight stage
   // one array per stage (see the ring kernel: the compiler's LDS-DMA tracking then
   // tells a stage's reads from the other stages' DMA)
   __shared__ __attribute__((aligned(1024))) uint8_t st0[8192];
@@ -1189,6 +1197,10 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const KArgs p) {
   __shared__ __attribute__((aligned(16))) uint32_t sa_tab[WMAX * 64];       // [w][row]
   __shared__ __attribute__((aligned(16))) uint32_t sb_tab[NBT * WMAX];      // [block][w], byte kb % 4
   __shared__ __attribute__((aligned(16))) uint8_t stage_out[NW * 64 * 32 * 4];  // epilogue: [wave][64][32] fp32
+  __shared__ __attribute__((aligned(1024))) uint8_t wt0[WST];
+  __shared__ __attribute__((aligned(1024))) uint8_t wt1[WST];
+  __shared__ __attribute__((aligned(1024))) uint8_t wt2[WST];
+  __shared__ __attribute__((aligned(1024))) uint8_t wt3[WST];
   static_assert(DB >= 2 && DB <= 4, "two to four stages");
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -1228,6 +1240,16 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const KArgs p) {
     else if constexpr (I == 2) return st2;
     else return st3;
   };
+  auto wstage = [&](auto tag) -> uint8_t* {
+    constexpr int I = decltype(tag)::value;
+    if constexpr (I == 0) return wt0;
+    else if constexpr (I == 1) return wt1;
+    else if constexpr (I == 2) return wt2;
+    else return wt3;
+  };
+  // WL weight DMA: instruction t of this wavefront covers rows 32 wave + 8 t + (l >> 3),
+  // LDS chunk l & 7 holding row chunk (l & 7) ^ (row & 7)
+  const uint32_t wdma_lane = (uint32_t)((lane >> 3) * p.K) + (uint32_t)((((lane & 7) ^ ((lane >> 3) & 7)) << 4));
 
   // activation DMA: instruction t of this wavefront covers K-half hh of rows
   // 16 rq .. 16 rq + 15 (rq, hh from the instruction index i = wave * IA + t:
@@ -1249,6 +1271,14 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const KArgs p) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, (__attribute__((address_space(3))) void*)dst, 16,
                                                (int)((aoff[t] + koff) | oob), 0, 0, 0);
     }
+    if constexpr (WL) {
+      uint8_t* wbase = wstage(tag) + wave * 32 * 128;
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, (__attribute__((address_space(3))) void*)(wbase + t * 1024), 16,
+                                                 (int)((wdma_lane + (uint32_t)((wave * 32 + 8 * t) * p.K) + koff) | oob),
+                                                 0, 0, 0);
+    }
   };
   // weight loads: lane l, row n0 + 32 wave + (l & 31), bytes 32 (l >> 5) + 64 h .. + 31.
   // SHUF: the same bytes from the pre-shuffled layout, where every 32-row group's
@@ -1257,6 +1287,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const KArgs p) {
                              : (uint32_t)((wave * 32 + (lane & 31)) * p.K) + (uint32_t)(32 * (lane >> 5));
   constexpr uint32_t KB_STEP = SHUF ? 4096u : 128u, H_STEP = SHUF ? 2048u : 64u, P_STEP = SHUF ? 1024u : 16u;
   auto load_b = [&](int j, v8i (&bh)[2]) {
+    if constexpr (WL) return;  // the weights come with the activation DMA
     const uint32_t off = (boff + (uint32_t)(kb0 + j) * KB_STEP) | (j < nk ? 0u : kOOB);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -1355,8 +1386,9 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const KArgs p) {
       if (idx < NBT * WMAX * 4) sbb[idx] = (uint8_t)((sbv[t] >> 23) & 0xFFu);
     }
   }
-  // VMEM instructions younger than the activation DMA of the current iteration
-  constexpr int YOUNGER = 4 + (DB - 2) * (IA + 4);
+  // VMEM instructions younger than the activation DMA of the current iteration (WL:
+  // the DMA groups of the next DB - 2 K-blocks; else also the weight loads of the next)
+  constexpr int YOUNGER = WL ? (DB - 2) * (IA + 4) : 4 + (DB - 2) * (IA + 4);
 
   const int lr = lane & 31, c0 = 2 * (lane >> 5);
   const uint32_t rd0 = (uint32_t)(lr * 64 + ((c0 ^ swz64(lr)) << 4));
@@ -1394,6 +1426,18 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const KArgs p) {
         sb = sb_tab[sb_blk * WMAX + (j >> 2)];
       }
       const uint8_t* base = stage(IntC<U % DB>{});
+      if constexpr (WL) {
+        // this wavefront's 32 rows from the weight stage: lane l, row l & 31, logical
+        // chunks 4 h + 2 (l >> 5) and the next (the register path's byte order)
+        const uint8_t* wb = wstage(IntC<U % DB>{}) + (wave * 32 + lr) * 128;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int wc = 4 * h + 2 * (lane >> 5);
+          const v4i lo = *reinterpret_cast<const v4i*>(wb + ((wc ^ (lr & 7)) << 4));
+          const v4i hi = *reinterpret_cast<const v4i*>(wb + (((wc + 1) ^ (lr & 7)) << 4));
+          bcur[h] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        }
+      }
       v8i af[2][IV];
 #pragma unroll
       for (int h = 0; h < 2; ++h)
@@ -1665,6 +1709,10 @@ const TileEntry kTiles[] = {
     {scaled_ring_kernel<256, 256, 2, 2, true>, 256, 256, kRingShuf, 4, 256, ring_wd_max<256, 256, 2, 2>()},
     {scaled_ring_kernel<128, 256, 2, 2, true>, 128, 256, kRingShuf, 4, 256, ring_wd_max<128, 256, 2, 2>()},
     {decode_kernel<4, 3, true, true>, 64, 128, kDecodeFloatShuf, 3, 256, DecodeShape<4, 3>::WMAX / 4},
+    // weights through LDS (whole 128-byte rows per DMA instruction) on the plain layout
+    {decode_kernel<4, 4, false, false, true>, 64, 128, kDecode, 4, 256, DecodeShape<4, 4>::WMAX},
+    {decode_kernel<4, 3, false, false, true>, 64, 128, kDecode, 3, 256, DecodeShape<4, 3>::WMAX},
+    {decode_kernel<4, 3, true, false, true>, 64, 128, kDecodeFloat, 3, 256, DecodeShape<4, 3>::WMAX / 4},
 };
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 // table entries the automatic choice uses
@@ -1677,17 +1725,17 @@ constexpr int kCfgRing128x256 = 19;        // 2 x 2 wavefronts, 128-row tiles
 constexpr int kCfgFloat64x128 = 26;        // float-scale VALU-scaled tiles
 constexpr int kCfgFloat128x128 = 27;
 constexpr int kCfgFloat128x256 = 29;
-constexpr int kCfgFloatDecode64x128 = 30;  // decode kernel, float scales
+constexpr int kCfgFloatDecode64x128 = 44;  // decode kernel, float scales, weights through LDS
 constexpr int kCfgFloatScaled128x128 = 31; // LDS-DMA tiles, float scales
 constexpr int kCfgFloatScaled128x256 = 32;
-constexpr int kCfgDecode64x128 = 22;       // decode kernel, 4 wavefronts, three K-blocks in flight
+constexpr int kCfgDecode64x128 = 43;       // decode kernel, 4 wavefronts, weights through a 3-stage LDS ring
 constexpr int kCfgShufDecode64x128 = 35;   // the same on pre-shuffled weights
 constexpr int kCfgShufRing256x256Rows = 38;  // pre-shuffled weights: ring 256x256, 1 x 4 wavefronts
 constexpr int kCfgShufRing256x256 = 39;      // 2 x 2 wavefronts
 constexpr int kCfgShufRing128x256 = 40;
 constexpr int kCfgFloatShufDecode64x128 = 41;  // float scales, pre-shuffled weights
 static_assert(kCfgDecode64x128 < kNumTiles && kCfgFloatScaled128x256 < kNumTiles, "tile table");
-static_assert(kCfgFloatShufDecode64x128 < kNumTiles, "tile table");
+static_assert(kCfgFloatShufDecode64x128 < kNumTiles && kCfgFloatDecode64x128 < kNumTiles, "tile table");
 
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -1850,8 +1898,10 @@ GemmConfig choose_gemm_config(const GemmProblem& p) {
     return cfg;
   }
   if (p.M <= 64) {
-    // decode: weight streaming over 128-column tiles with the activations shared
-    // through LDS, K split (and reduced in the kernel) until about 224 workgroups
+    // decode: weight streaming over 128-column tiles, weights and activations through
+    // an LDS ring (whole 128-byte weight rows per DMA instruction: 36.9 -> 33.1 us at
+    // 64x7168x18432 against operand-layout register loads), K split (and reduced in
+    // the kernel) until about 224 workgroups
     {
       const int64_t tiles = cdiv(p.N, kTiles[kCfgDecode64x128].bn);
       int splits = (int)(224 / (tiles > 0 ? tiles : 1));
