@@ -183,6 +183,8 @@ def test_config_table_choices():
     m = F.gemm_config(True, 256, 4096, 7168)
     assert m["splits"] == 1 and (m["bm"], m["bn"]) == (256, 256)
     s = F.gemm_config(False, 2048, 4096, 7168)  # 128 tiles of 256 x 256 would leave half the chip idle
+    assert (s["bm"], s["bn"]) == (256, 128)    # 256 tiles of 256 x 128: one whole round
+    s = F.gemm_config(False, 1024, 4096, 7168)  # 128 tiles of 256 x 128 would too
     assert (s["bm"], s["bn"]) == (128, 128)
     with pytest.raises(F.Fp8bsError):
         F.gemm_config(False, 64, 100, 512)
