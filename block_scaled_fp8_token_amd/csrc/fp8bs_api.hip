@@ -512,6 +512,7 @@ int fp8bs_gemm_config(int masked, int64_t M, int64_t N, int64_t K, int32_t* kern
   if (masked < 0 || masked > 6) return FP8BS_ERR_SHAPE;
   const fp8bs::GemmProblem p = host_problem(masked, M, N, K);
   const fp8bs::GemmConfig cfg = fp8bs::choose_gemm_config(p);
+  if (cfg.kernel < 0) return FP8BS_ERR_SHAPE;  // no entry takes this problem (K past every scale table)
   *kernel = cfg.kernel;
   *bm = cfg.bm;
   *bn = cfg.bn;

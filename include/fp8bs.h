@@ -223,7 +223,9 @@ int fp8_block_gemm_grouped_masked(const void* a, const uint32_t* sfa, const void
  * fp8_block_gemm_grouped_masked with the expert weights b in the layout of
  * fp8_weight_preshuffle (rows = E*N, so each expert's [N][K] block is shuffled on
  * its own); every other argument and the result are those of
- * fp8_block_gemm_grouped_masked.
+ * fp8_block_gemm_grouped_masked.  K <= 20480 (a masked group never splits K, and the
+ * kernels reading this layout hold the scales of at most 160 K-blocks); larger K
+ * returns FP8BS_ERR_SHAPE.
  */
 int fp8_block_gemm_grouped_masked_preshuffled(const void* a, const uint32_t* sfa, const void* b,
                                               const float* sfb, void* c, const int32_t* masked_m,

@@ -162,6 +162,14 @@ def test_preshuffle_validation():
     assert g(A, S, 64, B, T, C, 512, 0, 512, 512, None) == OK
 
 
+def test_preshuffled_masked_k_limit():
+    assert F.gemm_config(F.LAYOUT_MASKED_PRESHUFFLED, 256, 4096, 20480)["kernel"] >= 0
+    with pytest.raises(F.Fp8bsError):
+        F.gemm_config(F.LAYOUT_MASKED_PRESHUFFLED, 256, 4096, 20480 + 128)
+    # the plain masked layout falls back to weight streaming there
+    assert F.gemm_config(F.LAYOUT_MASKED, 256, 4096, 20480 + 128)["kernel"] >= 0
+
+
 def test_preshuffled_config_uses_shuffled_entries_only():
     cfg = F.gemm_config(F.LAYOUT_DENSE_PRESHUFFLED, 64, 7168, 18432)
     assert cfg["kernel"] >= 0 and cfg["splits"] >= 1
