@@ -1713,6 +1713,7 @@ const TileEntry kTiles[] = {
     {decode_kernel<4, 4, false, false, true>, 64, 128, kDecode, 4, 256, DecodeShape<4, 4>::WMAX},
     {decode_kernel<4, 3, false, false, true>, 64, 128, kDecode, 3, 256, DecodeShape<4, 3>::WMAX},
     {decode_kernel<4, 3, true, false, true>, 64, 128, kDecodeFloat, 3, 256, DecodeShape<4, 3>::WMAX / 4},
+    {decode_kernel<4, 3, false, false, true>, 64, 128, kDecodeSep, 3, 256, DecodeShape<4, 3>::WMAX},
 };
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 // table entries the automatic choice uses
@@ -1729,8 +1730,9 @@ constexpr int kCfgFloat128x256 = 29;
 constexpr int kCfgFloatDecode64x128 = 44;  // decode kernel, float scales, weights through LDS
 constexpr int kCfgFloatScaled128x128 = 31; // LDS-DMA tiles, float scales
 constexpr int kCfgFloatScaled128x256 = 32;
-constexpr int kCfgDecode64x128 = 43;       // decode kernel, 4 wavefronts, weights through a 3-stage LDS ring
-constexpr int kCfgShufDecode64x128 = 35;   // the same on pre-shuffled weights
+constexpr int kCfgDecode64x128 = 45;       // decode kernel, 4 wavefronts, weights through a 3-stage LDS ring,
+                                           // partials summed by splitk_reduce_kernel
+constexpr int kCfgShufDecode64x128 = 36;   // the same on pre-shuffled weights (register loads)
 constexpr int kCfgShufRing256x256Rows = 38;  // pre-shuffled weights: ring 256x256, 1 x 4 wavefronts
 constexpr int kCfgShufRing256x256 = 39;      // 2 x 2 wavefronts
 constexpr int kCfgShufRing128x256 = 40;
@@ -1835,10 +1837,10 @@ GemmConfig choose_gemm_config(const GemmProblem& p) {
   if (p.b_shuffled) {
     // pre-shuffled weights.  Masked: the 256 x 256 ring tiles with the wavefronts side
     // by side in N, as for the plain layout.  Dense M <= 64: the decode kernel, K split
-    // until about 224 workgroups and reduced by the last split of each tile.  Leaving
-    // the sum to splitk_reduce_kernel makes the call 0.9 us shorter back to back, but a
-    // quant + GEMM step replayed from a graph no faster (one more kernel boundary), so
-    // the single launch stays.
+    // until about 224 workgroups, its partials summed by splitk_reduce_kernel (against
+    // the reduction by the last split of each tile, whose three dependent round trips
+    // run on one CU per tile, 0.9 us shorter per call and 1.2 us per graph-replayed
+    // quant + GEMM step, A/B on one GPU).
     // Larger M: ring tiles, 256 x 256 once they fill the compute units, else 128 x 256.
     // The decode kernel takes whatever the ring's scale tables cannot hold.
     if (p.masked_m) {
@@ -1901,8 +1903,9 @@ GemmConfig choose_gemm_config(const GemmProblem& p) {
   if (p.M <= 64) {
     // decode: weight streaming over 128-column tiles, weights and activations through
     // an LDS ring (whole 128-byte weight rows per DMA instruction: 36.9 -> 33.1 us at
-    // 64x7168x18432 against operand-layout register loads), K split (and reduced in
-    // the kernel) until about 224 workgroups
+    // 64x7168x18432 against operand-layout register loads), K split until about 224
+    // workgroups and the partials summed by splitk_reduce_kernel (0.9 us shorter per
+    // call and per graph-replayed step than the reduction by the last split)
     {
       const int64_t tiles = cdiv(p.N, kTiles[kCfgDecode64x128].bn);
       int splits = (int)(224 / (tiles > 0 ? tiles : 1));
