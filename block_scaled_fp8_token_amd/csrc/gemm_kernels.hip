@@ -1631,11 +1631,12 @@ typedef void (*KernelFn)(const KArgs);
 
 enum Kind { kTile = 0, kStream = 1, kScaled = 2, kRing = 3, kDecode = 4, kTileFloat = 5, kDecodeFloat = 6,
             kScaledFloat = 7, kDecodeSep = 8, kDecodeShuf = 9, kDecodeShufSep = 10, kRingShuf = 11,
-            kDecodeFloatShuf = 12 };
+            kDecodeFloatShuf = 12, kDecodeFloatSep = 13, kDecodeFloatShufSep = 14 };
 
 // Entries that read the float-scale format.
 inline bool reads_float_scales(int kind) {
-  return kind == kTileFloat || kind == kDecodeFloat || kind == kScaledFloat || kind == kDecodeFloatShuf;
+  return kind == kTileFloat || kind == kDecodeFloat || kind == kScaledFloat || kind == kDecodeFloatShuf ||
+         kind == kDecodeFloatSep || kind == kDecodeFloatShufSep;
 }
 // LDS-DMA tile entries (dynamic LDS for the scale tables).
 inline bool is_scaled_tile(int kind) { return kind == kScaled || kind == kScaledFloat; }
@@ -1645,13 +1646,17 @@ inline bool reduces_in_kernel(int kind) {
 }
 // Entries that read the weights in the pre-shuffled layout.
 inline bool reads_shuffled(int kind) {
-  return kind == kDecodeShuf || kind == kDecodeShufSep || kind == kRingShuf || kind == kDecodeFloatShuf;
+  return kind == kDecodeShuf || kind == kDecodeShufSep || kind == kRingShuf || kind == kDecodeFloatShuf ||
+         kind == kDecodeFloatShufSep;
 }
 // Ring entries (K never split; the scale tables bound K).
 inline bool is_ring(int kind) { return kind == kRing || kind == kRingShuf; }
-// Decode-kernel entries (K split in whole scale words; kDecodeSep leaves the sum of
+// Decode-kernel entries (K split in whole scale words; the *Sep kinds leave the sum of
 // the partials to splitk_reduce_kernel).
-inline bool is_decode(int kind) { return reduces_in_kernel(kind) || kind == kDecodeSep || kind == kDecodeShufSep; }
+inline bool is_decode(int kind) {
+  return reduces_in_kernel(kind) || kind == kDecodeSep || kind == kDecodeShufSep || kind == kDecodeFloatSep ||
+         kind == kDecodeFloatShufSep;
+}
 
 struct TileEntry {
   KernelFn fn;
@@ -1714,6 +1719,9 @@ const TileEntry kTiles[] = {
     {decode_kernel<4, 3, false, false, true>, 64, 128, kDecode, 3, 256, DecodeShape<4, 3>::WMAX},
     {decode_kernel<4, 3, true, false, true>, 64, 128, kDecodeFloat, 3, 256, DecodeShape<4, 3>::WMAX / 4},
     {decode_kernel<4, 3, false, false, true>, 64, 128, kDecodeSep, 3, 256, DecodeShape<4, 3>::WMAX},
+    // float scales, partials summed by splitk_reduce_kernel: weights through LDS / pre-shuffled
+    {decode_kernel<4, 3, true, false, true>, 64, 128, kDecodeFloatSep, 3, 256, DecodeShape<4, 3>::WMAX / 4},
+    {decode_kernel<4, 3, true, true>, 64, 128, kDecodeFloatShufSep, 3, 256, DecodeShape<4, 3>::WMAX / 4},
 };
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 // table entries the automatic choice uses
@@ -1727,7 +1735,7 @@ constexpr int kCfgRing256x128 = 18;        // 2 x 2 wavefronts, 128-column tiles
 constexpr int kCfgFloat64x128 = 26;        // float-scale VALU-scaled tiles
 constexpr int kCfgFloat128x128 = 27;
 constexpr int kCfgFloat128x256 = 29;
-constexpr int kCfgFloatDecode64x128 = 44;  // decode kernel, float scales, weights through LDS
+constexpr int kCfgFloatDecode64x128 = 46;  // decode kernel, float scales, weights through LDS, reduction kernel
 constexpr int kCfgFloatScaled128x128 = 31; // LDS-DMA tiles, float scales
 constexpr int kCfgFloatScaled128x256 = 32;
 constexpr int kCfgDecode64x128 = 45;       // decode kernel, 4 wavefronts, weights through a 3-stage LDS ring,
@@ -1736,7 +1744,7 @@ constexpr int kCfgShufDecode64x128 = 36;   // the same on pre-shuffled weights (
 constexpr int kCfgShufRing256x256Rows = 38;  // pre-shuffled weights: ring 256x256, 1 x 4 wavefronts
 constexpr int kCfgShufRing256x256 = 39;      // 2 x 2 wavefronts
 constexpr int kCfgShufRing128x256 = 40;
-constexpr int kCfgFloatShufDecode64x128 = 41;  // float scales, pre-shuffled weights
+constexpr int kCfgFloatShufDecode64x128 = 47;  // float scales, pre-shuffled weights, reduction kernel
 static_assert(kCfgDecode64x128 < kNumTiles && kCfgFloatScaled128x256 < kNumTiles, "tile table");
 static_assert(kCfgFloatShufDecode64x128 < kNumTiles && kCfgFloatDecode64x128 < kNumTiles, "tile table");
 
