@@ -199,3 +199,36 @@ def test_silu_mul_quant_edge_counts():
     assert np.all(q[0] == 0xA5) and np.all(q[3] == 0xA5)
     assert np.all(q[4, 7:] == 0xA5)
     assert np.all(sf[1, 0, :] & 0xFF == 85)
+
+
+def _silu_run_and_check(E, M_max, H, counts, seed):
+    x = W.normal_bf16((E, M_max, 2 * H), seed=seed, tensor_id=W.T_X)
+    Wd = (H // 128 + 3) // 4
+    qd = torch.full((E, M_max, H), 0xA5, dtype=torch.uint8, device=DEV)
+    sfd = torch.full((E, Wd, M_max), 0x3C3C3C3C, dtype=torch.int32, device=DEV)
+    q, sf = F.silu_mul_quant_group_pack(to_dev(x), to_dev(counts), q=qd, sf=sfd)
+    sync()
+    q, sf = to_host(q), to_host(sf)
+    _silu_compare(x, counts, q, sf)
+    for e in range(E):  # rows at or past the clamped count untouched
+        c = int(min(max(counts[e], 0), M_max))
+        assert np.all(q[e, c:] == 0xA5), e
+        assert np.all(sf[e, :, c:] == 0x3C3C3C3C), e
+
+
+def test_silu_mul_quant_many_units_per_wavefront():
+    """18000 (row, word) units over the valid rows (more than the 4096 wavefronts of the
+    grid, so each takes several), three words per row (the stride wraps the word index),
+    empty and clamped experts between full ones, a partial last word (9 groups)."""
+    print("silu E=12 M_max=500 H=1152", flush=True)
+    counts = np.array([500, 0, 499, 500, 17, 500, -1, 600, 500, 250, 500, 1], np.int32)
+    _silu_run_and_check(12, 500, 1152, counts, seed=5)
+
+
+def test_silu_mul_quant_more_than_64_experts():
+    """70 experts: the padded-grid kernel (one unit per wavefront, grid over E)."""
+    print("silu E=70 M_max=6 H=256", flush=True)
+    rng = np.random.default_rng(9)
+    counts = rng.integers(-2, 9, 70).astype(np.int32)
+    counts[:3] = [0, 6, 7]
+    _silu_run_and_check(70, 6, 256, counts, seed=9)
