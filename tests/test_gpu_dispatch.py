@@ -61,6 +61,26 @@ def test_dispatch_many_experts_and_chunks():
     _check(x, ids, E, M_max, "many experts")
 
 
+def test_dispatch_wide_rows():
+    """K = 9216: 18 packed words per row (the grid strides over more units than it has
+    wavefronts' worth of one word each)."""
+    rng = np.random.default_rng(3)
+    T, topk, E, M_max, K = 20, 4, 6, 15, 9216
+    ids = rng.integers(0, E, (T, topk)).astype(np.int32)
+    x = W.normal_bf16((T, K), seed=3, tensor_id=W.T_X)
+    _check(x, ids, E, M_max, "wide rows")
+
+
+def test_dispatch_nine_chunks_with_overflow():
+    """1100 tokens x 8 choices (8800 pairs: nine 1024-pair rank chunks, the last partial),
+    Zipf-skewed ids, capacity overflow on the hot experts."""
+    rng = np.random.default_rng(4)
+    T, topk, E, M_max, K = 1100, 8, 64, 200, 256
+    ids = (rng.zipf(1.3, (T, topk)) % E).astype(np.int32)
+    x = W.normal_bf16((T, K), seed=4, tensor_id=W.T_X)
+    _check(x, ids, E, M_max, "two-pass")
+
+
 def test_dispatch_workload_bit_exact_and_deterministic():
     """512 tokens x top-8 of 32 experts with Zipf(1.1) weights, capacity 256, K = 7168."""
     E, M_max, K = W.MOE_E, W.MOE_M_MAX, W.MOE_GATE_UP["K"]
