@@ -172,7 +172,8 @@ int fp8_block_quant_128x128(const void* w, int64_t N, int64_t K, void* q, float*
  * replaced but never freed, so graphs captured earlier stay valid.  A captured
  * graph keeps the workspace of the stream it was captured on: replay it in
  * stream order with the other calls on that stream (a replay running at the same
- * time as calls on the capture stream would share the split-K counters with them).
+ * time as calls on the capture stream would share the split-K partials with them,
+ * and for the entries that reduce inside the kernel also the arrival counters).
  */
 int fp8_block_gemm_nt(const void* a, const uint32_t* sfa, int64_t ld_sfa, const void* b,
                       const float* sfb, void* c, int64_t ldc, int64_t M, int64_t N, int64_t K,
