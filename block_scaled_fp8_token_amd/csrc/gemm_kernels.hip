@@ -1722,6 +1722,9 @@ const TileEntry kTiles[] = {
     // float scales, partials summed by splitk_reduce_kernel: weights through LDS / pre-shuffled
     {decode_kernel<4, 3, true, false, true>, 64, 128, kDecodeFloatSep, 3, 256, DecodeShape<4, 3>::WMAX / 4},
     {decode_kernel<4, 3, true, true>, 64, 128, kDecodeFloatShufSep, 3, 256, DecodeShape<4, 3>::WMAX / 4},
+    {scaled_ring_kernel<128, 128, 2, 2>, 128, 128, kRing, 4, 256, ring_wd_max<128, 128, 2, 2>()},
+    {scaled_ring_kernel<128, 128, 1, 4>, 128, 128, kRing, 4, 256, ring_wd_max<128, 128, 1, 4>()},
+    {scaled_ring_kernel<128, 128, 2, 2, true>, 128, 128, kRingShuf, 4, 256, ring_wd_max<128, 128, 2, 2>()},
 };
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 // table entries the automatic choice uses
@@ -1745,8 +1748,11 @@ constexpr int kCfgShufRing256x256Rows = 38;  // pre-shuffled weights: ring 256x2
 constexpr int kCfgShufRing256x256 = 39;      // 2 x 2 wavefronts
 constexpr int kCfgShufRing128x256 = 40;
 constexpr int kCfgFloatShufDecode64x128 = 47;  // float scales, pre-shuffled weights, reduction kernel
+constexpr int kCfgRing128x128 = 49;          // ring 128x128, 1 x 4 wavefronts
+constexpr int kCfgShufRing128x128 = 50;      // the same (2 x 2) on pre-shuffled weights
 static_assert(kCfgDecode64x128 < kNumTiles && kCfgFloatScaled128x256 < kNumTiles, "tile table");
 static_assert(kCfgFloatShufDecode64x128 < kNumTiles && kCfgFloatDecode64x128 < kNumTiles, "tile table");
+static_assert(kCfgRing128x128 < kNumTiles && kCfgShufRing128x128 < kNumTiles, "tile table");
 
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -1854,6 +1860,10 @@ GemmConfig choose_gemm_config(const GemmProblem& p) {
     if (p.masked_m) {
       if (gemm_config_by_index(kCfgShufRing256x256Rows, p, 1, &cfg)) return cfg;
     } else if (p.M > 64) {
+      // at most one round of 128x128 tiles: the 128x128 ring (1024x4096x7168: 74.0 ->
+      // 46.9 us against 128x256 ring tiles on half the compute units)
+      if (cdiv(p.M, 128) * cdiv(p.N, 128) <= 256 && gemm_config_by_index(kCfgShufRing128x128, p, 1, &cfg))
+        return cfg;
       const int64_t big_tiles = cdiv(p.M, 256) * cdiv(p.N, 256);
       if (gemm_config_by_index(big_tiles >= 256 ? kCfgShufRing256x256 : kCfgShufRing128x256, p, 1, &cfg))
         return cfg;
@@ -1939,7 +1949,8 @@ GemmConfig choose_gemm_config(const GemmProblem& p) {
     // half the compute units would leave the rest idle for a whole tile time: run
     // the leading columns in whole rounds and the remaining columns with 128x128
     // tiles in a second launch (up to 512 of them: two per compute unit, which
-    // finish well within one 256x256 tile time).
+    // finish well within one 256x256 tile time); the 128x128 ring when they make
+    // at most one round, the two-stage tiles (two per compute unit) otherwise.
     const int64_t rem = big_tiles % 256;
     if (rem != 0 && rem <= 128 && p.E == 1 && !p.masked_m && !p.m_indices) {
       const int64_t lead_tn = (big_tiles / 256) * 256 / tm256;
@@ -1947,7 +1958,10 @@ GemmConfig choose_gemm_config(const GemmProblem& p) {
       GemmProblem tp = p;
       tp.N = p.N - n_split;
       GemmConfig tc;
-      if (n_split > 0 && n_split < p.N && gemm_config_by_index(kCfgScaled128x128, tp, 1, &tc)) {
+      const bool one_round = cdiv(tp.M, 128) * cdiv(tp.N, 128) <= 256;
+      if (n_split > 0 && n_split < p.N &&
+          ((one_round && gemm_config_by_index(kCfgRing128x128, tp, 1, &tc)) ||
+           gemm_config_by_index(kCfgScaled128x128, tp, 1, &tc))) {
         cfg.n_split = n_split;
         cfg.tail_kernel = tc.kernel;
         cfg.tail_bm = tc.bm;
@@ -1965,6 +1979,11 @@ GemmConfig choose_gemm_config(const GemmProblem& p) {
   if (mid_tiles >= 256 && (mid_tiles % 256 == 0 || mid_tiles % 256 > 128) &&
       gemm_config_by_index(kCfgRing256x128, p, 1, &cfg))
     return cfg;
+  // at most one round of 128x128 tiles: the 128x128 ring, four K-blocks in flight
+  // (1024x4096x7168: 63.2 -> 45.0 us against the two-stage tiles); more: the
+  // two-stage tiles, two per compute unit (the ring is slower there: 2048x4096x7168
+  // 87.7 us against 66.2 us for 256x128 ring tiles)
+  if (cdiv(p.M, 128) * cdiv(p.N, 128) <= 256 && gemm_config_by_index(kCfgRing128x128, p, 1, &cfg)) return cfg;
   if (gemm_config_by_index(kCfgScaled128x128, p, 1, &cfg)) return cfg;
   const int idx = 1;
   const int64_t tiles = cdiv(p.M, kTiles[idx].bm) * cdiv(p.N, kTiles[idx].bn);
