@@ -1864,9 +1864,29 @@ GemmConfig choose_gemm_config(const GemmProblem& p) {
       // 46.9 us against 128x256 ring tiles on half the compute units)
       if (cdiv(p.M, 128) * cdiv(p.N, 128) <= 256 && gemm_config_by_index(kCfgShufRing128x128, p, 1, &cfg))
         return cfg;
-      const int64_t big_tiles = cdiv(p.M, 256) * cdiv(p.N, 256);
-      if (gemm_config_by_index(big_tiles >= 256 ? kCfgShufRing256x256 : kCfgShufRing128x256, p, 1, &cfg))
+      const int64_t tm256 = cdiv(p.M, 256), big_tiles = tm256 * cdiv(p.N, 256);
+      if (gemm_config_by_index(big_tiles >= 256 ? kCfgShufRing256x256 : kCfgShufRing128x256, p, 1, &cfg)) {
+        // as for the plain layout: a last round of at most half the compute units
+        // runs its columns as 128x128 ring tiles in a second launch when they make
+        // at most one round (a 32-row group of the layout is 32 K contiguous bytes,
+        // so the column offset of the tail is the plain one)
+        const int64_t rem = big_tiles % 256;
+        if (big_tiles >= 256 && rem != 0 && rem <= 128 && p.E == 1) {
+          const int64_t n_split = (big_tiles / 256) * 256 / tm256 * 256;
+          GemmProblem tp = p;
+          tp.N = p.N - n_split;
+          GemmConfig tc;
+          if (n_split > 0 && n_split < p.N && cdiv(tp.M, 128) * cdiv(tp.N, 128) <= 256 &&
+              gemm_config_by_index(kCfgShufRing128x128, tp, 1, &tc)) {
+            cfg.n_split = n_split;
+            cfg.tail_kernel = tc.kernel;
+            cfg.tail_bm = tc.bm;
+            cfg.tail_bn = tc.bn;
+            cfg.tail_kb_per_split = tc.kb_per_split;
+          }
+        }
         return cfg;
+      }
     }
     const int64_t tiles = cdiv(p.M, kTiles[kCfgShufDecode64x128].bm) * cdiv(p.N, kTiles[kCfgShufDecode64x128].bn);
     int splits = p.masked_m ? 1 : (int)(224 / (tiles > 0 ? tiles : 1));

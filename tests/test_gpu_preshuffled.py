@@ -209,3 +209,24 @@ def test_preshuffled_masked_gate_up_shape_matches_plain():
         sel = np.array([r for r in rows if r < counts[e]], np.int64)
         if sel.size:
             gemm_tolerance_check(cs[e, sel], ref[e, sel], "gate_up expert %d" % e)
+
+
+def test_preshuffled_prefill_column_tail_matches_plain():
+    """2048 x 9216 x 256: 288 tiles of 256 x 256, so the automatic configuration runs the
+    first 8192 columns as 256 x 256 ring tiles and the last 1024 as a second launch of
+    128 x 128 ring tiles, on either weight layout; the two layouts agree bit for bit and
+    sampled rows meet the oracle's tolerance."""
+    M, N, K = 2048, 9216, 256
+    a = W.normal_bf16((M, K), seed=23)
+    b = W.normal_bf16((N, K), std=1.0, seed=23, tensor_id=W.T_B)
+    qa, sfa = O.quant_group_pack(a)
+    qb, sfb = O.block_quant_128x128(b)
+    da, dsa, db, dsb = to_dev(qa), to_dev(sfa), to_dev(qb), to_dev(sfb)
+    c_shuf = to_host(F.fp8_block_gemm_nt_preshuffled(da, dsa, F.fp8_weight_preshuffle(db), dsb,
+                                                     c=poisoned_bf16(M, N)))
+    c_plain = to_host(F.fp8_block_gemm_nt(da, dsa, db, dsb, c=poisoned_bf16(M, N)))
+    sync()
+    rows = np.unique(np.linspace(0, M - 1, 16).astype(np.int64))
+    ref = O.gemm_nt(qa, sfa, qb, sfb, rows=rows)
+    gemm_tolerance_check(c_shuf[rows], ref, "pre-shuffled, column tail")
+    assert np.array_equal(c_shuf, c_plain)
