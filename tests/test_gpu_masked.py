@@ -133,3 +133,21 @@ def test_silu_quant_then_masked_down_chain():
             gemm_tolerance_check(c[e, sel], ref[e, sel], "chain expert %d" % e)
         assert np.all(c[e, counts[e]:] == CANARY)
     assert np.isfinite(bf16_to_f64(c[0, :counts[0]])).all()
+
+
+def test_masked_ragged_round_both_layouts():
+    """16 experts x 256 rows x N = 4608: 288 tiles of 256 x 256 (a last round of 32),
+    counts from empty through partial 32-row groups to clamped.  Valid rows meet the
+    oracle's tolerance, rows past each count keep the canary, and pre-shuffled weights
+    give the same bits."""
+    print("masked E=16 M_max=256 N=4608 K=256", flush=True)
+    E, M_max, N, K = 16, 256, 4608, 256
+    a, sfa, b, sfb = _moe_operands(E, M_max, N, K, seed=6)
+    counts = np.array([256, 0, 129, 128, 1, 255, 300, -1, 64, 200, 256, 17, 130, 2, 256, 90], np.int32)
+    c = _run_masked(a, sfa, b, sfb, counts)
+    _check(c, a, sfa, b, sfb, counts, what="ragged round")
+    cs = torch.empty((E, M_max, N), dtype=torch.int16, device=DEV).fill_(CANARY).view(torch.bfloat16)
+    F.fp8_block_gemm_grouped_masked(to_dev(a), to_dev(sfa), F.fp8_weight_preshuffle(to_dev(b)), to_dev(sfb),
+                                    to_dev(counts), c=cs, preshuffled=True)
+    sync()
+    assert np.array_equal(to_host(cs), c)
