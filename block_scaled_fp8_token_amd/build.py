@@ -1,6 +1,9 @@
 """Build libfp8bs.so in-tree with hipcc for gfx950.
 
-Usage: python -m block_scaled_fp8_token_amd.build   (or call build())
+Usage: python block_scaled_fp8_token_amd/build.py   (or call build())
+
+Run it as a file, not as a module of the package: importing the package loads the
+built library, which fails when that library is older than the headers it binds.
 """
 from __future__ import annotations
 
