@@ -33,7 +33,7 @@ _LIB_PATH = os.path.join(_HERE, "libfp8bs.so")
 _HEADER = os.path.join(os.path.dirname(_HERE), "include", "fp8bs.h")
 
 if not os.path.exists(_LIB_PATH):
-    raise ImportError("libfp8bs.so is not built; run `python -m block_scaled_fp8_token_amd.build` "
+    raise ImportError("libfp8bs.so is not built; run `python block_scaled_fp8_token_amd/build.py` "
                       "(or __graft_entry__.build())")
 
 _lib = ctypes.CDLL(_LIB_PATH)
@@ -74,7 +74,11 @@ _SIGS = {
     "fp8bs_last_hip_error": [],
 }
 for _name, _args in _SIGS.items():
-    _fn = getattr(_lib, _name)
+    try:
+        _fn = getattr(_lib, _name)
+    except AttributeError:
+        raise ImportError("libfp8bs.so does not export %s: it is older than the sources; rebuild with "
+                          "`python block_scaled_fp8_token_amd/build.py`" % _name) from None
     _fn.argtypes = _args
     _fn.restype = ctypes.c_char_p if _name == "fp8bs_status_string" else ctypes.c_int
 
