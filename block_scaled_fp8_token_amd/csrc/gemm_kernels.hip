@@ -2004,6 +2004,10 @@ GemmConfig choose_gemm_config(const GemmProblem& p) {
   // two-stage tiles, two per compute unit (the ring is slower there: 2048x4096x7168
   // 87.7 us against 66.2 us for 256x128 ring tiles)
   if (cdiv(p.M, 128) * cdiv(p.N, 128) <= 256 && gemm_config_by_index(kCfgRing128x128, p, 1, &cfg)) return cfg;
+  // more than one round of 128x128 tiles but at most one of 256x128: the 256x128 ring,
+  // one tile per compute unit (against the two-stage 128x128 tiles: 1024x7168x7168
+  // 73.8 -> 66.4 us, 1536x4096x7168 64.9 -> 61.2 us, 768x8192x7168 68.2 -> 64.3 us)
+  if (mid_tiles <= 256 && gemm_config_by_index(kCfgRing256x128, p, 1, &cfg)) return cfg;
   if (gemm_config_by_index(kCfgScaled128x128, p, 1, &cfg)) return cfg;
   const int idx = 1;
   const int64_t tiles = cdiv(p.M, kTiles[idx].bm) * cdiv(p.N, kTiles[idx].bn);

@@ -193,7 +193,9 @@ def test_config_table_choices():
     s = F.gemm_config(False, 2048, 4096, 7168)  # 128 tiles of 256 x 256 would leave half the chip idle
     assert (s["bm"], s["bn"]) == (256, 128)    # 256 tiles of 256 x 128: one whole round
     s = F.gemm_config(False, 1024, 4096, 7168)  # 128 tiles of 256 x 128 would too
-    assert (s["bm"], s["bn"]) == (128, 128)
+    assert (s["bm"], s["bn"]) == (128, 128)     # 256 tiles of 128 x 128: one round
+    s = F.gemm_config(False, 1024, 7168, 7168)  # 448 tiles of 128 x 128, 224 of 256 x 128
+    assert (s["bm"], s["bn"]) == (256, 128)
     with pytest.raises(F.Fp8bsError):
         F.gemm_config(False, 64, 100, 512)
 
