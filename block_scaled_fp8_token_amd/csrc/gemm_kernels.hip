@@ -1156,7 +1156,11 @@ constexpr int ring_wd_max() { return RingShape<BM, BN, WGM, WGN>::WD_MAX; }
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 // An empty use of a register pair: the loads that wrote it must be issued.
 __device__ __forceinline__ void keep_issued(const v8i (&r)[2]) { asm volatile("" ::"v"(r[0]), "v"(r[1])); }
+__device__ __forceinline__ void keep_issued4(const v4i (&r)[4]) {
+  asm volatile("" ::"v"(r[0]), "v"(r[1]), "v"(r[2]), "v"(r[3]));
+}
 constexpr int kSC1 = 16;              // cache-policy bit sc1 of buffer loads/stores (gfx940 family)
+constexpr int kNT = 2;                // cache-policy bit nt: streamed data, not kept in the caches
 constexpr int kDecodeMaxSplits = 8;   // K splits the decode kernel reduces itself
 constexpr int kDecodeSepMaxSplits = 16;  // K splits of the decode kernel left to splitk_reduce_kernel
 constexpr int kCounterBytes = 65536;  // split-K arrival counters at the front of the workspace
@@ -1180,7 +1184,7 @@ struct DecodeShape {
 // c ^ (r & 7): the operand reads below are conflict-free), into a ring of DB stages
 // filled DB - 1 K-blocks ahead with the activations; the MFMA operands are then read
 // from LDS in the lane layout the register path loads directly.
-template <int NW, int DB_, bool FS = false, bool SHUF = false, bool WL = false>
+template <int NW, int DB_, bool FS = false, bool SHUF = false, bool WL = false, bool NTL = false>
 __global__ __launch_bounds__(NW * 64) void decode_kernel(const KArgs p) {
   using D = DecodeShape<NW, DB_>;
   constexpr int DB = D::DB, UN = D::UN, IA = D::IA, WMAX = D::WMAX, NBT = D::NBT;
@@ -1277,7 +1281,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const KArgs p) {
       for (int t = 0; t < 4; ++t)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, (__attribute__((address_space(3))) void*)(wbase + t * 1024), 16,
                                                  (int)((wdma_lane + (uint32_t)((wave * 32 + 8 * t) * p.K) + koff) | oob),
-                                                 0, 0, 0);
+                                                 0, 0, NTL ? kNT : 0);
     }
   };
   // weight loads: lane l, row n0 + 32 wave + (l & 31), bytes 32 (l >> 5) + 64 h .. + 31.
@@ -1291,8 +1295,8 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const KArgs p) {
     const uint32_t off = (boff + (uint32_t)(kb0 + j) * KB_STEP) | (j < nk ? 0u : kOOB);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const v4i lo = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rB, (int)(off + H_STEP * h), 0, 0));
-      const v4i hi = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rB, (int)(off + H_STEP * h + P_STEP), 0, 0));
+      const v4i lo = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rB, (int)(off + H_STEP * h), 0, NTL ? kNT : 0));
+      const v4i hi = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rB, (int)(off + H_STEP * h + P_STEP), 0, NTL ? kNT : 0));
       bh[h] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
     }
   };
@@ -1625,13 +1629,390 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const KArgs p) {
 }
 
 // ---------------------------------------------------------------------------
+// Weight-streaming decode kernel (dense M <= 64, weights in the pre-shuffled
+// layout).  Four wavefronts; wavefront w owns the 32 output columns n0 + 32 w ..
+// + 31 of a 64 x 128 tile, and K is split over workgroups.  The time of a
+// decode-sized GEMM is the time to stream its weights, and a workgroup streams at
+// the rate (bytes in flight) / (memory latency), so the kernel is built to keep
+// many weight bytes in flight with little else on the issue path:
+//   * weights: each lane loads its operand bytes straight into registers (one
+//     contiguous kilobyte per load instruction in the pre-shuffled layout), D
+//     K-blocks ahead of use, as non-temporal loads (streamed data that no other
+//     workgroup reads: on MI355X a streaming read reaches ~6.4 TB/s this way
+//     against ~5.7 TB/s with ordinary loads);
+//   * activations: the 64 x 128-byte K-blocks go to LDS by DMA in groups of four,
+//     one group ahead, so the workgroup meets at a barrier once per four K-blocks;
+//   * UE8M0 exponents from LDS tables are the MFMA scale operands.
+// With RED the K split is summed in the kernel: after its loop a workgroup takes a
+// ticket on its tile (device-scope atomic); all but the last store their fp32
+// partials with device-coherent stores and then count themselves ready; the last
+// waits until the others are ready (they hold tickets, so they are running and
+// will be), loads their partials and adds all of them in split order (so the sum
+// does not depend on who arrived last) and writes bf16.  It leaves both counters
+// at zero for the next call.  Without RED the partials go to splitk_reduce_kernel.
+template <int D, int RED>
+struct WsdShape {
+  static constexpr int AG = 4;                       // K-blocks per activation group
+  static constexpr int UN = D == 4 ? 8 : 24;         // unroll: weight ring, group buffer and scale byte static
+  static constexpr int WMAX = 40;                    // scale words per row per split
+  static constexpr int ASZ = AG * 8192;              // one activation group in LDS
+};
+
+template <int D, int RED>
+__global__ __launch_bounds__(256) void wsd_kernel(const KArgs p) {
+  using S_ = WsdShape<D, RED>;
+  constexpr int AG = S_::AG, UN = S_::UN, WMAX = S_::WMAX, ASZ = S_::ASZ;
+  static_assert(D == 3 || D == 4 || D == 6, "weight ring depth");
+  __shared__ __attribute__((aligned(1024))) uint8_t ab0[ASZ];
+  __shared__ __attribute__((aligned(1024))) uint8_t ab1[ASZ];
+  __shared__ __attribute__((aligned(16))) uint32_t sa_tab[WMAX * 64];  // [w][row]
+  __shared__ __attribute__((aligned(16))) uint32_t sb_tab[WMAX];       // [w], byte kb % 4
+  __shared__ int s_ticket;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // workgroup -> (column tile, split): workgroups are dispatched to the eight XCDs
+  // in turn (a workgroup's XCD is its linear id mod 8), so tile tn's splits get ids
+  // congruent to tn mod 8 and share one XCD and its L2.  The grid is padded to
+  // 8 ceil(T / 8) S workgroups; those past the last tile have nothing to do.
+  const int id = blockIdx.x, S = p.splits, T = p.tiles_n;
+  const int jj = id >> 3;
+  const int tn = (id & 7) + 8 * (jj / S), split = jj - (jj / S) * S;
+  if (tn >= T) return;
+  const int64_t m_limit = p.M;
+  const int64_t n0 = (int64_t)tn * 128;
+  const int KB = (int)(p.K / 128);
+  const int kb0 = split * p.kb_per_split;
+  const int nk = (KB - kb0 < p.kb_per_split) ? KB - kb0 : p.kb_per_split;  // >= 1 (host)
+  const int nk4 = (nk + 3) & ~3;
+  const int nfull = nk4 / UN * UN;
+  const int NB = (int)((p.N + 127) / 128);
+  const int64_t rows_valid = m_limit < 64 ? m_limit : 64;
+  int64_t cols_valid = p.N - n0;
+  cols_valid = cols_valid > 128 ? 128 : cols_valid;
+  const auto rA = make_rsrc(p.a, (uint32_t)(rows_valid * p.K));
+  const auto rB = make_rsrc(p.b + n0 * p.K, (uint32_t)(cols_valid * p.K));
+  const int Wd = (KB + 3) / 4;
+  const auto rSA = make_rsrc(p.sfa, (uint32_t)(Wd * p.ld_sfa * 4));
+  const auto rSB = make_rsrc(p.sfb, (uint32_t)(NB * KB * 4));
+
+  // activation DMA of K-block j into group buffer `buf` at position u: instruction t
+  // (0, 1) of this wavefront covers K-half hh = i >> 2 of rows 16 (i & 3) .. + 15,
+  // i = 2 wave + t; lane l -> row 16 (i & 3) + (l >> 2), LDS chunk l & 3 holding
+  // chunk (l & 3) ^ swz64(row) of the K-half
+  uint32_t aoff[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int i = wave * 2 + t;
+    const int r = (i & 3) * 16 + (lane >> 2);
+    aoff[t] = (uint32_t)(r * p.K) + (uint32_t)((i >> 2) * 64) + (uint32_t)((((lane & 3) ^ swz64(r)) << 4));
+  }
+  auto dma_group = [&](int g, uint8_t* buf) {
+#pragma unroll
+    for (int u = 0; u < AG; ++u) {
+      const int j = g * AG + u;
+      const uint32_t koff = (uint32_t)(kb0 + j) * 128u, oob = j < nk ? 0u : kOOB;
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int i = wave * 2 + t;
+        uint8_t* dst = buf + u * 8192 + (i >> 2) * 4096 + (i & 3) * 1024;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, (__attribute__((address_space(3))) void*)dst, 16,
+                                                 (int)((aoff[t] + koff) | oob), 0, 0, 0);
+      }
+    }
+  };
+  // weight loads of K-block j: lane l, 16 bytes at 1 KB steps (pre-shuffled layout,
+  // 32-row group of this wavefront)
+  const uint32_t boff = (uint32_t)(wave * 32 * p.K) + (uint32_t)(16 * lane);
+  auto load_w = [&](int j, v4i (&w)[4]) {
+    const uint32_t off = (boff + (uint32_t)(kb0 + j) * 4096u) | (j < nk ? 0u : kOOB);
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      w[q] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rB, (int)(off + 1024u * q), 0, kNT));
+  };
+
+  // scale tables of this split: activation words of the 64 rows (zero past the
+  // rows and for K-blocks past the split), weight exponent bytes of this tile's
+  // column block
+  const int w0 = kb0 / 4;  // kb0 is a multiple of 4 (host)
+  const int nw = nk4 / 4;  // <= WMAX (host)
+  constexpr int SA_PT = (WMAX * 64 + 255) / 256, SB_PT = (WMAX * 4 + 255) / 256;
+  uint32_t sav[SA_PT], sbv[SB_PT];
+  dma_group(0, ab0);
+#pragma unroll
+  for (int t = 0; t < SA_PT; ++t) {
+    const int idx = t * 256 + tid, w = idx >> 6, row = idx & 63;
+    const bool ok = idx < nw * 64 && row < m_limit && w0 + w < Wd;
+    sav[t] = bload4(rSA, ok ? (uint32_t)(((int64_t)(w0 + w) * p.ld_sfa + row) * 4) : kOOB);
+  }
+#pragma unroll
+  for (int t = 0; t < SB_PT; ++t) {
+    const int idx = t * 256 + tid;
+    const bool ok = idx < WMAX * 4 && idx < nk;
+    sbv[t] = bload4(rSB, ok ? (uint32_t)(((n0 >> 7) * KB + kb0 + idx) * 4) : kOOB);
+  }
+  v4i wr[D][4];
+#pragma unroll
+  for (int d = 0; d < D; ++d) load_w(d, wr[d]);
+#pragma unroll
+  for (int t = 0; t < SA_PT; ++t) {
+    const int idx = t * 256 + tid, w = idx >> 6;
+    uint32_t v = sav[t];
+    const int left = kb0 + nk - 4 * (w0 + w);  // K-blocks of this word inside the split
+    if (left < 4) v &= left <= 0 ? 0u : ((1u << (8 * left)) - 1u);
+    if (idx < WMAX * 64) sa_tab[idx] = v;
+  }
+  {
+    uint8_t* sbb = reinterpret_cast<uint8_t*>(sb_tab);
+#pragma unroll
+    for (int t = 0; t < SB_PT; ++t) {
+      const int idx = t * 256 + tid;
+      if (idx < WMAX * 4) sbb[idx] = (uint8_t)((sbv[t] >> 23) & 0xFFu);
+    }
+  }
+  // the first activation group and the tables in place everywhere (the weight loads
+  // issued after them may still be in flight)
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm(4 * D, 0));
+  __builtin_amdgcn_s_barrier();
+
+  const int lr = lane & 31, c0 = 2 * (lane >> 5);
+  const uint32_t rd0 = (uint32_t)(lr * 64 + ((c0 ^ swz64(lr)) << 4));
+  const uint32_t rd1 = (uint32_t)(lr * 64 + (((c0 + 1) ^ swz64(lr)) << 4));
+
+  auto body = [&](auto iv_tag) {
+    constexpr int IV = decltype(iv_tag)::value;  // 32-row groups with valid rows (1 or 2)
+    v16f acc[IV];
+#pragma unroll
+    for (int i = 0; i < IV; ++i)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[i][q] = 0.0f;
+    uint32_t sa[IV], sb = 0;
+
+    // iteration j = jb + U (jb a multiple of UN)
+    auto iter = [&](int jb, auto u_tag) {
+      constexpr int U = decltype(u_tag)::value;
+      constexpr int OPS = U % 4, SLOT = U % D, GB = (U / AG) % 2, POS = U % AG;
+      const int j = jb + U;
+      if constexpr (POS == 0) {
+        // a new activation group: its DMA (issued one group ago, followed by that
+        // group's AG x 4 weight loads) has landed here and everywhere, and nobody
+        // reads the other buffer any more: refill it with the next group
+        __builtin_amdgcn_sched_barrier(0);
+        if (j > 0) {  // the prologue's barrier opens group 0
+          __builtin_amdgcn_s_waitcnt(waitcnt_imm(4 * AG, 15));
+          __builtin_amdgcn_s_barrier();
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        dma_group(j / AG + 1, GB == 0 ? ab1 : ab0);
+        // the group barrier's wait counts exactly the AG x 4 weight loads issued
+        // after this DMA: nothing may move above it
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if constexpr (OPS == 0) {
+#pragma unroll
+        for (int i = 0; i < IV; ++i) sa[i] = sa_tab[(j >> 2) * 64 + 32 * i + lr];
+        sb = sb_tab[j >> 2];
+      }
+      const uint8_t* base = (GB == 0 ? ab0 : ab1) + POS * 8192;
+      v8i af[2][IV];
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int i = 0; i < IV; ++i) {
+          const uint8_t* q = base + h * 4096 + (32 * i) * 64;
+          const v4i lo = *reinterpret_cast<const v4i*>(q + rd0);
+          const v4i hi = *reinterpret_cast<const v4i*>(q + rd1);
+          af[h][i] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        }
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const v8i bw = __builtin_shufflevector(wr[SLOT][2 * h], wr[SLOT][2 * h + 1], 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+        for (int i = 0; i < IV; ++i)
+          acc[i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bw, af[h][i], acc[i], 0, 0, OPS, (int)sb, OPS,
+                                                                   (int)sa[i]);
+      }
+      load_w(j + D, wr[SLOT]);  // the registers of j are free again: fetch j + D
+      // issue the loads here: left to itself the scheduler sinks them towards the
+      // end of the activation group, which shortens the prefetch distance
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    for (int jb = 0; jb < nfull; jb += UN) {
+      iter(jb, IntC<0>{}); iter(jb, IntC<1>{}); iter(jb, IntC<2>{}); iter(jb, IntC<3>{});
+      iter(jb, IntC<4>{}); iter(jb, IntC<5>{}); iter(jb, IntC<6>{}); iter(jb, IntC<7>{});
+      if constexpr (UN == 24) {
+        iter(jb, IntC<8>{}); iter(jb, IntC<9>{}); iter(jb, IntC<10>{}); iter(jb, IntC<11>{});
+        iter(jb, IntC<12>{}); iter(jb, IntC<13>{}); iter(jb, IntC<14>{}); iter(jb, IntC<15>{});
+        iter(jb, IntC<16>{}); iter(jb, IntC<17>{}); iter(jb, IntC<18>{}); iter(jb, IntC<19>{});
+        iter(jb, IntC<20>{}); iter(jb, IntC<21>{}); iter(jb, IntC<22>{}); iter(jb, IntC<23>{});
+      }
+    }
+    // tail: the remaining K-blocks (a multiple of four, fewer than UN) continue the
+    // ring from U = 0, one activation group at a time
+    const int rest = nk4 - nfull;
+    if (rest >= 4) { iter(nfull, IntC<0>{}); iter(nfull, IntC<1>{}); iter(nfull, IntC<2>{}); iter(nfull, IntC<3>{}); }
+    if (rest >= 8) { iter(nfull, IntC<4>{}); iter(nfull, IntC<5>{}); iter(nfull, IntC<6>{}); iter(nfull, IntC<7>{}); }
+    if constexpr (UN == 24) {
+      if (rest >= 12) { iter(nfull, IntC<8>{}); iter(nfull, IntC<9>{}); iter(nfull, IntC<10>{}); iter(nfull, IntC<11>{}); }
+      if (rest >= 16) { iter(nfull, IntC<12>{}); iter(nfull, IntC<13>{}); iter(nfull, IntC<14>{}); iter(nfull, IntC<15>{}); }
+      if (rest >= 20) { iter(nfull, IntC<16>{}); iter(nfull, IntC<17>{}); iter(nfull, IntC<18>{}); iter(nfull, IntC<19>{}); }
+    }
+    // the loads issued past the range (out of range: zeros, into registers and the
+    // spare group buffer) must land before the LDS is reused or released
+#pragma unroll
+    for (int d = 0; d < D; ++d) keep_issued4(wr[d]);
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
+    __builtin_amdgcn_s_barrier();
+
+    // epilogue: stage the wavefront's 64 x 32 fp32 block in LDS (16-byte chunk c of
+    // row r at c ^ (r & 7)); lane l then holds 4 consecutive columns of row
+    // 8 t + (l >> 3) for t < 4 IV
+    float* so = reinterpret_cast<float*>(ab0 + wave * 64 * 128);
+#pragma unroll
+    for (int i = 0; i < IV; ++i) {
+      const int row = 32 * i + lr;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int chunk = 2 * q + (lane >> 5);
+        *reinterpret_cast<v4f*>(reinterpret_cast<uint8_t*>(so) + row * 128 + ((chunk ^ (row & 7)) << 4)) =
+            v4f{acc[i][4 * q], acc[i][4 * q + 1], acc[i][4 * q + 2], acc[i][4 * q + 3]};
+      }
+    }
+    const int ch = lane & 7;
+    const int64_t n = n0 + wave * 32 + 4 * ch;
+    v4f part[IV * 4];
+#pragma unroll
+    for (int t = 0; t < IV * 4; ++t) {
+      const int row = t * 8 + (lane >> 3);
+      part[t] = *reinterpret_cast<const v4f*>(reinterpret_cast<const uint8_t*>(so) + row * 128 + ((ch ^ (row & 7)) << 4));
+    }
+    auto store_c = [&](int t, v4f v) {
+      const int64_t m = t * 8 + (lane >> 3);
+      if (m >= m_limit || n >= p.N) return;
+      uint2 o;
+      o.x = bf16_rne(v[0]) | (bf16_rne(v[1]) << 16);
+      o.y = bf16_rne(v[2]) | (bf16_rne(v[3]) << 16);
+      *reinterpret_cast<uint2*>(p.c + m * p.ldc + n) = o;
+    };
+    if (S == 1) {
+#pragma unroll
+      for (int t = 0; t < IV * 4; ++t) store_c(t, part[t]);
+      return;
+    }
+    if constexpr (RED == 0) {
+      const size_t slice = (size_t)p.M * (size_t)p.N;
+#pragma unroll
+      for (int t = 0; t < IV * 4; ++t) {
+        const int64_t m = t * 8 + (lane >> 3);
+        if (m < m_limit && n < p.N) *reinterpret_cast<v4f*>(p.ws + (size_t)split * slice + (size_t)m * p.N + n) = part[t];
+      }
+      return;
+    } else {
+      // partials [split][M][N] fp32, as for splitk_reduce_kernel
+      const size_t slice = (size_t)p.M * (size_t)p.N;
+      uint32_t* cnt = p.counters + 2 * tn;
+      const auto rW = make_rsrc(p.ws, (uint32_t)((size_t)S * slice * 4));
+      auto poff = [&](int sp, int t) -> uint32_t {
+        const int64_t m = t * 8 + (lane >> 3);
+        return (m < m_limit && n < p.N) ? (uint32_t)(((size_t)sp * slice + (size_t)m * p.N + n) * 4) : kOOB;
+      };
+      auto sum_and_store = [&](auto pol_tag) {
+        constexpr int load_pol = decltype(pol_tag)::value;
+        v4f sum[IV * 4];
+#pragma unroll
+        for (int t = 0; t < IV * 4; ++t) sum[t] = v4f{0.f, 0.f, 0.f, 0.f};
+        for (int sb0 = 0; sb0 < S; sb0 += 4) {
+          v4f pt[4][IV * 4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int t = 0; t < IV * 4; ++t) {
+              const int sp = sb0 + u;
+              pt[u][t] = __builtin_bit_cast(
+                  v4f, __builtin_amdgcn_raw_buffer_load_b128(rW, (int)(sp < S && sp != split ? poff(sp, t) : kOOB), 0, load_pol));
+            }
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int t = 0; t < IV * 4; ++t)
+              if (sb0 + u < S) sum[t] += sb0 + u == split ? part[t] : pt[u][t];
+        }
+#pragma unroll
+        for (int t = 0; t < IV * 4; ++t) store_c(t, sum[t]);
+      };
+      if constexpr (RED == 1) {
+        // ticket first: all but the last store their partials and count themselves
+        // ready; the last waits for that, then sums (device-coherent accesses)
+        if (tid == 0) s_ticket = (int)__hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();
+        const int ticket = s_ticket;
+        if (ticket < S - 1) {
+#pragma unroll
+          for (int t = 0; t < IV * 4; ++t)
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, part[t]), rW, (int)poff(split, t), 0, kSC1);
+          __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
+          __syncthreads();
+          if (tid == 0) __hip_atomic_fetch_add(cnt + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          return;
+        }
+        if (tid == 0) {
+          for (int it = 0; it < (1 << 24); ++it) {
+            if (__hip_atomic_load(cnt + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= (uint32_t)(S - 1)) break;
+            __builtin_amdgcn_s_sleep(1);
+          }
+          __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          __hip_atomic_store(cnt + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        __syncthreads();
+        sum_and_store(IntC<kSC1>{});
+      } else {
+        // store first, then the ticket: the last to arrive finds every other partial
+        // stored.  Mode 2 keeps the partials in the L2 of the XCD the tile's splits
+        // share (plain stores, loads that skip only the CU cache) and checks from the
+        // ticket that they did share one; mode 3 writes them through to memory.
+        const uint32_t xcc = (uint32_t)__builtin_amdgcn_s_getreg((20) | (0 << 6) | ((4 - 1) << 11)) & 15u;
+#pragma unroll
+        for (int t = 0; t < IV * 4; ++t)
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, part[t]), rW, (int)poff(split, t), 0,
+                                                 RED == 2 ? 0 : kSC1);
+        __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
+        __syncthreads();
+        // ticket word: arrivals in bits 0-3, arrivals per XCD in 3-bit fields from bit 4
+        const uint32_t add = 1u | (xcc < 8 ? (1u << (4 + 3 * xcc)) : 0u);
+        if (tid == 0) s_ticket = (int)__hip_atomic_fetch_add(cnt, add, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();
+        const uint32_t all = (uint32_t)s_ticket + add;
+        if ((int)(all & 15u) != S) return;
+        if (tid == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (RED == 2 && (xcc >= 8 || (int)((all >> (4 + 3 * xcc)) & 7u) != S)) {
+          // the splits did not share an XCD: their partials are not all visible here
+#pragma unroll
+          for (int t = 0; t < IV * 4; ++t) {
+            const float nanv = __uint_as_float(0x7FC00000u);
+            store_c(t, v4f{nanv, nanv, nanv, nanv});
+          }
+          return;
+        }
+        sum_and_store(IntC<1>{});  // sc0: past the CU cache, from L2
+      }
+    }
+  };
+  if (rows_valid > 32) body(IntC<2>{});
+  else body(IntC<1>{});
+}
+
+// ---------------------------------------------------------------------------
 // compiled tile table
 
 typedef void (*KernelFn)(const KArgs);
 
 enum Kind { kTile = 0, kStream = 1, kScaled = 2, kRing = 3, kDecode = 4, kTileFloat = 5, kDecodeFloat = 6,
             kScaledFloat = 7, kDecodeSep = 8, kDecodeShuf = 9, kDecodeShufSep = 10, kRingShuf = 11,
-            kDecodeFloatShuf = 12, kDecodeFloatSep = 13, kDecodeFloatShufSep = 14 };
+            kDecodeFloatShuf = 12, kDecodeFloatSep = 13, kDecodeFloatShufSep = 14, kWsd = 15, kWsdSep = 16 };
+
+// Weight-streaming decode entries (pre-shuffled weights, dense M <= 64, 1-D grid).
+inline bool is_wsd(int kind) { return kind == kWsd || kind == kWsdSep; }
 
 // Entries that read the float-scale format.
 inline bool reads_float_scales(int kind) {
@@ -1642,12 +2023,12 @@ inline bool reads_float_scales(int kind) {
 inline bool is_scaled_tile(int kind) { return kind == kScaled || kind == kScaledFloat; }
 // Entries that reduce their own K split (arrival counters in the workspace).
 inline bool reduces_in_kernel(int kind) {
-  return kind == kDecode || kind == kDecodeFloat || kind == kDecodeShuf || kind == kDecodeFloatShuf;
+  return kind == kDecode || kind == kDecodeFloat || kind == kDecodeShuf || kind == kDecodeFloatShuf || kind == kWsd;
 }
 // Entries that read the weights in the pre-shuffled layout.
 inline bool reads_shuffled(int kind) {
   return kind == kDecodeShuf || kind == kDecodeShufSep || kind == kRingShuf || kind == kDecodeFloatShuf ||
-         kind == kDecodeFloatShufSep;
+         kind == kDecodeFloatShufSep || is_wsd(kind);
 }
 // Ring entries (K never split; the scale tables bound K).
 inline bool is_ring(int kind) { return kind == kRing || kind == kRingShuf; }
@@ -1655,7 +2036,7 @@ inline bool is_ring(int kind) { return kind == kRing || kind == kRingShuf; }
 // the partials to splitk_reduce_kernel).
 inline bool is_decode(int kind) {
   return reduces_in_kernel(kind) || kind == kDecodeSep || kind == kDecodeShufSep || kind == kDecodeFloatSep ||
-         kind == kDecodeFloatShufSep;
+         kind == kDecodeFloatShufSep || is_wsd(kind);
 }
 
 struct TileEntry {
@@ -1725,6 +2106,17 @@ const TileEntry kTiles[] = {
     {scaled_ring_kernel<128, 128, 2, 2>, 128, 128, kRing, 4, 256, ring_wd_max<128, 128, 2, 2>()},
     {scaled_ring_kernel<128, 128, 1, 4>, 128, 128, kRing, 4, 256, ring_wd_max<128, 128, 1, 4>()},
     {scaled_ring_kernel<128, 128, 2, 2, true>, 128, 128, kRingShuf, 4, 256, ring_wd_max<128, 128, 2, 2>()},
+    // weights loaded non-temporally (streamed past the caches)
+    {decode_kernel<4, 3, false, true, false, true>, 64, 128, kDecodeShufSep, 3, 256, DecodeShape<4, 3>::WMAX},
+    {decode_kernel<4, 3, false, false, true, true>, 64, 128, kDecodeSep, 3, 256, DecodeShape<4, 3>::WMAX},
+    {decode_kernel<8, 3, false, true, false, true>, 64, 256, kDecodeShufSep, 3, 512, DecodeShape<8, 3>::WMAX},
+    {decode_kernel<4, 2, false, true, false, true>, 64, 128, kDecodeShufSep, 2, 256, DecodeShape<4, 2>::WMAX},
+    // weight streaming: registers D K-blocks ahead, activation groups, split summed in the kernel or not
+    {wsd_kernel<4, 1>, 64, 128, kWsd, 4, 256, WsdShape<4, 1>::WMAX},
+    {wsd_kernel<4, 2>, 64, 128, kWsd, 4, 256, WsdShape<4, 2>::WMAX},
+    {wsd_kernel<4, 3>, 64, 128, kWsd, 4, 256, WsdShape<4, 3>::WMAX},
+    {wsd_kernel<4, 0>, 64, 128, kWsdSep, 4, 256, WsdShape<4, 0>::WMAX},
+    {wsd_kernel<3, 2>, 64, 128, kWsd, 3, 256, WsdShape<3, 2>::WMAX},
 };
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 // table entries the automatic choice uses
@@ -1802,12 +2194,14 @@ bool gemm_config_by_index(int idx, const GemmProblem& p, int splits, GemmConfig*
       ++splits;
     }
   }
+  if (is_wsd(kTiles[idx].kind) && (p.M > 64 || p.E != 1 || p.masked_m || p.m_indices)) return false;
   if (is_decode(kTiles[idx].kind)) {
     // K-blocks per split: a multiple of four (whole words of packed scales, so the
     // scale byte of every unrolled iteration is static), at most four per word of
     // the scale table
     const bool in_kernel = reduces_in_kernel(kTiles[idx].kind);
-    const int max_splits = in_kernel ? kDecodeMaxSplits : kDecodeSepMaxSplits;
+    // (the weight-streaming kernel's arrival word counts at most seven splits per XCD)
+    const int max_splits = kTiles[idx].kind == kWsd ? 7 : in_kernel ? kDecodeMaxSplits : kDecodeSepMaxSplits;
     if (splits > max_splits) splits = max_splits;
     int per = (int)cdiv(cdiv(KB, splits), 4) * 4;
     if (per > 4 * kTiles[idx].max_wd) {
@@ -1816,7 +2210,7 @@ bool gemm_config_by_index(int idx, const GemmProblem& p, int splits, GemmConfig*
     }
     const int64_t tiles = cdiv(p.M, kTiles[idx].bm) * cdiv(p.N, kTiles[idx].bn);
     if (cdiv(KB, per) > 1 &&
-        (cdiv(KB, per) > max_splits || (in_kernel && tiles > kCounterBytes / 4) ||
+        (cdiv(KB, per) > max_splits || (in_kernel && tiles > kCounterBytes / 8) ||
          cdiv(KB, per) * p.M * p.N * 4 > 0x7FFFFFFF))
       return false;
     out->kernel = idx;
@@ -2099,7 +2493,13 @@ hipError_t launch_gemm(const GemmProblem& p, const GemmConfig& cfg, void* ws, hi
       }
     }
   }
-  hipLaunchKernelGGL(t.fn, dim3((unsigned)tiles, (unsigned)cfg.splits, (unsigned)p.E), dim3(t.threads), dyn, stream, k);
+  if (is_wsd(t.kind)) {
+    if (p.E != 1 || k.tiles_m != 1) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(t.fn, dim3((unsigned)(cdiv(tiles, 8) * 8 * cfg.splits)), dim3(t.threads), 0, stream, k);
+  } else {
+    hipLaunchKernelGGL(t.fn, dim3((unsigned)tiles, (unsigned)cfg.splits, (unsigned)p.E), dim3(t.threads), dyn, stream,
+                       k);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || cfg.splits == 1 || reduces_in_kernel(t.kind)) return e;  // the decode kernels reduce themselves
   const int64_t threads = p.M * (p.N / 8);

@@ -210,7 +210,9 @@ def test_config_of_table_entries():
         e = F.gemm_config_of(c["kernel"], masked, M, N, K, c["splits"])
         assert e is not None and (e["bm"], e["bn"], e["splits"]) == (c["bm"], c["bn"], c["splits"])
     fl = [k for k in range(n) if F.gemm_config_of(k, F.LAYOUT_DENSE_FLOAT, 72, 192, 384) is not None]
-    sh = [k for k in range(n) if F.gemm_config_of(k, F.LAYOUT_DENSE_PRESHUFFLED, 72, 192, 384) is not None]
+    # (the weight-streaming decode entries take M <= 64 only)
+    sh = [k for k in range(n) if F.gemm_config_of(k, F.LAYOUT_DENSE_PRESHUFFLED, 72, 192, 384) is not None
+          or F.gemm_config_of(k, F.LAYOUT_DENSE_PRESHUFFLED, 64, 192, 384) is not None]
     fsh = [k for k in range(n) if F.gemm_config_of(k, F.LAYOUT_DENSE_FLOAT_PRESHUFFLED, 72, 192, 384) is not None]
     assert fl and sh and fsh and not set(fl) & set(sh) and not set(fsh) & set(fl + sh)
     assert all(F.gemm_config_of(k, True, 72, 192, 384) is not None for k in range(n) if k not in fl + sh + fsh)
@@ -223,7 +225,8 @@ def test_config_of_table_entries():
     assert all(F.gemm_config_of(k, False, 72, 192, 384) is None and F.gemm_config_of(k, True, 72, 192, 384) is None
                for k in fl)
     assert all(F.gemm_config_of(k, F.LAYOUT_DENSE_FLOAT, 72, 192, 384) is None for k in range(n) if k not in fl)
-    assert all(F.gemm_config_of(k, F.LAYOUT_DENSE_PRESHUFFLED, 72, 192, 384) is None for k in range(n) if k not in sh)
+    assert all(F.gemm_config_of(k, F.LAYOUT_DENSE_PRESHUFFLED, 72, 192, 384) is None
+               and F.gemm_config_of(k, F.LAYOUT_DENSE_PRESHUFFLED, 64, 192, 384) is None for k in range(n) if k not in sh)
     for M in (8, 64, 4096):
         assert F.gemm_config(F.LAYOUT_DENSE_FLOAT, M, 7168, 7168)["kernel"] in fl
     long_k = [F.gemm_config_of(k, True, 256, 4096, 128 * 1024) for k in range(n)]

@@ -555,6 +555,79 @@ def test_silu_mul_special_values():
     assert q[0, 3, 7] == int(want[0]) == 0xFB  # -366.2 -> -352
 
 
+@pytest.mark.parametrize("H", [640, 2048])
+def test_silu_quant_pack_equals_group_quant_of_exact_y(H):
+    """Fused == SiLU then the (separately pinned) per-token-group quant, on every valid row.
+
+    Gate values lie in [20, 60], where silu(g) = g / (1 + e^-g) differs from g by a relative
+    e^-g < 2.1e-9, far below half an fp32 ulp; up values are +-2^k.  So y = g * u exactly
+    (a bf16 value), and the fused oracle's bytes and packed words must equal those of
+    quant_group_pack applied to y.  k varies with row and group, so neighbouring groups have
+    different exponents: a wrong word index or byte shift in the masked [E][W][M_max] layout
+    cannot pass.  H = 640 gives 5 groups (a partial second word), H = 2048 gives 4 words."""
+    E, M_max = 3, 8
+    counts = np.array([5, 0, 8], np.int32)
+    rng = np.random.default_rng(H)
+    G = H // 128
+    gate = rng.uniform(20.0, 60.0, (E, M_max, H)).astype(np.float32)
+    gate = W.bf16_bits_to_f32(W.f32_to_bf16_bits(gate))
+    k = np.zeros((E, M_max, G), np.int64)
+    for e in range(E):
+        for r in range(M_max):
+            for g in range(G):
+                k[e, r, g] = (7 * r + 3 * g + 5 * e) % 13 - 6
+    up = np.repeat(np.ldexp(1.0, k), 128, axis=2) * rng.choice([-1.0, 1.0], (E, M_max, H))
+    x = W.f32_to_bf16_bits(np.concatenate([gate, up.astype(np.float32)], axis=2))
+    y = (gate.astype(np.float64) * up).astype(np.float32)
+    yb = W.f32_to_bf16_bits(y)
+    assert np.array_equal(W.bf16_bits_to_f32(yb), y), "y must be exact in bf16"
+    q, sf = O.silu_mul_quant_group_pack(x, counts)
+    Wd = (G + 3) // 4
+    assert q.shape == (E, M_max, H) and sf.shape == (E, Wd, M_max)
+    for e in range(E):
+        qr, sfr = O.quant_group_pack(yb[e], ld_sf=M_max)
+        c = counts[e]
+        assert np.array_equal(q[e, :c], qr[:c]), e
+        assert np.array_equal(sf[e, :, :c], sfr[:, :c]), e
+        # rows at or past the count are not written (the wrapper's zeros remain)
+        assert not q[e, c:].any() and not sf[e, :, c:].any()
+    # the test has power: exponents differ between neighbouring groups of a row
+    bytes_ = [(sf[2, g // 4, 0] >> (8 * (g % 4))) & 0xFF for g in range(G)]
+    assert len(set(bytes_)) > 1 and all(85 <= b <= 247 for b in bytes_)
+
+
+def test_silu_quant_pack_general_values_against_torch_cast():
+    """General SiLU inputs (N(0,1) with a different magnitude per group): each valid row's
+    bytes equal torch's e4m3 cast of fp32(y) * 2^-e, where y is the oracle's double SiLU
+    product (pinned to scipy above) and e is the smallest integer with 448 * 2^e >= max(amax,
+    1e-10), found by exact comparison; byte g % 4 of word g / 4 of the row holds e + 127."""
+    E, M_max, H = 2, 6, 640
+    G = H // 128
+    rng = np.random.default_rng(11)
+    xs = rng.standard_normal((E, M_max, 2 * H))
+    scale = np.ldexp(1.0, rng.integers(-12, 12, (E, M_max, G)))
+    xs[..., :H] *= np.repeat(scale, 128, axis=2)
+    xs[..., H:] *= np.repeat(scale[..., ::-1], 128, axis=2)
+    x = W.f32_to_bf16_bits(xs.astype(np.float32))
+    counts = np.array([6, 3], np.int32)
+    q, sf, y = O.silu_mul_quant_group_pack(x, counts, want_y=True)
+    for e in range(E):
+        for r in range(counts[e]):
+            for g in range(G):
+                y32 = y[e, r, 128 * g:128 * g + 128].astype(np.float32)
+                amax = max(float(np.max(np.abs(y32))), 1e-10)
+                ex = math.frexp(amax / 448.0)[1]
+                while Fraction(448) * Fraction(2) ** (ex - 1) >= Fraction(amax):
+                    ex -= 1
+                while Fraction(448) * Fraction(2) ** ex < Fraction(amax):
+                    ex += 1
+                assert (int(sf[e, g // 4, r]) >> (8 * (g % 4))) & 0xFF == ex + 127, (e, r, g)
+                want = torch.from_numpy(np.ldexp(y32, -ex).astype(np.float32)).to(torch.float8_e4m3fn)
+                assert np.array_equal(q[e, r, 128 * g:128 * g + 128], want.view(torch.uint8).numpy()), (e, r, g)
+            # bytes of the missing groups 5..7 of the last word are zero
+            assert (int(sf[e, 1, r]) >> 8) == 0
+
+
 # ---------------------------------------------------------------- bf16 rounding
 
 def test_bf16_rne_matches_torch():
