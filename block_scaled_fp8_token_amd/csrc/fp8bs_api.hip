@@ -44,9 +44,24 @@ int check_device() {
   return it->second ? FP8BS_OK : FP8BS_ERR_DEVICE;
 }
 
+// Fill kernel: clears the arrival counters at the front of a fresh workspace on the
+// caller's stream (stream-ordered, and a kernel rather than a memset node when the
+// call is being captured into a HIP graph).
+__global__ __launch_bounds__(256) void zero_words_kernel(uint32_t* __restrict__ p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = 0u;
+}
+
+hipError_t zero_words(void* p, size_t bytes, hipStream_t stream) {
+  const int64_t n = (int64_t)(bytes / 4);
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(zero_words_kernel, dim3(64), dim3(256), 0, stream, static_cast<uint32_t*>(p), n);
+  return hipGetLastError();
+}
+
 // Split-K workspace: one buffer per (device, stream), grown on demand.  It holds
-// the per-tile arrival counters of the fused split-K reduction (zeroed once when
-// the buffer is allocated; every call leaves them at zero) and the fp32 partials
+// the per-tile arrival counters of the fused split-K reduction (zeroed once, on the
+// caller's stream, when the buffer is allocated; every call leaves them at zero)
+// and the fp32 partials
 // of the call in flight on that stream, which every split overwrites before they
 // are read.  A buffer that is outgrown is kept, never freed: a HIP graph captured
 // earlier on the stream still launches kernels that use it.
@@ -85,7 +100,7 @@ int get_workspace(size_t need, hipStream_t stream, void** out) {
     g_last_hip_error = (int)e;
     return FP8BS_ERR_ALLOC;
   }
-  e = hipMemset(p, 0, fp8bs::gemm_workspace_zeroed_prefix());
+  e = zero_words(p, fp8bs::gemm_workspace_zeroed_prefix(), stream);
   if (e != hipSuccess) {
     (void)hipFree(p);
     return fail_hip(e);

@@ -2136,6 +2136,7 @@ constexpr int kCfgFloatScaled128x256 = 32;
 constexpr int kCfgDecode64x128 = 45;       // decode kernel, 4 wavefronts, weights through a 3-stage LDS ring,
                                            // partials summed by splitk_reduce_kernel
 constexpr int kCfgShufDecode64x128 = 36;   // the same on pre-shuffled weights (register loads)
+constexpr int kCfgWsd64x128 = 56;          // weight streaming, pre-shuffled, split summed within one XCD
 constexpr int kCfgShufRing256x256Rows = 38;  // pre-shuffled weights: ring 256x256, 1 x 4 wavefronts
 constexpr int kCfgShufRing256x256 = 39;      // 2 x 2 wavefronts
 constexpr int kCfgShufRing128x256 = 40;
@@ -2145,6 +2146,7 @@ constexpr int kCfgShufRing128x128 = 50;      // the same (2 x 2) on pre-shuffled
 static_assert(kCfgDecode64x128 < kNumTiles && kCfgFloatScaled128x256 < kNumTiles, "tile table");
 static_assert(kCfgFloatShufDecode64x128 < kNumTiles && kCfgFloatDecode64x128 < kNumTiles, "tile table");
 static_assert(kCfgRing128x128 < kNumTiles && kCfgShufRing128x128 < kNumTiles, "tile table");
+static_assert(kCfgWsd64x128 < kNumTiles, "tile table");
 
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -2285,6 +2287,10 @@ GemmConfig choose_gemm_config(const GemmProblem& p) {
     const int64_t tiles = cdiv(p.M, kTiles[kCfgShufDecode64x128].bm) * cdiv(p.N, kTiles[kCfgShufDecode64x128].bn);
     int splits = p.masked_m ? 1 : (int)(224 / (tiles > 0 ? tiles : 1));
     if (splits < 1) splits = 1;
+    // dense M <= 64: the weight-streaming kernel, its K split summed in the kernel
+    // within one XCD's L2 (64x7168x18432: 29.7 us per call against 30.5 us for the
+    // decode kernel and the reduction kernel)
+    if (!p.masked_m && p.M <= 64 && gemm_config_by_index(kCfgWsd64x128, p, splits, &cfg)) return cfg;
     if (!gemm_config_by_index(kCfgShufDecode64x128, p, splits, &cfg)) cfg.kernel = -1;
     return cfg;
   }
