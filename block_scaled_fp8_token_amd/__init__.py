@@ -26,6 +26,7 @@ __all__ = [
     "fp8_quant_group_pack_to_experts", "fp8_block_gemm_grouped_contiguous",
     "fp8_quant_group_float", "fp8_block_quant_128x128_float", "fp8_block_gemm_nt_float_scales",
     "fp8_weight_preshuffle", "fp8_block_gemm_nt_preshuffled", "fp8_block_gemm_grouped_masked_preshuffled",
+    "fp8_block_gemm_nt_preshuffled_noalloc",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -57,6 +58,7 @@ _SIGS = {
     "fp8_weight_preshuffle": [_P, _I64, _I64, _P, _P],
     "fp8_block_gemm_nt_preshuffled": [_P, _P, _I64, _P, _P, _P, _I64, _I64, _I64, _I64, _P],
     "fp8_block_gemm_nt_preshuffled_cfg": [_P, _P, _I64, _P, _P, _P, _I64, _I64, _I64, _I64, _I32, _I32, _P],
+    "fp8_block_gemm_nt_preshuffled_noalloc": [_P, _P, _I64, _P, _P, _P, _I64, _I64, _I64, _I64, _P],
     "fp8_block_gemm_grouped_masked_preshuffled": [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _P],
     "fp8_block_gemm_grouped_masked_preshuffled_cfg": [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I32, _P],
     "fp8_block_gemm_nt_float_scales_preshuffled": [_P, _P, _I64, _P, _P, _P, _I64, _I64, _I64, _I64, _P],
@@ -341,6 +343,32 @@ def fp8_block_gemm_nt_preshuffled(a: torch.Tensor, sfa: torch.Tensor, b: torch.T
             kernel = gemm_config(LAYOUT_DENSE_PRESHUFFLED, M, N, K)["kernel"]
         st = _lib.fp8_block_gemm_nt_preshuffled_cfg(*args, int(kernel), int(splits or 1), s)
     _check("fp8_block_gemm_nt_preshuffled", st)
+    return c
+
+
+def fp8_block_gemm_nt_preshuffled_noalloc(a: torch.Tensor, sfa: torch.Tensor, b: torch.Tensor, sfb: torch.Tensor,
+                                          c: torch.Tensor, stream=None) -> torch.Tensor:
+    """fp8_block_gemm_nt_preshuffled into a caller-allocated c, with the split-K scratch in the
+    library's static device buffer: the call allocates nothing (for graph capture and serving
+    loops).  Calls that overlap on one GPU share that buffer and race."""
+    _expect(a, "a", _E4M3, 2)
+    _contig(a, "a")
+    _expect(b, "b", _E4M3, 2)
+    _contig(b, "b")
+    _expect(sfa, "sfa", (torch.int32, torch.uint32), 2)
+    _expect(sfb, "sfb", (torch.float32,), 2)
+    _contig(sfb, "sfb")
+    M, K = a.shape
+    N = b.shape[0]
+    if b.shape[1] != K:
+        raise ValueError("a and b disagree on K")
+    _expect(c, "c", _BF16, 2)
+    if tuple(c.shape) != (M, N):
+        raise ValueError("c must be [M, N]")
+    st = _lib.fp8_block_gemm_nt_preshuffled_noalloc(a.data_ptr(), sfa.data_ptr(), sfa.stride(0), b.data_ptr(),
+                                                    sfb.data_ptr(), c.data_ptr(), c.stride(0), M, N, K,
+                                                    _stream(stream))
+    _check("fp8_block_gemm_nt_preshuffled_noalloc", st)
     return c
 
 

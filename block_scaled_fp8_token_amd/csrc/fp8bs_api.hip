@@ -112,6 +112,36 @@ int get_workspace(size_t need, hipStream_t stream, void** out) {
   return FP8BS_OK;
 }
 
+// Scratch of the entry point that allocates nothing: one file-scope device array
+// (each GPU the library runs on holds its own copy until the process ends).  Host
+// code never uses the array's name as an address: its device address comes from
+// hipGetSymbolAddress, once per device, with that device current.  The arrival
+// counters at its front are cleared by a fill kernel on the first call's stream;
+// every call leaves them at zero.  All calls on one GPU share it.
+constexpr size_t kStaticScratchBytes = size_t(8) << 20;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+int static_scratch(hipStream_t stream, void** out) {
+  static std::mutex mu;
+  static std::map<int, void*> ptrs;
+  *out = nullptr;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail_hip(e);
+  std::lock_guard<std::mutex> lk(mu);
+  auto it = ptrs.find(dev);
+  if (it == ptrs.end()) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || ptr == nullptr) return fail_hip(e != hipSuccess ? e : hipErrorInvalidSymbol);
+    e = zero_words(ptr, fp8bs::gemm_workspace_zeroed_prefix(), stream);
+    if (e != hipSuccess) return fail_hip(e);
+    it = ptrs.emplace(dev, ptr).first;
+  }
+  *out = it->second;
+  return FP8BS_OK;
+}
+
 int run_gemm(const fp8bs::GemmProblem& prob, const fp8bs::GemmConfig& cfg, hipStream_t stream) {
   void* ws = nullptr;
   const size_t need = fp8bs::gemm_workspace_bytes(prob, cfg);
@@ -371,6 +401,28 @@ int fp8_block_gemm_nt_preshuffled(const void* a, const uint32_t* sfa, int64_t ld
   return run_gemm(p, cfg, static_cast<hipStream_t>(stream));
 }
 
+int fp8_block_gemm_nt_preshuffled_noalloc(const void* a, const uint32_t* sfa, int64_t ld_sfa, const void* b,
+                                          const float* sfb, void* c, int64_t ldc, int64_t M, int64_t N, int64_t K,
+                                          void* stream) {
+  int st = check_dense(a, sfa, ld_sfa, b, sfb, c, ldc, M, N, K);
+  if (st != FP8BS_OK) return st > 0 ? FP8BS_OK : st;
+  st = check_device();
+  if (st != FP8BS_OK) return st;
+  fp8bs::GemmProblem p = dense_problem(a, sfa, ld_sfa, b, sfb, c, ldc, M, N, K);
+  p.b_shuffled = true;
+  const fp8bs::GemmConfig cfg = fp8bs::choose_gemm_config(p);
+  if (cfg.kernel < 0) return FP8BS_ERR_SHAPE;
+  const size_t need = fp8bs::gemm_workspace_bytes(p, cfg);
+  if (need > kStaticScratchBytes) return FP8BS_ERR_SCRATCH;
+  void* ws = nullptr;
+  if (need > 0) {
+    st = static_scratch(static_cast<hipStream_t>(stream), &ws);
+    if (st != FP8BS_OK) return st;
+  }
+  hipError_t e = fp8bs::launch_gemm(p, cfg, ws, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FP8BS_OK : fail_hip(e);
+}
+
 int fp8_block_gemm_nt_preshuffled_cfg(const void* a, const uint32_t* sfa, int64_t ld_sfa, const void* b,
                                       const float* sfb, void* c, int64_t ldc, int64_t M, int64_t N, int64_t K,
                                       int32_t kernel, int32_t splits, void* stream) {
@@ -558,6 +610,7 @@ const char* fp8bs_status_string(int status) {
     case FP8BS_ERR_DEVICE: return "device is not gfx950";
     case FP8BS_ERR_LAUNCH: return "HIP call failed";
     case FP8BS_ERR_ALLOC: return "workspace allocation failed or refused during graph capture";
+    case FP8BS_ERR_SCRATCH: return "the problem needs more scratch than the static buffer of the no-allocation entry holds";
     default: return "unknown status";
   }
 }

@@ -54,7 +54,8 @@ enum {
   FP8BS_ERR_ALIGN = -3,  /* a pointer or row stride breaks the alignment rule       */
   FP8BS_ERR_DEVICE = -4, /* the current device is not gfx950                        */
   FP8BS_ERR_LAUNCH = -5, /* a HIP call failed; see fp8bs_last_hip_error()           */
-  FP8BS_ERR_ALLOC = -6   /* the split-K workspace could not be allocated            */
+  FP8BS_ERR_ALLOC = -6,  /* the split-K workspace could not be allocated            */
+  FP8BS_ERR_SCRATCH = -7 /* fp8_block_gemm_nt_preshuffled_noalloc: scratch too small */
 };
 
 /*
@@ -204,6 +205,24 @@ int fp8_weight_preshuffle(const void* w, int64_t rows, int64_t K, void* out, voi
 int fp8_block_gemm_nt_preshuffled(const void* a, const uint32_t* sfa, int64_t ld_sfa, const void* b,
                                   const float* sfb, void* c, int64_t ldc, int64_t M, int64_t N,
                                   int64_t K, void* stream);
+
+/*
+ * fp8_block_gemm_nt_preshuffled for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Arguments, kernels and result are those of
+ * fp8_block_gemm_nt_preshuffled (bit-identical output); the split-K scratch
+ * (arrival counters and fp32 partials) is a static device array of 8 MiB per GPU
+ * instead of the per-stream workspace, so this call never allocates or frees.  For
+ * M <= 64 and K <= 143360 (the weight-streaming kernel) the automatic configuration
+ * needs at most 64 KiB + 224 * 64 * 128 * 4 bytes (7.4 MB), for larger M none; a
+ * problem needing more than 8 MiB returns FP8BS_ERR_SCRATCH without launching.  Every call on one GPU shares that array:
+ * calls that overlap on one GPU (different streams, or a graph replay running
+ * beside another call) race and give undefined results.  The first call on a device
+ * clears the counters with a fill kernel on its stream; every call leaves them clear.
+ */
+int fp8_block_gemm_nt_preshuffled_noalloc(const void* a, const uint32_t* sfa, int64_t ld_sfa,
+                                          const void* b, const float* sfb, void* c, int64_t ldc,
+                                          int64_t M, int64_t N, int64_t K, void* stream);
 
 /*
  * Masked grouped GEMM (PR #19111: m_grouped GEMM, masked, over [E, max_tokens, K]

@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings():
-    for st in range(-6, 1):
+    for st in range(-7, 1):
         s = lib.fp8bs_status_string(st).decode()
         assert s and s != "unknown status"
     assert lib.fp8bs_status_string(-99).decode() == "unknown status"
