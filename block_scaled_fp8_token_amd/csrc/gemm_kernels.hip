@@ -833,7 +833,21 @@ __device__ __forceinline__ void mfma_read_dma_pattern() {
   }
 }
 
-template <int BM, int BN, int WGM, int WGN, bool SHUF = false>
+// The same with the operand reads front-loaded: two reads after each of the first
+// MFMAs, so that the last read of the half-step is issued long before its end.
+template <int NM, int NR, int NV, int Q = 0>
+__device__ __forceinline__ void mfma_front_read_dma_pattern() {
+  if constexpr (Q < NM) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    constexpr int r0 = 2 * Q < NR ? 2 * Q : NR, r1 = 2 * (Q + 1) < NR ? 2 * (Q + 1) : NR;
+    if constexpr (r1 > r0) __builtin_amdgcn_sched_group_barrier(0x100, r1 - r0, 0);
+    constexpr int v = (Q + 1) * NV / NM - Q * NV / NM;
+    if constexpr (v > 0) __builtin_amdgcn_sched_group_barrier(0x010, v, 0);
+    mfma_front_read_dma_pattern<NM, NR, NV, Q + 1>();
+  }
+}
+
+template <int BM, int BN, int WGM, int WGN, bool SHUF = false, int RP = 0>
 __global__ __launch_bounds__(256) void scaled_ring_kernel(const KArgs p) {
   using R = RingShape<BM, BN, WGM, WGN>;
   constexpr int S = kRingSlots;
@@ -1049,7 +1063,8 @@ __global__ __launch_bounds__(256) void scaled_ring_kernel(const KArgs p) {
       // reads than MFMAs) and the DMA spread over the half-step: a DMA that waits
       // for room in the memory queue then stalls this wavefront's issue while an
       // MFMA runs, rather than holding back the first MFMA
-      mfma_read_dma_pattern<IV * SN, 2 * (IV > 0 ? IV + SN : 0), IPW>();
+      if constexpr (RP == 1) mfma_front_read_dma_pattern<IV * SN, 2 * (IV > 0 ? IV + SN : 0), IPW>();
+      else mfma_read_dma_pattern<IV * SN, 2 * (IV > 0 ? IV + SN : 0), IPW>();
 #pragma unroll
       for (int i = 0; i < IV; ++i) xf[i] = xn[i];
 #pragma unroll
@@ -1132,6 +1147,310 @@ __global__ __launch_bounds__(256) void scaled_ring_kernel(const KArgs p) {
 
 template <int BM, int BN, int WGM, int WGN>
 constexpr int ring_wd_max() { return RingShape<BM, BN, WGM, WGN>::WD_MAX; }
+
+// ---------------------------------------------------------------------------
+// Full-row ring kernel.  The same tile, wavefront grid, scaled MFMA and scale
+// tables as the ring kernel above, but the LDS stages hold whole 128-wide
+// K-blocks, so each LDS-DMA instruction of a wavefront moves 8 rows x 128 bytes:
+// every 128-byte line of A and B is fetched from L2 by one request.  (A stage of
+// K-halves, 16 rows x 64 bytes per instruction, requests each line twice; at
+// 4096 x 4096 x 7168 that put 1.75x the lines through the L1-to-L2 path and kept the
+// texture units busy ~68% of the time.)  16-byte chunk c of a row r sits at
+// position c ^ ((r >> 1) & 7): sixteen consecutive rows (two per 256-byte cycle of
+// the banks) then cover all 64 banks four bytes at a time, so the operand reads,
+// which take one row per lane, are conflict-free (c ^ (r & 7) left rows r and
+// r + 8 on the same banks: 7.7e6 conflict cycles at 4096 x 4096 x 7168).  With S stages, K-block j:
+//   half 0: the MFMAs of j's first K-half (operands read during the previous
+//           half), interleaved with the operand reads of j's second K-half;
+//   half 1: wait for this wavefront's DMA of j + 1 and its reads, barrier (every
+//           wavefront's DMA of j + 1 has landed and nobody reads j's stage any
+//           more), DMA of j + S into j's stage, then the MFMAs of j's second half
+//           interleaved with the operand reads of j + 1's first half and the DMA.
+// One barrier per K-block; a DMA has S - 1 K-blocks to land.
+template <int BM, int BN, int WGM, int WGN, int S>
+struct Ring2Shape {
+  static constexpr int WM = BM / WGM, WN = BN / WGN;
+  static constexpr int SM = WM / 32, SN = WN / 32;
+  static constexpr int SLOT = (BM + BN) * 128;
+  static constexpr int IPA = BM / 32, IPB = BN / 32;  // 1 KiB DMA instructions per wavefront per K-block
+  static constexpr int IPW = IPA + IPB;
+  static constexpr int NBT = BN / 128;
+  static constexpr int FIT = (160 * 1024 - S * SLOT - 256) / (BM * 4 + NBT * 4);
+  static constexpr int WD_MAX = FIT < 32 ? FIT : 32;
+};
+
+template <int BM, int BN, int WGM, int WGN, int S>
+__global__ __launch_bounds__(256) void ring2_kernel(const KArgs p) {
+  using R = Ring2Shape<BM, BN, WGM, WGN, S>;
+  constexpr int WM = R::WM, WN = R::WN, SM = R::SM, SN = R::SN, IPW = R::IPW, IPA = R::IPA;
+  constexpr int WD_MAX = R::WD_MAX, NBT = R::NBT;
+  static_assert(WGM * WGN == 4 && WM % 32 == 0 && WN % 32 == 0 && BN % 128 == 0 && BM % 32 == 0, "tile shape");
+  static_assert(S == 2 || S == 4, "stages (a divisor of the four K-blocks of a scale word)");
+  static_assert(WD_MAX >= 1, "scale tables do not fit");
+  __shared__ __attribute__((aligned(1024))) uint8_t sl0[R::SLOT];
+  __shared__ __attribute__((aligned(1024))) uint8_t sl1[R::SLOT];
+  __shared__ __attribute__((aligned(1024))) uint8_t sl2[S > 2 ? R::SLOT : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t sl3[S > 2 ? R::SLOT : 16];
+  __shared__ __attribute__((aligned(16))) uint32_t sa_tab[WD_MAX * BM];   // [w][row]
+  __shared__ __attribute__((aligned(16))) uint32_t sb_tab[NBT * WD_MAX];  // [block][w], byte kb % 4
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WGN, wn = wave % WGN;
+  const int64_t e = blockIdx.z;
+  int tm, tn;
+  xcd_tile(p, blockIdx.x, tm, tn);
+
+  int64_t m_limit = p.M;
+  if (p.masked_m) {
+    const int64_t cnt = p.masked_m[e];
+    m_limit = cnt < 0 ? 0 : (cnt > p.M ? p.M : cnt);
+  }
+  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+  if (m0 >= m_limit) return;
+  const int64_t eb = weight_group(p, e, m0);
+  if (eb < 0) return;
+
+  const int KB = (int)(p.K / 128);
+  const int Wd = (KB + 3) / 4;  // <= WD_MAX (checked by the host)
+  const int NB = (int)((p.N + 127) / 128);
+  const int KB4 = 4 * Wd;       // K-blocks, padded to whole groups of four
+  const int64_t rows_valid = (m_limit - m0 < BM) ? m_limit - m0 : BM;
+  int64_t cols_valid = p.N - n0;
+  cols_valid = cols_valid > BN ? BN : cols_valid;
+  const auto rA = make_rsrc(p.a + e * p.sa_e + m0 * p.K, (uint32_t)(rows_valid * p.K));
+  const auto rB = make_rsrc(p.b + eb * p.sb_e + n0 * p.K, (uint32_t)(cols_valid * p.K));
+  const auto rSA = make_rsrc(p.sfa + e * p.ssfa_e, (uint32_t)(Wd * p.ld_sfa * 4));
+  const auto rSB = make_rsrc(p.sfb + eb * p.ssfb_e, (uint32_t)(NB * KB * 4));
+
+  auto slot = [&](auto sl_tag) -> uint8_t* {
+    constexpr int I = decltype(sl_tag)::value;
+    if constexpr (I == 0) return sl0;
+    else if constexpr (I == 1) return sl1;
+    else if constexpr (I == 2) return sl2;
+    else return sl3;
+  };
+
+  // DMA: instruction t < IPA of this wavefront covers A rows 8 ri .. 8 ri + 7 with
+  // ri = wave * IPA + t, the others B rows likewise; lane l -> row 8 ri + (l >> 3),
+  // LDS position l & 7 holding chunk (l & 7) ^ swizzle: for row 8 ri + (l >> 3) the
+  // swizzle is (l >> 4) ^ 4 (ri & 1), so one offset serves even ri and one odd ri
+  const uint32_t lane_row = (uint32_t)((lane >> 3) * p.K);
+  const uint32_t lane_off0 = lane_row + (uint32_t)(((lane & 7) ^ (lane >> 4)) << 4);
+  const uint32_t lane_off1 = lane_row + (uint32_t)(((lane & 7) ^ (lane >> 4) ^ 4) << 4);
+  auto issue = [&](int kb, auto sl_tag) {
+    uint8_t* base = slot(sl_tag);
+    const uint32_t koff = (uint32_t)kb * 128u, oob = kb < KB ? 0u : kOOB;
+#pragma unroll
+    for (int t = 0; t < IPW; ++t) {
+      const bool isA = t < IPA;  // static after unrolling
+      const int ri = isA ? wave * IPA + t : wave * R::IPB + (t - IPA);
+      uint8_t* dst = base + (isA ? 0 : BM * 128) + ri * 1024;
+      const uint32_t off = ((ri & 1 ? lane_off1 : lane_off0) + (uint32_t)(ri * 8 * p.K) + koff) | oob;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(isA ? rA : rB, (__attribute__((address_space(3))) void*)dst, 16,
+                                               (int)off, 0, 0, 0);
+    }
+  };
+
+  // scale tables (as in the ring kernel)
+  constexpr int SA_IT = (WD_MAX * BM + 255) / 256;
+  constexpr int SB_IT = (NBT * WD_MAX * 4 + 255) / 256;
+  uint32_t sav[SA_IT], sbv[SB_IT];
+#pragma unroll
+  for (int t = 0; t < SA_IT; ++t) {
+    const int idx = t * 256 + tid;
+    const int w = idx / BM, row = idx - w * BM;
+    const bool ok = idx < WD_MAX * BM && w < Wd && m0 + row < m_limit;
+    sav[t] = bload4(rSA, ok ? (uint32_t)(((int64_t)w * p.ld_sfa + m0 + row) * 4) : kOOB);
+  }
+#pragma unroll
+  for (int t = 0; t < SB_IT; ++t) {
+    const int idx = t * 256 + tid;
+    const int b = idx / (WD_MAX * 4), k = idx - b * (WD_MAX * 4);
+    const int nb = (int)(n0 >> 7) + b;
+    const bool ok = idx < NBT * WD_MAX * 4 && nb < NB && k < KB;
+    sbv[t] = bload4(rSB, ok ? (uint32_t)((nb * KB + k) * 4) : kOOB);
+  }
+  issue(0, IntC<0>{});
+  issue(1, IntC<1>{});
+  if constexpr (S > 2) {
+    issue(2, IntC<2>{});
+    issue(3, IntC<3>{});
+  }
+#pragma unroll
+  for (int t = 0; t < SA_IT; ++t) {
+    const int idx = t * 256 + tid;
+    const int w = idx / BM;
+    uint32_t v = sav[t];
+    const int left = KB - 4 * w;
+    if (left < 4) v &= left <= 0 ? 0u : ((1u << (8 * left)) - 1u);
+    if (idx < WD_MAX * BM) sa_tab[idx] = v;
+  }
+  uint8_t* sb_bytes = reinterpret_cast<uint8_t*>(sb_tab);
+#pragma unroll
+  for (int t = 0; t < SB_IT; ++t) {
+    const int idx = t * 256 + tid;
+    if (idx < NBT * WD_MAX * 4) sb_bytes[idx] = (uint8_t)((sbv[t] >> 23) & 0xFFu);
+  }
+  // the first stage and the tables in place everywhere
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm((S - 1) * IPW, 0));
+  __builtin_amdgcn_s_barrier();
+
+  // operand reads: lane l takes row l & 31 of a 32-row group and 32 bytes of K-half
+  // h: chunks 4 h + 2 (l >> 5) and the next, at positions chunk ^ ((row >> 1) & 7)
+  const int lr = lane & 31, cc = 2 * (lane >> 5);
+  auto rdo = [&](int h, int j) -> uint32_t {
+    return (uint32_t)(lr * 128 + (((4 * h + cc + j) ^ ((lr >> 1) & 7)) << 4));
+  };
+  const uint32_t rd00 = rdo(0, 0), rd01 = rdo(0, 1), rd10 = rdo(1, 0), rd11 = rdo(1, 1);
+  const int sb_blk = (wn * WN) >> 7;
+  uint16_t* __restrict__ C = p.c + e * p.sc_e;
+
+  auto body = [&](auto iv_tag) {
+    constexpr int IV = decltype(iv_tag)::value;
+    // operands of K-half h of the K-block in stage sl_tag
+    auto read_frags = [&](auto sl_tag, auto h_tag, v8i (&xf)[SM], v8i (&wf)[SN]) {
+      constexpr int H = decltype(h_tag)::value;
+      const uint8_t* base = slot(sl_tag);
+      const uint32_t r0 = H == 0 ? rd00 : rd10, r1 = H == 0 ? rd01 : rd11;
+#pragma unroll
+      for (int i = 0; i < IV; ++i) {
+        const uint8_t* q = base + (wm * WM + 32 * i) * 128;
+        const v4i lo = *reinterpret_cast<const v4i*>(q + r0);
+        const v4i hi = *reinterpret_cast<const v4i*>(q + r1);
+        xf[i] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      }
+      if constexpr (IV > 0) {
+#pragma unroll
+        for (int j = 0; j < SN; ++j) {
+          const uint8_t* q = base + (BM + wn * WN + 32 * j) * 128;
+          const v4i lo = *reinterpret_cast<const v4i*>(q + r0);
+          const v4i hi = *reinterpret_cast<const v4i*>(q + r1);
+          wf[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        }
+      }
+    };
+
+    uint32_t sa[SM], sa_n[SM];
+    uint32_t sb = 0, sb_n = sb_tab[sb_blk * WD_MAX];
+#pragma unroll
+    for (int i = 0; i < SM; ++i) sa_n[i] = i < IV ? sa_tab[wm * WM + 32 * i + lr] : 0u;
+    v8i xc[SM], wc[SN], xn[SM], wn_[SN];
+    read_frags(IntC<0>{}, IntC<0>{}, xc, wc);
+
+    v16f acc[SM][SN];
+#pragma unroll
+    for (int i = 0; i < SM; ++i)
+#pragma unroll
+      for (int j = 0; j < SN; ++j)
+#pragma unroll
+        for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
+
+    auto mfmas = [&](const v8i (&xf)[SM], const v8i (&wf)[SN], auto ops_tag) {
+      constexpr int OPS = decltype(ops_tag)::value;
+#pragma unroll
+      for (int i = 0; i < IV; ++i)
+#pragma unroll
+        for (int j = 0; j < SN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wf[j], xf[i], acc[i][j], 0, 0, OPS, (int)sb,
+                                                                      OPS, (int)sa[i]);
+    };
+
+    // K-block kb = kb4 + U (kb4 a multiple of 4): scale byte U, stage U % S
+    auto kblock = [&](int kb4, auto u_tag) {
+      constexpr int U = decltype(u_tag)::value;
+      constexpr int ST = U % S, STN = (U + 1) % S;
+      const int kb = kb4 + U;
+      // half 0: MFMAs of the first K-half, reads of the second
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (U == 0) {
+#pragma unroll
+        for (int i = 0; i < SM; ++i) sa[i] = sa_n[i];
+        sb = sb_n;
+      }
+      read_frags(IntC<ST>{}, IntC<1>{}, xn, wn_);
+      mfmas(xc, wc, IntC<U>{});
+      mfma_read_dma_pattern<IV * SN, 2 * (IV > 0 ? IV + SN : 0), 0>();
+      if constexpr (U == 2) {
+        // scale words of the next group (clamped to the table; unused past the end)
+        const int wnx = (kb4 >> 2) + 1 < WD_MAX ? (kb4 >> 2) + 1 : WD_MAX - 1;
+#pragma unroll
+        for (int i = 0; i < SM; ++i) sa_n[i] = i < IV ? sa_tab[wnx * BM + wm * WM + 32 * i + lr] : 0u;
+        sb_n = sb_tab[sb_blk * WD_MAX + wnx];
+      }
+      // half 1: this wavefront's DMA of kb + 1 and its reads are in; then everyone's
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_waitcnt(waitcnt_imm((S - 2) * IPW, 0));
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      issue(kb + S, IntC<ST>{});
+      read_frags(IntC<STN>{}, IntC<0>{}, xc, wc);
+      mfmas(xn, wn_, IntC<U>{});
+      mfma_read_dma_pattern<IV * SN, 2 * (IV > 0 ? IV + SN : 0), IPW>();
+    };
+
+    for (int kb4 = 0; kb4 < KB4; kb4 += 4) {
+      kblock(kb4, IntC<0>{});
+      kblock(kb4, IntC<1>{});
+      kblock(kb4, IntC<2>{});
+      kblock(kb4, IntC<3>{});
+    }
+    // the DMAs issued past the end must land, and every wavefront must be done with
+    // the stages, before they are reused below
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
+    __builtin_amdgcn_s_barrier();
+    if constexpr (IV == 0) return;
+
+    // epilogue through LDS (as in the ring kernel): each wavefront stages its bf16
+    // sub-tile in its own LDS region and stores whole rows
+    constexpr int RB = WN * 2, CPR = RB / 16, RPI = 64 / CPR;
+    static_assert(4 * WM * RB <= S * R::SLOT, "staging needs the stages");
+    uint8_t* stg = (wave < 2 ? sl0 : sl1) + (wave & 1) * (WM * RB);
+    static_assert(2 * WM * RB <= R::SLOT, "two wavefronts per stage");
+#pragma unroll
+    for (int i = 0; i < IV; ++i) {
+      const int row = 32 * i + lr;
+#pragma unroll
+      for (int j = 0; j < SN; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int chunk = 4 * j + q;
+          uint2 o;
+          o.x = bf16_rne(acc[i][j][4 * q]) | (bf16_rne(acc[i][j][4 * q + 1]) << 16);
+          o.y = bf16_rne(acc[i][j][4 * q + 2]) | (bf16_rne(acc[i][j][4 * q + 3]) << 16);
+          *reinterpret_cast<uint2*>(stg + row * RB + ((chunk ^ (row % CPR)) << 4) + 8 * (lane >> 5)) = o;
+        }
+    }
+    const int c = lane % CPR;
+    const int64_t n = n0 + wn * WN + 8 * c;
+#pragma unroll
+    for (int t = 0; t < (IV * 32) / RPI; ++t) {
+      const int row = t * RPI + lane / CPR;
+      const v4i v = *reinterpret_cast<const v4i*>(stg + row * RB + ((c ^ (row % CPR)) << 4));
+      const int64_t m = m0 + wm * WM + row;
+      if (m < m_limit && n < p.N) *reinterpret_cast<v4i*>(C + m * p.ldc + n) = v;
+    }
+  };
+
+  int64_t mine = m_limit - (m0 + wm * WM);
+  mine = mine < 0 ? 0 : (mine > WM ? WM : mine);
+  const int iv = __builtin_amdgcn_readfirstlane((int)((mine + 31) / 32));
+  switch (iv) {
+    case 0: body(IntC<0>{}); break;
+    case 1: body(IntC<1>{}); break;
+    case 2: if constexpr (SM >= 2) body(IntC<2 <= SM ? 2 : SM>{}); break;
+    case 3: if constexpr (SM >= 3) body(IntC<3 <= SM ? 3 : SM>{}); break;
+    case 4: if constexpr (SM >= 4) body(IntC<4 <= SM ? 4 : SM>{}); break;
+    case 5: if constexpr (SM >= 5) body(IntC<5 <= SM ? 5 : SM>{}); break;
+    case 6: if constexpr (SM >= 6) body(IntC<6 <= SM ? 6 : SM>{}); break;
+    case 7: if constexpr (SM >= 7) body(IntC<7 <= SM ? 7 : SM>{}); break;
+    default: if constexpr (SM >= 8) body(IntC<8 <= SM ? 8 : SM>{}); break;
+  }
+}
+
+template <int BM, int BN, int WGM, int WGN, int S>
+constexpr int ring2_wd_max() { return Ring2Shape<BM, BN, WGM, WGN, S>::WD_MAX; }
+
 
 // ---------------------------------------------------------------------------
 // Decode kernel: weight streaming for small M.  NW wavefronts, each owning 32
@@ -2117,16 +2436,31 @@ const TileEntry kTiles[] = {
     {wsd_kernel<4, 3>, 64, 128, kWsd, 4, 256, WsdShape<4, 3>::WMAX},
     {wsd_kernel<4, 0>, 64, 128, kWsdSep, 4, 256, WsdShape<4, 0>::WMAX},
     {wsd_kernel<3, 2>, 64, 128, kWsd, 3, 256, WsdShape<3, 2>::WMAX},
+    // ring tiles with the operand reads front-loaded in each half-step
+    {scaled_ring_kernel<256, 256, 2, 2, false, 1>, 256, 256, kRing, 4, 256, ring_wd_max<256, 256, 2, 2>()},
+    {scaled_ring_kernel<256, 128, 2, 2, false, 1>, 256, 128, kRing, 4, 256, ring_wd_max<256, 128, 2, 2>()},
+    {scaled_ring_kernel<128, 128, 1, 4, false, 1>, 128, 128, kRing, 4, 256, ring_wd_max<128, 128, 1, 4>()},
+    // full-row stages: one L2 request per 128-byte line
+    {ring2_kernel<256, 256, 2, 2, 2>, 256, 256, kRing, 2, 256, ring2_wd_max<256, 256, 2, 2, 2>()},
+    {ring2_kernel<256, 128, 2, 2, 2>, 256, 128, kRing, 2, 256, ring2_wd_max<256, 128, 2, 2, 2>()},
+    {ring2_kernel<128, 128, 1, 4, 4>, 128, 128, kRing, 4, 256, ring2_wd_max<128, 128, 1, 4, 4>()},
+    {ring2_kernel<128, 256, 2, 2, 2>, 128, 256, kRing, 2, 256, ring2_wd_max<128, 256, 2, 2, 2>()},
+    {ring2_kernel<256, 256, 1, 4, 2>, 256, 256, kRing, 2, 256, ring2_wd_max<256, 256, 1, 4, 2>()},
 };
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 // table entries the automatic choice uses
 constexpr int kCfgStream64x128 = 4;
 constexpr int kCfgScaled128x128 = 13;
 constexpr int kCfgScaled256x256 = 15;
-constexpr int kCfgRing256x256 = 17;        // 2 x 2 wavefronts
-constexpr int kCfgRing256x256Rows = 20;    // 1 x 4 wavefronts (all share the rows)
-constexpr int kCfgRing128x256 = 19;        // 2 x 2 wavefronts, 128-row tiles
-constexpr int kCfgRing256x128 = 18;        // 2 x 2 wavefronts, 128-column tiles
+// (the ring entries the automatic choice uses are the full-row ones: one L2 request
+// per 128-byte line; 4096x4096x7168 99 -> 90 us, 2048x4096x7168 69 -> 64 us,
+// 1024x4096x7168 45.5 -> 37.2 us against the K-half ring entries 17, 18, 49)
+// The masked and contiguous grouped GEMMs, bound by their weight streams, keep the
+// K-half ring (masked gate_up 214 against 217 us, contiguous 272.5 against 276 us).
+constexpr int kCfgRing256x256 = 63;        // 2 x 2 wavefronts, two full K-block stages
+constexpr int kCfgRing256x256Rows = 20;    // K-half ring, 1 x 4 wavefronts (all share the rows)
+constexpr int kCfgRing128x256 = 19;        // K-half ring, 2 x 2 wavefronts, 128-row tiles
+constexpr int kCfgRing256x128 = 64;        // 2 x 2 wavefronts, 128-column tiles, two full K-block stages
 constexpr int kCfgFloat64x128 = 26;        // float-scale VALU-scaled tiles
 constexpr int kCfgFloat128x128 = 27;
 constexpr int kCfgFloat128x256 = 29;
@@ -2141,11 +2475,13 @@ constexpr int kCfgShufRing256x256Rows = 38;  // pre-shuffled weights: ring 256x2
 constexpr int kCfgShufRing256x256 = 39;      // 2 x 2 wavefronts
 constexpr int kCfgShufRing128x256 = 40;
 constexpr int kCfgFloatShufDecode64x128 = 47;  // float scales, pre-shuffled weights, reduction kernel
-constexpr int kCfgRing128x128 = 49;          // ring 128x128, 1 x 4 wavefronts
+constexpr int kCfgRing128x128 = 65;          // ring 128x128, 1 x 4 wavefronts, four full K-block stages
 constexpr int kCfgShufRing128x128 = 50;      // the same (2 x 2) on pre-shuffled weights
 static_assert(kCfgDecode64x128 < kNumTiles && kCfgFloatScaled128x256 < kNumTiles, "tile table");
 static_assert(kCfgFloatShufDecode64x128 < kNumTiles && kCfgFloatDecode64x128 < kNumTiles, "tile table");
 static_assert(kCfgRing128x128 < kNumTiles && kCfgShufRing128x128 < kNumTiles, "tile table");
+static_assert(kCfgRing256x256 < kNumTiles && kCfgRing256x256Rows < kNumTiles && kCfgRing128x256 < kNumTiles &&
+                  kCfgRing256x128 < kNumTiles, "tile table");
 static_assert(kCfgWsd64x128 < kNumTiles, "tile table");
 
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
