@@ -26,7 +26,7 @@ __all__ = [
     "fp8_quant_group_pack_to_experts", "fp8_block_gemm_grouped_contiguous",
     "fp8_quant_group_float", "fp8_block_quant_128x128_float", "fp8_block_gemm_nt_float_scales",
     "fp8_weight_preshuffle", "fp8_block_gemm_nt_preshuffled", "fp8_block_gemm_grouped_masked_preshuffled",
-    "fp8_block_gemm_nt_preshuffled_noalloc",
+    "fp8_block_gemm_nt_preshuffled_noalloc", "check_dense_shapes", "check_masked_shapes", "check_contiguous_shapes",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -146,6 +146,68 @@ def _contig(t: torch.Tensor, name: str) -> None:
         raise ValueError("%s must be contiguous" % name)
 
 
+# Shape rules of the C ABI (include/fp8bs.h), checked on shapes and strides only so
+# that a wrong tensor raises ValueError before any kernel could read or write past it.
+
+def _words(K: int) -> int:
+    return (K // 128 + 3) // 4
+
+
+def _need_shape(t: torch.Tensor, name: str, shape) -> None:
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must be %s, got %s" % (name, list(shape), list(t.shape)))
+
+
+def _need_cols(t: torch.Tensor, name: str, rows: int, cols: int) -> None:
+    """2-D [rows, >= cols] with unit column stride and a row stride of at least cols."""
+    if t.dim() != 2 or t.shape[0] != rows or t.shape[1] < cols or t.stride(1) != 1 or t.stride(0) < cols:
+        raise ValueError("%s must be [%d, >= %d] with row stride >= %d, got shape %s strides %s"
+                         % (name, rows, cols, cols, list(t.shape), list(t.stride())))
+
+
+def check_dense_shapes(a, sfa, b, sfb, c, float_scales: bool = False) -> None:
+    """a [M, K], b [N, K], c [M, >= N] (row stride >= N), sfb [ceil(N/128), K/128], and
+    sfa [ceil(K/512), >= M] (packed UE8M0 words) or [K/128, >= M] (float scales)."""
+    if a.dim() != 2 or b.dim() != 2 or c.dim() != 2:
+        raise ValueError("a, b and c must have 2 dims")
+    M, K = a.shape
+    N = b.shape[0]
+    if b.shape[1] != K:
+        raise ValueError("a and b disagree on K")
+    _need_cols(c, "c", M, N)
+    _need_cols(sfa, "sfa", K // 128 if float_scales else _words(K), M)
+    _need_shape(sfb, "sfb", ((N + 127) // 128, K // 128))
+
+
+def check_masked_shapes(a, sfa, b, sfb, c, masked_m) -> None:
+    """a [E, M_max, K], sfa [E, ceil(K/512), M_max], b [E, N, K], sfb [E, ceil(N/128), K/128],
+    c [E, M_max, N], masked_m [E]."""
+    if a.dim() != 3 or b.dim() != 3:
+        raise ValueError("a and b must have 3 dims")
+    E, M_max, K = a.shape
+    N = b.shape[1]
+    _need_shape(b, "b", (E, N, K))
+    _need_shape(sfa, "sfa", (E, _words(K), M_max))
+    _need_shape(sfb, "sfb", (E, (N + 127) // 128, K // 128))
+    _need_shape(c, "c", (E, M_max, N))
+    _need_shape(masked_m, "masked_m", (E,))
+
+
+def check_contiguous_shapes(a, sfa, b, sfb, c, m_indices) -> None:
+    """a [M, K], sfa [ceil(K/512), >= M], b [E, N, K], sfb [E, ceil(N/128), K/128],
+    c [M, >= N], m_indices [M]."""
+    if a.dim() != 2 or b.dim() != 3:
+        raise ValueError("a must have 2 dims and b 3")
+    M, K = a.shape
+    E, N = b.shape[0], b.shape[1]
+    if b.shape[2] != K:
+        raise ValueError("a and b disagree on K")
+    _need_cols(sfa, "sfa", _words(K), M)
+    _need_shape(sfb, "sfb", (E, (N + 127) // 128, K // 128))
+    _need_cols(c, "c", M, N)
+    _need_shape(m_indices, "m_indices", (M,))
+
+
 # ----------------------------------------------------------------------------
 
 def fp8_quant_group_pack(x: torch.Tensor, q: torch.Tensor | None = None, sf: torch.Tensor | None = None,
@@ -162,8 +224,8 @@ def fp8_quant_group_pack(x: torch.Tensor, q: torch.Tensor | None = None, sf: tor
         sf = torch.empty((W, ld), dtype=torch.int32, device=x.device)
     _expect(q, "q", _E4M3, 2)
     _expect(sf, "sf", (torch.int32, torch.uint32), 2)
-    if tuple(q.shape) != (M, K) or sf.shape[0] != W:
-        raise ValueError("output shapes do not match x")
+    _need_cols(q, "q", M, K)
+    _need_cols(sf, "sf", W, M)
     st = _lib.fp8_quant_group_pack(x.data_ptr(), x.stride(0), M, K, q.data_ptr(), q.stride(0),
                                    sf.data_ptr(), sf.stride(0), _stream(stream))
     _check("fp8_quant_group_pack", st)
@@ -214,6 +276,8 @@ def fp8_block_quant_128x128(w: torch.Tensor, q: torch.Tensor | None = None, sfb:
     _contig(q, "q")
     _expect(sfb, "sfb", (torch.float32,), 2)
     _contig(sfb, "sfb")
+    _need_shape(q, "q", (N, K))
+    _need_shape(sfb, "sfb", ((N + 127) // 128, K // 128))
     st = _lib.fp8_block_quant_128x128(w.data_ptr(), N, K, q.data_ptr(), sfb.data_ptr(), _stream(stream))
     _check("fp8_block_quant_128x128", st)
     return q, sfb
@@ -252,6 +316,7 @@ def fp8_quant_group_pack_to_experts(x: torch.Tensor, topk_ids: torch.Tensor, E: 
     _contig(slot_of, "slot_of")
     if tuple(q.shape) != (E, M_max, K) or tuple(sf.shape) != (E, Wd, M_max) or tuple(slot_of.shape) != (T, topk):
         raise ValueError("output shapes do not match E, M_max, K, T, topk")
+    _need_shape(masked_m, "masked_m", (E,))
     st = _lib.fp8_quant_group_pack_to_experts(x.data_ptr(), x.stride(0), T, K, topk_ids.data_ptr(), topk, E, M_max,
                                               q.data_ptr(), sf.data_ptr(), masked_m.data_ptr(), slot_of.data_ptr(),
                                               _stream(stream))
@@ -280,6 +345,7 @@ def fp8_block_gemm_nt(a: torch.Tensor, sfa: torch.Tensor, b: torch.Tensor, sfb: 
     _expect(c, "c", _BF16, 2)
     if tuple(c.shape) != (M, N):
         raise ValueError("c must be [M, N]")
+    check_dense_shapes(a, sfa, b, sfb, c)
     s = _stream(stream)
     if kernel is None and splits is None:
         st = _lib.fp8_block_gemm_nt(a.data_ptr(), sfa.data_ptr(), sfa.stride(0), b.data_ptr(), sfb.data_ptr(),
@@ -333,6 +399,7 @@ def fp8_block_gemm_nt_preshuffled(a: torch.Tensor, sfa: torch.Tensor, b: torch.T
     _expect(c, "c", _BF16, 2)
     if tuple(c.shape) != (M, N):
         raise ValueError("c must be [M, N]")
+    check_dense_shapes(a, sfa, b, sfb, c)
     s = _stream(stream)
     args = (a.data_ptr(), sfa.data_ptr(), sfa.stride(0), b.data_ptr(), sfb.data_ptr(), c.data_ptr(), c.stride(0),
             M, N, K)
@@ -365,6 +432,7 @@ def fp8_block_gemm_nt_preshuffled_noalloc(a: torch.Tensor, sfa: torch.Tensor, b:
     _expect(c, "c", _BF16, 2)
     if tuple(c.shape) != (M, N):
         raise ValueError("c must be [M, N]")
+    check_dense_shapes(a, sfa, b, sfb, c)
     st = _lib.fp8_block_gemm_nt_preshuffled_noalloc(a.data_ptr(), sfa.data_ptr(), sfa.stride(0), b.data_ptr(),
                                                     sfb.data_ptr(), c.data_ptr(), c.stride(0), M, N, K,
                                                     _stream(stream))
@@ -394,6 +462,7 @@ def fp8_block_gemm_grouped_masked(a: torch.Tensor, sfa: torch.Tensor, b: torch.T
         c = torch.empty((E, M_max, N), dtype=torch.bfloat16, device=a.device)
     _expect(c, "c", _BF16, 3)
     _contig(c, "c")
+    check_masked_shapes(a, sfa, b, sfb, c, masked_m)
     s = _stream(stream)
     name = "fp8_block_gemm_grouped_masked" + ("_preshuffled" if preshuffled else "")
     args = (a.data_ptr(), sfa.data_ptr(), b.data_ptr(), sfb.data_ptr(), c.data_ptr(), masked_m.data_ptr(),
@@ -436,6 +505,7 @@ def fp8_block_gemm_grouped_contiguous(a: torch.Tensor, sfa: torch.Tensor, b: tor
     _expect(c, "c", _BF16, 2)
     if tuple(c.shape) != (M, N):
         raise ValueError("c must be [M, N]")
+    check_contiguous_shapes(a, sfa, b, sfb, c, m_indices)
     s = _stream(stream)
     args = (a.data_ptr(), sfa.data_ptr(), sfa.stride(0), b.data_ptr(), sfb.data_ptr(), c.data_ptr(), c.stride(0),
             m_indices.data_ptr(), E, M, N, K)
@@ -464,6 +534,8 @@ def fp8_quant_group_float(x: torch.Tensor, q: torch.Tensor | None = None, sf: to
         sf = torch.empty((K // 128, ld), dtype=torch.float32, device=x.device)
     _expect(q, "q", _E4M3, 2)
     _expect(sf, "sf", (torch.float32,), 2)
+    _need_cols(q, "q", M, K)
+    _need_cols(sf, "sf", K // 128, M)
     st = _lib.fp8_quant_group_float(x.data_ptr(), x.stride(0), M, K, q.data_ptr(), q.stride(0), sf.data_ptr(),
                                     sf.stride(0), _stream(stream))
     _check("fp8_quant_group_float", st)
@@ -505,6 +577,7 @@ def fp8_block_gemm_nt_float_scales(a: torch.Tensor, sfa: torch.Tensor, b: torch.
     _expect(c, "c", _BF16, 2)
     if tuple(c.shape) != (M, N):
         raise ValueError("c must be [M, N]")
+    check_dense_shapes(a, sfa, b, sfb, c, float_scales=True)
     s = _stream(stream)
     args = (a.data_ptr(), sfa.data_ptr(), sfa.stride(0), b.data_ptr(), sfb.data_ptr(), c.data_ptr(), c.stride(0),
             M, N, K)

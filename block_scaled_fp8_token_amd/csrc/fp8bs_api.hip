@@ -143,6 +143,7 @@ int static_scratch(hipStream_t stream, void** out) {
 }
 
 int run_gemm(const fp8bs::GemmProblem& prob, const fp8bs::GemmConfig& cfg, hipStream_t stream) {
+  if (cfg.kernel < 0) return FP8BS_ERR_SHAPE;  // no table entry takes this problem
   void* ws = nullptr;
   const size_t need = fp8bs::gemm_workspace_bytes(prob, cfg);
   int st = get_workspace(need, stream, &ws);

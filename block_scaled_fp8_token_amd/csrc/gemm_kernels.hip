@@ -285,7 +285,10 @@ __global__ __launch_bounds__(256) void gemm_kernel(const KArgs p) {
 #pragma unroll
     for (int j = 0; j < SN; ++j) {
       const int64_t n = n0 + wn * WN + 16 * j;
-      sb[j] = (n < p.N) ? SB[(n >> 7) * KB + kb] : 0.0f;
+      // UE8M0 entries read a weight block scale's exponent field only (its power of
+      // two), as the scaled-MFMA kernels do; float-scale entries take the whole value
+      const float s = (n < p.N) ? SB[(n >> 7) * KB + kb] : 0.0f;
+      sb[j] = FS ? s : __uint_as_float(__float_as_uint(s) & 0x7F800000u);
     }
 
     const uint8_t* As = lds[buf];
@@ -426,7 +429,7 @@ __global__ __launch_bounds__(256) void stream_kernel(const KArgs p) {
     const int b = idx / per, kk = idx - b * per;
     const int k = kb0 + kk, nb = nb0 + b;
     const uint32_t off = (k < kb1 && nb < NB) ? (uint32_t)((nb * KB + k) * 4) : kOOB;
-    lds_sb[b * per + kk] = __uint_as_float(bload4(rSB, off));
+    lds_sb[b * per + kk] = __uint_as_float(bload4(rSB, off) & 0x7F800000u);  // exponent field only (UE8M0)
   }
   astore(0, 0);
   __syncthreads();
@@ -2528,7 +2531,7 @@ bool gemm_config_by_index(int idx, const GemmProblem& p, int splits, GemmConfig*
   if ((kTiles[idx].kind == kStream)) {
     // split K further if the scale tables would not fit next to the A stages
     while (splits < KB && stream_lds_bytes(kTiles[idx].bm, kTiles[idx].bn, (int)cdiv(KB, splits)) > kMaxLds) {
-      if (p.masked_m) return false;
+      if (p.masked_m || p.m_indices) return false;  // grouped layouts never split K
       ++splits;
     }
   }
@@ -2543,7 +2546,7 @@ bool gemm_config_by_index(int idx, const GemmProblem& p, int splits, GemmConfig*
     if (splits > max_splits) splits = max_splits;
     int per = (int)cdiv(cdiv(KB, splits), 4) * 4;
     if (per > 4 * kTiles[idx].max_wd) {
-      if (p.masked_m) return false;
+      if (p.masked_m || p.m_indices) return false;  // grouped layouts never split K
       per = 4 * kTiles[idx].max_wd;
     }
     const int64_t tiles = cdiv(p.M, kTiles[idx].bm) * cdiv(p.N, kTiles[idx].bn);
@@ -2645,7 +2648,7 @@ GemmConfig choose_gemm_config(const GemmProblem& p) {
       const int max_splits = KB / 4 > 1 ? KB / 4 : 1;
       if (splits > max_splits) splits = max_splits;
       if (splits < 1) splits = 1;
-      gemm_config_by_index(kCfgFloat64x128, p, splits, &cfg);
+      if (!gemm_config_by_index(kCfgFloat64x128, p, splits, &cfg)) cfg.kernel = -1;
       return cfg;
     }
     // larger M: LDS-DMA tiles (128 x 256 once they fill the compute units), the
@@ -2653,7 +2656,7 @@ GemmConfig choose_gemm_config(const GemmProblem& p) {
     const int64_t t256 = cdiv(p.M, 128) * cdiv(p.N, 256);
     if (t256 >= 256 && gemm_config_by_index(kCfgFloatScaled128x256, p, 1, &cfg)) return cfg;
     if (gemm_config_by_index(kCfgFloatScaled128x128, p, 1, &cfg)) return cfg;
-    gemm_config_by_index(t256 >= 256 ? kCfgFloat128x256 : kCfgFloat128x128, p, 1, &cfg);
+    if (!gemm_config_by_index(t256 >= 256 ? kCfgFloat128x256 : kCfgFloat128x128, p, 1, &cfg)) cfg.kernel = -1;
     return cfg;
   }
   if (p.m_indices) {
@@ -2662,7 +2665,7 @@ GemmConfig choose_gemm_config(const GemmProblem& p) {
     if (gemm_config_by_index(kCfgRing128x256, p, 1, &cfg)) return cfg;
     if (gemm_config_by_index(kCfgScaled128x128, p, 1, &cfg)) return cfg;
     if (gemm_config_by_index(kCfgStream64x128, p, 1, &cfg)) return cfg;
-    gemm_config_by_index(1, p, 1, &cfg);
+    if (!gemm_config_by_index(1, p, 1, &cfg)) cfg.kernel = -1;
     return cfg;
   }
   if (p.masked_m) {
@@ -2671,7 +2674,7 @@ GemmConfig choose_gemm_config(const GemmProblem& p) {
     // over all four SIMDs (no operand reads or MFMAs for 32-row groups past the
     // count); weight streaming over 64-row tiles when K is past the scale tables
     if (gemm_config_by_index(kCfgRing256x256Rows, p, 1, &cfg)) return cfg;
-    gemm_config_by_index(kCfgStream64x128, p, 1, &cfg);
+    if (!gemm_config_by_index(kCfgStream64x128, p, 1, &cfg)) cfg.kernel = -1;
     return cfg;
   }
   if (p.M <= 64) {
@@ -2692,7 +2695,7 @@ GemmConfig choose_gemm_config(const GemmProblem& p) {
     const int max_splits = KB / 8 > 1 ? KB / 8 : 1;
     if (splits > max_splits) splits = max_splits;
     if (splits < 1) splits = 1;
-    gemm_config_by_index(idx, p, splits, &cfg);
+    if (!gemm_config_by_index(idx, p, splits, &cfg)) cfg.kernel = -1;
     return cfg;
   }
   // prefill: LDS-DMA tiles + scaled MFMA.  256x256 ring tiles once they fill the
@@ -2753,7 +2756,7 @@ GemmConfig choose_gemm_config(const GemmProblem& p) {
     const int max_splits = KB / 8 > 1 ? KB / 8 : 1;
     if (splits > max_splits) splits = max_splits;
   }
-  gemm_config_by_index(idx, p, splits, &cfg);
+  if (!gemm_config_by_index(idx, p, splits, &cfg)) cfg.kernel = -1;
   return cfg;
 }
 

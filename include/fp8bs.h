@@ -34,8 +34,13 @@
  * bytes of groups past G are zero.  Words are stored M-major: word w of row r is
  * sf[w*ld_sf + r] (the column-major, padded layout the benchmark post's section
  * 4.1 describes for DeepGEMM; ld_sf = round_up(M, 4) gives 16-byte columns).
- * Weight block scales ("sfb") are fp32 [ceil(N/128)][K/128], row-major, and
- * must be powers of two (UE8M0 values), as the weight block quant produces.
+ * Weight block scales ("sfb") are fp32 [ceil(N/128)][K/128], row-major: the
+ * UE8M0 values the weight block quant produces (powers of two).  Every UE8M0 entry
+ * point, whatever kernel it picks, reads only each scale's exponent field, i.e.
+ * uses 2^floor(log2 |s|): a power of two is used as it is, any other finite scale
+ * is taken as the power of two at or below its magnitude (sign and mantissa bits
+ * ignored).  The float-scale entry points (fp8_block_gemm_nt_float_scales...) use
+ * the whole fp32 value.
  */
 #ifndef FP8BS_H
 #define FP8BS_H

@@ -233,3 +233,18 @@ def test_config_of_table_entries():
     assert any(x is None for x in long_k) and any(x is not None for x in long_k)
     assert all(x is None or x["splits"] == 1 for x in long_k)
     assert F.gemm_config_of(n, False, 64, 128, 128) is None
+
+
+def test_config_refuses_what_no_entry_takes():
+    """A problem no table entry accepts is refused (FP8BS_ERR_SHAPE), never handed to a
+    default entry: a masked call with K past every masked kernel's scale tables, and
+    every grouped-layout configuration keeps K unsplit."""
+    with pytest.raises(F.Fp8bsError) as ei:
+        F.gemm_config(True, 256, 4096, 128 * 4096)
+    assert ei.value.status == ERR_SHAPE
+    for K in (7168, 128 * 1024, 128 * 4096):
+        cfg = F.gemm_config(F.LAYOUT_CONTIGUOUS, 256, 4096, K)
+        assert cfg["kernel"] >= 0 and cfg["splits"] == 1
+        for k in range(F.gemm_config_count()):
+            e = F.gemm_config_of(k, F.LAYOUT_CONTIGUOUS, 256, 4096, K)
+            assert e is None or e["splits"] == 1, (k, K)

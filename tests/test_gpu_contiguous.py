@@ -81,9 +81,10 @@ def test_contiguous_rejects_tiles_taller_than_a_run():
     assert F.gemm_config(CONTIGUOUS, 8192, 4096, 7168)["bm"] <= 128
 
 
-def test_contiguous_gate_up_full_shape_sampled_rows():
+def test_contiguous_gate_up_full_shape_every_valid_row():
     """The masked gate_up workload in the contiguous layout: 32 experts, Zipf(1.1)
-    counts (2780 valid rows) in 128-row runs, N = 4096, K = 7168, plus a padding block."""
+    counts (2780 valid rows) in 128-row runs, N = 4096, K = 7168, plus a padding block;
+    every element of every valid row against the oracle."""
     E, N, K = W.MOE_E, W.MOE_GATE_UP["N"], W.MOE_GATE_UP["K"]
     counts = W.zipf_counts()
     mi = W.contiguous_layout(counts, tail_blocks=1)
@@ -91,8 +92,5 @@ def test_contiguous_gate_up_full_shape_sampled_rows():
     print("contiguous gate_up M=%d auto config %s" % (len(mi), F.gemm_config(CONTIGUOUS, len(mi), N, K)), flush=True)
     c = _run(qa, sfa, qb, sfb, mi)
     starts = np.concatenate([[0], np.cumsum(-(-counts // 128) * 128)])
-    rows = []
-    for g in range(E):
-        if counts[g] > 0:
-            rows += sorted({int(starts[g]), int(starts[g] + counts[g] // 2), int(starts[g] + counts[g] - 1)})
-    _check(c, qa, sfa, qb, sfb, mi, rows=np.array(rows, np.int64), what="gate_up contiguous")
+    rows = np.concatenate([np.arange(starts[g], starts[g] + counts[g]) for g in range(E) if counts[g] > 0])
+    _check(c, qa, sfa, qb, sfb, mi, rows=rows.astype(np.int64), what="gate_up contiguous")

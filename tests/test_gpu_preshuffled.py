@@ -73,7 +73,7 @@ def test_preshuffled_gemm_every_entry(M, N, K):
 def test_preshuffled_decode_shape_matches_plain_and_oracle():
     """64 x 7168 x 18432 with 1% x50 outliers: the automatic pre-shuffled call equals the
     plain-layout decode kernel with the same tile and split bit for bit, is
-    deterministic, and agrees with the oracle on 16 sampled rows (every column)."""
+    deterministic, and agrees with the oracle on every output element."""
     s = W.DENSE_DECODE
     a, b = W.dense_inputs(s)
     qa, sfa = O.quant_group_pack(a)
@@ -97,9 +97,9 @@ def test_preshuffled_decode_shape_matches_plain_and_oracle():
         sync()
         matched = matched or np.array_equal(cp, c1)
     assert matched, "no plain-layout entry with the same tile and split reproduces the bits"
-    rows = np.unique(np.linspace(0, s.M - 1, 16).astype(np.int64))
-    ref = O.gemm_nt(qa, sfa, qb, sfb, rows=rows)
-    gemm_tolerance_check(c1[rows], ref, s.name)
+    ref = O.gemm_nt(qa, sfa, qb, sfb)
+    st = gemm_tolerance_check(c1, ref, s.name)
+    print("%s: max |err|/bound %.3f" % (s.name, st["max_err_over_bound"]), flush=True)
 
 
 CANARY = 0x7E7E
