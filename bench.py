@@ -5,13 +5,17 @@ Headline step (the workload the metric is quoted on): the dense decode GEMM
 M=64, N=7168, K=18432 -- per-token 1x128 quant + UE8M0 pack of A (bf16, N(0,1)
 with 1% x50 outliers) followed by the block-scaled NT GEMM against e4m3 weights
 with 128x128 UE8M0 block scales, bf16 out.  Weights are quantized once, outside
-the timed region (as the DeepGEMM benchmark post does, section 4.1).  Several
-weight copies are rotated so that every step streams its weights from HBM rather
-than from the 256 MB last-level cache.
+the timed region (as the DeepGEMM benchmark post does, section 4.1).  The inputs
+are the GPU parity tests' own seeded tensors; several weight copies (128-row-block
+rotations of the one weight set) are rotated so that every step streams its
+weights from HBM rather than from the 256 MB last-level cache.
 
-Prints one JSON line on stdout.  --sweep also times every workload (dense small
-case, decode, prefill sweep, masked MoE gate_up, fused SiLU-quant + masked down)
-and prints a table on stderr (and JSON lines to --sweep-out).
+Prints one JSON line on stdout: the headline, then sub-objects for the prefill
+sweep, the masked MoE gate_up GEMM and the fused SiLU-quant + masked down GEMM
+(each per call: mean and p10/median/p90 over batches, TFLOPS, GB/s, roofline
+fraction), the oracle timed on the host cores, and a check of the timed call's
+output against the oracle's.  --sweep also times the other layouts and entry
+points and prints a table on stderr (and JSON lines to --sweep-out).
 
 Metric definitions follow the benchmark post (section 4.3): TFLOPS = 2*M*N*K/t,
 GB/s = (M*K + N*K + 2*M*N)/t (FP8 inputs 1 byte/element, bf16 output 2 bytes;
@@ -23,6 +27,7 @@ from __future__ import annotations
 import argparse
 import json
 import os
+import platform
 import sys
 import time
 
@@ -153,6 +158,39 @@ def kernel_times(stream, launches, steps, settle_ms=SETTLE_MS):
     return out
 
 
+def kernel_time_stats(stream, fn, batches=11, per_batch=10, settle_ms=SETTLE_MS):
+    """Per-call GPU time of one launch type as (mean, p10, median, p90) in ms: `batches`
+    batches of `per_batch` back-to-back calls, each batch between two HIP events on the
+    launch stream, queued behind a spin kernel (short calls) or after >= settle_ms of the
+    same call (long ones, so that the clock has settled), as kernel_times does; the
+    percentiles are over the batch means."""
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        e0.record(stream)
+        for s in range(3):
+            fn(s)
+        e1.record(stream)
+    stream.synchronize()
+    t_est = e0.elapsed_time(e1) / 3
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(batches + 1)]
+    with torch.cuda.stream(stream):
+        if t_est < SHORT_LAUNCH_MS:
+            torch.cuda._sleep(int(2e7))
+        else:
+            for s in range(int(min(SETTLE_MAX_LAUNCHES, np.ceil(settle_ms / t_est)))):
+                fn(s)
+        evs[0].record(stream)
+        for b in range(batches):
+            for s in range(per_batch):
+                fn(b * per_batch + s)
+            evs[b + 1].record(stream)
+    stream.synchronize()
+    per = np.array([evs[b].elapsed_time(evs[b + 1]) / per_batch for b in range(batches)])
+    total = evs[0].elapsed_time(evs[batches]) / (batches * per_batch)
+    return total, float(np.percentile(per, 10)), float(np.median(per)), float(np.percentile(per, 90))
+
+
 def graph_step_time(stream, step_fn, n_variants, steps, warmup):
     """Wall ms per step over exactly `steps` steps, with synchronizations on both
     sides of the timed loop.  Steps are replayed from HIP graphs that each hold a run
@@ -214,12 +252,56 @@ def setup_dense(F, M, N, K, outliers, seed=0):
     return a, copies, qa, sfa, c
 
 
-def bench_dense(F, stream, shape, steps, warmup, preshuffled=False, hot=False):
+def bf16_dev(bits):
+    """numpy uint16 bf16 bit patterns -> device bfloat16 tensor."""
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to("cuda").view(torch.bfloat16)
+
+
+def rotated_copies(qb0, sfb0, n, dim=0):
+    """n weight copies for HBM-cold timing: copy 0 is the weight itself, copy c its 128-row
+    blocks rotated by 11c blocks along `dim` (the same quantized weight set in another row
+    order, scales rotated with their blocks)."""
+    nb = sfb0.shape[dim]
+    out = [(qb0, sfb0)]
+    for c in range(1, n):
+        sh = (11 * c) % nb if nb > 1 else 0
+        out.append((torch.roll(qb0, 128 * sh, dim) if sh else qb0.clone(),
+                    torch.roll(sfb0, sh, dim) if sh else sfb0.clone()))
+    torch.cuda.synchronize()
+    return out
+
+
+def setup_dense_parity(F, host, shape):
+    """The dense workload on the parity tests' own tensors: A and B as the seeded input
+    generators draw them (host = (A bits, B bits), seed 0: the tensors the GPU parity tests
+    compare with the oracle), B block-quantized on the GPU (bit-exact with the oracle's block
+    quant), and rotated copies of it (rotated_copies) that keep every timed call HBM-cold."""
+    M, N, K = shape.M, shape.N, shape.K
+    a_np, b_np = host
+    a = bf16_dev(a_np)
+    b = bf16_dev(b_np)
+    qb0, sfb0 = F.fp8_block_quant_128x128(b)
+    del b
+    copies = rotated_copies(qb0, sfb0, n_copies_for(N * K))
+    qa = torch.empty((M, K), dtype=torch.uint8, device="cuda")
+    sfa = torch.empty(((K // 128 + 3) // 4, max(4, (M + 3) // 4 * 4)), dtype=torch.int32, device="cuda")
+    c = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    torch.cuda.synchronize()
+    return a, copies, qa, sfa, c
+
+
+def bench_dense(F, stream, shape, steps, warmup, preshuffled=False, hot=False, host=None, stats=False,
+                keep_out=True):
     """The dense step: quant/pack of A, then the GEMM.  preshuffled: the weight copies
     are put into the pre-shuffled layout once, outside timing (offline weight
-    preparation, like the quantization), and fp8_block_gemm_nt_preshuffled runs."""
+    preparation, like the quantization), and fp8_block_gemm_nt_preshuffled runs.
+    host: (A bits, B bits) from the seeded generators, to time the parity tests' own
+    tensors; the result then carries the output of one step on weight copy 0."""
     M, N, K = shape.M, shape.N, shape.K
-    a, copies, qa, sfa, c = setup_dense(F, M, N, K, shape.outliers)
+    if host is not None:
+        a, copies, qa, sfa, c = setup_dense_parity(F, host, shape)
+    else:
+        a, copies, qa, sfa, c = setup_dense(F, M, N, K, shape.outliers)
     if preshuffled:
         copies = [(F.fp8_weight_preshuffle(qb), sfb) for qb, sfb in copies]
         torch.cuda.synchronize()
@@ -246,7 +328,15 @@ def bench_dense(F, stream, shape, steps, warmup, preshuffled=False, hot=False):
             step(i)
     t_quant, t_gemm = kernel_times(stream, [quant, gemm], steps)
     t_hot = kernel_times(stream, [gemm_hot], steps)[0] if hot else None
+    st = kernel_time_stats(stream, gemm, per_batch=max(2, steps // 10)) if stats else None
     ms = graph_step_time(stream, step, nv, steps, warmup)
+    out0 = None
+    if host is not None and keep_out:
+        with torch.cuda.stream(stream):
+            quant(0)
+            gemm(0)
+        stream.synchronize()
+        out0 = c.view(torch.int16).cpu().numpy().view(np.uint16).copy()
     r = {
         "workload": shape.name + ("_preshuffled" if preshuffled else ""), "M": M, "N": N, "K": K,
         "ms_per_step": ms,
@@ -260,6 +350,10 @@ def bench_dense(F, stream, shape, steps, warmup, preshuffled=False, hot=False):
     }
     r["frac_hbm"] = r["gemm_gbs"] / HBM_PEAK_GBS
     r["frac_mfma"] = r["gemm_tflops"] / FP8_PEAK_TFLOPS
+    if st is not None:
+        r["gemm_us_p10"], r["gemm_us_median"], r["gemm_us_p90"] = st[1] * 1e3, st[2] * 1e3, st[3] * 1e3
+    if out0 is not None:
+        r["_out0"] = out0
     del a, copies, qa, sfa, c
     return r
 
@@ -315,18 +409,34 @@ def _preshuffle_copies(F, copies):
     return out
 
 
+def expert_weights(F, W, E, N, K):
+    """Per-expert weights [E, N, K] from N(0, 0.02) (seed 0, tensor id T_B: the masked
+    parity tests' weights), block-quantized on the GPU one expert at a time."""
+    w = W.normal_bf16((E * N, K), std=0.02, seed=0, tensor_id=W.T_B)
+    qb = torch.empty((E, N, K), dtype=torch.uint8, device="cuda")
+    sfb = torch.empty((E, (N + 127) // 128, K // 128), dtype=torch.float32, device="cuda")
+    for e in range(E):
+        q, s = F.fp8_block_quant_128x128(bf16_dev(w[e * N:(e + 1) * N]))
+        qb[e].copy_(q)
+        sfb[e].copy_(s)
+    del w
+    torch.cuda.synchronize()
+    return qb, sfb
+
+
 def bench_masked_gate_up(F, W, stream, steps, warmup, preshuffled=False):
     E, M_max, N, K = W.MOE_E, W.MOE_M_MAX, W.MOE_GATE_UP["N"], W.MOE_GATE_UP["K"]
     counts = torch.from_numpy(W.zipf_counts()).to("cuda")
     S = int(counts.clamp(0, M_max).sum())
     E_active = int((counts > 0).sum())
-    x = randn_bf16((E * M_max, K), seed=11)
+    # the masked parity test's tensors: x and w from the seeded generators (seed 0)
+    x = bf16_dev(W.normal_bf16((E * M_max, K), seed=0))
     qa, sfa_flat = F.fp8_quant_group_pack(x, ld_sf=E * M_max)
     Wd = (K // 128 + 3) // 4
     a = qa.view(E, M_max, K)
     sfa = sfa_flat.view(Wd, E, M_max).permute(1, 0, 2).contiguous()
     del x
-    copies = quantized_weights(F, n_copies_for(E * N * K, floor=1), N, K, 21, experts=E)
+    copies = rotated_copies(*expert_weights(F, W, E, N, K), n_copies_for(E * N * K, floor=1), dim=1)
     if preshuffled:
         copies = _preshuffle_copies(F, copies)
     nv = len(copies)
@@ -340,7 +450,9 @@ def bench_masked_gate_up(F, W, stream, steps, warmup, preshuffled=False):
         for i in range(warmup):
             gemm(i)
     (t,) = kernel_times(stream, [gemm], steps)
+    st = kernel_time_stats(stream, gemm, per_batch=max(2, steps // 10))
     r = {"workload": "moe_gate_up_masked_E32_Mmax256_N4096_K7168" + ("_preshuffled" if preshuffled else ""),
+         "gemm_us_p10": st[1] * 1e3, "gemm_us_median": st[2] * 1e3, "gemm_us_p90": st[3] * 1e3,
          "S": S, "E_active": E_active,
          "gemm_us": t * 1e3, "gemm_tflops": masked_flops(S, N, K) / (t * 1e-3) / 1e12,
          "gemm_gbs": masked_bytes(S, E_active, N, K) / (t * 1e-3) / 1e9, "weight_copies": nv,
@@ -425,8 +537,9 @@ def bench_silu_down(F, W, stream, steps, warmup, preshuffled=False):
     counts = torch.from_numpy(W.zipf_counts()).to("cuda")
     S = int(counts.clamp(0, M_max).sum())
     E_active = int((counts > 0).sum())
-    x = randn_bf16((E, M_max, 2 * H), seed=31)
-    copies = quantized_weights(F, n_copies_for(E * N * K, floor=1), N, K, 41, experts=E)
+    # the SiLU -> down parity test's tensors (seed 0)
+    x = bf16_dev(W.normal_bf16((E, M_max, 2 * H), seed=0, tensor_id=W.T_X))
+    copies = rotated_copies(*expert_weights(F, W, E, N, K), n_copies_for(E * N * K, floor=1), dim=1)
     if preshuffled:
         copies = _preshuffle_copies(F, copies)
     nv = len(copies)
@@ -446,7 +559,11 @@ def bench_silu_down(F, W, stream, steps, warmup, preshuffled=False):
             silu(i)
             gemm(i)
     t_silu, t_gemm = kernel_times(stream, [silu, gemm], steps)
+    st_s = kernel_time_stats(stream, silu, per_batch=max(2, steps // 10))
+    st_g = kernel_time_stats(stream, gemm, per_batch=max(2, steps // 10))
     r = {"workload": "moe_silu_quant_then_down_masked_E32_Mmax256_H2048_N7168" + ("_preshuffled" if preshuffled else ""),
+         "silu_us_p10": st_s[1] * 1e3, "silu_us_median": st_s[2] * 1e3, "silu_us_p90": st_s[3] * 1e3,
+         "gemm_us_p10": st_g[1] * 1e3, "gemm_us_median": st_g[2] * 1e3, "gemm_us_p90": st_g[3] * 1e3,
          "S": S, "config": F.gemm_config(F.LAYOUT_MASKED_PRESHUFFLED if preshuffled else F.LAYOUT_MASKED, M_max, N, K),
          "silu_us": t_silu * 1e3, "silu_gbs": silu_bytes(S, H) / (t_silu * 1e-3) / 1e9,
          "gemm_us": t_gemm * 1e3, "gemm_tflops": masked_flops(S, N, K) / (t_gemm * 1e-3) / 1e12,
@@ -459,41 +576,140 @@ def bench_silu_down(F, W, stream, steps, warmup, preshuffled=False):
 
 # ----------------------------------------------------------------------------- CPU baseline
 
-def cpu_baseline(W, shape, budget_s):
-    """The oracle (as it stands) running the headline step -- quant/pack of A, then the
-    block-scaled GEMM in double -- on host copies of the same workload, for a bounded
-    sample: whole output rows, as many as fit the time budget."""
+def cpu_model():
+    """The host CPU's model name, as /proc/cpuinfo (and lscpu) report it."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
+def _timed_reps(fn, budget_s, max_reps):
+    """Run fn at least once and until budget_s of its own time has passed; (reps, seconds,
+    last result)."""
+    reps, t, out = 0, 0.0, None
+    while reps == 0 or (t < budget_s and reps < max_reps):
+        t0 = time.perf_counter()
+        out = fn()
+        t += time.perf_counter() - t0
+        reps += 1
+    return reps, t, out
+
+
+def cpu_baseline(W, shape, host, budget_s):
+    """The oracle (as it stands) running the headline step -- quant/pack of all M rows of
+    A, then the block-scaled GEMM accumulated in double -- on the same host tensors the GPU
+    step timed, the whole step repeated for about budget_s; plus single-thread figures for
+    the small dense case and for the SiLU-mul-quant kernel.  Returns the baseline object
+    and the oracle's output of the step (for the parity check of the timed GPU call)."""
     import oracle as O
     M, N, K = shape.M, shape.N, shape.K
-    a, b = W.dense_inputs(shape)
-    qb, sfb = O.block_quant_128x128(b)  # offline weight step: not timed
-    del b
-    rows_done = 0
-    t_total = 0.0
-    rows_per_call = 8
-    while t_total < budget_s and rows_done < 64 * M:
-        sel = np.arange(rows_done, rows_done + rows_per_call) % M
-        t0 = time.perf_counter()
-        qa, sfa = O.quant_group_pack(np.ascontiguousarray(a[sel]))
-        O.gemm_nt(qa, sfa, qb, sfb)
-        t_total += time.perf_counter() - t0
-        rows_done += rows_per_call
-    flops = 2.0 * rows_done * N * K
-    return {"value": flops / t_total / 1e12, "unit": "TFLOPS", "cores": O.num_threads(), "kind": "oracle",
-            "sample": "%d output rows (x all %d columns, K=%d) of the %dx%dx%d step: quant/pack of those rows "
-                      "+ double-accumulated block GEMM; %.1f s" % (rows_done, N, K, M, N, K, t_total)}
+    a, b = host
+    qb, sfb = O.block_quant_128x128(b)  # offline weight step, as on the GPU: not timed
+
+    def step():
+        qa, sfa = O.quant_group_pack(a)
+        return O.gemm_nt(qa, sfa, qb, sfb)
+
+    cores = O.num_threads()
+    reps, t, ref = _timed_reps(step, budget_s, 64)
+    res = {"value": reps * gemm_flops(M, N, K) / t / 1e12, "unit": "TFLOPS", "cores": cores, "kind": "oracle",
+           "cpu_model": cpu_model(), "step_ms": t / reps * 1e3,
+           "sample": "the whole %dx%dx%d step (quant/pack of all %d rows + double-accumulated block GEMM, "
+                     "%d distinct outputs) run %d times on the timed tensors; %.1f s"
+                     % (M, N, K, M, M * N, reps, t)}
+    single = {}
+    O.set_num_threads(1)
+    try:
+        s1 = W.DENSE_SMALL
+        a1, b1 = W.dense_inputs(s1)
+        qb1, sfb1 = O.block_quant_128x128(b1)
+
+        def small():
+            qa1, sfa1 = O.quant_group_pack(a1)
+            return O.gemm_nt(qa1, sfa1, qb1, sfb1)
+
+        n1, t1, _ = _timed_reps(small, 2.0, 10000)
+        single[s1.name + "_step"] = {"us": t1 / n1 * 1e6, "tflops": n1 * gemm_flops(s1.M, s1.N, s1.K) / t1 / 1e12,
+                                     "reps": n1}
+        E, M_max, H = W.MOE_E, W.MOE_M_MAX, W.MOE_DOWN["H"]
+        x = W.normal_bf16((E, M_max, 2 * H), seed=0, tensor_id=W.T_X)
+        counts = W.zipf_counts()
+        S = int(np.minimum(np.maximum(counts, 0), M_max).sum())
+        n2, t2, _ = _timed_reps(lambda: O.silu_mul_quant_group_pack(x, counts), 3.0, 100)
+        single["silu_mul_quant_group_pack_E%d_Mmax%d_H%d" % (E, M_max, H)] = {
+            "us": t2 / n2 * 1e6, "gbs": silu_bytes(S, H) / (t2 / n2) / 1e9, "valid_rows": S, "reps": n2}
+    finally:
+        O.set_num_threads(cores)
+    res["single_thread"] = single
+    return res, ref
+
+
+def parity_check(c_bits, ref):
+    """The timed GPU call's output against the oracle's, element by element:
+    |c - ref| <= 1e-2 |ref| + 1e-2 rms(ref), and calc_diff (1 - 2 sum(c ref) / sum(c^2 + ref^2))."""
+    import oracle as O
+    import workloads as W
+    c = W.bf16_bits_to_f32(c_bits).astype(np.float64)
+    rms = float(np.sqrt(np.mean(ref * ref)))
+    bound = 1e-2 * np.abs(ref) + 1e-2 * rms
+    err = np.abs(c - ref)
+    ok = bool(np.all(err <= bound))
+    return {"elements": int(ref.size), "within_tolerance": ok,
+            "outside": int(np.sum(~(err <= bound))),
+            "max_err_over_bound": float(np.max(err / bound)), "calc_diff": float(O.calc_diff(c, ref)),
+            "against": "oracle output of the same step on weight copy 0 (cpu_baseline leg)"}
 
 
 # ----------------------------------------------------------------------------- main
+
+KERNEL_NAMES = {56: "wsd_kernel: pre-shuffled weight streaming, split-K partials summed in the kernel by the "
+                    "last-arriving workgroup of each split group, one launch"}
+
+
+RIDGE_FLOP_PER_BYTE = FP8_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)  # 625: MFMA-bound above
+
+
+def sub_object(r, bound_flops=None):
+    """Per-workload figures for the JSON line: mean and p10/median/p90 per call, TFLOPS,
+    GB/s and the roofline fraction, against the FP8 MFMA peak when the workload's
+    arithmetic intensity (algorithmic flops per algorithmic HBM byte) is above the ridge
+    point, else against HBM bandwidth (bound_flops forces one)."""
+    if bound_flops is None:
+        bound_flops = r["gemm_tflops"] * 1e3 / r["gemm_gbs"] > RIDGE_FLOP_PER_BYTE
+    o = {"gemm_us": round(r["gemm_us"], 2)}
+    for q in ("p10", "median", "p90"):
+        if "gemm_us_" + q in r:
+            o["gemm_us_" + q] = round(r["gemm_us_" + q], 2)
+    o["gemm_tflops"] = round(r["gemm_tflops"], 1)
+    o["gemm_gbs"] = round(r["gemm_gbs"], 1)
+    if bound_flops:
+        o["roofline"] = {"bound": "mfma", "achieved": round(r["gemm_tflops"], 1), "peak": FP8_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(r["gemm_tflops"] / FP8_PEAK_TFLOPS, 4)}
+    else:
+        o["roofline"] = {"bound": "hbm", "achieved": round(r["gemm_gbs"], 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(r["gemm_gbs"] / HBM_PEAK_GBS, 4)}
+    o["frac_mfma"] = round(r["frac_mfma"], 4)
+    o["frac_hbm"] = round(r["frac_hbm"], 4)
+    o["tile"] = r["config"]
+    o["weight_copies"] = r["weight_copies"]
+    return o
+
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--sweep", action="store_true", help="time every workload, table on stderr")
+    ap.add_argument("--sweep", action="store_true", help="also time every other workload, table on stderr")
     ap.add_argument("--sweep-out", default=None, help="file for per-workload JSON lines")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-targets", action="store_true",
+                    help="skip the prefill and MoE sub-objects (headline only)")
     ap.add_argument("--no-hot", action="store_true",
                     help="skip the warm-cache GEMM timing (kernel traces then hold cold-cache calls only)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -528,9 +744,13 @@ def main():
         else:
             counters_workload(F, shape, args.steps, preshuffled=args.counters_shape == "decode")
         return
-    r = bench_dense(F, stream, shape, args.steps, args.warmup, preshuffled=True, hot=not args.no_hot)
+    host = W.dense_inputs(shape)
+    r = bench_dense(F, stream, shape, args.steps, args.warmup, preshuffled=True, hot=not args.no_hot, host=host,
+                    stats=True)
+    out0 = r.pop("_out0")
     print("[bench] %s" % json.dumps(r), file=sys.stderr, flush=True)
-    plain = bench_dense(F, stream, shape, args.steps, args.warmup, hot=not args.no_hot)
+    plain = bench_dense(F, stream, shape, args.steps, args.warmup, hot=not args.no_hot, host=host, stats=True)
+    plain.pop("_out0", None)
     print("[bench] %s" % json.dumps(plain), file=sys.stderr, flush=True)
 
     traffic = None
@@ -543,6 +763,7 @@ def main():
             traffic = None
 
     gb = gemm_bytes(shape.M, shape.N, shape.K)
+    kname = KERNEL_NAMES.get(r["config"]["kernel"], "table entry %d" % r["config"]["kernel"])
     line = {
         "metric": "TFLOPS and HBM GB/s per (M,N,K) shape; % of FP8 MFMA / HBM roofline",
         "value": round(r["step_tflops"], 2),
@@ -558,37 +779,64 @@ def main():
         "data": "synthetic",
         "config": {"workload": "dense_decode_gemm_M64_N7168_K18432", "M": shape.M, "N": shape.N,
                    "K": shape.K, "step": "fp8_quant_group_pack(A) + fp8_block_gemm_nt_preshuffled",
+                   "inputs": "the parity tests' seeded tensors (A N(0,1) with 1% x50 outliers, B N(0,0.02)), "
+                             "seed 0",
                    "weights": "e4m3 + 128x128 UE8M0 block scales, pre-shuffled offline (byte permutation, "
-                              "outside timing like the quantization), %d rotating copies (HBM-cold)"
-                              % r["weight_copies"],
+                              "outside timing like the quantization), %d rotating copies (row-block rotations "
+                              "of the one weight set, HBM-cold)" % r["weight_copies"],
                    "tile": r["config"]},
         "gemm_us": round(r["gemm_us"], 2),
+        "gemm_us_p10": round(r["gemm_us_p10"], 2),
+        "gemm_us_median": round(r["gemm_us_median"], 2),
+        "gemm_us_p90": round(r["gemm_us_p90"], 2),
         "gemm_gbs": round(r["gemm_gbs"], 1),
         "gemm_tflops": round(r["gemm_tflops"], 2),
         "quant_us": round(r["quant_us"], 2),
         "gemm_us_hot": None if r["gemm_us_hot"] is None else round(r["gemm_us_hot"], 2),
         "roofline": {"bound": "hbm",
-                     "kernel": "fp8_block_gemm_nt_preshuffled (decode_kernel + splitk_reduce_kernel, one call)",
+                     "kernel": "fp8_block_gemm_nt_preshuffled (%s)" % kname,
                      "achieved": round(r["gemm_gbs"], 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(r["gemm_gbs"] / HBM_PEAK_GBS, 4),
                      "algorithmic_bytes_per_launch": gb, "traffic": traffic},
         "plain_layout": {"step": "fp8_quant_group_pack(A) + fp8_block_gemm_nt (weights [N][K] as quantized)",
                          "ms_per_step": round(plain["ms_per_step"], 5),
-                         "step_tflops": round(plain["step_tflops"], 2), "gemm_us": round(plain["gemm_us"], 2),
+                         "step_tflops": round(plain["step_tflops"], 2),
                          "gemm_us_hot": None if plain["gemm_us_hot"] is None else round(plain["gemm_us_hot"], 2),
-                         "gemm_gbs": round(plain["gemm_gbs"], 1),
-                         "frac_hbm": round(plain["gemm_gbs"] / HBM_PEAK_GBS, 4), "tile": plain["config"]},
+                         **sub_object(plain, bound_flops=False)},
     }
+    if not args.no_targets:
+        pre_steps = max(10, args.steps // 4)
+        prefill = {}
+        for s in W.DENSE_PREFILL:
+            x = bench_dense(F, stream, s, pre_steps, args.warmup, host=W.dense_inputs(s), stats=True, keep_out=False)
+            print("[bench] %s" % json.dumps(x), file=sys.stderr, flush=True)
+            o = sub_object(x)
+            o["target_us_60pct_mfma"] = round(gemm_flops(s.M, s.N, s.K) / (0.6 * FP8_PEAK_TFLOPS * 1e12) * 1e6, 1)
+            prefill[s.name] = o
+        line["prefill"] = prefill
+        x = bench_masked_gate_up(F, W, stream, pre_steps, args.warmup)
+        print("[bench] %s" % json.dumps(x), file=sys.stderr, flush=True)
+        line["moe_gate_up_masked"] = dict(workload=x["workload"], valid_rows=x["S"], experts_active=x["E_active"],
+                                          **sub_object(x))
+        x = bench_silu_down(F, W, stream, pre_steps, args.warmup)
+        print("[bench] %s" % json.dumps(x), file=sys.stderr, flush=True)
+        o = dict(workload=x["workload"], valid_rows=x["S"], **sub_object(x))
+        o["silu_us"] = round(x["silu_us"], 2)
+        for q in ("p10", "median", "p90"):
+            o["silu_us_" + q] = round(x["silu_us_" + q], 2)
+        o["silu_gbs"] = round(x["silu_gbs"], 1)
+        o["silu_frac_hbm"] = round(x["silu_gbs"] / HBM_PEAK_GBS, 4)
+        line["moe_silu_then_down_masked"] = o
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(W, shape, args.cpu_seconds)
+        line["cpu_baseline"], ref = cpu_baseline(W, shape, host, args.cpu_seconds)
+        line["parity_check"] = parity_check(out0, ref)
 
     if args.sweep:
         rows = [r, plain]
         rows.append(bench_dense(F, stream, W.DENSE_SMALL, args.steps, args.warmup))
         for s in W.DENSE_PREFILL:
-            for pre in (False, True):
-                rows.append(bench_dense(F, stream, s, max(10, args.steps // 4), args.warmup, preshuffled=pre))
-                print("[bench] %s" % json.dumps(rows[-1]), file=sys.stderr, flush=True)
+            rows.append(bench_dense(F, stream, s, max(10, args.steps // 4), args.warmup, preshuffled=True))
+            print("[bench] %s" % json.dumps(rows[-1]), file=sys.stderr, flush=True)
         for pre in (False, True):
             rows.append(bench_masked_gate_up(F, W, stream, max(10, args.steps // 4), args.warmup, preshuffled=pre))
             print("[bench] %s" % json.dumps(rows[-1]), file=sys.stderr, flush=True)
@@ -614,6 +862,9 @@ def main():
                 for x in rows:
                     f.write(json.dumps(x) + "\n")
     print(json.dumps(line), flush=True)
+    if "parity_check" in line and not line["parity_check"]["within_tolerance"]:
+        print("[bench] the timed call's output is outside the oracle tolerance", file=sys.stderr, flush=True)
+        sys.exit(1)
 
 
 def counters_workload(F, shape, steps, preshuffled=False):

@@ -79,6 +79,8 @@ def _load():
     lib.orc_calc_diff.restype = ctypes.c_double
     lib.orc_num_threads.argtypes = []
     lib.orc_num_threads.restype = ctypes.c_int
+    lib.orc_set_num_threads.argtypes = [ctypes.c_int]
+    lib.orc_set_num_threads.restype = None
     _lib = lib
     return lib
 
@@ -133,6 +135,11 @@ def bf16_rne_array(v: np.ndarray) -> np.ndarray:
 
 def num_threads() -> int:
     return int(_load().orc_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Threads of the oracle's OpenMP loops (for timing; the results do not depend on it)."""
+    _load().orc_set_num_threads(int(n))
 
 
 # --------------------------------------------------------------------------

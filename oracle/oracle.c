@@ -492,6 +492,15 @@ double orc_calc_diff(const double* x, const double* y, int64_t n) {
   return 1.0 - 2.0 * num / den;
 }
 
+/* Thread count for the OpenMP loops above (timing only: results do not depend on it). */
+void orc_set_num_threads(int n) {
+#ifdef _OPENMP
+  if (n > 0) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
+
 int orc_num_threads(void) {
 #ifdef _OPENMP
   return omp_get_max_threads();

@@ -6,50 +6,98 @@ contiguous grouped layout.  It contains none of the
 method's arithmetic (no quantization, no scales, no GEMM), and it imports
 neither the oracle nor the HIP library.
 
-Every tensor has its own numpy PCG64 stream, ``default_rng([seed, tensor_id])``,
-so any tensor can be regenerated alone.
+Every tensor is drawn in fixed chunks of 2^20 elements (row-major order), chunk i
+from its own numpy PCG64 stream ``default_rng([seed, tensor_id, i])``: any tensor can
+be regenerated alone, and the chunks are drawn on several threads with a result that
+does not depend on how many.
 """
 from __future__ import annotations
 
 import dataclasses
+import os
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
+
+CHUNK = 1 << 20  # elements per independent stream
+
+
+def _threads() -> int:
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def _chunked(n: int, fn) -> None:
+    """fn(i, lo, hi) for every chunk [lo, hi) of [0, n), on a thread pool."""
+    nch = -(-n // CHUNK)
+    if nch <= 1:
+        if n:
+            fn(0, 0, n)
+        return
+    with ThreadPoolExecutor(max_workers=min(_threads(), nch)) as ex:
+        list(ex.map(lambda i: fn(i, i * CHUNK, min(n, (i + 1) * CHUNK)), range(nch)))
 
 # tensor ids for the per-tensor streams
 T_A, T_B, T_OUTLIER, T_X = 1, 2, 3, 5
 
 
 def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
-    """Round float32 values to bf16 (nearest, ties to even) and return the uint16 bits."""
+    """Round float32 values to bf16 (nearest, ties to even) and return the uint16 bits.
+
+    In uint32: for every finite value, bits + 0x7FFF + lsb stays below 2^32 (the largest
+    finite pattern is 0xFF7FFFFF), so nothing wraps; NaNs are set afterwards."""
     a = np.ascontiguousarray(a, dtype=np.float32)
-    u = a.view(np.uint32).astype(np.uint64)
-    lsb = (u >> 16) & 1
-    r = ((u + 0x7FFF + lsb) >> 16).astype(np.uint16)
-    nan = np.isnan(a)
-    if nan.any():
-        r[nan] = 0x7FC0
-    return r
+    u = a.reshape(-1).view(np.uint32)
+    out = np.empty(u.size, np.uint16)
+
+    def part(i, lo, hi):
+        x = u[lo:hi]
+        r = x >> 16
+        r &= 1
+        r += x
+        r += 0x7FFF
+        r >>= 16
+        o = out[lo:hi]
+        o[:] = r
+        nan = np.isnan(a.reshape(-1)[lo:hi])
+        if nan.any():
+            o[nan] = 0x7FC0
+
+    _chunked(u.size, part)
+    return out.reshape(a.shape)
 
 
 def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
     return (np.ascontiguousarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
 
 
+def _normal_f32(shape, std: float, seed: int, tensor_id: int, outliers=None) -> np.ndarray:
+    """float32 N(0, std) draws; outliers = (frac, factor) multiplies a Bernoulli(frac) set
+    of entries (their own streams, tensor id T_OUTLIER) by factor."""
+    n = int(np.prod(shape))
+    v = np.empty(n, np.float32)
+
+    def part(i, lo, hi):
+        x = v[lo:hi]
+        np.random.default_rng([seed, tensor_id, i]).standard_normal(size=hi - lo, dtype=np.float32, out=x)
+        x *= np.float32(std)
+        if outliers is not None:
+            frac, factor = outliers
+            mask = np.random.default_rng([seed, T_OUTLIER, i]).random(size=hi - lo) < frac
+            x[mask] *= np.float32(factor)
+
+    _chunked(n, part)
+    return v.reshape(shape)
+
+
 def normal_bf16(shape, std: float = 1.0, seed: int = 0, tensor_id: int = T_A) -> np.ndarray:
-    rng = np.random.default_rng([seed, tensor_id])
-    v = rng.standard_normal(size=shape, dtype=np.float32) * np.float32(std)
-    return f32_to_bf16_bits(v)
+    return f32_to_bf16_bits(_normal_f32(shape, std, seed, tensor_id))
 
 
 def normal_bf16_outliers(shape, std: float = 1.0, frac: float = 0.01, factor: float = 50.0,
                          seed: int = 0, tensor_id: int = T_A) -> np.ndarray:
     """N(0, std) with an independent Bernoulli(frac) mask of entries multiplied by factor,
     applied before the bf16 rounding."""
-    rng = np.random.default_rng([seed, tensor_id])
-    v = rng.standard_normal(size=shape, dtype=np.float32) * np.float32(std)
-    mask = np.random.default_rng([seed, T_OUTLIER]).random(size=shape) < frac
-    v = np.where(mask, v * np.float32(factor), v).astype(np.float32)
-    return f32_to_bf16_bits(v)
+    return f32_to_bf16_bits(_normal_f32(shape, std, seed, tensor_id, outliers=(frac, factor)))
 
 
 def zipf_counts(E: int = 32, tokens: int = 4096, s: float = 1.1, cap: int = 256, seed: int = 0) -> np.ndarray:
