@@ -718,9 +718,11 @@ def main():
     ap.add_argument("--counters", action="store_true",
                     help="workload for rocprofv3 --pmc passes: a 256 MiB torch copy (counter calibration), "
                          "then --steps eager steps of --counters-shape; no timing")
-    ap.add_argument("--counters-shape", default="decode", choices=["decode", "decode_plain", "prefill", "masked"],
+    ap.add_argument("--counters-shape", default="decode",
                     help="decode: M=64 N=7168 K=18432 with pre-shuffled weights (the headline step); "
-                         "decode_plain: the same with weights [N][K]; prefill: M=4096 N=4096 K=7168")
+                         "decode_plain: the same with weights [N][K]; prefill: M=4096 N=4096 K=7168; "
+                         "masked: the MoE gate_up GEMM; or a prefill shape name such as "
+                         "dense_prefill_2048x4096x7168")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -737,12 +739,17 @@ def main():
     stream = torch.cuda.Stream()
     shape = W.DENSE_DECODE
     if args.counters:
+        named = {s.name: s for s in W.DENSE_PREFILL}
         if args.counters_shape == "masked":
             counters_masked_workload(F, W, args.steps)
         elif args.counters_shape == "prefill":
             counters_workload(F, W.DENSE_PREFILL[2], args.steps)
-        else:
+        elif args.counters_shape in named:
+            counters_workload(F, named[args.counters_shape], args.steps)
+        elif args.counters_shape in ("decode", "decode_plain"):
             counters_workload(F, shape, args.steps, preshuffled=args.counters_shape == "decode")
+        else:
+            ap.error("unknown --counters-shape %s" % args.counters_shape)
         return
     host = W.dense_inputs(shape)
     r = bench_dense(F, stream, shape, args.steps, args.warmup, preshuffled=True, hot=not args.no_hot, host=host,
@@ -869,14 +876,15 @@ def main():
 
 def counters_workload(F, shape, steps, preshuffled=False):
     """Kernels for the counter passes: three copies of 256 MiB (a plain copy kernel of
-    known size, to calibrate FETCH_SIZE / WRITE_SIZE), then eager dense steps (with
-    pre-shuffled weights for the headline decode step)."""
+    known size, to calibrate FETCH_SIZE / WRITE_SIZE), then eager dense steps on the
+    timed tensors (with pre-shuffled weights for the headline decode step)."""
     x = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
     y = torch.empty_like(x)
     for _ in range(3):
         y.copy_(x)
     torch.cuda.synchronize()
-    a, copies, qa, sfa, c = setup_dense(F, shape.M, shape.N, shape.K, shape.outliers)
+    import workloads as W
+    a, copies, qa, sfa, c = setup_dense_parity(F, W.dense_inputs(shape), shape)
     if preshuffled:
         copies = [(F.fp8_weight_preshuffle(qb), sfb) for qb, sfb in copies]
     gemm_fn = F.fp8_block_gemm_nt_preshuffled if preshuffled else F.fp8_block_gemm_nt

@@ -2706,10 +2706,11 @@ GemmConfig choose_gemm_config(const GemmProblem& p) {
   if (big_tiles >= 256 && gemm_config_by_index(kCfgRing256x256, p, 1, &cfg)) {
     // With 256x256 tiles, one per compute unit at a time, a last round of at most
     // half the compute units would leave the rest idle for a whole tile time: run
-    // the leading columns in whole rounds and the remaining columns with 128x128
-    // tiles in a second launch (up to 512 of them: two per compute unit, which
-    // finish well within one 256x256 tile time); the 128x128 ring when they make
-    // at most one round, the two-stage tiles (two per compute unit) otherwise.
+    // the leading columns in whole rounds and the remaining columns with smaller
+    // tiles in a second launch: the 128x128 ring when its tiles make at most one
+    // round, else the 256x128 ring when its tiles do (4096x18432x7168: the 4096x2048
+    // tail 80 -> ~64 us against 512 two-stage 128x128 tiles at 35% MFMA use), else
+    // the two-stage 128x128 tiles (two per compute unit).
     const int64_t rem = big_tiles % 256;
     if (rem != 0 && rem <= 128 && p.E == 1 && !p.masked_m && !p.m_indices) {
       const int64_t lead_tn = (big_tiles / 256) * 256 / tm256;
@@ -2718,8 +2719,10 @@ GemmConfig choose_gemm_config(const GemmProblem& p) {
       tp.N = p.N - n_split;
       GemmConfig tc;
       const bool one_round = cdiv(tp.M, 128) * cdiv(tp.N, 128) <= 256;
+      const bool one_round_mid = cdiv(tp.M, 256) * cdiv(tp.N, 128) <= 256;
       if (n_split > 0 && n_split < p.N &&
           ((one_round && gemm_config_by_index(kCfgRing128x128, tp, 1, &tc)) ||
+           (one_round_mid && gemm_config_by_index(kCfgRing256x128, tp, 1, &tc)) ||
            gemm_config_by_index(kCfgScaled128x128, tp, 1, &tc))) {
         cfg.n_split = n_split;
         cfg.tail_kernel = tc.kernel;
