@@ -721,7 +721,8 @@ def main():
     ap.add_argument("--counters-shape", default="decode",
                     help="decode: M=64 N=7168 K=18432 with pre-shuffled weights (the headline step); "
                          "decode_plain: the same with weights [N][K]; prefill: M=4096 N=4096 K=7168; "
-                         "masked: the MoE gate_up GEMM; or a prefill shape name such as "
+                         "masked: the MoE gate_up GEMM; scale_ablation: UE8M0 in the MFMA against "
+                         "unscaled MFMA + VALU scale at 1024x4096x7168; or a prefill shape name such as "
                          "dense_prefill_2048x4096x7168")
     args = ap.parse_args()
 
@@ -742,6 +743,8 @@ def main():
         named = {s.name: s for s in W.DENSE_PREFILL}
         if args.counters_shape == "masked":
             counters_masked_workload(F, W, args.steps)
+        elif args.counters_shape == "scale_ablation":
+            counters_scale_ablation_workload(F, W, args.steps)
         elif args.counters_shape == "prefill":
             counters_workload(F, W.DENSE_PREFILL[2], args.steps)
         elif args.counters_shape in named:
@@ -896,6 +899,40 @@ def counters_workload(F, shape, steps, preshuffled=False):
     layout = F.LAYOUT_DENSE_PRESHUFFLED if preshuffled else F.LAYOUT_DENSE
     print(json.dumps({"copy_bytes_each_way": 256 << 20, "steps": steps, "preshuffled": preshuffled,
                       "config": F.gemm_config(layout, shape.M, shape.N, shape.K)}))
+
+
+def counters_scale_ablation_workload(F, W, steps):
+    """Kernels for counter passes on the scale ablation at 1024x4096x7168, where both
+    automatic choices are 128x128 full-row ring tiles: --steps calls with UE8M0 scales
+    applied inside the MFMA, then --steps calls on the same codes with the same scales
+    as fp32 powers of two (float-scale format: unscaled MFMAs, the scale FMA on the
+    VALU).  The two outputs are compared bit for bit."""
+    x = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+    y = torch.empty_like(x)
+    for _ in range(3):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    del x, y
+    shape = W.DENSE_PREFILL[0]
+    M, N, K = shape.M, shape.N, shape.K
+    KB = K // 128
+    a, copies, qa, sfa, c = setup_dense_parity(F, W.dense_inputs(shape), shape)
+    qb, sfb = copies[0]
+    F.fp8_quant_group_pack(a, q=qa, sf=sfa)
+    wd = sfa.shape[0]
+    by = sfa.contiguous().view(torch.uint8).view(wd, sfa.shape[1], 4).permute(0, 2, 1).reshape(4 * wd, sfa.shape[1])[:KB]
+    sfa_f = torch.ldexp(torch.ones_like(by, dtype=torch.float32), by.int() - 127).contiguous()
+    c2 = torch.empty_like(c)
+    for i in range(steps):
+        F.fp8_block_gemm_nt(qa, sfa, qb, sfb, c=c)
+    torch.cuda.synchronize()
+    for i in range(steps):
+        F.fp8_block_gemm_nt_float_scales(qa, sfa_f, qb, sfb, c=c2)
+    torch.cuda.synchronize()
+    same = bool(torch.equal(c.view(torch.int16), c2.view(torch.int16)))
+    print(json.dumps({"copy_bytes_each_way": 256 << 20, "steps_per_variant": steps, "outputs_equal": same,
+                      "ue8m0_config": F.gemm_config(F.LAYOUT_DENSE, M, N, K),
+                      "float_config": F.gemm_config(F.LAYOUT_DENSE_FLOAT, M, N, K)}))
 
 
 def counters_masked_workload(F, W, steps):

@@ -1170,7 +1170,14 @@ constexpr int ring_wd_max() { return RingShape<BM, BN, WGM, WGN>::WD_MAX; }
 //           more), DMA of j + S into j's stage, then the MFMAs of j's second half
 //           interleaved with the operand reads of j + 1's first half and the DMA.
 // One barrier per K-block; a DMA has S - 1 K-blocks to land.
-template <int BM, int BN, int WGM, int WGN, int S>
+// FS: the float-scale format (fp32 activation scales per row and K-block, fp32 weight
+// block scales).  The MFMA then runs unscaled: the two MFMAs of a K-block (its two
+// K-halves) add into a block partial P, and P * (sa * sb) is added to the
+// accumulator on the VALU, which needs the accumulators in the architectural
+// registers: only the 1 x 4 wavefront grid of 128 x 128 tiles (64 accumulators and
+// 64 partials per lane) leaves room for the operands.  The tables then hold one fp32
+// per K-block instead of one packed word per four K-blocks.
+template <int BM, int BN, int WGM, int WGN, int S, bool FS = false>
 struct Ring2Shape {
   static constexpr int WM = BM / WGM, WN = BN / WGN;
   static constexpr int SM = WM / 32, SN = WN / 32;
@@ -1179,17 +1186,18 @@ struct Ring2Shape {
   static constexpr int IPW = IPA + IPB;
   static constexpr int NBT = BN / 128;
   static constexpr int FIT = (160 * 1024 - S * SLOT - 256) / (BM * 4 + NBT * 4);
-  static constexpr int WD_MAX = FIT < 32 ? FIT : 32;
+  static constexpr int WD_MAX = FIT < (FS ? 128 : 32) ? FIT : (FS ? 128 : 32);  // table entries per row
 };
 
-template <int BM, int BN, int WGM, int WGN, int S>
+template <int BM, int BN, int WGM, int WGN, int S, bool FS = false>
 __global__ __launch_bounds__(256) void ring2_kernel(const KArgs p) {
-  using R = Ring2Shape<BM, BN, WGM, WGN, S>;
+  using R = Ring2Shape<BM, BN, WGM, WGN, S, FS>;
   constexpr int WM = R::WM, WN = R::WN, SM = R::SM, SN = R::SN, IPW = R::IPW, IPA = R::IPA;
   constexpr int WD_MAX = R::WD_MAX, NBT = R::NBT;
   static_assert(WGM * WGN == 4 && WM % 32 == 0 && WN % 32 == 0 && BN % 128 == 0 && BM % 32 == 0, "tile shape");
   static_assert(S == 2 || S == 4, "stages (a divisor of the four K-blocks of a scale word)");
   static_assert(WD_MAX >= 1, "scale tables do not fit");
+  static_assert(!FS || (WGM == 1 && BM == 128 && BN == 128), "float scales: 128 x 128 tiles, 1 x 4 wavefronts");
   __shared__ __attribute__((aligned(1024))) uint8_t sl0[R::SLOT];
   __shared__ __attribute__((aligned(1024))) uint8_t sl1[R::SLOT];
   __shared__ __attribute__((aligned(1024))) uint8_t sl2[S > 2 ? R::SLOT : 16];
@@ -1255,23 +1263,30 @@ __global__ __launch_bounds__(256) void ring2_kernel(const KArgs p) {
     }
   };
 
-  // scale tables (as in the ring kernel)
+  // scale tables (as in the ring kernel; FS: one fp32 per row and K-block, one fp32
+  // per weight block and K-block)
   constexpr int SA_IT = (WD_MAX * BM + 255) / 256;
-  constexpr int SB_IT = (NBT * WD_MAX * 4 + 255) / 256;
+  constexpr int SB_IT = (NBT * WD_MAX * (FS ? 1 : 4) + 255) / 256;
   uint32_t sav[SA_IT], sbv[SB_IT];
+  const auto rSAF = make_rsrc(p.sfa_f, (uint32_t)(FS ? KB * p.ld_sfa * 4 : 0));
 #pragma unroll
   for (int t = 0; t < SA_IT; ++t) {
     const int idx = t * 256 + tid;
     const int w = idx / BM, row = idx - w * BM;
-    const bool ok = idx < WD_MAX * BM && w < Wd && m0 + row < m_limit;
-    sav[t] = bload4(rSA, ok ? (uint32_t)(((int64_t)w * p.ld_sfa + m0 + row) * 4) : kOOB);
+    if constexpr (FS) {
+      const bool ok = idx < WD_MAX * BM && w < KB && m0 + row < m_limit;
+      sav[t] = bload4(rSAF, ok ? (uint32_t)(((int64_t)w * p.ld_sfa + m0 + row) * 4) : kOOB);
+    } else {
+      const bool ok = idx < WD_MAX * BM && w < Wd && m0 + row < m_limit;
+      sav[t] = bload4(rSA, ok ? (uint32_t)(((int64_t)w * p.ld_sfa + m0 + row) * 4) : kOOB);
+    }
   }
 #pragma unroll
   for (int t = 0; t < SB_IT; ++t) {
     const int idx = t * 256 + tid;
-    const int b = idx / (WD_MAX * 4), k = idx - b * (WD_MAX * 4);
+    const int b = idx / (WD_MAX * (FS ? 1 : 4)), k = idx - b * (WD_MAX * (FS ? 1 : 4));
     const int nb = (int)(n0 >> 7) + b;
-    const bool ok = idx < NBT * WD_MAX * 4 && nb < NB && k < KB;
+    const bool ok = idx < NBT * WD_MAX * (FS ? 1 : 4) && nb < NB && k < KB;
     sbv[t] = bload4(rSB, ok ? (uint32_t)((nb * KB + k) * 4) : kOOB);
   }
   issue(0, IntC<0>{});
@@ -1285,15 +1300,25 @@ __global__ __launch_bounds__(256) void ring2_kernel(const KArgs p) {
     const int idx = t * 256 + tid;
     const int w = idx / BM;
     uint32_t v = sav[t];
-    const int left = KB - 4 * w;
-    if (left < 4) v &= left <= 0 ? 0u : ((1u << (8 * left)) - 1u);
+    if constexpr (!FS) {
+      const int left = KB - 4 * w;
+      if (left < 4) v &= left <= 0 ? 0u : ((1u << (8 * left)) - 1u);
+    }
     if (idx < WD_MAX * BM) sa_tab[idx] = v;
   }
-  uint8_t* sb_bytes = reinterpret_cast<uint8_t*>(sb_tab);
+  if constexpr (FS) {
 #pragma unroll
-  for (int t = 0; t < SB_IT; ++t) {
-    const int idx = t * 256 + tid;
-    if (idx < NBT * WD_MAX * 4) sb_bytes[idx] = (uint8_t)((sbv[t] >> 23) & 0xFFu);
+    for (int t = 0; t < SB_IT; ++t) {
+      const int idx = t * 256 + tid;
+      if (idx < NBT * WD_MAX) sb_tab[idx] = sbv[t];
+    }
+  } else {
+    uint8_t* sb_bytes = reinterpret_cast<uint8_t*>(sb_tab);
+#pragma unroll
+    for (int t = 0; t < SB_IT; ++t) {
+      const int idx = t * 256 + tid;
+      if (idx < NBT * WD_MAX * 4) sb_bytes[idx] = (uint8_t)((sbv[t] >> 23) & 0xFFu);
+    }
   }
   // the first stage and the tables in place everywhere
   __builtin_amdgcn_s_waitcnt(waitcnt_imm((S - 1) * IPW, 0));
@@ -1348,6 +1373,8 @@ __global__ __launch_bounds__(256) void ring2_kernel(const KArgs p) {
       for (int j = 0; j < SN; ++j)
 #pragma unroll
         for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
+    // FS: block partials of the current K-block (unscaled MFMAs)
+    v16f part[FS ? SM : 1][FS ? SN : 1];
 
     auto mfmas = [&](const v8i (&xf)[SM], const v8i (&wf)[SN], auto ops_tag) {
       constexpr int OPS = decltype(ops_tag)::value;
@@ -1358,6 +1385,35 @@ __global__ __launch_bounds__(256) void ring2_kernel(const KArgs p) {
           acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wf[j], xf[i], acc[i][j], 0, 0, OPS, (int)sb,
                                                                       OPS, (int)sa[i]);
     };
+    // FS: K-half h of a K-block into the block partials (h = 0 starts them at zero)
+    auto mfmas_fs = [&](const v8i (&xf)[SM], const v8i (&wf)[SN], auto h_tag) {
+      constexpr int H = decltype(h_tag)::value;
+      if constexpr (FS) {
+#pragma unroll
+        for (int i = 0; i < IV; ++i)
+#pragma unroll
+          for (int j = 0; j < SN; ++j) {
+            v16f c = {};
+            if constexpr (H == 1) c = part[i][j];
+            part[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wf[j], xf[i], c, 0, 0, 0, 0, 0, 0);
+          }
+      }
+    };
+    // FS: acc += P * (sa * sb) for K-block kb: one activation scale per lane (its
+    // output row) and one weight scale per wavefront (its 128-column block)
+    auto scale_add = [&](int kb) {
+      if constexpr (FS) {
+        const float sbf = __uint_as_float(sb_tab[sb_blk * WD_MAX + kb]);
+#pragma unroll
+        for (int i = 0; i < IV; ++i) {
+          const float s = __uint_as_float(sa_tab[kb * BM + wm * WM + 32 * i + lr]) * sbf;
+#pragma unroll
+          for (int j = 0; j < SN; ++j)
+#pragma unroll
+            for (int q = 0; q < 16; ++q) acc[i][j][q] = __builtin_fmaf(part[i][j][q], s, acc[i][j][q]);
+        }
+      }
+    };
 
     // K-block kb = kb4 + U (kb4 a multiple of 4): scale byte U, stage U % S
     auto kblock = [&](int kb4, auto u_tag) {
@@ -1366,15 +1422,16 @@ __global__ __launch_bounds__(256) void ring2_kernel(const KArgs p) {
       const int kb = kb4 + U;
       // half 0: MFMAs of the first K-half, reads of the second
       __builtin_amdgcn_sched_barrier(0);
-      if constexpr (U == 0) {
+      if constexpr (U == 0 && !FS) {
 #pragma unroll
         for (int i = 0; i < SM; ++i) sa[i] = sa_n[i];
         sb = sb_n;
       }
       read_frags(IntC<ST>{}, IntC<1>{}, xn, wn_);
-      mfmas(xc, wc, IntC<U>{});
+      if constexpr (FS) mfmas_fs(xc, wc, IntC<0>{});
+      else mfmas(xc, wc, IntC<U>{});
       mfma_read_dma_pattern<IV * SN, 2 * (IV > 0 ? IV + SN : 0), 0>();
-      if constexpr (U == 2) {
+      if constexpr (U == 2 && !FS) {
         // scale words of the next group (clamped to the table; unused past the end)
         const int wnx = (kb4 >> 2) + 1 < WD_MAX ? (kb4 >> 2) + 1 : WD_MAX - 1;
 #pragma unroll
@@ -1388,8 +1445,10 @@ __global__ __launch_bounds__(256) void ring2_kernel(const KArgs p) {
       __builtin_amdgcn_sched_barrier(0);
       issue(kb + S, IntC<ST>{});
       read_frags(IntC<STN>{}, IntC<0>{}, xc, wc);
-      mfmas(xn, wn_, IntC<U>{});
+      if constexpr (FS) mfmas_fs(xn, wn_, IntC<1>{});
+      else mfmas(xn, wn_, IntC<U>{});
       mfma_read_dma_pattern<IV * SN, 2 * (IV > 0 ? IV + SN : 0), IPW>();
+      if constexpr (FS) scale_add(kb < WD_MAX ? kb : WD_MAX - 1);  // (K-blocks past the end: zero partials)
     };
 
     for (int kb4 = 0; kb4 < KB4; kb4 += 4) {
@@ -1451,8 +1510,8 @@ __global__ __launch_bounds__(256) void ring2_kernel(const KArgs p) {
   }
 }
 
-template <int BM, int BN, int WGM, int WGN, int S>
-constexpr int ring2_wd_max() { return Ring2Shape<BM, BN, WGM, WGN, S>::WD_MAX; }
+template <int BM, int BN, int WGM, int WGN, int S, bool FS = false>
+constexpr int ring2_wd_max() { return Ring2Shape<BM, BN, WGM, WGN, S, FS>::WD_MAX; }
 
 
 // ---------------------------------------------------------------------------
@@ -2331,7 +2390,8 @@ typedef void (*KernelFn)(const KArgs);
 
 enum Kind { kTile = 0, kStream = 1, kScaled = 2, kRing = 3, kDecode = 4, kTileFloat = 5, kDecodeFloat = 6,
             kScaledFloat = 7, kDecodeSep = 8, kDecodeShuf = 9, kDecodeShufSep = 10, kRingShuf = 11,
-            kDecodeFloatShuf = 12, kDecodeFloatSep = 13, kDecodeFloatShufSep = 14, kWsd = 15, kWsdSep = 16 };
+            kDecodeFloatShuf = 12, kDecodeFloatSep = 13, kDecodeFloatShufSep = 14, kWsd = 15, kWsdSep = 16,
+            kRingFloat = 17 };
 
 // Weight-streaming decode entries (pre-shuffled weights, dense M <= 64, 1-D grid).
 inline bool is_wsd(int kind) { return kind == kWsd || kind == kWsdSep; }
@@ -2339,7 +2399,7 @@ inline bool is_wsd(int kind) { return kind == kWsd || kind == kWsdSep; }
 // Entries that read the float-scale format.
 inline bool reads_float_scales(int kind) {
   return kind == kTileFloat || kind == kDecodeFloat || kind == kScaledFloat || kind == kDecodeFloatShuf ||
-         kind == kDecodeFloatSep || kind == kDecodeFloatShufSep;
+         kind == kDecodeFloatSep || kind == kDecodeFloatShufSep || kind == kRingFloat;
 }
 // LDS-DMA tile entries (dynamic LDS for the scale tables).
 inline bool is_scaled_tile(int kind) { return kind == kScaled || kind == kScaledFloat; }
@@ -2353,7 +2413,7 @@ inline bool reads_shuffled(int kind) {
          kind == kDecodeFloatShufSep || is_wsd(kind);
 }
 // Ring entries (K never split; the scale tables bound K).
-inline bool is_ring(int kind) { return kind == kRing || kind == kRingShuf; }
+inline bool is_ring(int kind) { return kind == kRing || kind == kRingShuf || kind == kRingFloat; }
 // Decode-kernel entries (K split in whole scale words; the *Sep kinds leave the sum of
 // the partials to splitk_reduce_kernel).
 inline bool is_decode(int kind) {
@@ -2368,7 +2428,8 @@ struct TileEntry {
                // kScaled: LDS-DMA tiles + scaled MFMA (no K split)
   int stages;  // LDS ring depth of kScaled / kRing
   int threads;  // workgroup size
-  int max_wd;   // kRing: most activation-scale words per row (K-blocks / 4) its tables hold;
+  int max_wd;   // kRing: most activation-scale words per row (K-blocks / 4) its tables hold
+                // (kRingFloat: most K-blocks, one fp32 each);
                 // kDecode: the same per K split
 };
 
@@ -2449,6 +2510,8 @@ const TileEntry kTiles[] = {
     {ring2_kernel<128, 128, 1, 4, 4>, 128, 128, kRing, 4, 256, ring2_wd_max<128, 128, 1, 4, 4>()},
     {ring2_kernel<128, 256, 2, 2, 2>, 128, 256, kRing, 2, 256, ring2_wd_max<128, 256, 2, 2, 2>()},
     {ring2_kernel<256, 256, 1, 4, 2>, 256, 256, kRing, 2, 256, ring2_wd_max<256, 256, 1, 4, 2>()},
+    // float scales: the full-row 128x128 ring, unscaled MFMAs, block partials scaled on the VALU
+    {ring2_kernel<128, 128, 1, 4, 4, true>, 128, 128, kRingFloat, 4, 256, ring2_wd_max<128, 128, 1, 4, 4, true>()},
 };
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 // table entries the automatic choice uses
@@ -2470,6 +2533,7 @@ constexpr int kCfgFloat128x256 = 29;
 constexpr int kCfgFloatDecode64x128 = 46;  // decode kernel, float scales, weights through LDS, reduction kernel
 constexpr int kCfgFloatScaled128x128 = 31; // LDS-DMA tiles, float scales
 constexpr int kCfgFloatScaled128x256 = 32;
+constexpr int kCfgRingFloat128x128 = 68;   // full-row ring 128x128, float scales on the VALU
 constexpr int kCfgDecode64x128 = 45;       // decode kernel, 4 wavefronts, weights through a 3-stage LDS ring,
                                            // partials summed by splitk_reduce_kernel
 constexpr int kCfgShufDecode64x128 = 36;   // the same on pre-shuffled weights (register loads)
@@ -2481,6 +2545,7 @@ constexpr int kCfgFloatShufDecode64x128 = 47;  // float scales, pre-shuffled wei
 constexpr int kCfgRing128x128 = 65;          // ring 128x128, 1 x 4 wavefronts, four full K-block stages
 constexpr int kCfgShufRing128x128 = 50;      // the same (2 x 2) on pre-shuffled weights
 static_assert(kCfgDecode64x128 < kNumTiles && kCfgFloatScaled128x256 < kNumTiles, "tile table");
+static_assert(kCfgRingFloat128x128 < kNumTiles, "tile table");
 static_assert(kCfgFloatShufDecode64x128 < kNumTiles && kCfgFloatDecode64x128 < kNumTiles, "tile table");
 static_assert(kCfgRing128x128 < kNumTiles && kCfgShufRing128x128 < kNumTiles, "tile table");
 static_assert(kCfgRing256x256 < kNumTiles && kCfgRing256x256Rows < kNumTiles && kCfgRing128x256 < kNumTiles &&
@@ -2517,8 +2582,9 @@ bool gemm_config_by_index(int idx, const GemmProblem& p, int splits, GemmConfig*
   // contiguous grouped layout: a tile must not straddle two aligned runs
   if (p.m_indices && kContiguousAlign % kTiles[idx].bm != 0) return false;
   if (is_ring(kTiles[idx].kind)) {
-    splits = 1;  // never splits K; the scale tables bound K
-    if ((KB + 3) / 4 > kTiles[idx].max_wd) return false;
+    splits = 1;  // never splits K; the scale tables bound K (words of four K-blocks, or
+                 // one fp32 per K-block in the float-scale format)
+    if ((kTiles[idx].kind == kRingFloat ? KB : (KB + 3) / 4) > kTiles[idx].max_wd) return false;
   }
   if (is_scaled_tile(kTiles[idx].kind)) {
     splits = 1;  // this family never splits K
@@ -2651,8 +2717,12 @@ GemmConfig choose_gemm_config(const GemmProblem& p) {
       if (!gemm_config_by_index(kCfgFloat64x128, p, splits, &cfg)) cfg.kernel = -1;
       return cfg;
     }
-    // larger M: LDS-DMA tiles (128 x 256 once they fill the compute units), the
-    // VALU-scaled register-staged tiles when the scale tables do not fit
+    // larger M: the full-row 128 x 128 ring with the scales on the VALU when its
+    // tables hold K (1024x4096x7168: 71.2 -> 41.8 us, 4096x4096x7168: 231 -> 165 us,
+    // 2048x18432x7168: 586 -> 369 us against the LDS-DMA 128 x 128 / 128 x 256 tiles);
+    // else LDS-DMA tiles (128 x 256 once they fill the compute units), the VALU-scaled
+    // register-staged tiles when no scale table fits
+    if (gemm_config_by_index(kCfgRingFloat128x128, p, 1, &cfg)) return cfg;
     const int64_t t256 = cdiv(p.M, 128) * cdiv(p.N, 256);
     if (t256 >= 256 && gemm_config_by_index(kCfgFloatScaled128x256, p, 1, &cfg)) return cfg;
     if (gemm_config_by_index(kCfgFloatScaled128x128, p, 1, &cfg)) return cfg;
