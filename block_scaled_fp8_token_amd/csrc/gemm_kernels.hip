@@ -13,18 +13,27 @@
 // [E][M_max][K] activations where only the first masked_m[e] rows of group e
 // are valid; the counts stay on the device.
 //
-// Design (CDNA4): a K-block of 128 is exactly one v_mfma_f32_16x16x128_f8f6f4,
-// so each MFMA produces one block partial P for a 16x16 sub-tile and the scale
-// is applied as acc += P * (2^ea * sfb) with four FMAs per lane.  The MFMA is
-// issued with the weight tile as its first operand so that each lane's four
-// results share one output row m: one activation scale per lane per sub-tile,
-// and four consecutive bf16 columns per lane in the epilogue.  A and B tiles go
-// global -> registers -> LDS, double-buffered, with a 16-byte pad per 128-byte
-// row so that the 16 rows read by one MFMA operand fall in distinct banks.
-// Workgroups whose rows all lie past the mask return before any load; sub-tiles
-// past the mask issue no MFMA.  Decode-sized M splits K across workgroups; the
-// last workgroup of a tile to finish sums the fp32 partials in split order
-// (deterministic) and writes bf16.
+// Kernel families in this file (the automatic choice is in choose_gemm_config):
+//   * wsd_kernel: dense M <= 64 on pre-shuffled weights.  Weight streaming: each
+//     lane loads its MFMA operand bytes (one contiguous kilobyte per wavefront load)
+//     straight into registers several K-blocks ahead, the activation K-blocks go to
+//     LDS by LDS-DMA, K is split over workgroups and the splits of a tile sum their
+//     fp32 partials inside the kernel (last arriver, in part order: deterministic).
+//   * decode_kernel: dense M <= 64 on the plain [N][K] layout (weights through an LDS
+//     ring) and the float-scale decode; partials summed by splitk_reduce_kernel.
+//   * ring2_kernel: prefill and masked.  LDS-DMA rings of whole 128-byte K-block rows,
+//     one barrier per K-block, v_mfma_scale_f32_32x32x64_f8f6f4 with the packed UE8M0
+//     bytes as scale operands (the scale-then-accumulate of each K-block happens in the
+//     matrix core), bf16 epilogue staged through LDS, XCD-aware tile order.  Its
+//     float-scale form runs the MFMAs unscaled and adds P * (sa * sb) on the VALU.
+//   * scaled_ring_kernel (K-half stages; the masked and pre-shuffled prefill entries),
+//     scaled_tile_kernel (two-stage tiles), stream_kernel and gemm_kernel (the
+//     first design: LDS via registers, 16x16x128 MFMA on zero then a VALU scale FMA):
+//     fallbacks for shapes and K ranges the others do not take.
+// The MFMA is issued with the weight tile as its first operand, so all of a lane's
+// results share one output row m: one activation scale per lane.  Workgroups whose
+// rows all lie past the mask return before any load; 32-row groups past the mask
+// issue no operand reads or MFMAs.
 #include <atomic>
 
 #include "fp8bs_device.hpp"

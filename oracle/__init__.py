@@ -21,6 +21,8 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
+# a prebuilt copy to load instead (the sanitizer test builds one with -fsanitize)
+_LIB_OVERRIDE = os.environ.get("FP8BS_ORACLE_LIB")
 
 _lib = None
 
@@ -36,13 +38,26 @@ def build(force: bool = True) -> str:
     return _LIB
 
 
+def build_sanitized(path: str) -> str:
+    """Compile oracle.c with AddressSanitizer and UndefinedBehaviorSanitizer into `path`
+    (load it with FP8BS_ORACLE_LIB=path in a process that preloads libasan)."""
+    cmd = ["gcc", "-O1", "-g", "-std=c11", "-ffp-contract=off", "-fopenmp", "-fPIC", "-shared",
+           "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined", "-fno-omit-frame-pointer",
+           _SRC, "-o", path, "-lm"]
+    subprocess.run(cmd, check=True)
+    return path
+
+
 def _load():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
-        build(force=True)
-    lib = ctypes.CDLL(_LIB)
+    if _LIB_OVERRIDE:
+        lib = ctypes.CDLL(_LIB_OVERRIDE)
+    else:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build(force=True)
+        lib = ctypes.CDLL(_LIB)
     P = ctypes.c_void_p
     I = ctypes.c_int64
     lib.orc_e4m3_decode.argtypes = [ctypes.c_uint8]
