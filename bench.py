@@ -814,21 +814,25 @@ def main():
                          "gemm_us_hot": None if plain["gemm_us_hot"] is None else round(plain["gemm_us_hot"], 2),
                          **sub_object(plain, bound_flops=False)},
     }
+    target_rows = []
     if not args.no_targets:
         pre_steps = max(10, args.steps // 4)
         prefill = {}
         for s in W.DENSE_PREFILL:
             x = bench_dense(F, stream, s, pre_steps, args.warmup, host=W.dense_inputs(s), stats=True, keep_out=False)
+            target_rows.append(x)
             print("[bench] %s" % json.dumps(x), file=sys.stderr, flush=True)
             o = sub_object(x)
             o["target_us_60pct_mfma"] = round(gemm_flops(s.M, s.N, s.K) / (0.6 * FP8_PEAK_TFLOPS * 1e12) * 1e6, 1)
             prefill[s.name] = o
         line["prefill"] = prefill
         x = bench_masked_gate_up(F, W, stream, pre_steps, args.warmup)
+        target_rows.append(x)
         print("[bench] %s" % json.dumps(x), file=sys.stderr, flush=True)
         line["moe_gate_up_masked"] = dict(workload=x["workload"], valid_rows=x["S"], experts_active=x["E_active"],
                                           **sub_object(x))
         x = bench_silu_down(F, W, stream, pre_steps, args.warmup)
+        target_rows.append(x)
         print("[bench] %s" % json.dumps(x), file=sys.stderr, flush=True)
         o = dict(workload=x["workload"], valid_rows=x["S"], **sub_object(x))
         o["silu_us"] = round(x["silu_us"], 2)
@@ -842,12 +846,14 @@ def main():
         line["parity_check"] = parity_check(out0, ref)
 
     if args.sweep:
-        rows = [r, plain]
-        rows.append(bench_dense(F, stream, W.DENSE_SMALL, args.steps, args.warmup))
+        rows = [r, plain] + target_rows
+        rows.append(bench_dense(F, stream, W.DENSE_SMALL, args.steps, args.warmup, host=W.dense_inputs(W.DENSE_SMALL)))
+        rows[-1].pop("_out0", None)
         for s in W.DENSE_PREFILL:
-            rows.append(bench_dense(F, stream, s, max(10, args.steps // 4), args.warmup, preshuffled=True))
+            rows.append(bench_dense(F, stream, s, max(10, args.steps // 4), args.warmup, preshuffled=True,
+                                    host=W.dense_inputs(s), keep_out=False))
             print("[bench] %s" % json.dumps(rows[-1]), file=sys.stderr, flush=True)
-        for pre in (False, True):
+        for pre in ((True,) if target_rows else (False, True)):
             rows.append(bench_masked_gate_up(F, W, stream, max(10, args.steps // 4), args.warmup, preshuffled=pre))
             print("[bench] %s" % json.dumps(rows[-1]), file=sys.stderr, flush=True)
             rows.append(bench_silu_down(F, W, stream, max(10, args.steps // 4), args.warmup, preshuffled=pre))
@@ -856,7 +862,8 @@ def main():
         print("[bench] %s" % json.dumps(rows[-1]), file=sys.stderr, flush=True)
         rows.append(bench_dispatch_quant(F, W, stream, args.steps, args.warmup))
         print("[bench] %s" % json.dumps(rows[-1]), file=sys.stderr, flush=True)
-        for fs, pre in ((W.DENSE_DECODE, False), (W.DENSE_DECODE, True), (W.DENSE_PREFILL[2], False)):
+        for fs, pre in ((W.DENSE_DECODE, False), (W.DENSE_DECODE, True), (W.DENSE_PREFILL[0], False),
+                        (W.DENSE_PREFILL[1], False), (W.DENSE_PREFILL[2], False), (W.DENSE_PREFILL[4], False)):
             rows.append(bench_dense_float(F, stream, fs, max(10, args.steps // 4), args.warmup, preshuffled=pre))
             print("[bench] %s" % json.dumps(rows[-1]), file=sys.stderr, flush=True)
         print("%-58s %10s %10s %10s %8s %8s" % ("workload", "us", "TFLOPS", "GB/s", "%MFMA", "%HBM"),
