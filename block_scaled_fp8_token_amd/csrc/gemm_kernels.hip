@@ -2529,6 +2529,8 @@ const TileEntry kTiles[] = {
     {ring2_kernel<128, 128, 1, 4, 4, true>, 128, 128, kRingFloat, 4, 256, ring2_wd_max<128, 128, 1, 4, 4, true>()},
     // masked: the full-row ring with the wavefronts side by side in N, weights streamed non-temporally
     {ring2_kernel<256, 256, 1, 4, 2, false, true>, 256, 256, kRing, 2, 256, ring2_wd_max<256, 256, 1, 4, 2>()},
+    // contiguous grouped: the same at 128-row tiles (one aligned run each)
+    {ring2_kernel<128, 256, 1, 4, 2, false, true>, 128, 256, kRing, 2, 256, ring2_wd_max<128, 256, 1, 4, 2>()},
 };
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 // table entries the automatic choice uses
@@ -2543,6 +2545,7 @@ constexpr int kCfgScaled256x256 = 15;
 constexpr int kCfgRing256x256 = 63;        // 2 x 2 wavefronts, two full K-block stages
 constexpr int kCfgRing256x256Rows = 20;    // K-half ring, 1 x 4 wavefronts (all share the rows)
 constexpr int kCfgRing2Masked = 69;        // full-row ring, 1 x 4 wavefronts, non-temporal weight DMA
+constexpr int kCfgRing2Contiguous = 70;    // the same, 128 x 256 tiles
 constexpr int kCfgRing128x256 = 19;        // K-half ring, 2 x 2 wavefronts, 128-row tiles
 constexpr int kCfgRing256x128 = 64;        // 2 x 2 wavefronts, 128-column tiles, two full K-block stages
 constexpr int kCfgFloat64x128 = 26;        // float-scale VALU-scaled tiles
@@ -2563,7 +2566,8 @@ constexpr int kCfgFloatShufDecode64x128 = 47;  // float scales, pre-shuffled wei
 constexpr int kCfgRing128x128 = 65;          // ring 128x128, 1 x 4 wavefronts, four full K-block stages
 constexpr int kCfgShufRing128x128 = 50;      // the same (2 x 2) on pre-shuffled weights
 static_assert(kCfgDecode64x128 < kNumTiles && kCfgFloatScaled128x256 < kNumTiles, "tile table");
-static_assert(kCfgRingFloat128x128 < kNumTiles && kCfgRing2Masked < kNumTiles, "tile table");
+static_assert(kCfgRingFloat128x128 < kNumTiles && kCfgRing2Masked < kNumTiles && kCfgRing2Contiguous < kNumTiles,
+              "tile table");
 static_assert(kCfgFloatShufDecode64x128 < kNumTiles && kCfgFloatDecode64x128 < kNumTiles, "tile table");
 static_assert(kCfgRing128x128 < kNumTiles && kCfgShufRing128x128 < kNumTiles, "tile table");
 static_assert(kCfgRing256x256 < kNumTiles && kCfgRing256x256Rows < kNumTiles && kCfgRing128x256 < kNumTiles &&
@@ -2748,8 +2752,11 @@ GemmConfig choose_gemm_config(const GemmProblem& p) {
     return cfg;
   }
   if (p.m_indices) {
-    // contiguous grouped layout: 128-row tiles (one aligned run each); 128 x 256 ring
-    // tiles when the scale tables hold K, else the 128 x 128 scaled tiles
+    // contiguous grouped layout: 128-row tiles (one aligned run each); the full-row
+    // 128 x 256 ring with non-temporal weight DMA (gate_up workload: 273 -> 247 us
+    // against the K-half 128 x 256 ring), the K-half ring when K is past its tables,
+    // then the 128 x 128 scaled tiles
+    if (gemm_config_by_index(kCfgRing2Contiguous, p, 1, &cfg)) return cfg;
     if (gemm_config_by_index(kCfgRing128x256, p, 1, &cfg)) return cfg;
     if (gemm_config_by_index(kCfgScaled128x128, p, 1, &cfg)) return cfg;
     if (gemm_config_by_index(kCfgStream64x128, p, 1, &cfg)) return cfg;
