@@ -11,10 +11,12 @@ rotations of the one weight set) are rotated so that every step streams its
 weights from HBM rather than from the 256 MB last-level cache.
 
 Prints one JSON line on stdout: the headline, then sub-objects for the prefill
-sweep, the masked MoE gate_up GEMM and the fused SiLU-quant + masked down GEMM
-(each per call: mean and p10/median/p90 over batches, TFLOPS, GB/s, roofline
-fraction), the oracle timed on the host cores, and a check of the timed call's
-output against the oracle's.  --sweep also times the other layouts and entry
+sweep (weights pre-shuffled, the plain layout timed beside it), the masked MoE
+gate_up GEMM (pre-shuffled weights) and the fused SiLU-quant + masked down GEMM
+(plain weights; each MoE GEMM also timed on the other layout), each per call:
+mean and p10/median/p90 over batches, TFLOPS, GB/s, roofline fraction; then the
+oracle timed on the host cores, and a check of the timed call's output against
+the oracle's.  --sweep also times the other layouts and entry
 points and prints a table on stderr (and JSON lines to --sweep-out).
 
 Metric definitions follow the benchmark post (section 4.3): TFLOPS = 2*M*N*K/t,
@@ -817,24 +819,41 @@ def main():
     target_rows = []
     if not args.no_targets:
         pre_steps = max(10, args.steps // 4)
+        # prefill: weights pre-shuffled offline, as for the headline step (the ring tiles
+        # then move one contiguous kilobyte per weight DMA instruction); the plain layout
+        # timed beside it
         prefill = {}
         for s in W.DENSE_PREFILL:
-            x = bench_dense(F, stream, s, pre_steps, args.warmup, host=W.dense_inputs(s), stats=True, keep_out=False)
-            target_rows.append(x)
+            host_s = W.dense_inputs(s)
+            x = bench_dense(F, stream, s, pre_steps, args.warmup, preshuffled=True, host=host_s, stats=True,
+                            keep_out=False)
+            xp = bench_dense(F, stream, s, pre_steps, args.warmup, host=host_s, keep_out=False)
+            target_rows += [x, xp]
             print("[bench] %s" % json.dumps(x), file=sys.stderr, flush=True)
-            o = sub_object(x)
+            print("[bench] %s" % json.dumps(xp), file=sys.stderr, flush=True)
+            o = {"weights": "pre-shuffled", **sub_object(x)}
             o["target_us_60pct_mfma"] = round(gemm_flops(s.M, s.N, s.K) / (0.6 * FP8_PEAK_TFLOPS * 1e12) * 1e6, 1)
+            o["plain_layout"] = {"gemm_us": round(xp["gemm_us"], 2), "gemm_tflops": round(xp["gemm_tflops"], 1),
+                                 "frac_mfma": round(xp["frac_mfma"], 4), "tile": xp["config"]}
             prefill[s.name] = o
         line["prefill"] = prefill
-        x = bench_masked_gate_up(F, W, stream, pre_steps, args.warmup)
-        target_rows.append(x)
+        # MoE: each expert weight set in the layout its GEMM runs faster on (gate_up
+        # pre-shuffled, down plain), the other layout timed beside it
+        x = bench_masked_gate_up(F, W, stream, pre_steps, args.warmup, preshuffled=True)
+        xp = bench_masked_gate_up(F, W, stream, pre_steps, args.warmup)
+        target_rows += [x, xp]
         print("[bench] %s" % json.dumps(x), file=sys.stderr, flush=True)
-        line["moe_gate_up_masked"] = dict(workload=x["workload"], valid_rows=x["S"], experts_active=x["E_active"],
-                                          **sub_object(x))
+        print("[bench] %s" % json.dumps(xp), file=sys.stderr, flush=True)
+        line["moe_gate_up_masked"] = dict(workload=x["workload"], weights="pre-shuffled", valid_rows=x["S"],
+                                          experts_active=x["E_active"], **sub_object(x),
+                                          plain_layout={"gemm_us": round(xp["gemm_us"], 2), "tile": xp["config"]})
         x = bench_silu_down(F, W, stream, pre_steps, args.warmup)
-        target_rows.append(x)
+        xs = bench_silu_down(F, W, stream, pre_steps, args.warmup, preshuffled=True)
+        target_rows += [x, xs]
         print("[bench] %s" % json.dumps(x), file=sys.stderr, flush=True)
-        o = dict(workload=x["workload"], valid_rows=x["S"], **sub_object(x))
+        print("[bench] %s" % json.dumps(xs), file=sys.stderr, flush=True)
+        o = dict(workload=x["workload"], weights="plain", valid_rows=x["S"], **sub_object(x),
+                 preshuffled_layout={"gemm_us": round(xs["gemm_us"], 2), "tile": xs["config"]})
         o["silu_us"] = round(x["silu_us"], 2)
         for q in ("p10", "median", "p90"):
             o["silu_us_" + q] = round(x["silu_us_" + q], 2)
@@ -849,15 +868,18 @@ def main():
         rows = [r, plain] + target_rows
         rows.append(bench_dense(F, stream, W.DENSE_SMALL, args.steps, args.warmup, host=W.dense_inputs(W.DENSE_SMALL)))
         rows[-1].pop("_out0", None)
-        for s in W.DENSE_PREFILL:
-            rows.append(bench_dense(F, stream, s, max(10, args.steps // 4), args.warmup, preshuffled=True,
-                                    host=W.dense_inputs(s), keep_out=False))
-            print("[bench] %s" % json.dumps(rows[-1]), file=sys.stderr, flush=True)
-        for pre in ((True,) if target_rows else (False, True)):
-            rows.append(bench_masked_gate_up(F, W, stream, max(10, args.steps // 4), args.warmup, preshuffled=pre))
-            print("[bench] %s" % json.dumps(rows[-1]), file=sys.stderr, flush=True)
-            rows.append(bench_silu_down(F, W, stream, max(10, args.steps // 4), args.warmup, preshuffled=pre))
-            print("[bench] %s" % json.dumps(rows[-1]), file=sys.stderr, flush=True)
+        if not target_rows:  # (--no-targets) every prefill and MoE row on both weight layouts
+            for s in W.DENSE_PREFILL:
+                for pre in (True, False):
+                    rows.append(bench_dense(F, stream, s, max(10, args.steps // 4), args.warmup, preshuffled=pre,
+                                            host=W.dense_inputs(s), keep_out=False))
+                    print("[bench] %s" % json.dumps(rows[-1]), file=sys.stderr, flush=True)
+            for pre in (True, False):
+                rows.append(bench_masked_gate_up(F, W, stream, max(10, args.steps // 4), args.warmup,
+                                                 preshuffled=pre))
+                print("[bench] %s" % json.dumps(rows[-1]), file=sys.stderr, flush=True)
+                rows.append(bench_silu_down(F, W, stream, max(10, args.steps // 4), args.warmup, preshuffled=pre))
+                print("[bench] %s" % json.dumps(rows[-1]), file=sys.stderr, flush=True)
         rows.append(bench_contiguous_gate_up(F, W, stream, max(10, args.steps // 4), args.warmup))
         print("[bench] %s" % json.dumps(rows[-1]), file=sys.stderr, flush=True)
         rows.append(bench_dispatch_quant(F, W, stream, args.steps, args.warmup))

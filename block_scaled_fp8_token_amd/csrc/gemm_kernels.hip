@@ -1200,7 +1200,13 @@ struct Ring2Shape {
 
 // NTB: the weight DMA carries the non-temporal cache policy (the weights of a masked
 // call are streamed once per column tile: 939 MB at the MoE gate_up shape).
-template <int BM, int BN, int WGM, int WGN, int S, bool FS = false, bool NTB = false>
+// SHUF: the weights are in the pre-shuffled layout, where K-block kb of 32-row group g
+// is 4 contiguous KiB at ((g KB + kb) 4 + q) 1 KiB, q = 0..3, each KiB holding 16 bytes
+// per lane in MFMA operand order.  Each DMA instruction then moves one such KiB into LDS
+// lane by lane, and a lane's operand for K-half h is the two 16-byte pieces q = 2h, 2h+1
+// at its own lane position (consecutive lanes, consecutive 16 bytes: conflict-free): the
+// same bytes as the plain layout's operand reads, so the results are identical.
+template <int BM, int BN, int WGM, int WGN, int S, bool FS = false, bool NTB = false, bool SHUF = false>
 __global__ __launch_bounds__(256) void ring2_kernel(const KArgs p) {
   using R = Ring2Shape<BM, BN, WGM, WGN, S, FS>;
   constexpr int WM = R::WM, WN = R::WN, SM = R::SM, SN = R::SN, IPW = R::IPW, IPA = R::IPA;
@@ -1268,7 +1274,10 @@ __global__ __launch_bounds__(256) void ring2_kernel(const KArgs p) {
       const bool isA = t < IPA;  // static after unrolling
       const int ri = isA ? wave * IPA + t : wave * R::IPB + (t - IPA);
       uint8_t* dst = base + (isA ? 0 : BM * 128) + ri * 1024;
-      const uint32_t off = ((ri & 1 ? lane_off1 : lane_off0) + (uint32_t)(ri * 8 * p.K) + koff) | oob;
+      // pre-shuffled weights: KiB ri of the B stage is piece q = ri & 3 of 32-row group ri >> 2
+      const uint32_t off =
+          (isA || !SHUF) ? ((ri & 1 ? lane_off1 : lane_off0) + (uint32_t)(ri * 8 * p.K) + koff) | oob
+                         : ((uint32_t)((((ri >> 2) * KB + kb) * 4 + (ri & 3)) * 1024) + (uint32_t)(lane * 16)) | oob;
       if (isA || !NTB)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(isA ? rA : rB, (__attribute__((address_space(3))) void*)dst, 16,
                                                  (int)off, 0, 0, 0);
@@ -1346,6 +1355,7 @@ __global__ __launch_bounds__(256) void ring2_kernel(const KArgs p) {
     return (uint32_t)(lr * 128 + (((4 * h + cc + j) ^ ((lr >> 1) & 7)) << 4));
   };
   const uint32_t rd00 = rdo(0, 0), rd01 = rdo(0, 1), rd10 = rdo(1, 0), rd11 = rdo(1, 1);
+  const uint32_t rds = (uint32_t)lane * 16u;  // SHUF: this lane's 16 bytes in each kilobyte
   const int sb_blk = (wn * WN) >> 7;
   uint16_t* __restrict__ C = p.c + e * p.sc_e;
 
@@ -1366,10 +1376,21 @@ __global__ __launch_bounds__(256) void ring2_kernel(const KArgs p) {
       if constexpr (IV > 0) {
 #pragma unroll
         for (int j = 0; j < SN; ++j) {
-          const uint8_t* q = base + (BM + wn * WN + 32 * j) * 128;
-          const v4i lo = *reinterpret_cast<const v4i*>(q + r0);
-          const v4i hi = *reinterpret_cast<const v4i*>(q + r1);
-          wf[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+          if constexpr (SHUF) {
+            // one offset per read, added to the stage's base once: the compiler marks
+            // an LDS access as disjoint from other stages only when its address is a
+            // short chain of offsets from the stage (else every operand read would
+            // wait for all DMA in flight)
+            const uint32_t o = (uint32_t)(BM * 128 + (((wn * WN) / 32 + j) * 4 + 2 * H) * 1024) + rds;
+            const v4i lo = *reinterpret_cast<const v4i*>(base + o);
+            const v4i hi = *reinterpret_cast<const v4i*>(base + (o + 1024u));
+            wf[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+          } else {
+            const uint8_t* q = base + (BM + wn * WN + 32 * j) * 128;
+            const v4i lo = *reinterpret_cast<const v4i*>(q + r0);
+            const v4i hi = *reinterpret_cast<const v4i*>(q + r1);
+            wf[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+          }
         }
       }
     };
@@ -2531,6 +2552,11 @@ const TileEntry kTiles[] = {
     {ring2_kernel<256, 256, 1, 4, 2, false, true>, 256, 256, kRing, 2, 256, ring2_wd_max<256, 256, 1, 4, 2>()},
     // contiguous grouped: the same at 128-row tiles (one aligned run each)
     {ring2_kernel<128, 256, 1, 4, 2, false, true>, 128, 256, kRing, 2, 256, ring2_wd_max<128, 256, 1, 4, 2>()},
+    // the full-row ring on pre-shuffled weights (dense 256x256 / 256x128 / 128x128, masked)
+    {ring2_kernel<256, 256, 2, 2, 2, false, false, true>, 256, 256, kRingShuf, 2, 256, ring2_wd_max<256, 256, 2, 2, 2>()},
+    {ring2_kernel<256, 128, 2, 2, 2, false, false, true>, 256, 128, kRingShuf, 2, 256, ring2_wd_max<256, 128, 2, 2, 2>()},
+    {ring2_kernel<128, 128, 1, 4, 4, false, false, true>, 128, 128, kRingShuf, 4, 256, ring2_wd_max<128, 128, 1, 4, 4>()},
+    {ring2_kernel<256, 256, 1, 4, 2, false, true, true>, 256, 256, kRingShuf, 2, 256, ring2_wd_max<256, 256, 1, 4, 2>()},
 };
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 // table entries the automatic choice uses
@@ -2565,6 +2591,10 @@ constexpr int kCfgShufRing128x256 = 40;
 constexpr int kCfgFloatShufDecode64x128 = 47;  // float scales, pre-shuffled weights, reduction kernel
 constexpr int kCfgRing128x128 = 65;          // ring 128x128, 1 x 4 wavefronts, four full K-block stages
 constexpr int kCfgShufRing128x128 = 50;      // the same (2 x 2) on pre-shuffled weights
+constexpr int kCfgShufRing2_256x256 = 71;    // full-row ring on pre-shuffled weights, 2 x 2 wavefronts
+constexpr int kCfgShufRing2_256x128 = 72;
+constexpr int kCfgShufRing2_128x128 = 73;    // 1 x 4 wavefronts, four stages
+constexpr int kCfgShufRing2Masked = 74;      // 1 x 4 wavefronts, non-temporal weight DMA
 static_assert(kCfgDecode64x128 < kNumTiles && kCfgFloatScaled128x256 < kNumTiles, "tile table");
 static_assert(kCfgRingFloat128x128 < kNumTiles && kCfgRing2Masked < kNumTiles && kCfgRing2Contiguous < kNumTiles,
               "tile table");
@@ -2573,6 +2603,8 @@ static_assert(kCfgRing128x128 < kNumTiles && kCfgShufRing128x128 < kNumTiles, "t
 static_assert(kCfgRing256x256 < kNumTiles && kCfgRing256x256Rows < kNumTiles && kCfgRing128x256 < kNumTiles &&
                   kCfgRing256x128 < kNumTiles, "tile table");
 static_assert(kCfgWsd64x128 < kNumTiles, "tile table");
+static_assert(kCfgShufRing2_256x256 < kNumTiles && kCfgShufRing2_256x128 < kNumTiles &&
+                  kCfgShufRing2_128x128 < kNumTiles && kCfgShufRing2Masked < kNumTiles, "tile table");
 
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -2672,35 +2704,34 @@ GemmConfig choose_gemm_config(const GemmProblem& p) {
     return cfg;
   }
   if (p.b_shuffled) {
-    // pre-shuffled weights.  Masked: the 256 x 256 ring tiles with the wavefronts side
-    // by side in N, as for the plain layout.  Dense M <= 64: the decode kernel, K split
-    // until about 224 workgroups, its partials summed by splitk_reduce_kernel (against
-    // the reduction by the last split of each tile, whose three dependent round trips
-    // run on one CU per tile, 0.9 us shorter per call and 1.2 us per graph-replayed
-    // quant + GEMM step, A/B on one GPU).
-    // Larger M: ring tiles, 256 x 256 once they fill the compute units, else 128 x 256.
-    // The decode kernel takes whatever the ring's scale tables cannot hold.
+    // pre-shuffled weights.  Masked: the 256 x 256 full-row ring with the wavefronts
+    // side by side in N and non-temporal weight DMA, as for the plain layout.  Dense
+    // M <= 64: the weight-streaming kernel (below).  Larger M: the full-row ring
+    // tiles chosen as for the plain layout (the layout only changes where a B stage's
+    // kilobytes come from); the K-half ring tiles when K is past the full-row ring's
+    // tables, the decode kernel past those.
     if (p.masked_m) {
+      if (gemm_config_by_index(kCfgShufRing2Masked, p, 1, &cfg)) return cfg;
       if (gemm_config_by_index(kCfgShufRing256x256Rows, p, 1, &cfg)) return cfg;
     } else if (p.M > 64) {
-      // at most one round of 128x128 tiles: the 128x128 ring (1024x4096x7168: 74.0 ->
-      // 46.9 us against 128x256 ring tiles on half the compute units)
-      if (cdiv(p.M, 128) * cdiv(p.N, 128) <= 256 && gemm_config_by_index(kCfgShufRing128x128, p, 1, &cfg))
-        return cfg;
       const int64_t tm256 = cdiv(p.M, 256), big_tiles = tm256 * cdiv(p.N, 256);
-      if (gemm_config_by_index(big_tiles >= 256 ? kCfgShufRing256x256 : kCfgShufRing128x256, p, 1, &cfg)) {
-        // as for the plain layout: a last round of at most half the compute units
-        // runs its columns as 128x128 ring tiles in a second launch when they make
-        // at most one round (a 32-row group of the layout is 32 K contiguous bytes,
-        // so the column offset of the tail is the plain one)
+      const int64_t mid_tiles = tm256 * cdiv(p.N, 128);
+      const bool one_round_128 = cdiv(p.M, 128) * cdiv(p.N, 128) <= 256;
+      if (big_tiles >= 256 && gemm_config_by_index(kCfgShufRing2_256x256, p, 1, &cfg)) {
+        // a last round of at most half the compute units: its columns in a second
+        // launch, as for the plain layout (a 32-row group of the layout is 32 K
+        // contiguous bytes, so the column offset of the tail is the plain one)
         const int64_t rem = big_tiles % 256;
-        if (big_tiles >= 256 && rem != 0 && rem <= 128 && p.E == 1) {
+        if (rem != 0 && rem <= 128 && p.E == 1) {
           const int64_t n_split = (big_tiles / 256) * 256 / tm256 * 256;
           GemmProblem tp = p;
           tp.N = p.N - n_split;
           GemmConfig tc;
-          if (n_split > 0 && n_split < p.N && cdiv(tp.M, 128) * cdiv(tp.N, 128) <= 256 &&
-              gemm_config_by_index(kCfgShufRing128x128, tp, 1, &tc)) {
+          const bool one_round = cdiv(tp.M, 128) * cdiv(tp.N, 128) <= 256;
+          const bool one_round_mid = cdiv(tp.M, 256) * cdiv(tp.N, 128) <= 256;
+          if (n_split > 0 && n_split < p.N &&
+              ((one_round && gemm_config_by_index(kCfgShufRing2_128x128, tp, 1, &tc)) ||
+               (one_round_mid && gemm_config_by_index(kCfgShufRing2_256x128, tp, 1, &tc)))) {
             cfg.n_split = n_split;
             cfg.tail_kernel = tc.kernel;
             cfg.tail_bm = tc.bm;
@@ -2710,6 +2741,15 @@ GemmConfig choose_gemm_config(const GemmProblem& p) {
         }
         return cfg;
       }
+      if (mid_tiles >= 256 && (mid_tiles % 256 == 0 || mid_tiles % 256 > 128) &&
+          gemm_config_by_index(kCfgShufRing2_256x128, p, 1, &cfg))
+        return cfg;
+      if (one_round_128 && gemm_config_by_index(kCfgShufRing2_128x128, p, 1, &cfg)) return cfg;
+      if (mid_tiles <= 256 && gemm_config_by_index(kCfgShufRing2_256x128, p, 1, &cfg)) return cfg;
+      // K past the full-row ring's tables: the K-half ring tiles
+      if (one_round_128 && gemm_config_by_index(kCfgShufRing128x128, p, 1, &cfg)) return cfg;
+      if (gemm_config_by_index(big_tiles >= 256 ? kCfgShufRing256x256 : kCfgShufRing128x256, p, 1, &cfg))
+        return cfg;
     }
     const int64_t tiles = cdiv(p.M, kTiles[kCfgShufDecode64x128].bm) * cdiv(p.N, kTiles[kCfgShufDecode64x128].bn);
     int splits = p.masked_m ? 1 : (int)(224 / (tiles > 0 ? tiles : 1));
