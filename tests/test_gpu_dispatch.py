@@ -106,7 +106,7 @@ def test_dispatch_empty_and_limits():
 
 def test_dispatch_then_masked_gate_up_chain():
     """Routed tokens -> quant into the expert layout -> masked gate_up GEMM with the
-    counts the dispatch produced on the device; sampled rows against the oracle chain."""
+    counts the dispatch produced on the device; every valid row against the oracle chain."""
     E, M_max, N, K = W.MOE_E, W.MOE_M_MAX, W.MOE_GATE_UP["N"], W.MOE_GATE_UP["K"]
     ids = W.topk_routing(T=256)
     x = W.normal_bf16((ids.shape[0], K), seed=3, tensor_id=W.T_X)
@@ -121,9 +121,8 @@ def test_dispatch_then_masked_gate_up_chain():
     c = to_host(c)
     q_ref, sf_ref, mm_ref, _ = O.quant_group_pack_to_experts(x, ids, E, M_max)
     assert np.array_equal(mm.cpu().numpy(), mm_ref)
-    rows = np.array([0, 1, 50, 127, 200, 255], np.int64)
-    ref = O.gemm_grouped_masked(q_ref, sf_ref, qb, sfb, mm_ref, rows=rows)
+    ref = O.gemm_grouped_masked(q_ref, sf_ref, qb, sfb, mm_ref)
     for e in range(E):
-        sel = np.array([r for r in rows if r < mm_ref[e]], np.int64)
-        if sel.size:
-            gemm_tolerance_check(c[e, sel], ref[e, sel], "chain expert %d" % e)
+        ce = int(min(mm_ref[e], M_max))
+        if ce:
+            gemm_tolerance_check(c[e, :ce], ref[e, :ce], "chain expert %d (every valid row)" % e)
