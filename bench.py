@@ -722,7 +722,8 @@ def main():
                          "then --steps eager steps of --counters-shape; no timing")
     ap.add_argument("--counters-shape", default="decode",
                     help="decode: M=64 N=7168 K=18432 with pre-shuffled weights (the headline step); "
-                         "decode_plain: the same with weights [N][K]; prefill: M=4096 N=4096 K=7168; "
+                         "decode_plain: the same with weights [N][K]; prefill: M=4096 N=4096 K=7168 "
+                         "(pre-shuffled weights, as for every prefill shape name); "
                          "masked: the MoE gate_up GEMM; scale_ablation: UE8M0 in the MFMA against "
                          "unscaled MFMA + VALU scale at 1024x4096x7168; or a prefill shape name such as "
                          "dense_prefill_2048x4096x7168")
@@ -748,9 +749,9 @@ def main():
         elif args.counters_shape == "scale_ablation":
             counters_scale_ablation_workload(F, W, args.steps)
         elif args.counters_shape == "prefill":
-            counters_workload(F, W.DENSE_PREFILL[2], args.steps)
+            counters_workload(F, W.DENSE_PREFILL[2], args.steps, preshuffled=True)
         elif args.counters_shape in named:
-            counters_workload(F, named[args.counters_shape], args.steps)
+            counters_workload(F, named[args.counters_shape], args.steps, preshuffled=True)
         elif args.counters_shape in ("decode", "decode_plain"):
             counters_workload(F, shape, args.steps, preshuffled=args.counters_shape == "decode")
         else:
@@ -909,7 +910,8 @@ def main():
 def counters_workload(F, shape, steps, preshuffled=False):
     """Kernels for the counter passes: three copies of 256 MiB (a plain copy kernel of
     known size, to calibrate FETCH_SIZE / WRITE_SIZE), then eager dense steps on the
-    timed tensors (with pre-shuffled weights for the headline decode step)."""
+    timed tensors (pre-shuffled weights, as the headline decode step and the prefill
+    sub-objects time them; decode_plain: the plain layout)."""
     x = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
     y = torch.empty_like(x)
     for _ in range(3):
@@ -965,9 +967,10 @@ def counters_scale_ablation_workload(F, W, steps):
 
 
 def counters_masked_workload(F, W, steps):
-    """Kernels for counter passes on the masked gate_up GEMM: the calibration copies,
-    then --steps calls with the Zipf counts, --steps with every count halved and
-    --steps with all counts zero (HBM bytes should follow the valid rows)."""
+    """Kernels for counter passes on the masked gate_up GEMM on pre-shuffled weights (as
+    the bench line times it): the calibration copies, then --steps calls with the Zipf
+    counts, --steps with every count halved and --steps with all counts zero (HBM bytes
+    should follow the valid rows)."""
     x = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
     y = torch.empty_like(x)
     for _ in range(3):
@@ -983,15 +986,16 @@ def counters_masked_workload(F, W, steps):
     sfa = sfa_flat.view(Wd, E, M_max).permute(1, 0, 2).contiguous()
     del xa
     (qb, sfb), = quantized_weights(F, 1, N, K, 21, experts=E)
+    qb = F.fp8_weight_preshuffle(qb)
     c = torch.empty((E, M_max, N), dtype=torch.bfloat16, device="cuda")
     sets = [("zipf", zipf), ("halved", (zipf + 1) // 2), ("zero", torch.zeros_like(zipf))]
     for name, counts in sets:
         for i in range(steps):
-            F.fp8_block_gemm_grouped_masked(a, sfa, qb, sfb, counts, c=c)
+            F.fp8_block_gemm_grouped_masked(a, sfa, qb, sfb, counts, c=c, preshuffled=True)
         torch.cuda.synchronize()
     print(json.dumps({"copy_bytes_each_way": 256 << 20, "steps_per_set": steps,
                       "sets": {n: {"S": int(cn.sum()), "E_active": int((cn > 0).sum())} for n, cn in sets},
-                      "config": F.gemm_config(True, M_max, N, K)}))
+                      "config": F.gemm_config(F.LAYOUT_MASKED_PRESHUFFLED, M_max, N, K)}))
 
 
 def _kernel_hash():
