@@ -999,13 +999,17 @@ def counters_masked_workload(F, W, steps):
 
 
 def _kernel_hash():
-    """Hash of the sources the decode GEMM kernel is built from (the GEMM kernels and the
-    two headers they include): stored traffic counters stay valid until these change."""
+    """Hash of the code the decode GEMM kernel is built from (the GEMM kernels and the two
+    headers they include, without their // comments and blank lines): stored traffic
+    counters stay valid until the code changes."""
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "block_scaled_fp8_token_amd", "csrc")
     for name in ("fp8bs_device.hpp", "fp8bs_launch.hpp", "gemm_kernels.hip"):
-        h.update(open(os.path.join(csrc, name), "rb").read())
+        for line in open(os.path.join(csrc, name), encoding="utf-8"):
+            code = line.split("//", 1)[0].strip()
+            if code:
+                h.update(code.encode() + b"\n")
     return h.hexdigest()[:16]
 
 

@@ -21,12 +21,15 @@
 //     fp32 partials inside the kernel (last arriver, in part order: deterministic).
 //   * decode_kernel: dense M <= 64 on the plain [N][K] layout (weights through an LDS
 //     ring) and the float-scale decode; partials summed by splitk_reduce_kernel.
-//   * ring2_kernel: prefill and masked.  LDS-DMA rings of whole 128-byte K-block rows,
-//     one barrier per K-block, v_mfma_scale_f32_32x32x64_f8f6f4 with the packed UE8M0
-//     bytes as scale operands (the scale-then-accumulate of each K-block happens in the
-//     matrix core), bf16 epilogue staged through LDS, XCD-aware tile order.  Its
-//     float-scale form runs the MFMAs unscaled and adds P * (sa * sb) on the VALU.
-//   * scaled_ring_kernel (K-half stages; the masked and pre-shuffled prefill entries),
+//   * ring2_kernel: prefill, masked and contiguous grouped, on either weight layout.
+//     LDS-DMA rings of whole 128-byte K-block rows (or, on pre-shuffled weights, one
+//     contiguous kilobyte per weight DMA instruction), one barrier per K-block,
+//     v_mfma_scale_f32_32x32x64_f8f6f4 with the packed UE8M0 bytes as scale operands
+//     (the scale-then-accumulate of each K-block happens in the matrix core), bf16
+//     epilogue staged through LDS, XCD-aware tile order; the grouped forms stream their
+//     weights with non-temporal DMA.  Its float-scale form runs the MFMAs unscaled and
+//     adds P * (sa * sb) on the VALU.
+//   * scaled_ring_kernel (K-half stages; where K is past ring2_kernel's scale tables),
 //     scaled_tile_kernel (two-stage tiles), stream_kernel and gemm_kernel (the
 //     first design: LDS via registers, 16x16x128 MFMA on zero then a VALU scale FMA):
 //     fallbacks for shapes and K ranges the others do not take.
