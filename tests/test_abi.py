@@ -214,8 +214,13 @@ def test_config_of_table_entries():
     sh = [k for k in range(n) if F.gemm_config_of(k, F.LAYOUT_DENSE_PRESHUFFLED, 72, 192, 384) is not None
           or F.gemm_config_of(k, F.LAYOUT_DENSE_PRESHUFFLED, 64, 192, 384) is not None]
     fsh = [k for k in range(n) if F.gemm_config_of(k, F.LAYOUT_DENSE_FLOAT_PRESHUFFLED, 72, 192, 384) is not None]
-    assert fl and sh and fsh and not set(fl) & set(sh) and not set(fsh) & set(fl + sh)
-    assert all(F.gemm_config_of(k, True, 72, 192, 384) is not None for k in range(n) if k not in fl + sh + fsh)
+    # masked weight streaming: masked calls on pre-shuffled weights only
+    msh = [k for k in range(n) if F.gemm_config_of(k, F.LAYOUT_MASKED_PRESHUFFLED, 72, 192, 384) is not None
+           and k not in sh and F.gemm_config_of(k, True, 72, 192, 384) is None]
+    assert fl and sh and fsh and msh and not set(fl) & set(sh) and not set(fsh) & set(fl + sh)
+    assert not set(msh) & set(fl + sh + fsh)
+    assert all(F.gemm_config_of(k, False, 72, 192, 384) is None for k in msh)
+    assert all(F.gemm_config_of(k, True, 72, 192, 384) is not None for k in range(n) if k not in fl + sh + fsh + msh)
     assert all(F.gemm_config_of(k, True, 72, 192, 384) is None and F.gemm_config_of(k, False, 72, 192, 384) is None
                for k in fsh)
     # the pre-shuffled entries read only that layout (dense calls)

@@ -79,6 +79,18 @@ def test_gemm_integer_identity_exact(kernel, splits):
                                             c=poisoned_bf16(M, N), kernel=kernel, splits=splits)
         sync()
         c = to_host(c)
+    elif (F.gemm_config_of(kernel, F.LAYOUT_MASKED_PRESHUFFLED, M, N, K) is not None
+          and F.gemm_config_of(kernel, F.LAYOUT_DENSE, M, N, K) is None):
+        # a masked-only entry on pre-shuffled weights: one expert whose count is M
+        if splits != 1:
+            pytest.skip("masked entries never split K")
+        sfa3 = np.full((1, 1, M), 127 | (127 << 8), np.uint32)
+        db = F.fp8_weight_preshuffle(to_dev(_int_codes(bi)[None]))
+        c = F.fp8_block_gemm_grouped_masked(to_dev(_int_codes(ai)[None]), to_dev(sfa3), db, to_dev(sfb[None]),
+                                            to_dev(np.array([M], np.int32)), c=poisoned_bf16(1, M, N),
+                                            kernel=kernel, preshuffled=True)
+        sync()
+        c = to_host(c)[0]
     else:
         sfa = np.full((1, 40), 127 | (127 << 8), np.uint32)
         c = _run(_int_codes(ai), sfa, _int_codes(bi), sfb, kernel=kernel, splits=splits)

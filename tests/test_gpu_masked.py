@@ -64,6 +64,9 @@ def test_masked_small_all_kernels_edge_counts():
             continue  # dense entry on pre-shuffled weights (the weight-streaming ones take M <= 64 only)
         if F.gemm_config_of(kernel, F.LAYOUT_DENSE_FLOAT_PRESHUFFLED, M_max, N, K) is not None:
             continue  # float scales on pre-shuffled weights
+        if (F.gemm_config_of(kernel, F.LAYOUT_MASKED_PRESHUFFLED, M_max, N, K) is not None
+                and F.gemm_config_of(kernel, F.LAYOUT_MASKED, M_max, N, K) is None):
+            continue  # masked entry on pre-shuffled weights only (test_gpu_preshuffled.py)
         assert F.gemm_config_of(kernel, True, M_max, N, K) is not None, kernel
         c = _run_masked(a, sfa, b, sfb, counts, kernel=kernel)
         _check(c, a, sfa, b, sfb, counts, what="kernel %d" % kernel)

@@ -230,3 +230,31 @@ def test_preshuffled_prefill_column_tail_matches_plain():
     ref = O.gemm_nt(qa, sfa, qb, sfb, rows=rows)
     gemm_tolerance_check(c_shuf[rows], ref, "pre-shuffled, column tail")
     assert np.array_equal(c_shuf, c_plain)
+
+
+def test_preshuffled_masked_weight_streaming_all_row_groups():
+    """The masked weight-streaming entry (every valid row of an expert in one workgroup)
+    with M_max = 256 and counts that end inside and on every kind of 16- and 32-row
+    boundary, up to all eight 32-row groups and past M_max: every valid row within the
+    oracle's tolerance, rows past the count untouched, and bit-equal to the automatic
+    plain-layout call."""
+    counts = np.array([0, 1, 15, 16, 31, 32, 33, 64, 100, 200, 255, 256, 300], np.int32)
+    E, M_max, N, K = len(counts), 256, 384, 1152
+    a, sfa, qb, sfb = _moe_operands(E, M_max, N, K, seed=6)
+    ref = O.gemm_grouped_masked(a, sfa, qb, sfb, counts)
+    db, dbs = to_dev(qb), F.fp8_weight_preshuffle(to_dev(qb))
+    streaming = [k for k in range(F.gemm_config_count())
+                 if (F.gemm_config_of(k, F.LAYOUT_MASKED_PRESHUFFLED, M_max, N, K) or {}).get("bn") == 128
+                 and F.gemm_config_of(k, F.LAYOUT_MASKED, M_max, N, K) is None
+                 and F.gemm_config_of(k, F.LAYOUT_DENSE_PRESHUFFLED, 64, N, K) is None]
+    assert streaming
+    plain = _masked(a, sfa, db, sfb, counts)
+    for kernel in streaming:
+        print("masked weight streaming kernel %d" % kernel, flush=True)
+        c = _masked(a, sfa, dbs, sfb, counts, kernel=kernel, preshuffled=True)
+        for e in range(E):
+            ce = int(min(max(counts[e], 0), M_max))
+            if ce:
+                gemm_tolerance_check(c[e, :ce], ref[e, :ce], "kernel %d expert %d" % (kernel, e))
+            assert np.all(c[e, ce:] == CANARY), "kernel %d expert %d: padded rows written" % (kernel, e)
+        assert np.array_equal(c, plain), "kernel %d differs from the plain-layout call" % kernel
