@@ -1181,7 +1181,12 @@ constexpr int ring_wd_max() { return RingShape<BM, BN, WGM, WGN>::WD_MAX; }
 //           wavefront's DMA of j + 1 has landed and nobody reads j's stage any
 //           more), DMA of j + S into j's stage, then the MFMAs of j's second half
 //           interleaved with the operand reads of j + 1's first half and the DMA.
-// One barrier per K-block; a DMA has S - 1 K-blocks to land.
+// One barrier per K-block; a DMA has S - 1 K-blocks to land.  At one tile per compute
+// unit the two-stage ring waits on that DMA: its K-block time follows the latency of
+// the L2 misses among a stage's lines, not the MFMA time, and a third stage (2048 x 4096
+// x 7168 on 256 x 128 tiles: 64.8 -> 54.4 us) gives each DMA two K-blocks.  S = 3 turns
+// the ring in trips of twelve K-blocks (three turns, three scale words) so that the stage
+// and the scale byte of every K-block stay static.
 // FS: the float-scale format (fp32 activation scales per row and K-block, fp32 weight
 // block scales).  The MFMA then runs unscaled: the two MFMAs of a K-block (its two
 // K-halves) add into a block partial P, and P * (sa * sb) is added to the
@@ -1215,13 +1220,15 @@ __global__ __launch_bounds__(256) void ring2_kernel(const KArgs p) {
   constexpr int WM = R::WM, WN = R::WN, SM = R::SM, SN = R::SN, IPW = R::IPW, IPA = R::IPA;
   constexpr int WD_MAX = R::WD_MAX, NBT = R::NBT;
   static_assert(WGM * WGN == 4 && WM % 32 == 0 && WN % 32 == 0 && BN % 128 == 0 && BM % 32 == 0, "tile shape");
-  static_assert(S == 2 || S == 4, "stages (a divisor of the four K-blocks of a scale word)");
+  static_assert(S >= 2 && S <= 4, "stages");
   static_assert(WD_MAX >= 1, "scale tables do not fit");
-  static_assert(!FS || (WGM == 1 && BM == 128 && BN == 128), "float scales: 128 x 128 tiles, 1 x 4 wavefronts");
+  static_assert(!FS || (WGM == 1 && BM == 128 && BN == 128 && S != 3), "float scales: 128 x 128 tiles, 1 x 4 wavefronts");
+  // K-blocks per unrolled trip: whole scale words (four K-blocks) and whole turns of the ring
+  constexpr int UNR = S == 3 ? 12 : 4;
   __shared__ __attribute__((aligned(1024))) uint8_t sl0[R::SLOT];
   __shared__ __attribute__((aligned(1024))) uint8_t sl1[R::SLOT];
   __shared__ __attribute__((aligned(1024))) uint8_t sl2[S > 2 ? R::SLOT : 16];
-  __shared__ __attribute__((aligned(1024))) uint8_t sl3[S > 2 ? R::SLOT : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t sl3[S > 3 ? R::SLOT : 16];
   __shared__ __attribute__((aligned(16))) uint32_t sa_tab[WD_MAX * BM];   // [w][row]
   __shared__ __attribute__((aligned(16))) uint32_t sb_tab[NBT * WD_MAX];  // [block][w], byte kb % 4
 
@@ -1318,10 +1325,8 @@ __global__ __launch_bounds__(256) void ring2_kernel(const KArgs p) {
   }
   issue(0, IntC<0>{});
   issue(1, IntC<1>{});
-  if constexpr (S > 2) {
-    issue(2, IntC<2>{});
-    issue(3, IntC<3>{});
-  }
+  if constexpr (S > 2) issue(2, IntC<2>{});
+  if constexpr (S > 3) issue(3, IntC<3>{});
 #pragma unroll
   for (int t = 0; t < SA_IT; ++t) {
     const int idx = t * 256 + tid;
@@ -1454,25 +1459,25 @@ __global__ __launch_bounds__(256) void ring2_kernel(const KArgs p) {
       }
     };
 
-    // K-block kb = kb4 + U (kb4 a multiple of 4): scale byte U, stage U % S
-    auto kblock = [&](int kb4, auto u_tag) {
+    // K-block kb = kbu + U (kbu a multiple of UNR): scale byte U % 4, stage U % S
+    auto kblock = [&](int kbu, auto u_tag) {
       constexpr int U = decltype(u_tag)::value;
-      constexpr int ST = U % S, STN = (U + 1) % S;
-      const int kb = kb4 + U;
+      constexpr int ST = U % S, STN = (U + 1) % S, OPS = U % 4;
+      const int kb = kbu + U;
       // half 0: MFMAs of the first K-half, reads of the second
       __builtin_amdgcn_sched_barrier(0);
-      if constexpr (U == 0 && !FS) {
+      if constexpr (OPS == 0 && !FS) {
 #pragma unroll
         for (int i = 0; i < SM; ++i) sa[i] = sa_n[i];
         sb = sb_n;
       }
       read_frags(IntC<ST>{}, IntC<1>{}, xn, wn_);
       if constexpr (FS) mfmas_fs(xc, wc, IntC<0>{});
-      else mfmas(xc, wc, IntC<U>{});
+      else mfmas(xc, wc, IntC<OPS>{});
       mfma_read_dma_pattern<IV * SN, 2 * (IV > 0 ? IV + SN : 0), 0>();
-      if constexpr (U == 2 && !FS) {
+      if constexpr (OPS == 2 && !FS) {
         // scale words of the next group (clamped to the table; unused past the end)
-        const int wnx = (kb4 >> 2) + 1 < WD_MAX ? (kb4 >> 2) + 1 : WD_MAX - 1;
+        const int wnx = (kb >> 2) + 1 < WD_MAX ? (kb >> 2) + 1 : WD_MAX - 1;
 #pragma unroll
         for (int i = 0; i < SM; ++i) sa_n[i] = i < IV ? sa_tab[wnx * BM + wm * WM + 32 * i + lr] : 0u;
         sb_n = sb_tab[sb_blk * WD_MAX + wnx];
@@ -1485,16 +1490,30 @@ __global__ __launch_bounds__(256) void ring2_kernel(const KArgs p) {
       issue(kb + S, IntC<ST>{});
       read_frags(IntC<STN>{}, IntC<0>{}, xc, wc);
       if constexpr (FS) mfmas_fs(xn, wn_, IntC<1>{});
-      else mfmas(xn, wn_, IntC<U>{});
+      else mfmas(xn, wn_, IntC<OPS>{});
       mfma_read_dma_pattern<IV * SN, 2 * (IV > 0 ? IV + SN : 0), IPW>();
       if constexpr (FS) scale_add(kb < WD_MAX ? kb : WD_MAX - 1);  // (K-blocks past the end: zero partials)
     };
 
-    for (int kb4 = 0; kb4 < KB4; kb4 += 4) {
-      kblock(kb4, IntC<0>{});
-      kblock(kb4, IntC<1>{});
-      kblock(kb4, IntC<2>{});
-      kblock(kb4, IntC<3>{});
+    int kbu = 0;
+    for (; kbu + UNR <= KB4; kbu += UNR) {
+      kblock(kbu, IntC<0>{});
+      kblock(kbu, IntC<1>{});
+      kblock(kbu, IntC<2>{});
+      kblock(kbu, IntC<3>{});
+      if constexpr (UNR == 12) {
+        kblock(kbu, IntC<4>{}); kblock(kbu, IntC<5>{}); kblock(kbu, IntC<6>{}); kblock(kbu, IntC<7>{});
+        kblock(kbu, IntC<8>{}); kblock(kbu, IntC<9>{}); kblock(kbu, IntC<10>{}); kblock(kbu, IntC<11>{});
+      }
+    }
+    if constexpr (UNR == 12) {
+      // the last 4 or 8 K-blocks continue the ring where the trips left it
+      if (kbu < KB4) {
+        kblock(kbu, IntC<0>{}); kblock(kbu, IntC<1>{}); kblock(kbu, IntC<2>{}); kblock(kbu, IntC<3>{});
+      }
+      if (kbu + 4 < KB4) {
+        kblock(kbu, IntC<4>{}); kblock(kbu, IntC<5>{}); kblock(kbu, IntC<6>{}); kblock(kbu, IntC<7>{});
+      }
     }
     // the DMAs issued past the end must land, and every wavefront must be done with
     // the stages, before they are reused below
@@ -2813,6 +2832,11 @@ const TileEntry kTiles[] = {
     // masked, pre-shuffled weights: weight streaming, every valid row of an expert per
     // workgroup (M_max <= 256), the whole K (K <= 8192)
     {mwsd_kernel<8>, 256, 128, kMwsd, 0, 256, MwsdShape<8>::WMAX},
+    // three-stage 256x128 rings (DMA two K-blocks ahead), plain and pre-shuffled weights
+    {ring2_kernel<256, 128, 2, 2, 3>, 256, 128, kRing, 3, 256, ring2_wd_max<256, 128, 2, 2, 3>()},
+    {ring2_kernel<256, 128, 2, 2, 3, false, false, true>, 256, 128, kRingShuf, 3, 256, ring2_wd_max<256, 128, 2, 2, 3>()},
+    // contiguous grouped: the 128x256 ring with three stages
+    {ring2_kernel<128, 256, 1, 4, 3, false, true>, 128, 256, kRing, 3, 256, ring2_wd_max<128, 256, 1, 4, 3>()},
 };
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 // table entries the automatic choice uses
@@ -2852,6 +2876,10 @@ constexpr int kCfgShufRing2_256x128 = 72;
 constexpr int kCfgShufRing2_128x128 = 73;    // 1 x 4 wavefronts, four stages
 constexpr int kCfgShufRing2Masked = 74;      // 1 x 4 wavefronts, non-temporal weight DMA
 constexpr int kCfgMwsd = 75;                 // masked weight streaming, all rows of an expert per workgroup
+// three-stage rings (DMA two K-blocks ahead; their scale tables hold K <= 7680 / 15872)
+constexpr int kCfgRing256x128S3 = 76;        // 2 x 2 wavefronts, plain weights
+constexpr int kCfgShufRing2_256x128S3 = 77;  // the same on pre-shuffled weights
+constexpr int kCfgRing2ContiguousS3 = 78;    // 128 x 256, 1 x 4 wavefronts, non-temporal weight DMA
 static_assert(kCfgDecode64x128 < kNumTiles && kCfgFloatScaled128x256 < kNumTiles, "tile table");
 static_assert(kCfgRingFloat128x128 < kNumTiles && kCfgRing2Masked < kNumTiles && kCfgRing2Contiguous < kNumTiles,
               "tile table");
@@ -2862,6 +2890,8 @@ static_assert(kCfgRing256x256 < kNumTiles && kCfgRing256x256Rows < kNumTiles && 
 static_assert(kCfgWsd64x128 < kNumTiles, "tile table");
 static_assert(kCfgShufRing2_256x256 < kNumTiles && kCfgShufRing2_256x128 < kNumTiles &&
                   kCfgShufRing2_128x128 < kNumTiles && kCfgShufRing2Masked < kNumTiles && kCfgMwsd < kNumTiles,
+              "tile table");
+static_assert(kCfgRing256x128S3 < kNumTiles && kCfgShufRing2_256x128S3 < kNumTiles && kCfgRing2ContiguousS3 < kNumTiles,
               "tile table");
 
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -2967,7 +2997,9 @@ GemmConfig choose_gemm_config(const GemmProblem& p) {
     return cfg;
   }
   if (p.b_shuffled) {
-    // pre-shuffled weights.  Masked: weight streaming with every valid row of an expert
+    // pre-shuffled weights (256 x 128 ring tiles with three stages where their tables
+    // hold K, as for the plain layout: 2048x4096x7168 63.2 -> 54.9 us).  Masked: weight
+    // streaming with every valid row of an expert
     // in one workgroup when M_max <= 256 and K <= 8192 (MoE down 124.5 -> 113.8 us, gate_up
     // 192.7 -> 193.4 us against the full-row ring), else the 256 x 256 full-row ring with
     // the wavefronts side by side in N and non-temporal weight DMA.  Dense
@@ -2997,7 +3029,8 @@ GemmConfig choose_gemm_config(const GemmProblem& p) {
           const bool one_round_mid = cdiv(tp.M, 256) * cdiv(tp.N, 128) <= 256;
           if (n_split > 0 && n_split < p.N &&
               ((one_round && gemm_config_by_index(kCfgShufRing2_128x128, tp, 1, &tc)) ||
-               (one_round_mid && gemm_config_by_index(kCfgShufRing2_256x128, tp, 1, &tc)))) {
+               (one_round_mid && (gemm_config_by_index(kCfgShufRing2_256x128S3, tp, 1, &tc) ||
+                                  gemm_config_by_index(kCfgShufRing2_256x128, tp, 1, &tc))))) {
             cfg.n_split = n_split;
             cfg.tail_kernel = tc.kernel;
             cfg.tail_bm = tc.bm;
@@ -3008,10 +3041,13 @@ GemmConfig choose_gemm_config(const GemmProblem& p) {
         return cfg;
       }
       if (mid_tiles >= 256 && (mid_tiles % 256 == 0 || mid_tiles % 256 > 128) &&
-          gemm_config_by_index(kCfgShufRing2_256x128, p, 1, &cfg))
+          (gemm_config_by_index(kCfgShufRing2_256x128S3, p, 1, &cfg) ||
+           gemm_config_by_index(kCfgShufRing2_256x128, p, 1, &cfg)))
         return cfg;
       if (one_round_128 && gemm_config_by_index(kCfgShufRing2_128x128, p, 1, &cfg)) return cfg;
-      if (mid_tiles <= 256 && gemm_config_by_index(kCfgShufRing2_256x128, p, 1, &cfg)) return cfg;
+      if (mid_tiles <= 256 && (gemm_config_by_index(kCfgShufRing2_256x128S3, p, 1, &cfg) ||
+                               gemm_config_by_index(kCfgShufRing2_256x128, p, 1, &cfg)))
+        return cfg;
       // K past the full-row ring's tables: the K-half ring tiles
       if (one_round_128 && gemm_config_by_index(kCfgShufRing128x128, p, 1, &cfg)) return cfg;
       if (gemm_config_by_index(big_tiles >= 256 ? kCfgShufRing256x256 : kCfgShufRing128x256, p, 1, &cfg))
@@ -3059,9 +3095,11 @@ GemmConfig choose_gemm_config(const GemmProblem& p) {
   }
   if (p.m_indices) {
     // contiguous grouped layout: 128-row tiles (one aligned run each); the full-row
-    // 128 x 256 ring with non-temporal weight DMA (gate_up workload: 273 -> 247 us
-    // against the K-half 128 x 256 ring), the K-half ring when K is past its tables,
-    // then the 128 x 128 scaled tiles
+    // 128 x 256 ring with non-temporal weight DMA, three stages when its tables hold K
+    // (gate_up workload: 273 -> 247 us against the K-half 128 x 256 ring, 247 -> 215.5 us
+    // with the third stage), the K-half ring when K is past its tables, then the
+    // 128 x 128 scaled tiles
+    if (gemm_config_by_index(kCfgRing2ContiguousS3, p, 1, &cfg)) return cfg;
     if (gemm_config_by_index(kCfgRing2Contiguous, p, 1, &cfg)) return cfg;
     if (gemm_config_by_index(kCfgRing128x256, p, 1, &cfg)) return cfg;
     if (gemm_config_by_index(kCfgScaled128x128, p, 1, &cfg)) return cfg;
@@ -3127,7 +3165,8 @@ GemmConfig choose_gemm_config(const GemmProblem& p) {
       const bool one_round_mid = cdiv(tp.M, 256) * cdiv(tp.N, 128) <= 256;
       if (n_split > 0 && n_split < p.N &&
           ((one_round && gemm_config_by_index(kCfgRing128x128, tp, 1, &tc)) ||
-           (one_round_mid && gemm_config_by_index(kCfgRing256x128, tp, 1, &tc)) ||
+           (one_round_mid && (gemm_config_by_index(kCfgRing256x128S3, tp, 1, &tc) ||
+                              gemm_config_by_index(kCfgRing256x128, tp, 1, &tc))) ||
            gemm_config_by_index(kCfgScaled128x128, tp, 1, &tc))) {
         cfg.n_split = n_split;
         cfg.tail_kernel = tc.kernel;
@@ -3141,10 +3180,12 @@ GemmConfig choose_gemm_config(const GemmProblem& p) {
   if (big_tiles >= 256 && gemm_config_by_index(kCfgScaled256x256, p, 1, &cfg)) return cfg;
   // 256x128 ring tiles when they fill whole rounds of the compute units, or leave a
   // last round more than half full (2048x4096x7168: 67.5 us against 70.5 us for the
-  // 128x128 tiles below)
+  // 128x128 tiles below), with three stages when the tables hold K: at one tile per
+  // compute unit the ring waits on its DMA, and the third stage issues it two K-blocks
+  // ahead instead of one (2048x4096x7168: 64.8 -> 54.4 us)
   const int64_t mid_tiles = tm256 * cdiv(p.N, 128);
   if (mid_tiles >= 256 && (mid_tiles % 256 == 0 || mid_tiles % 256 > 128) &&
-      gemm_config_by_index(kCfgRing256x128, p, 1, &cfg))
+      (gemm_config_by_index(kCfgRing256x128S3, p, 1, &cfg) || gemm_config_by_index(kCfgRing256x128, p, 1, &cfg)))
     return cfg;
   // at most one round of 128x128 tiles: the 128x128 ring, four K-blocks in flight
   // (1024x4096x7168: 63.2 -> 45.0 us against the two-stage tiles); more: the
@@ -3154,7 +3195,9 @@ GemmConfig choose_gemm_config(const GemmProblem& p) {
   // more than one round of 128x128 tiles but at most one of 256x128: the 256x128 ring,
   // one tile per compute unit (against the two-stage 128x128 tiles: 1024x7168x7168
   // 73.8 -> 66.4 us, 1536x4096x7168 64.9 -> 61.2 us, 768x8192x7168 68.2 -> 64.3 us)
-  if (mid_tiles <= 256 && gemm_config_by_index(kCfgRing256x128, p, 1, &cfg)) return cfg;
+  if (mid_tiles <= 256 &&
+      (gemm_config_by_index(kCfgRing256x128S3, p, 1, &cfg) || gemm_config_by_index(kCfgRing256x128, p, 1, &cfg)))
+    return cfg;
   if (gemm_config_by_index(kCfgScaled128x128, p, 1, &cfg)) return cfg;
   const int idx = 1;
   const int64_t tiles = cdiv(p.M, kTiles[idx].bm) * cdiv(p.N, kTiles[idx].bn);
