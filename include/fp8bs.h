@@ -205,7 +205,7 @@ int fp8_weight_preshuffle(const void* w, int64_t rows, int64_t K, void* out, voi
  * of fp8_block_gemm_nt.  M <= 64 runs the weight-streaming kernel, whose loads this
  * layout makes contiguous; larger M the ring tiles of fp8_block_gemm_nt, each weight
  * DMA instruction then moving one contiguous kilobyte (bit-identical results; at
- * prefill sizes 3-6% shorter than fp8_block_gemm_nt on the plain layout).
+ * prefill sizes 1-6% shorter than fp8_block_gemm_nt on the plain layout).
  */
 int fp8_block_gemm_nt_preshuffled(const void* a, const uint32_t* sfa, int64_t ld_sfa, const void* b,
                                   const float* sfb, void* c, int64_t ldc, int64_t M, int64_t N,
