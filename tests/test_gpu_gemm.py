@@ -99,7 +99,10 @@ def test_gemm_integer_identity_exact(kernel, splits):
     assert np.array_equal(got, want)
 
 
-SMALL = [(1, 64, 128), (17, 192, 384), (64, 512, 1024), (100, 640, 640), (130, 256, 512), (257, 384, 1152)]
+# K from one K-block up; the three-stage ring turns in trips of twelve K-blocks, so K = 1152
+# is one whole trip, 2048 a trip and a four-block tail, 2560 a trip and an eight-block tail
+SMALL = [(1, 64, 128), (17, 192, 384), (64, 512, 1024), (100, 640, 640), (130, 256, 512), (257, 384, 1152),
+         (130, 256, 2048)]
 
 
 @pytest.mark.parametrize("M,N,K", SMALL)

@@ -43,7 +43,10 @@ def test_preshuffle_experts_flattened():
         assert np.array_equal(out[e], O.weight_preshuffle(w[e]))
 
 
-SMALL = [(1, 64, 128), (17, 192, 384), (64, 512, 1024), (100, 640, 640), (130, 256, 512), (64, 128, 2560)]
+# K from one K-block up; the three-stage ring turns in trips of twelve K-blocks, so K = 2048
+# is a trip and a four-block tail, 2560 a trip and an eight-block tail
+SMALL = [(1, 64, 128), (17, 192, 384), (64, 512, 1024), (100, 640, 640), (130, 256, 512), (64, 128, 2560),
+         (130, 256, 2048)]
 
 
 @pytest.mark.parametrize("M,N,K", SMALL)
