@@ -1214,7 +1214,8 @@ struct Ring2Shape {
 // lane by lane, and a lane's operand for K-half h is the two 16-byte pieces q = 2h, 2h+1
 // at its own lane position (consecutive lanes, consecutive 16 bytes: conflict-free): the
 // same bytes as the plain layout's operand reads, so the results are identical.
-template <int BM, int BN, int WGM, int WGN, int S, bool FS = false, bool NTB = false, bool SHUF = false>
+template <int BM, int BN, int WGM, int WGN, int S, bool FS = false, bool NTB = false, bool SHUF = false,
+          bool NTC = false>
 __global__ __launch_bounds__(256) void ring2_kernel(const KArgs p) {
   using R = Ring2Shape<BM, BN, WGM, WGN, S, FS>;
   constexpr int WM = R::WM, WN = R::WN, SM = R::SM, SN = R::SN, IPW = R::IPW, IPA = R::IPA;
@@ -1548,7 +1549,12 @@ __global__ __launch_bounds__(256) void ring2_kernel(const KArgs p) {
       const int row = t * RPI + lane / CPR;
       const v4i v = *reinterpret_cast<const v4i*>(stg + row * RB + ((c ^ (row % CPR)) << 4));
       const int64_t m = m0 + wm * WM + row;
-      if (m < m_limit && n < p.N) *reinterpret_cast<v4i*>(C + m * p.ldc + n) = v;
+      if (m < m_limit && n < p.N) {
+        // NTC: streaming stores (C is not read back here; with one tile per compute unit the
+        // whole of C is stored at the end of the call: 2048x4096x7168 52.6 -> 51.3 us)
+        if constexpr (NTC) __builtin_nontemporal_store(v, reinterpret_cast<v4i*>(C + m * p.ldc + n));
+        else *reinterpret_cast<v4i*>(C + m * p.ldc + n) = v;
+      }
     }
   };
 
@@ -2832,11 +2838,15 @@ const TileEntry kTiles[] = {
     // masked, pre-shuffled weights: weight streaming, every valid row of an expert per
     // workgroup (M_max <= 256), the whole K (K <= 8192)
     {mwsd_kernel<8>, 256, 128, kMwsd, 0, 256, MwsdShape<8>::WMAX},
-    // three-stage 256x128 rings (DMA two K-blocks ahead), plain and pre-shuffled weights
-    {ring2_kernel<256, 128, 2, 2, 3>, 256, 128, kRing, 3, 256, ring2_wd_max<256, 128, 2, 2, 3>()},
-    {ring2_kernel<256, 128, 2, 2, 3, false, false, true>, 256, 128, kRingShuf, 3, 256, ring2_wd_max<256, 128, 2, 2, 3>()},
+    // three-stage 256x128 rings (DMA two K-blocks ahead; streaming stores of C), plain and
+    // pre-shuffled weights
+    {ring2_kernel<256, 128, 2, 2, 3, false, false, false, true>, 256, 128, kRing, 3, 256, ring2_wd_max<256, 128, 2, 2, 3>()},
+    {ring2_kernel<256, 128, 2, 2, 3, false, false, true, true>, 256, 128, kRingShuf, 3, 256, ring2_wd_max<256, 128, 2, 2, 3>()},
     // contiguous grouped: the 128x256 ring with three stages
     {ring2_kernel<128, 256, 1, 4, 3, false, true>, 128, 256, kRing, 3, 256, ring2_wd_max<128, 256, 1, 4, 3>()},
+    // one round of 256x256 tiles: the same with streaming stores of C, plain and pre-shuffled weights
+    {ring2_kernel<256, 256, 2, 2, 2, false, false, false, true>, 256, 256, kRing, 2, 256, ring2_wd_max<256, 256, 2, 2, 2>()},
+    {ring2_kernel<256, 256, 2, 2, 2, false, false, true, true>, 256, 256, kRingShuf, 2, 256, ring2_wd_max<256, 256, 2, 2, 2>()},
 };
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 // table entries the automatic choice uses
@@ -2880,6 +2890,8 @@ constexpr int kCfgMwsd = 75;                 // masked weight streaming, all row
 constexpr int kCfgRing256x128S3 = 76;        // 2 x 2 wavefronts, plain weights
 constexpr int kCfgShufRing2_256x128S3 = 77;  // the same on pre-shuffled weights
 constexpr int kCfgRing2ContiguousS3 = 78;    // 128 x 256, 1 x 4 wavefronts, non-temporal weight DMA
+constexpr int kCfgRing256x256NTC = 79;       // 256 x 256 with streaming stores of C (one round of tiles)
+constexpr int kCfgShufRing2_256x256NTC = 80;  // the same on pre-shuffled weights
 static_assert(kCfgDecode64x128 < kNumTiles && kCfgFloatScaled128x256 < kNumTiles, "tile table");
 static_assert(kCfgRingFloat128x128 < kNumTiles && kCfgRing2Masked < kNumTiles && kCfgRing2Contiguous < kNumTiles,
               "tile table");
@@ -2891,7 +2903,8 @@ static_assert(kCfgWsd64x128 < kNumTiles, "tile table");
 static_assert(kCfgShufRing2_256x256 < kNumTiles && kCfgShufRing2_256x128 < kNumTiles &&
                   kCfgShufRing2_128x128 < kNumTiles && kCfgShufRing2Masked < kNumTiles && kCfgMwsd < kNumTiles,
               "tile table");
-static_assert(kCfgRing256x128S3 < kNumTiles && kCfgShufRing2_256x128S3 < kNumTiles && kCfgRing2ContiguousS3 < kNumTiles,
+static_assert(kCfgRing256x128S3 < kNumTiles && kCfgShufRing2_256x128S3 < kNumTiles && kCfgRing2ContiguousS3 < kNumTiles &&
+                  kCfgRing256x256NTC < kNumTiles && kCfgShufRing2_256x256NTC < kNumTiles,
               "tile table");
 
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -3015,6 +3028,8 @@ GemmConfig choose_gemm_config(const GemmProblem& p) {
       const int64_t tm256 = cdiv(p.M, 256), big_tiles = tm256 * cdiv(p.N, 256);
       const int64_t mid_tiles = tm256 * cdiv(p.N, 128);
       const bool one_round_128 = cdiv(p.M, 128) * cdiv(p.N, 128) <= 256;
+      // one round of 256 x 256 tiles: the entry with streaming stores of C
+      if (big_tiles == 256 && gemm_config_by_index(kCfgShufRing2_256x256NTC, p, 1, &cfg)) return cfg;
       if (big_tiles >= 256 && gemm_config_by_index(kCfgShufRing2_256x256, p, 1, &cfg)) {
         // a last round of at most half the compute units: its columns in a second
         // launch, as for the plain layout (a 32-row group of the layout is 32 K
@@ -3146,6 +3161,9 @@ GemmConfig choose_gemm_config(const GemmProblem& p) {
   // scale tables), 128x128 tiles (two workgroups per compute unit) below that;
   // the VALU-scaled tile kernel when no scale table fits
   const int64_t tm256 = cdiv(p.M, 256), tn256 = cdiv(p.N, 256), big_tiles = tm256 * tn256;
+  // one round of 256x256 tiles: the entry with streaming stores of C (4096x4096x7168 89.0 ->
+  // 88.1 us); several rounds keep ordinary stores (4096x16384x7168: 345 against 346 us)
+  if (big_tiles == 256 && gemm_config_by_index(kCfgRing256x256NTC, p, 1, &cfg)) return cfg;
   if (big_tiles >= 256 && gemm_config_by_index(kCfgRing256x256, p, 1, &cfg)) {
     // With 256x256 tiles, one per compute unit at a time, a last round of at most
     // half the compute units would leave the rest idle for a whole tile time: run
