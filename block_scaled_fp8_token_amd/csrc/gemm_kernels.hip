@@ -1551,7 +1551,8 @@ __global__ __launch_bounds__(256) void ring2_kernel(const KArgs p) {
       const int64_t m = m0 + wm * WM + row;
       if (m < m_limit && n < p.N) {
         // NTC: streaming stores (C is not read back here; with one tile per compute unit the
-        // whole of C is stored at the end of the call: 2048x4096x7168 52.6 -> 51.3 us)
+        // whole of C is stored at the end of the call: 2048x4096x7168 52.6 -> 51.3 us,
+        // 2048x2048x7168 on 128x128 tiles 34.1 -> 33.1 us)
         if constexpr (NTC) __builtin_nontemporal_store(v, reinterpret_cast<v4i*>(C + m * p.ldc + n));
         else *reinterpret_cast<v4i*>(C + m * p.ldc + n) = v;
       }
@@ -2466,7 +2467,7 @@ struct MwsdShape {
   static constexpr int ASZ = AG * KBB;
 };
 
-template <int RG>
+template <int RG, bool NTC = false>
 __global__ __launch_bounds__(256) void mwsd_kernel(const KArgs p) {
   using S_ = MwsdShape<RG>;
   constexpr int AG = S_::AG, D = S_::D, UN = S_::UN, WMAX = S_::WMAX, KBB = S_::KBB, ASZ = S_::ASZ;
@@ -2679,7 +2680,11 @@ __global__ __launch_bounds__(256) void mwsd_kernel(const KArgs p) {
           uint2 o;
           o.x = bf16_rne(v[0]) | (bf16_rne(v[1]) << 16);
           o.y = bf16_rne(v[2]) | (bf16_rne(v[3]) << 16);
-          *reinterpret_cast<uint2*>(C + m * p.ldc + n) = o;
+          // NTC: streaming stores, so that C does not stand in the weight stream's way through
+          // the caches (masked gate_up 195-198 -> 186.5-187 us)
+          if constexpr (NTC)
+            __builtin_nontemporal_store(((uint64_t)o.y << 32) | o.x, reinterpret_cast<uint64_t*>(C + m * p.ldc + n));
+          else *reinterpret_cast<uint2*>(C + m * p.ldc + n) = o;
         }
       }
     }
@@ -2821,29 +2826,31 @@ const TileEntry kTiles[] = {
     // full-row stages: one L2 request per 128-byte line
     {ring2_kernel<256, 256, 2, 2, 2>, 256, 256, kRing, 2, 256, ring2_wd_max<256, 256, 2, 2, 2>()},
     {ring2_kernel<256, 128, 2, 2, 2>, 256, 128, kRing, 2, 256, ring2_wd_max<256, 128, 2, 2, 2>()},
-    {ring2_kernel<128, 128, 1, 4, 4>, 128, 128, kRing, 4, 256, ring2_wd_max<128, 128, 1, 4, 4>()},
+    // (128x128: chosen for one round of tiles only, so C goes out with streaming stores)
+    {ring2_kernel<128, 128, 1, 4, 4, false, false, false, true>, 128, 128, kRing, 4, 256, ring2_wd_max<128, 128, 1, 4, 4>()},
     {ring2_kernel<128, 256, 2, 2, 2>, 128, 256, kRing, 2, 256, ring2_wd_max<128, 256, 2, 2, 2>()},
     {ring2_kernel<256, 256, 1, 4, 2>, 256, 256, kRing, 2, 256, ring2_wd_max<256, 256, 1, 4, 2>()},
     // float scales: the full-row 128x128 ring, unscaled MFMAs, block partials scaled on the VALU
     {ring2_kernel<128, 128, 1, 4, 4, true>, 128, 128, kRingFloat, 4, 256, ring2_wd_max<128, 128, 1, 4, 4, true>()},
     // masked: the full-row ring with the wavefronts side by side in N, weights streamed non-temporally
-    {ring2_kernel<256, 256, 1, 4, 2, false, true>, 256, 256, kRing, 2, 256, ring2_wd_max<256, 256, 1, 4, 2>()},
+    // (the grouped GEMMs, bound by their weight streams, also store C with streaming stores)
+    {ring2_kernel<256, 256, 1, 4, 2, false, true, false, true>, 256, 256, kRing, 2, 256, ring2_wd_max<256, 256, 1, 4, 2>()},
     // contiguous grouped: the same at 128-row tiles (one aligned run each)
-    {ring2_kernel<128, 256, 1, 4, 2, false, true>, 128, 256, kRing, 2, 256, ring2_wd_max<128, 256, 1, 4, 2>()},
+    {ring2_kernel<128, 256, 1, 4, 2, false, true, false, true>, 128, 256, kRing, 2, 256, ring2_wd_max<128, 256, 1, 4, 2>()},
     // the full-row ring on pre-shuffled weights (dense 256x256 / 256x128 / 128x128, masked)
     {ring2_kernel<256, 256, 2, 2, 2, false, false, true>, 256, 256, kRingShuf, 2, 256, ring2_wd_max<256, 256, 2, 2, 2>()},
     {ring2_kernel<256, 128, 2, 2, 2, false, false, true>, 256, 128, kRingShuf, 2, 256, ring2_wd_max<256, 128, 2, 2, 2>()},
-    {ring2_kernel<128, 128, 1, 4, 4, false, false, true>, 128, 128, kRingShuf, 4, 256, ring2_wd_max<128, 128, 1, 4, 4>()},
-    {ring2_kernel<256, 256, 1, 4, 2, false, true, true>, 256, 256, kRingShuf, 2, 256, ring2_wd_max<256, 256, 1, 4, 2>()},
+    {ring2_kernel<128, 128, 1, 4, 4, false, false, true, true>, 128, 128, kRingShuf, 4, 256, ring2_wd_max<128, 128, 1, 4, 4>()},
+    {ring2_kernel<256, 256, 1, 4, 2, false, true, true, true>, 256, 256, kRingShuf, 2, 256, ring2_wd_max<256, 256, 1, 4, 2>()},
     // masked, pre-shuffled weights: weight streaming, every valid row of an expert per
     // workgroup (M_max <= 256), the whole K (K <= 8192)
-    {mwsd_kernel<8>, 256, 128, kMwsd, 0, 256, MwsdShape<8>::WMAX},
+    {mwsd_kernel<8, true>, 256, 128, kMwsd, 0, 256, MwsdShape<8>::WMAX},
     // three-stage 256x128 rings (DMA two K-blocks ahead; streaming stores of C), plain and
     // pre-shuffled weights
     {ring2_kernel<256, 128, 2, 2, 3, false, false, false, true>, 256, 128, kRing, 3, 256, ring2_wd_max<256, 128, 2, 2, 3>()},
     {ring2_kernel<256, 128, 2, 2, 3, false, false, true, true>, 256, 128, kRingShuf, 3, 256, ring2_wd_max<256, 128, 2, 2, 3>()},
     // contiguous grouped: the 128x256 ring with three stages
-    {ring2_kernel<128, 256, 1, 4, 3, false, true>, 128, 256, kRing, 3, 256, ring2_wd_max<128, 256, 1, 4, 3>()},
+    {ring2_kernel<128, 256, 1, 4, 3, false, true, false, true>, 128, 256, kRing, 3, 256, ring2_wd_max<128, 256, 1, 4, 3>()},
     // one round of 256x256 tiles: the same with streaming stores of C, plain and pre-shuffled weights
     {ring2_kernel<256, 256, 2, 2, 2, false, false, false, true>, 256, 256, kRing, 2, 256, ring2_wd_max<256, 256, 2, 2, 2>()},
     {ring2_kernel<256, 256, 2, 2, 2, false, false, true, true>, 256, 256, kRingShuf, 2, 256, ring2_wd_max<256, 256, 2, 2, 2>()},
@@ -3128,7 +3135,8 @@ GemmConfig choose_gemm_config(const GemmProblem& p) {
     // over all four SIMDs (no operand reads or MFMAs for 32-row groups past the
     // count).  The full-row ring with non-temporal weight DMA first (the weights are
     // streamed once: MoE gate_up 213.4 -> 198.3 us, down 123.4 -> 117.3 us against
-    // the K-half ring; with ordinary DMA the two rings are within 1.5%), the K-half
+    // the K-half ring; with ordinary DMA the two rings are within 1.5%; streaming stores of
+    // C: 199 -> 193 us, 120 -> 115 us), the K-half
     // ring when K is past its tables, weight streaming over 64-row tiles past both
     if (gemm_config_by_index(kCfgRing2Masked, p, 1, &cfg)) return cfg;
     if (gemm_config_by_index(kCfgRing256x256Rows, p, 1, &cfg)) return cfg;
