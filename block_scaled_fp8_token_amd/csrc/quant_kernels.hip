@@ -70,7 +70,9 @@ __global__ __launch_bounds__(256) void quant_group_pack_kernel(
     unpack8(v, f);
     uint32_t eb;
     const uint2 o = quant8(f, valid, &eb);
-    if (valid) *reinterpret_cast<uint2*>(q + r * ldq + col) = o;
+    // streaming store: the codes are read by the next kernel, not through this CU's caches
+    // (2048x7168: 9.28 -> 8.32 us)
+    if (valid) __builtin_nontemporal_store(((uint64_t)o.y << 32) | o.x, reinterpret_cast<uint64_t*>(q + r * ldq + col));
     const uint32_t word = gather_word(eb);
     if (lane == 0) sf[w * ld_sf + r] = word;
   }
@@ -232,7 +234,8 @@ __global__ __launch_bounds__(256) void silu_mul_quant_compact_kernel(
     for (int k = 0; k < 8; ++k) g[k] = g[k] * __builtin_amdgcn_rcpf(1.0f + expf(-g[k])) * up[k];
     uint32_t eb;
     const uint2 o = quant8(g, valid, &eb);
-    if (valid) *reinterpret_cast<uint2*>(q + cur_row * H + col) = o;
+    // streaming store ([32, 256, 4096] with Zipf counts: 8.96 -> 8.64 us)
+    if (valid) __builtin_nontemporal_store(((uint64_t)o.y << 32) | o.x, reinterpret_cast<uint64_t*>(q + cur_row * H + col));
     const uint32_t word = gather_word(eb);
     if (lane == 0) sf[((int64_t)cur_e * W + cur_w) * M_max + cur_r] = word;
     return more;
@@ -468,7 +471,9 @@ __global__ __launch_bounds__(256) void quant_to_experts_kernel(
       const int32_t s = __builtin_amdgcn_readlane(my_slot, j);
       if (s < 0) continue;  // uniform per wavefront
       const int64_t e = __builtin_amdgcn_readlane(my_e, j);
-      if (valid) *reinterpret_cast<uint2*>(q + (e * M_max + s) * K + col) = o;
+      // streaming store (512 tokens x top-8 into the expert layout: 13.8 -> 12.3 us)
+      if (valid)
+        __builtin_nontemporal_store(((uint64_t)o.y << 32) | o.x, reinterpret_cast<uint64_t*>(q + (e * M_max + s) * K + col));
       if (lane == 0) sf[(e * W + w) * M_max + s] = word;
     }
   }
