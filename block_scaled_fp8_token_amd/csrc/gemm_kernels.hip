@@ -2831,7 +2831,7 @@ const TileEntry kTiles[] = {
     {ring2_kernel<128, 256, 2, 2, 2>, 128, 256, kRing, 2, 256, ring2_wd_max<128, 256, 2, 2, 2>()},
     {ring2_kernel<256, 256, 1, 4, 2>, 256, 256, kRing, 2, 256, ring2_wd_max<256, 256, 1, 4, 2>()},
     // float scales: the full-row 128x128 ring, unscaled MFMAs, block partials scaled on the VALU
-    // (C with streaming stores: 1024x4096x7168 45.0 -> 42.6 us, larger shapes 0.3-0.8% shorter)
+    // (C with streaming stores: 2048x4096 to 2048x18432 (K 7168) 0.3-0.8% shorter)
     {ring2_kernel<128, 128, 1, 4, 4, true, false, false, true>, 128, 128, kRingFloat, 4, 256, ring2_wd_max<128, 128, 1, 4, 4, true>()},
     // masked: the full-row ring with the wavefronts side by side in N, weights streamed non-temporally
     // (the grouped GEMMs, bound by their weight streams, also store C with streaming stores)
