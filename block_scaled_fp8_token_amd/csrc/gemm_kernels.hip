@@ -2826,8 +2826,10 @@ const TileEntry kTiles[] = {
     // full-row stages: one L2 request per 128-byte line
     {ring2_kernel<256, 256, 2, 2, 2>, 256, 256, kRing, 2, 256, ring2_wd_max<256, 256, 2, 2, 2>()},
     {ring2_kernel<256, 128, 2, 2, 2>, 256, 128, kRing, 2, 256, ring2_wd_max<256, 128, 2, 2, 2>()},
-    // (128x128: chosen for one round of tiles only, so C goes out with streaming stores)
-    {ring2_kernel<128, 128, 1, 4, 4, false, false, false, true>, 128, 128, kRing, 4, 256, ring2_wd_max<128, 128, 1, 4, 4>()},
+    // (128x128: chosen for one round of tiles only, so C goes out with streaming stores; 2 x 2
+    // wavefronts read 64 KB of operands from LDS per K-block against 80 KB for 1 x 4:
+    // 2048x2048x7168 33.2 -> 32.5 us, 1024x4096x7168 36.7 -> 36.3 us)
+    {ring2_kernel<128, 128, 2, 2, 4, false, false, false, true>, 128, 128, kRing, 4, 256, ring2_wd_max<128, 128, 2, 2, 4>()},
     {ring2_kernel<128, 256, 2, 2, 2>, 128, 256, kRing, 2, 256, ring2_wd_max<128, 256, 2, 2, 2>()},
     {ring2_kernel<256, 256, 1, 4, 2>, 256, 256, kRing, 2, 256, ring2_wd_max<256, 256, 1, 4, 2>()},
     // float scales: the full-row 128x128 ring, unscaled MFMAs, block partials scaled on the VALU
@@ -2841,7 +2843,7 @@ const TileEntry kTiles[] = {
     // the full-row ring on pre-shuffled weights (dense 256x256 / 256x128 / 128x128, masked)
     {ring2_kernel<256, 256, 2, 2, 2, false, false, true>, 256, 256, kRingShuf, 2, 256, ring2_wd_max<256, 256, 2, 2, 2>()},
     {ring2_kernel<256, 128, 2, 2, 2, false, false, true>, 256, 128, kRingShuf, 2, 256, ring2_wd_max<256, 128, 2, 2, 2>()},
-    {ring2_kernel<128, 128, 1, 4, 4, false, false, true, true>, 128, 128, kRingShuf, 4, 256, ring2_wd_max<128, 128, 1, 4, 4>()},
+    {ring2_kernel<128, 128, 2, 2, 4, false, false, true, true>, 128, 128, kRingShuf, 4, 256, ring2_wd_max<128, 128, 2, 2, 4>()},
     {ring2_kernel<256, 256, 1, 4, 2, false, true, true, true>, 256, 256, kRingShuf, 2, 256, ring2_wd_max<256, 256, 1, 4, 2>()},
     // masked, pre-shuffled weights: weight streaming, every valid row of an expert per
     // workgroup (M_max <= 256), the whole K (K <= 8192)
@@ -2887,11 +2889,11 @@ constexpr int kCfgShufRing256x256Rows = 38;  // pre-shuffled weights: ring 256x2
 constexpr int kCfgShufRing256x256 = 39;      // 2 x 2 wavefronts
 constexpr int kCfgShufRing128x256 = 40;
 constexpr int kCfgFloatShufDecode64x128 = 47;  // float scales, pre-shuffled weights, reduction kernel
-constexpr int kCfgRing128x128 = 65;          // ring 128x128, 1 x 4 wavefronts, four full K-block stages
+constexpr int kCfgRing128x128 = 65;          // ring 128x128, 2 x 2 wavefronts, four full K-block stages
 constexpr int kCfgShufRing128x128 = 50;      // the same (2 x 2) on pre-shuffled weights
 constexpr int kCfgShufRing2_256x256 = 71;    // full-row ring on pre-shuffled weights, 2 x 2 wavefronts
 constexpr int kCfgShufRing2_256x128 = 72;
-constexpr int kCfgShufRing2_128x128 = 73;    // 1 x 4 wavefronts, four stages
+constexpr int kCfgShufRing2_128x128 = 73;    // 2 x 2 wavefronts, four stages
 constexpr int kCfgShufRing2Masked = 74;      // 1 x 4 wavefronts, non-temporal weight DMA
 constexpr int kCfgMwsd = 75;                 // masked weight streaming, all rows of an expert per workgroup
 // three-stage rings (DMA two K-blocks ahead; their scale tables hold K <= 7680 / 15872)
